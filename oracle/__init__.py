@@ -1,0 +1,220 @@
+"""CPU oracle for fine-grained FP8 quantization and the block-scaled FP8 GEMM.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may use it; the GPU library never does, and the
+two share no code.
+
+Quantization runs in the scalar C file ``fp8_oracle.c`` (binary32 IEEE, see
+its header for the readings). The GEMM is its plain definition: dequantize both
+FP8 operands exactly in float64 (E4M3 value times its FP32 scale) and multiply
+them with numpy's float64 matmul:
+
+    C[m][n] = sum_k (dec(qA[m,k]) * sA(m,k)) * (dec(qB[n,k]) * sB(n,k))
+
+which is what the FP8 GEMM of the pages computes up to rounding order: FP8
+operands in, per-group scales applied during accumulation, BF16 or FP32 out
+(page "Deepseek Ai News Expert Interview", passages on promotion to FP32
+registers and on BF16/FP32 GEMM outputs; page "Is aI Hitting a Wall?",
+passage on the dequantization overhead).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load (building if needed) the C oracle."""
+    global _LIB
+    if _LIB is None:
+        path = _build.build(force=False)
+        L = ctypes.CDLL(path)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        i64 = ctypes.c_int64
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode_bits.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode_bits.restype = ctypes.c_uint8
+        L.oracle_e4m3_encode_search.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode_search.restype = ctypes.c_uint8
+        for name in ("oracle_quant_act_1x128", "oracle_quant_act_128x1",
+                     "oracle_quant_weight_128x128"):
+            getattr(L, name).argtypes = [u16p, i64, i64, i64, u8p, i64, f32p, i64]
+            getattr(L, name).restype = None
+        L.oracle_encoders_disagree.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                               ctypes.POINTER(ctypes.c_uint32)]
+        L.oracle_encoders_disagree.restype = ctypes.c_int64
+        L.oracle_quant_pairs.argtypes = [u16p, u16p, i64, u8p]
+        L.oracle_quant_pairs.restype = None
+        _LIB = L
+    return _LIB
+
+
+def _p(a: np.ndarray, ctype):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+# ------------------------------------------------------------------ formats
+
+def e4m3_decode_table() -> np.ndarray:
+    """float64[256]: the value of every E4M3 code (NaN for 0x7F and 0xFF)."""
+    L = lib()
+    return np.array([L.oracle_e4m3_decode(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_encode(v: float, method: str = "bits") -> int:
+    L = lib()
+    f = L.oracle_e4m3_encode_bits if method == "bits" else L.oracle_e4m3_encode_search
+    return int(f(ctypes.c_float(v)))
+
+
+def encoders_disagree(lo_bits: int, hi_bits: int, stride: int = 1) -> tuple[int, int]:
+    """Count fp32 patterns lo, lo+stride, ... <= hi (both signs) where the two encoders differ."""
+    first = ctypes.c_uint32(0)
+    n = lib().oracle_encoders_disagree(lo_bits, hi_bits, stride, ctypes.byref(first))
+    return int(n), int(first.value)
+
+
+# --------------------------------------------------------------- quantizers
+
+def quant_act_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits X[rows][cols] -> (Q uint8[rows][cols], S float32[cols/128][rows])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rows, cols = x.shape
+    assert cols % 128 == 0
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((cols // 128, rows), dtype=np.float32)
+    lib().oracle_quant_act_1x128(_p(x, ctypes.c_uint16), rows, cols, cols,
+                                 _p(q, ctypes.c_uint8), cols, _p(s, ctypes.c_float), rows)
+    return q, s
+
+
+def quant_act_128x1(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits X[tokens][cols] -> (QT uint8[cols][tokens], S float32[tokens/128][cols])."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rows, cols = x.shape
+    assert rows % 128 == 0
+    qt = np.empty((cols, rows), dtype=np.uint8)
+    s = np.empty((rows // 128, cols), dtype=np.float32)
+    lib().oracle_quant_act_128x1(_p(x, ctypes.c_uint16), rows, cols, cols,
+                                 _p(qt, ctypes.c_uint8), rows, _p(s, ctypes.c_float), cols)
+    return qt, s
+
+
+def quant_weight_128x128(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """bf16 bits W[n][k] -> (Q uint8[n][k], S float32[n/128][k/128])."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    n, k = w.shape
+    assert n % 128 == 0 and k % 128 == 0
+    q = np.empty((n, k), dtype=np.uint8)
+    s = np.empty((n // 128, k // 128), dtype=np.float32)
+    lib().oracle_quant_weight_128x128(_p(w, ctypes.c_uint16), n, k, k,
+                                      _p(q, ctypes.c_uint8), k, _p(s, ctypes.c_float), k // 128)
+    return q, s
+
+
+def quant_pairs(x: np.ndarray, amax: np.ndarray) -> np.ndarray:
+    """E4M3(fl32(x / fl32(|amax| / 448))) element-wise on bf16 bit arrays."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    amax = np.ascontiguousarray(amax, dtype=np.uint16)
+    assert x.shape == amax.shape
+    q = np.empty(x.shape, dtype=np.uint8)
+    lib().oracle_quant_pairs(_p(x, ctypes.c_uint16), _p(amax, ctypes.c_uint16), x.size,
+                             _p(q, ctypes.c_uint8))
+    return q
+
+
+# ---------------------------------------------------------- dequantization
+
+_DEC = None
+
+
+def _dec() -> np.ndarray:
+    global _DEC
+    if _DEC is None:
+        _DEC = e4m3_decode_table()
+    return _DEC
+
+
+def dequant_rows_1x128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """float64 operand from K-contiguous codes q[r][k] with slab-major scales s[k/128][r]."""
+    rows, k = q.shape
+    assert s.shape[0] == k // 128 and s.shape[1] >= rows
+    scale = np.repeat(s[:, :rows].astype(np.float64).T, 128, axis=1)
+    return _dec()[q] * scale
+
+
+def dequant_block_128x128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """float64 operand from codes q[n][k] with block scales s[n/128][k/128]."""
+    n, k = q.shape
+    scale = np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1)[:n, :k]
+    return _dec()[q] * scale
+
+
+# -------------------------------------------------------------------- GEMM
+
+def gemm(a_q: np.ndarray, a_s: np.ndarray, b_q: np.ndarray, b_s: np.ndarray,
+         b_scale_kind: str = "block") -> np.ndarray:
+    """float64 C[m][n] = deq(A)[m][:] . deq(B)[n][:], unrounded.
+
+    A: codes [m][k] (K contiguous) with slab-major 1x128 scales [k/128][m].
+    B: codes [n][k] (K contiguous) with scales either 128x128 blocks
+    [n/128][k/128] (``"block"``) or one per (slab, row) [k/128][n] (``"row"``,
+    the Wgrad case where both operands were quantized in 128x1 token tiles).
+    """
+    A = dequant_rows_1x128(a_q, a_s)
+    if b_scale_kind == "block":
+        B = dequant_block_128x128(b_q, b_s)
+    elif b_scale_kind == "row":
+        B = dequant_rows_1x128(b_q, b_s)
+    else:
+        raise ValueError(b_scale_kind)
+    return A @ B.T
+
+
+def gemm_rows(row_idx: np.ndarray, a_q: np.ndarray, a_s: np.ndarray, b_q: np.ndarray,
+              b_s: np.ndarray, b_scale_kind: str = "block") -> np.ndarray:
+    """Selected rows of :func:`gemm` (float64 [len(row_idx)][n])."""
+    row_idx = np.asarray(row_idx)
+    return gemm(np.ascontiguousarray(a_q[row_idx]), np.ascontiguousarray(a_s[:, row_idx]),
+                b_q, b_s, b_scale_kind)
+
+
+def grouped_gemm(offsets: np.ndarray, rows: np.ndarray, a_q: np.ndarray, a_s: np.ndarray,
+                 b_q: np.ndarray, b_s: np.ndarray) -> np.ndarray:
+    """Per expert e: C[off_e : off_e + rows_e] = GEMM(A segment, W_e); padding rows are 0.
+
+    a_q [m_total][k], a_s [k/128][m_total], b_q [E][n][k], b_s [E][n/128][k/128].
+    """
+    m_total = a_q.shape[0]
+    n = b_q.shape[1]
+    out = np.zeros((m_total, n), dtype=np.float64)
+    for e in range(len(rows)):
+        r0, r = int(offsets[e]), int(rows[e])
+        if r == 0:
+            continue
+        out[r0:r0 + r] = gemm(np.ascontiguousarray(a_q[r0:r0 + r]),
+                              np.ascontiguousarray(a_s[:, r0:r0 + r]), b_q[e], b_s[e], "block")
+    return out
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (via float32, nearest-even each step) as float64.
+
+    Diagnostic only: the pass criteria compare against the unrounded result.
+    """
+    f = a.astype(np.float32)
+    u = f.view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)
+    return r.view(np.float32).astype(np.float64)

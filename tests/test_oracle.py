@@ -1,0 +1,438 @@
+"""Pins for the CPU oracle (no GPU): format definition, brute force, invariants,
+closed forms and exact special cases. Each test names what it pins.
+
+The oracle is test infrastructure; these tests are what let the GPU parity
+tests trust it.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import brute
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield line.split()
+
+
+def _bf16(values) -> np.ndarray:
+    return wl.f32_to_bf16_bits(np.asarray(values, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- E4M3 codec
+
+def test_decode_matches_hand_table():
+    """Pin: hand-worked code values from the E4M3 definition (golden file)."""
+    table = oracle.e4m3_decode_table()
+    for code_hex, val in _golden_lines("e4m3_decode_hand.txt"):
+        code = int(code_hex, 16)
+        if val == "nan":
+            assert math.isnan(table[code])
+        elif val == "-0":
+            assert table[code] == 0.0 and math.copysign(1.0, table[code]) < 0
+        else:
+            assert table[code] == float(Fraction(val)), (code_hex, table[code], val)
+
+
+def test_decode_matches_torch_float8_e4m3fn():
+    """Pin: all 256 codes agree with torch's float8_e4m3fn (a library routine, OCP E4M3FN)."""
+    table = oracle.e4m3_decode_table()
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    both_nan = np.isnan(table) & np.isnan(ref)
+    assert np.array_equal(np.isnan(table), np.isnan(ref))
+    assert np.array_equal(table[~both_nan], ref[~both_nan])
+    assert np.array_equal(np.signbit(table[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+def test_decode_matches_brute_definition():
+    """Pin: the oracle's decoder equals the independent Fraction definition on every finite code."""
+    table = oracle.e4m3_decode_table()
+    for code in range(256):
+        if code & 0x7F == 0x7F:
+            continue
+        assert table[code] == float(brute.e4m3_value(code))
+
+
+def test_round_trip_all_finite_codes():
+    """Pin: encode(decode(c)) == c for all 254 finite codes (incl. 0x80), both encoders."""
+    table = oracle.e4m3_decode_table()
+    for code in range(256):
+        if code & 0x7F == 0x7F:
+            continue
+        v = float(table[code])
+        if code == 0x80:
+            v = -0.0
+        assert oracle.e4m3_encode(v, "bits") == code
+        assert oracle.e4m3_encode(v, "search") == code
+
+
+def test_encode_hand_ties():
+    """Pin: hand-worked ties, carries, saturation and signed zeros (golden file)."""
+    for row in _golden_lines("e4m3_encode_hand.txt"):
+        v, code = float.fromhex(row[0]), int(row[1], 16)
+        assert oracle.e4m3_encode(v, "bits") == code, row
+        assert oracle.e4m3_encode(v, "search") == code, row
+
+
+def test_encoders_agree_exhaustive_band():
+    """Pin: the bit-arithmetic and table-search encoders agree on every binary32
+    pattern with 2^-12 <= |v| <= 2^10 (everything that can round to a nonzero
+    code below saturation), and on a strided sample of the rest."""
+    lo, hi = 0x39800000, 0x44800000          # 2^-12 .. 2^10
+    bad, first = oracle.encoders_disagree(lo, hi, 1)
+    assert bad == 0, hex(first)
+    bad, first = oracle.encoders_disagree(0, lo, 997)       # zero, subnormals, tiny
+    assert bad == 0, hex(first)
+    bad, first = oracle.encoders_disagree(hi, 0x7F7FFFFF, 991)  # up to FLT_MAX
+    assert bad == 0, hex(first)
+
+
+def test_encode_matches_torch_cast_below_saturation():
+    """Pin: agreement with torch's float32 -> float8_e4m3fn cast (a library
+    routine) for |v| < 464, where torch is defined; ties and random values."""
+    rng = np.random.default_rng(1)
+    vals = [rng.standard_normal(20000).astype(np.float32) * np.float32(s)
+            for s in (1e-3, 1e-2, 0.1, 1, 10, 100)]
+    table = oracle.e4m3_decode_table()
+    finite = table[:0x7F]
+    mids = ((finite[:-1] + finite[1:]) / 2).astype(np.float32)  # every midpoint (exact in fp32)
+    vals.append(mids)
+    vals.append(-mids)
+    v = np.concatenate(vals)
+    v = v[np.abs(v) < 464]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = np.array([oracle.e4m3_encode(float(x), "bits") for x in v], dtype=np.uint8)
+    assert np.array_equal(ours, ref)
+
+
+# -------------------------------------------------------------- quantizers
+
+def test_hand_worked_tile():
+    """Pin: a 1x128 tile worked by hand (golden file): s = 2^-3, q = E4M3(8x)."""
+    x = np.zeros((1, 128), dtype=np.uint16)
+    expect = np.zeros(128, dtype=np.uint8)
+    scale = None
+    with open(os.path.join(GOLDEN, "quant_tile_hand.txt")) as f:
+        for line in f:
+            if line.startswith("# scale"):
+                scale = float(line.split()[2])
+    for idx, b, code, *_ in _golden_lines("quant_tile_hand.txt"):
+        x[0, int(idx)] = int(b, 16)
+        expect[int(idx)] = int(code, 16)
+    q, s = oracle.quant_act_1x128(x)
+    assert s[0, 0] == np.float32(scale)
+    assert np.array_equal(q[0], expect)
+
+
+def _edge_tiles(rng) -> np.ndarray:
+    """A few 128-wide rows of bf16 bits hitting the special cases."""
+    rows = []
+    rows.append(_bf16(rng.standard_normal(128)))                          # plain
+    z = np.zeros(128, dtype=np.uint16); z[::3] = 0x8000; rows.append(z)  # all +-0
+    r = _bf16(rng.standard_normal(128) * 1e-3); r[17] = _bf16([1000.0])[0]; rows.append(r)  # outlier
+    sub = rng.integers(1, 0x80, 128).astype(np.uint16)                    # bf16 subnormals
+    sub[::2] |= 0x8000; rows.append(sub)
+    big = _bf16(rng.standard_normal(128)); big[5] = 0x7F7F; rows.append(big)  # amax = bf16 max
+    tiny = _bf16(rng.standard_normal(128) * 1e-38); rows.append(tiny)       # subnormal fp32 scale
+    one = np.zeros(128, dtype=np.uint16); one[77] = _bf16([-3.0])[0]; rows.append(one)  # single value
+    ties = _bf16(np.full(128, 448.0 * 17 / 64)); ties[0] = _bf16([448.0])[0]; rows.append(ties)
+    return np.stack(rows)
+
+
+def test_quantizer_matches_exact_rational_brute_force():
+    """Pin: 1x128 quantization equals the exact-rational brute force (hand
+    binary32 rounding + linear nearest-code scan) on random and edge tiles."""
+    rng = np.random.default_rng(2)
+    x = _edge_tiles(rng)
+    extra = wl.activation(0, "tiny_fprop", 7, 4, 128, 100.0)
+    x = np.concatenate([x, extra])
+    q, s = oracle.quant_act_1x128(x)
+    for r in range(x.shape[0]):
+        s_ref, codes = brute.quantize_group([int(b) for b in x[r]])
+        assert Fraction(float(s[0, r])) == s_ref, r
+        assert list(q[r]) == codes, r
+
+
+def test_max_code_is_448_in_every_normal_tile():
+    """Invariant: every tile with a normal scale has max |q| decoding to 448
+    (the amax element maps to ~448); all-zero tiles have s = 0."""
+    d = wl.dense_fprop(0, m=64, n=128, k=1024)
+    q, s = oracle.quant_act_1x128(d["x"])
+    table = oracle.e4m3_decode_table()
+    mag = np.abs(table[q]).reshape(64, -1, 128).max(axis=2)  # [rows][slabs]
+    assert np.all(mag == 448.0)
+    assert np.all(s > np.float32(2.0 ** -126))
+
+
+def test_power_of_two_scaling_invariance():
+    """Invariant: quant(2^p X) gives the same codes and scales times 2^p."""
+    x = wl.activation(0, "tiny_fprop", 3, 16, 256, 100.0)
+    q0, s0 = oracle.quant_act_1x128(x)
+    xf = wl.bf16_bits_to_f32(x)
+    for p in (-20, -3, 5, 30):
+        xp = wl.f32_to_bf16_bits(xf * np.float32(2.0 ** p))  # exact scaling
+        q1, s1 = oracle.quant_act_1x128(xp)
+        assert np.array_equal(q0, q1)
+        assert np.array_equal(s1, s0 * np.float32(2.0 ** p))
+
+
+def test_negation_flips_sign_bits_only():
+    """Invariant: quant(-X) = quant(X) with the sign bit flipped, same scales."""
+    x = wl.activation(0, "tiny_fprop", 4, 16, 256, 100.0)
+    q0, s0 = oracle.quant_act_1x128(x)
+    q1, s1 = oracle.quant_act_1x128(x ^ np.uint16(0x8000))
+    assert np.array_equal(q1, q0 ^ np.uint8(0x80))
+    assert np.array_equal(s0, s1)
+
+
+def test_row_permutation_commutes():
+    """Invariant: 1x128 quantization commutes with a row permutation (quantize
+    before dispatch: page "Eliminate Deepseek Ai News For Good", passage on
+    quantizing activations before the MoE up-projection dispatch)."""
+    x = wl.activation(0, "tiny_fprop", 5, 64, 384, 100.0)
+    perm = np.random.default_rng(3).permutation(64)
+    q0, s0 = oracle.quant_act_1x128(x)
+    q1, s1 = oracle.quant_act_1x128(x[perm])
+    assert np.array_equal(q1, q0[perm])
+    assert np.array_equal(s1, s0[:, perm])
+
+
+def test_weight_blocks_commute_with_transpose():
+    """Invariant: 128x128 block quantization of W^T is the transpose of that of W."""
+    w = wl.weight(0, "tiny_fprop", 6, 256, 384)
+    q0, s0 = oracle.quant_weight_128x128(w)
+    q1, s1 = oracle.quant_weight_128x128(np.ascontiguousarray(w.T))
+    assert np.array_equal(q1, q0.T)
+    assert np.array_equal(s1, s0.T)
+
+
+def test_weight_block_matches_brute_force():
+    """Pin: one 128x128 block equals the brute-force group quantization of its 16384 values."""
+    w = wl.weight(0, "tiny_fprop", 8, 128, 128)
+    w[3, 4] = _bf16([-0.5])[0]
+    q, s = oracle.quant_weight_128x128(w)
+    s_ref, codes = brute.quantize_group([int(b) for b in w.reshape(-1)])
+    assert Fraction(float(s[0, 0])) == s_ref
+    assert list(q.reshape(-1)) == codes
+
+
+def test_128x1_is_1x128_of_transpose():
+    """Invariant: 128x1 token tiles on X equal 1x128 tiles on X^T (output is X^T-shaped)."""
+    x = wl.activation(0, "wgrad", 9, 256, 200, 50.0)
+    qt, s = oracle.quant_act_128x1(x)
+    q_ref, s_ref = oracle.quant_act_1x128(np.ascontiguousarray(x.T))
+    assert np.array_equal(qt, q_ref)
+    assert np.array_equal(s, s_ref)
+
+
+def test_scale_closed_form_power_of_two_amax():
+    """Closed form: amax = 448 * 2^p gives s = 2^p exactly and q = E4M3(x * 2^-p)."""
+    rng = np.random.default_rng(4)
+    for p in (-10, 0, 3):
+        v = rng.standard_normal(128).astype(np.float32)
+        v[0] = 448.0
+        v = np.clip(v, -448, 448) * np.float32(2.0 ** p)
+        x = _bf16(v)[None, :]
+        q, s = oracle.quant_act_1x128(x)
+        assert s[0, 0] == np.float32(2.0 ** p)
+        expect = [oracle.e4m3_encode(float(f) * 2.0 ** -p) for f in wl.bf16_bits_to_f32(x[0])]
+        assert list(q[0]) == expect
+
+
+def test_quant_pairs_matches_tile_quantizer():
+    """The (x, amax) pair form equals the tile quantizer when amax is the tile's amax."""
+    x = wl.activation(0, "tiny_fprop", 10, 8, 128, 100.0)
+    q, _ = oracle.quant_act_1x128(x)
+    amax_bits = (x & np.uint16(0x7FFF)).max(axis=1, keepdims=True)
+    qp = oracle.quant_pairs(x, np.broadcast_to(amax_bits, x.shape).copy())
+    assert np.array_equal(q, qp)
+
+
+# -------------------------------------------------------------------- GEMM
+
+def _expand_block(s, rows, k):
+    return np.repeat(np.repeat(s, 128, 0), 128, 1)[:rows, :k]
+
+
+def test_gemm_matches_exact_rational_brute_force():
+    """Pin: tiny GEMM (M,N <= 6, K = 384) equals the exact rational sum."""
+    x = wl.activation(0, "tiny_fprop", 11, 5, 384, 100.0)
+    w = wl.weight(0, "tiny_fprop", 12, 128, 384)
+    qa, sa = oracle.quant_act_1x128(x)
+    qb, sb = oracle.quant_weight_128x128(w)
+    c = oracle.gemm(qa, sa, qb, sb, "block")
+    a_sc = np.repeat(sa.T, 128, axis=1)
+    b_sc = _expand_block(sb, 128, 384)
+    exact = brute.gemm_exact(qa.tolist(), a_sc.tolist(), qb[:6].tolist(), b_sc[:6].tolist())
+    for m in range(5):
+        for n in range(6):
+            e = exact[m][n]
+            assert abs(Fraction(c[m, n]) - e) <= abs(e) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 200)
+
+
+def test_gemm_row_kind_matches_brute_force():
+    """Pin: the Wgrad form (per-row scales on both operands) against the exact sum."""
+    dy = wl.activation(0, "wgrad", 13, 256, 4, None)
+    x = wl.activation(0, "wgrad", 14, 256, 5, 50.0)
+    qa, sa = oracle.quant_act_128x1(dy)   # [4][256], [2][4]
+    qb, sb = oracle.quant_act_128x1(x)    # [5][256], [2][5]
+    c = oracle.gemm(qa, sa, qb, sb, "row")
+    a_sc = np.repeat(sa.T, 128, axis=1)
+    b_sc = np.repeat(sb.T, 128, axis=1)
+    exact = brute.gemm_exact(qa.tolist(), a_sc.tolist(), qb.tolist(), b_sc.tolist())
+    for m in range(4):
+        for n in range(5):
+            e = exact[m][n]
+            assert abs(Fraction(c[m, n]) - e) <= abs(e) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 200)
+
+
+def test_gemm_k128_is_scaled_integer_gemm():
+    """Special case: with K = 128 the result is sA[m] * sB * (textbook GEMM of the
+    decoded values), and the decoded values times 2^9 are integers."""
+    x = wl.activation(0, "tiny_fprop", 15, 32, 128, 100.0)
+    w = wl.weight(0, "tiny_fprop", 16, 128, 128)
+    qa, sa = oracle.quant_act_1x128(x)
+    qb, sb = oracle.quant_weight_128x128(w)
+    table = oracle.e4m3_decode_table()
+    ia = (table[qa] * 512).astype(np.int64)
+    ib = (table[qb] * 512).astype(np.int64)
+    assert np.array_equal(ia / 512.0, table[qa])
+    scale = sa[0].astype(np.float64)[:, None] * float(sb[0, 0]) / 2.0 ** 18
+    ref = (ia @ ib.T).astype(np.float64) * scale          # one rounding
+    mag = (np.abs(ia) @ np.abs(ib).T).astype(np.float64) * scale
+    c = oracle.gemm(qa, sa, qb, sb, "block")
+    # float64 dot-product error bound: K * 2^-53 * sum |terms| (+ ref's own rounding)
+    bound = 128 * 2.0 ** -53 * mag + 2.0 ** -52 * np.abs(ref)
+    assert np.all(np.abs(c - ref) <= bound)
+
+
+def test_gemm_exact_power_of_two_case():
+    """Exact case: integer-valued codes (|q| <= 16) and power-of-two scales make
+    every partial sum an integer times a power of two, so the float64 result
+    must equal the integer GEMM bit for bit."""
+    rng = np.random.default_rng(5)
+    M, N, K = 24, 256, 512
+    ints = [0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16]
+    int_codes = {int(v): oracle.e4m3_encode(float(v)) for v in ints}
+    va = rng.integers(-16, 17, (M, K))
+    vb = rng.integers(-16, 17, (N, K))
+    enc = lambda v: np.vectorize(lambda t: int_codes[abs(int(t))] | (0x80 if t < 0 else 0))(v).astype(np.uint8)
+    qa, qb = enc(va), enc(vb)
+    sa = (2.0 ** rng.integers(-4, 5, (K // 128, M))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-4, 5, (N // 128, K // 128))).astype(np.float32)
+    c = oracle.gemm(qa, sa, qb, sb, "block")
+    ref = np.zeros((M, N))
+    for j in range(K // 128):
+        part = va[:, 128 * j:128 * j + 128] @ vb[:, 128 * j:128 * j + 128].T
+        ref += part * (sa[j].astype(np.float64)[:, None] * np.repeat(sb[:, j], 128)[None, :N])
+    assert np.array_equal(c, ref)
+
+
+def test_gemm_linearity_and_zero():
+    """Invariants: zero operand -> zero output; doubling A's scales doubles C; negating B's codes negates C."""
+    x = wl.activation(0, "tiny_fprop", 17, 16, 256, 100.0)
+    w = wl.weight(0, "tiny_fprop", 18, 128, 256)
+    qa, sa = oracle.quant_act_1x128(x)
+    qb, sb = oracle.quant_weight_128x128(w)
+    c = oracle.gemm(qa, sa, qb, sb)
+    assert np.array_equal(oracle.gemm(np.zeros_like(qa), sa, qb, sb), np.zeros_like(c))
+    assert np.array_equal(oracle.gemm(qa, sa * np.float32(2), qb, sb), 2 * c)
+    assert np.array_equal(oracle.gemm(qa, sa, qb ^ np.uint8(0x80), sb), -c)
+
+
+def test_grouped_is_per_expert_gemm_with_zero_padding():
+    """Invariant: grouped GEMM equals per-expert GEMM on each segment; padding rows are 0."""
+    rows = np.array([0, 1, 127, 128, 129, 5])
+    g = wl.grouped_fprop(0, n=256, k=256, experts=len(rows), rows=rows)
+    qa, sa = oracle.quant_act_1x128(g["x"])
+    qb = np.empty(g["w"].shape, dtype=np.uint8)
+    sb = np.empty((len(rows), 2, 2), dtype=np.float32)
+    for e in range(len(rows)):
+        qb[e], sb[e] = oracle.quant_weight_128x128(g["w"][e])
+    c = oracle.grouped_gemm(g["offsets"], rows, qa, sa, qb, sb)
+    off = g["offsets"]
+    for e in range(len(rows)):
+        r0, r = off[e], rows[e]
+        if r:
+            ref = oracle.gemm(qa[r0:r0 + r], np.ascontiguousarray(sa[:, r0:r0 + r]), qb[e], sb[e])
+            assert np.array_equal(c[r0:r0 + r], ref)
+        assert np.all(c[r0 + r:off[e + 1]] == 0)
+
+
+def test_bf16_round_diagnostic():
+    """The bf16 rounding helper (diagnostic only) matches torch's float32 -> bf16 cast."""
+    v = np.random.default_rng(6).standard_normal(10000) * 10
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(oracle.bf16_round(v), ref)
+
+
+# ------------------------------------------------- tile placement (closed form)
+
+def _planted(rng, shape, tile_r, tile_c):
+    """Values in [-1, 1] with each (tile_r x tile_c) tile's amax planted at 448 * 2^p,
+    p distinct per tile; returns (bf16 bits, p per tile)."""
+    R, C = shape
+    tr, tc = R // tile_r, C // tile_c
+    p = rng.permutation(tr * tc).reshape(tr, tc) - 20
+    v = rng.uniform(-1, 1, shape).astype(np.float32) * np.float32(448.0 * 0.99)
+    for i in range(tr):
+        for j in range(tc):
+            blk = v[i * tile_r:(i + 1) * tile_r, j * tile_c:(j + 1) * tile_c]
+            blk[rng.integers(tile_r), rng.integers(tile_c)] = 448.0
+            blk *= np.float32(2.0 ** p[i, j])
+    return wl.f32_to_bf16_bits(v), p
+
+
+def test_1x128_scale_placement_closed_form():
+    """Closed form: tile (row r, slab j) with amax 448 * 2^p has s[j][r] = 2^p and
+    codes E4M3(x * 2^-p) -- pins the slab-major scale layout and tile indexing."""
+    rng = np.random.default_rng(7)
+    x, p = _planted(rng, (6, 512), 1, 128)
+    q, s = oracle.quant_act_1x128(x)
+    assert np.array_equal(s, (2.0 ** p.T).astype(np.float32))
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    for r in range(6):
+        for j in range(4):
+            expect = [oracle.e4m3_encode(float(v) * 2.0 ** -p[r, j]) for v in xf[r, 128 * j:128 * j + 128]]
+            assert list(q[r, 128 * j:128 * j + 128]) == expect
+
+
+def test_128x1_scale_placement_closed_form():
+    """Closed form for 128x1 token tiles: s[j][c] = 2^p(j, c); output is token-contiguous."""
+    rng = np.random.default_rng(8)
+    x, p = _planted(rng, (384, 5), 128, 1)
+    qt, s = oracle.quant_act_128x1(x)
+    assert np.array_equal(s, (2.0 ** p).astype(np.float32))
+    xf = wl.bf16_bits_to_f32(x).astype(np.float64)
+    for c in range(5):
+        for j in range(3):
+            expect = [oracle.e4m3_encode(float(v) * 2.0 ** -p[j, c]) for v in xf[128 * j:128 * j + 128, c]]
+            assert list(qt[c, 128 * j:128 * j + 128]) == expect
+
+
+def test_128x128_scale_placement_closed_form():
+    """Closed form for 128x128 blocks: s[bn][bk] = 2^p(bn, bk)."""
+    rng = np.random.default_rng(9)
+    w, p = _planted(rng, (256, 384), 128, 128)
+    q, s = oracle.quant_weight_128x128(w)
+    assert np.array_equal(s, (2.0 ** p).astype(np.float32))
+    xf = wl.bf16_bits_to_f32(w).astype(np.float64)
+    for bn in range(2):
+        for bk in range(3):
+            blk = xf[128 * bn:128 * bn + 128, 128 * bk:128 * bk + 128].reshape(-1)[::37]
+            got = q[128 * bn:128 * bn + 128, 128 * bk:128 * bk + 128].reshape(-1)[::37]
+            assert list(got) == [oracle.e4m3_encode(float(v) * 2.0 ** -p[bn, bk]) for v in blk]
