@@ -1,0 +1,282 @@
+"""fine_grained_fp8_quantize_amd -- fine-grained FP8 quantization and block-scaled
+FP8 GEMM for AMD Instinct MI355X (gfx950).
+
+A thin binding over the C ABI of ``libfp8q.so`` (declared in
+``include/fp8q.h``). The functions carry the same names as the C entry
+points; they only marshal torch tensors into pointers, sizes and the current
+HIP stream, and allocate outputs with torch when the caller does not pass
+them. Every step of the computation runs in the library's gfx950 kernels;
+there is no fallback: if the library is not built, or a tensor is not on the
+GPU, the call raises.
+
+Layouts (row-major, K contiguous for GEMM operands):
+
+* ``fp8_quantize_act(x)`` -- bf16 ``x[rows][cols]`` -> E4M3 codes
+  ``q[rows][cols]`` and FP32 scales ``scale[cols/128][rows]`` (1x128 tiles);
+  with ``tiling="128x1"`` the codes come out transposed, ``q[cols][rows]``,
+  with scales ``scale[rows/128][cols]``.
+* ``fp8_quantize_weight(w)`` -- bf16 ``w[n][k]`` -> ``q[n][k]``,
+  ``scale[n/128][k/128]`` (128x128 blocks), optionally also the transpose.
+* ``fp8_gemm(a, a_scale, b, b_scale)`` -- ``C[m][n] = dequant(A) dequant(B)^T``.
+* ``fp8_grouped_gemm(offsets, rows, a, a_scale, b, b_scale)`` -- per-expert
+  Fprop over an expert-sorted, 128-padded row layout.
+
+E4M3 tensors are returned as ``torch.float8_e4m3fn`` (OCP E4M3FN bytes);
+``uint8`` tensors are accepted wherever codes are inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "fp8_quantize_act",
+    "fp8_quantize_weight",
+    "fp8_gemm",
+    "fp8_grouped_gemm",
+    "fp8q_status_string",
+    "fp8q_last_hip_error",
+    "Fp8qError",
+    "library_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+TILE_1x128 = 0
+TILE_128x1 = 1
+BSCALE_BLOCK128 = 0
+BSCALE_ROW128 = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+
+_lib = None
+
+
+class Fp8qError(RuntimeError):
+    """A libfp8q entry point returned a non-zero status."""
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise Fp8qError(
+            "libfp8q.so is not built (expected at %s); build it with "
+            "`python -m fine_grained_fp8_quantize_amd.build`" % _LIB_PATH)
+    L = ctypes.CDLL(_LIB_PATH)
+    p, i64, i32, cint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    L.fp8_quantize_act.argtypes = [p, i64, i64, i64, cint, p, i64, p, i64, p]
+    L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+    L.fp8_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, cint, p, i64, cint, p]
+    L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
+                                   i64, p, i64, cint, p]
+    for name in ("fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm", "fp8_grouped_gemm"):
+        getattr(L, name).restype = cint
+    L.fp8q_status_string.argtypes = [cint]
+    L.fp8q_status_string.restype = ctypes.c_char_p
+    L.fp8q_last_hip_error.argtypes = []
+    L.fp8q_last_hip_error.restype = cint
+    _lib = L
+    return L
+
+
+def fp8q_status_string(status: int) -> str:
+    return _load().fp8q_status_string(status).decode()
+
+
+def fp8q_last_hip_error() -> int:
+    return int(_load().fp8q_last_hip_error())
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        msg = "%s failed: %s (status %d)" % (what, fp8q_status_string(status), status)
+        if status == 5:
+            msg += ", hipError %d" % fp8q_last_hip_error()
+        raise Fp8qError(msg)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need_gpu(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise Fp8qError("fp8q tensors must live on the GPU (got a %s tensor)" % t.device)
+
+
+def _rowmajor(t: torch.Tensor, name: str) -> None:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise Fp8qError("%s must be a 2-D tensor with unit column stride" % name)
+
+
+def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == torch.float8_e4m3fn:
+        return t
+    if t.dtype == torch.uint8:
+        return t
+    raise Fp8qError("%s must hold E4M3 codes (float8_e4m3fn or uint8), got %s" % (name, t.dtype))
+
+
+# ------------------------------------------------------------- quantization
+
+def fp8_quantize_act(x: torch.Tensor, tiling: str = "1x128", q: torch.Tensor | None = None,
+                     scale: torch.Tensor | None = None, stream=None):
+    """Quantize bf16 activations to E4M3 with one FP32 scale per tile.
+
+    ``tiling="1x128"``: returns ``q[rows][cols]``, ``scale[cols/128][rows]``.
+    ``tiling="128x1"``: returns ``q[cols][rows]`` (transposed, token-contiguous)
+    and ``scale[rows/128][cols]``.
+    """
+    _need_gpu(x)
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise Fp8qError("x must be bfloat16")
+    rows, cols = x.shape
+    t = {"1x128": TILE_1x128, "128x1": TILE_128x1}.get(tiling)
+    if t is None:
+        raise Fp8qError("tiling must be '1x128' or '128x1'")
+    dev = x.device
+    if t == TILE_1x128:
+        if q is None:
+            q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
+        if scale is None:
+            scale = torch.empty((cols // 128, rows), dtype=torch.float32, device=dev)
+    else:
+        if q is None:
+            q = torch.empty((cols, rows), dtype=torch.float8_e4m3fn, device=dev)
+        if scale is None:
+            scale = torch.empty((rows // 128, cols), dtype=torch.float32, device=dev)
+    _need_gpu(q, scale)
+    _codes(q, "q")
+    st = _load().fp8_quantize_act(_ptr(x), rows, cols, x.stride(0), t, _ptr(q), q.stride(0),
+                                  _ptr(scale), scale.stride(0), _stream(stream))
+    _check(st, "fp8_quantize_act")
+    return q, scale
+
+
+def fp8_quantize_weight(w: torch.Tensor, transposed: bool = False, q: torch.Tensor | None = None,
+                        scale: torch.Tensor | None = None, q_t: torch.Tensor | None = None,
+                        scale_t: torch.Tensor | None = None, stream=None):
+    """Quantize a bf16 weight ``w[n][k]`` in 128x128 blocks.
+
+    Returns ``(q, scale)``, or ``(q, scale, q_t, scale_t)`` when ``transposed``
+    (``q_t[k][n]``, ``scale_t[k/128][n/128]``: the exact transpose, for Dgrad).
+    """
+    _need_gpu(w)
+    _rowmajor(w, "w")
+    if w.dtype != torch.bfloat16:
+        raise Fp8qError("w must be bfloat16")
+    n, k = w.shape
+    dev = w.device
+    if q is None:
+        q = torch.empty((n, k), dtype=torch.float8_e4m3fn, device=dev)
+    if scale is None:
+        scale = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
+    if transposed:
+        if q_t is None:
+            q_t = torch.empty((k, n), dtype=torch.float8_e4m3fn, device=dev)
+        if scale_t is None:
+            scale_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device=dev)
+    _need_gpu(q, scale, q_t, scale_t)
+    st = _load().fp8_quantize_weight(
+        _ptr(w), n, k, w.stride(0), _ptr(q), q.stride(0), _ptr(scale), scale.stride(0),
+        _ptr(q_t if transposed else None), q_t.stride(0) if transposed else 0,
+        _ptr(scale_t if transposed else None), scale_t.stride(0) if transposed else 0,
+        _stream(stream))
+    _check(st, "fp8_quantize_weight")
+    return (q, scale, q_t, scale_t) if transposed else (q, scale)
+
+
+# --------------------------------------------------------------------- GEMM
+
+def _out_code(out_dtype) -> int:
+    if out_dtype == torch.bfloat16:
+        return OUT_BF16
+    if out_dtype == torch.float32:
+        return OUT_F32
+    raise Fp8qError("out_dtype must be torch.bfloat16 or torch.float32")
+
+
+def fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
+             b_scale_kind: str = "block", out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """``C[m][n] = sum_k deq(A)[m][k] deq(B)[n][k]`` with per-128-slab promotion.
+
+    ``a[m][k]`` codes with ``a_scale[k/128][m]``; ``b[n][k]`` codes with
+    ``b_scale[n/128][k/128]`` (``"block"``) or ``b_scale[k/128][n]`` (``"row"``).
+    """
+    _need_gpu(a, a_scale, b, b_scale, out)
+    _rowmajor(a, "a")
+    _rowmajor(b, "b")
+    _codes(a, "a")
+    _codes(b, "b")
+    m, k = a.shape
+    n, kb = b.shape
+    if kb != k:
+        raise Fp8qError("a and b disagree on K (%d vs %d)" % (k, kb))
+    kind = {"block": BSCALE_BLOCK128, "row": BSCALE_ROW128}.get(b_scale_kind)
+    if kind is None:
+        raise Fp8qError("b_scale_kind must be 'block' or 'row'")
+    oc = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    elif out.dtype != out_dtype:
+        raise Fp8qError("out has dtype %s, expected %s" % (out.dtype, out_dtype))
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise Fp8qError("scales must be float32")
+    st = _load().fp8_gemm(m, n, k, _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
+                          _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0), kind,
+                          _ptr(out), out.stride(0), oc, _stream(stream))
+    _check(st, "fp8_gemm")
+    return out
+
+
+def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | None,
+                     a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
+                     out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                     stream=None) -> torch.Tensor:
+    """MoE expert Fprop: rows ``[off[e], off[e+1])`` of ``a`` times ``W_e = b[e]``.
+
+    ``group_offsets``: int32 GPU tensor ``[E+1]`` (multiples of 128);
+    ``group_rows``: int32 GPU tensor ``[E]`` of real rows, or None; padding rows
+    of the output are zero. ``b[E][n][k]`` codes, ``b_scale[E][n/128][k/128]``.
+    """
+    _need_gpu(group_offsets, group_rows, a, a_scale, b, b_scale, out)
+    _rowmajor(a, "a")
+    _codes(a, "a")
+    _codes(b, "b")
+    if group_offsets.dtype != torch.int32 or (group_rows is not None and group_rows.dtype != torch.int32):
+        raise Fp8qError("group_offsets / group_rows must be int32")
+    if b.dim() != 3 or b.stride(2) != 1 or b_scale.dim() != 3:
+        raise Fp8qError("b must be [E][n][k] and b_scale [E][n/128][k/128]")
+    groups = b.shape[0]
+    if group_offsets.numel() != groups + 1:
+        raise Fp8qError("group_offsets needs E+1 entries")
+    m_total, k = a.shape
+    n = b.shape[1]
+    oc = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((m_total, n), dtype=out_dtype, device=a.device)
+    st = _load().fp8_grouped_gemm(
+        groups, _ptr(group_offsets), _ptr(group_rows), m_total, n, k,
+        _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
+        _ptr(b), b.stride(1), b.stride(0), _ptr(b_scale), b_scale.stride(1), b_scale.stride(0),
+        _ptr(out), out.stride(0), oc, _stream(stream))
+    _check(st, "fp8_grouped_gemm")
+    return out

@@ -1,0 +1,144 @@
+// api.cpp -- the C ABI of libfp8q (declared in include/fp8q.h).
+//
+// Every entry point validates its arguments on the host, returns a status
+// code without launching anything on error, and otherwise enqueues the
+// kernels on the caller's stream. Nothing here allocates, frees or
+// synchronizes.
+#include "fp8q.h"
+
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return FP8Q_OK;
+    g_last_hip_error = (int)e;
+    return FP8Q_ERR_HIP;
+}
+
+// A grid of more than 2^31 - 1 blocks is not launchable.
+bool grid_ok(int64_t blocks) { return blocks >= 0 && blocks <= 0x7FFFFFFFLL; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8q_status_string(int status) {
+    switch (status) {
+        case FP8Q_OK: return "ok";
+        case FP8Q_ERR_NULL: return "a required pointer is NULL";
+        case FP8Q_ERR_SHAPE: return "bad shape (negative size, divisibility or leading dimension)";
+        case FP8Q_ERR_ALIGN: return "pointer or leading dimension breaks the required alignment";
+        case FP8Q_ERR_ENUM: return "enum argument out of range";
+        case FP8Q_ERR_HIP: return "HIP launch failed (see fp8q_last_hip_error)";
+        default: return "unknown status";
+    }
+}
+
+int fp8q_last_hip_error(void) { return g_last_hip_error; }
+
+int fp8_quantize_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int tiling,
+                     uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream) {
+    if (tiling != FP8Q_TILE_1x128 && tiling != FP8Q_TILE_128x1) return FP8Q_ERR_ENUM;
+    if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!x || !q || !scale) return FP8Q_ERR_NULL;
+    if (ld_x < cols) return FP8Q_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || ld_x % 8 != 0 || ld_q % 16 != 0)
+        return FP8Q_ERR_ALIGN;
+    if (tiling == FP8Q_TILE_1x128) {
+        if (cols % 128 != 0 || ld_q < cols || ld_s < rows) return FP8Q_ERR_SHAPE;
+        if (!grid_ok((rows + 15) / 16 * (cols / 128) / 4 + 1)) return FP8Q_ERR_SHAPE;
+        return hip_status(fp8q::launch_quant_act_1x128(x, rows, cols, ld_x, q, ld_q, scale, ld_s, stream));
+    }
+    if (rows % 128 != 0 || cols % 8 != 0 || ld_q < rows || ld_s < cols) return FP8Q_ERR_SHAPE;
+    if (!grid_ok(rows / 128 * ((cols + 127) / 128))) return FP8Q_ERR_SHAPE;
+    return hip_status(fp8q::launch_quant_act_128x1(x, rows, cols, ld_x, q, ld_q, scale, ld_s, stream));
+}
+
+int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                        uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                        uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
+                        hipStream_t stream) {
+    if (n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    if (n == 0 || k == 0) return FP8Q_OK;
+    if (!w || !q || !scale) return FP8Q_ERR_NULL;
+    if (q_t && !scale_t) return FP8Q_ERR_NULL;
+    if (n % 128 != 0 || k % 128 != 0 || ld_w < k || ld_q < k || ld_s < k / 128) return FP8Q_ERR_SHAPE;
+    if (q_t && (ld_qt < n || ld_st < n / 128)) return FP8Q_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4) || ld_w % 8 != 0 || ld_q % 16 != 0)
+        return FP8Q_ERR_ALIGN;
+    if (q_t && (!aligned(q_t, 16) || !aligned(scale_t, 4) || ld_qt % 16 != 0)) return FP8Q_ERR_ALIGN;
+    if (!grid_ok(n / 128 * (k / 128))) return FP8Q_ERR_SHAPE;
+    return hip_status(fp8q::launch_quant_weight(w, n, k, ld_w, q, ld_q, scale, ld_s,
+                                                q_t, ld_qt, scale_t, ld_st, stream));
+}
+
+static int check_gemm_common(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
+                             const float* a_scale, int64_t ld_as, const uint8_t* b, int64_t ldb,
+                             const float* b_scale, void* c, int64_t ldc, int out_dtype) {
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
+    if (!a || !b || !c || (k > 0 && (!a_scale || !b_scale))) return FP8Q_ERR_NULL;
+    if (k % 128 != 0 || lda < k || ldb < k || ldc < n || (k > 0 && ld_as < m)) return FP8Q_ERR_SHAPE;
+    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16) || !aligned(a_scale, 4) ||
+        !aligned(b_scale, 4) || lda % 16 != 0 || ldb % 16 != 0 || ldc % 8 != 0)
+        return FP8Q_ERR_ALIGN;
+    return FP8Q_OK;
+}
+
+int fp8_gemm(int64_t m, int64_t n, int64_t k,
+             const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
+             const uint8_t* b, int64_t ldb, const float* b_scale, int64_t ld_bs, int b_scale_kind,
+             void* c, int64_t ldc, int out_dtype, hipStream_t stream) {
+    if (b_scale_kind != FP8Q_BSCALE_BLOCK128 && b_scale_kind != FP8Q_BSCALE_ROW128) return FP8Q_ERR_ENUM;
+    if (m < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    if (m == 0 || n == 0) return FP8Q_OK;
+    int st = check_gemm_common(m, n, k, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
+    if (st != FP8Q_OK) return st;
+    if (k > 0 && b_scale_kind == FP8Q_BSCALE_BLOCK128 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
+    if (k > 0 && b_scale_kind == FP8Q_BSCALE_ROW128 && ld_bs < n) return FP8Q_ERR_SHAPE;
+    if (!grid_ok(((m + 255) / 256) * ((n + 255) / 256) + 8)) return FP8Q_ERR_SHAPE;
+    fp8q::GemmProblem g = {};
+    g.m = m; g.n = n; g.k = k;
+    g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;
+    g.b = b; g.ldb = ldb; g.b_scale = b_scale; g.ld_bs = ld_bs;
+    g.b_rowscale = b_scale_kind == FP8Q_BSCALE_ROW128;
+    g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
+    return hip_status(fp8q::launch_gemm(g, stream));
+}
+
+int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t* group_rows,
+                     int64_t m_total, int64_t n, int64_t k,
+                     const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
+                     const uint8_t* b, int64_t ldb, int64_t stride_b,
+                     const float* b_scale, int64_t ld_bs, int64_t stride_bs,
+                     void* c, int64_t ldc, int out_dtype, hipStream_t stream) {
+    if (groups < 0 || m_total < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
+    if (groups == 0 || m_total == 0 || n == 0) return FP8Q_OK;
+    if (!group_offsets) return FP8Q_ERR_NULL;
+    int st = check_gemm_common(m_total, n, k, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
+    if (st != FP8Q_OK) return st;
+    if (m_total % 128 != 0 || n % 128 != 0 || m_total > 0x7FFFFFFFLL) return FP8Q_ERR_SHAPE;
+    if (k > 0 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
+    if (stride_b < n * ldb || (k > 0 && stride_bs < (n / 128) * ld_bs)) return FP8Q_ERR_SHAPE;
+    if (stride_b % 16 != 0) return FP8Q_ERR_ALIGN;
+    if (!grid_ok((m_total / 128) * ((n + 255) / 256) + 8)) return FP8Q_ERR_SHAPE;
+    fp8q::GemmProblem g = {};
+    g.m = m_total; g.n = n; g.k = k;
+    g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;
+    g.b = b; g.ldb = ldb; g.b_scale = b_scale; g.ld_bs = ld_bs;
+    g.b_rowscale = false;
+    g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
+    g.groups = groups; g.group_offsets = group_offsets; g.group_rows = group_rows;
+    g.stride_b = stride_b; g.stride_bs = stride_bs;
+    return hip_status(fp8q::launch_grouped_gemm(g, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// launch.h -- host-side kernel launchers of libfp8q (internal; arguments are
+// already validated by the C ABI layer in api.cpp).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                                  hipStream_t stream);
+
+hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
+                                  uint8_t* qt, int64_t ld_q, float* scale, int64_t ld_s,
+                                  hipStream_t stream);
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                               uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
+                               hipStream_t stream);
+
+struct GemmProblem {
+    int64_t m, n, k;
+    const uint8_t* a;
+    int64_t lda;
+    const float* a_scale;
+    int64_t ld_as;
+    const uint8_t* b;
+    int64_t ldb;
+    const float* b_scale;
+    int64_t ld_bs;
+    bool b_rowscale;  // false: 128x128 blocks, true: per (slab, row)
+    void* c;
+    int64_t ldc;
+    bool out_f32;
+    // grouped (MoE) problems only
+    int32_t groups;
+    const int32_t* group_offsets;
+    const int32_t* group_rows;
+    int64_t stride_b;
+    int64_t stride_bs;
+};
+
+hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+
+}  // namespace fp8q

@@ -1,0 +1,279 @@
+// quant.hip -- fine-grained FP8 (E4M3) quantization kernels for gfx950.
+//
+// Groups (page dssusan.co.kr Q&A board, passage on Figure 7(a)): 1x128 tiles
+// for activations (per token per 128 channels), 128x128 blocks for weights;
+// 128x1 token tiles for the Wgrad operands. Every group gets one FP32 scale
+// s = amax / 448 and its elements become E4M3 codes of x / s (page "Deepseek
+// Ai News Expert Interview", passages on E4M3 for all tensors and on sharing
+// exponent bits within small groups). All three kernels are HBM-bound:
+// 2 bytes read, 1 byte written and 4/128 (or 4/16384) bytes of scale per
+// element.
+#include "fp8q_device.h"
+#include "launch.h"
+
+namespace fp8q {
+namespace {
+
+// ------------------------------------------------------------------ 1x128
+
+// One wave quantizes 16 rows of one 128-column slab (16 tiles). Lane
+// 16*rr + c holds the 16-byte chunk c (8 bf16) of rows 4u + rr, u = 0..3, so
+// each 1x128 tile is one DPP row of 16 lanes and its amax reduces in-row.
+constexpr int kActRowsPerWave = 16;
+constexpr int kActWavesPerBlock = 4;
+
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    int64_t units) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * kActWavesPerBlock + (threadIdx.x >> 6);
+    if (unit >= units) return;  // whole wave
+    const int64_t rg = unit / slabs;
+    const int64_t j = unit - rg * slabs;
+    const int rr = lane >> 4, c = lane & 15;
+
+    uint4 v[4];
+    int64_t row[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        row[u] = rg * kActRowsPerWave + u * 4 + rr;
+        v[u] = make_uint4(0, 0, 0, 0);
+        if (row[u] < rows)
+            v[u] = load_nt16(x + row[u] * ld_x + j * 128 + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t mask = 0x7FFF7FFFu;
+        uint32_t m = pk_max_u16(pk_max_u16(v[u].x & mask, v[u].y & mask),
+                                pk_max_u16(v[u].z & mask, v[u].w & mask));
+        m = row16_max(umax32(m & 0xFFFFu, m >> 16));
+        const GroupScale g = group_scale(m);
+
+        float a[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                      bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+        float qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = quot_fast(__builtin_fabsf(a[i]), g);
+        if (g.slow) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[i] = quot_slow(__builtin_fabsf(a[i]), g);
+        }
+        const uint32_t w0 = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[u].x, v[u].y));
+        const uint32_t w1 = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[u].z, v[u].w));
+        if (row[u] < rows) {
+            *reinterpret_cast<uint2*>(q + row[u] * ld_q + j * 128 + c * 8) = make_uint2(w0, w1);
+            if (c == 0) scale[j * ld_s + row[u]] = g.s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ 128x1
+
+// One 256-thread block quantizes a 128-token x 128-channel panel: thread
+// (token group r = t/16, channel chunk g = t%16) loads 8 tokens x 8 channels.
+// Column amax: per-thread max over its 8 tokens, cross-lane max inside the
+// wave, then across the 4 waves through LDS. Codes are transposed through LDS
+// so that each output row (one channel, 128 consecutive tokens) is written
+// with full 16-byte stores.
+constexpr int kTrStride = 144;  // bytes per transposed row (128 + 16 pad)
+
+__global__ __launch_bounds__(256) void quant_act_128x1_kernel(
+    const uint16_t* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ qt, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    int64_t cblocks) {
+    __shared__ uint32_t red[4][16][4];
+    __shared__ float s_sh[128];
+    __shared__ float y_sh[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int g = t & 15, r = t >> 4;
+    const int64_t tb = blockIdx.x / cblocks, cb = blockIdx.x - tb * cblocks;
+    const int64_t t0 = tb * 128, c0 = cb * 128;
+    const int64_t ch = c0 + 8 * g;
+    const bool valid = ch < cols;  // cols % 8 == 0: a chunk is all in or all out
+
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (valid)
+            v[i] = load_nt16(x + (t0 + 8 * r + i) * ld_x + ch);
+    }
+    const uint32_t mask = 0x7FFF7FFFu;
+    uint32_t m[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        m[0] = pk_max_u16(m[0], v[i].x & mask);
+        m[1] = pk_max_u16(m[1], v[i].y & mask);
+        m[2] = pk_max_u16(m[2], v[i].z & mask);
+        m[3] = pk_max_u16(m[3], v[i].w & mask);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        m[d] = pk_max_u16(m[d], (uint32_t)__shfl_xor((int)m[d], 16));
+        m[d] = pk_max_u16(m[d], (uint32_t)__shfl_xor((int)m[d], 32));
+    }
+    if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) red[w][g][d] = m[d];
+    }
+    __syncthreads();
+    if (t < 128) {
+        const int chunk = t >> 3, pair = (t & 7) >> 1;
+        uint32_t mm = 0;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) mm = pk_max_u16(mm, red[ww][chunk][pair]);
+        const uint32_t bits = (t & 1) ? (mm >> 16) : (mm & 0xFFFFu);
+        const GroupScale gs = group_scale(bits);
+        s_sh[t] = gs.s;
+        y_sh[t] = gs.y;
+        if (c0 + t < cols) scale[tb * ld_s + c0 + t] = gs.s;
+    }
+    __syncthreads();
+
+    if (valid) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            GroupScale gs;
+            gs.s = s_sh[8 * g + k];
+            gs.y = y_sh[8 * g + k];
+            gs.slow = !(gs.s >= kSmallScale);
+            const int d = k >> 1;
+            float a[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t word = d == 0 ? v[i].x : d == 1 ? v[i].y : d == 2 ? v[i].z : v[i].w;
+                a[i] = (k & 1) ? bf16_hi(word) : bf16_lo(word);
+            }
+            float qv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[i] = quot_fast(__builtin_fabsf(a[i]), gs);
+            if (gs.slow) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) qv[i] = quot_slow(__builtin_fabsf(a[i]), gs);
+            }
+            uint32_t wd[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                wd[i] = d == 0 ? v[i].x : d == 1 ? v[i].y : d == 2 ? v[i].z : v[i].w;
+            const uint32_t byte = (k & 1) ? 3u : 1u;
+            const uint32_t s0 = gather_byte4(wd[0], wd[1], wd[2], wd[3], byte);
+            const uint32_t s1 = gather_byte4(wd[4], wd[5], wd[6], wd[7], byte);
+            const uint32_t w0 = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], s0);
+            const uint32_t w1 = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], s1);
+            *reinterpret_cast<uint2*>(&tr[(8 * g + k) * kTrStride + 8 * r]) = make_uint2(w0, w1);
+        }
+    }
+    __syncthreads();
+    const int cc = t >> 1, h = t & 1;
+    if (c0 + cc < cols) {
+        uint8_t* dst = qt + (c0 + cc) * ld_q + t0 + 64 * h;
+        const uint8_t* src = &tr[cc * kTrStride + 64 * h];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(src + 16 * i);
+    }
+}
+
+// ---------------------------------------------------------------- 128x128
+
+// One 256-thread block quantizes one 128x128 weight block: thread (row group
+// rg = t/16, chunk g = t%16) holds rows 8rg..8rg+7 x columns 8g..8g+7. The
+// optional transposed copy is produced from the thread's 8x8 byte tile with
+// byte permutes, so block (bn, bk) of W^T gets exactly the same codes.
+__global__ __launch_bounds__(256) void quant_weight_kernel(
+    const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st) {
+    __shared__ uint32_t red[4];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int g = t & 15, rg = t >> 4;
+    const int64_t bn = blockIdx.x / kblocks, bk = blockIdx.x - bn * kblocks;
+    const int64_t n0 = bn * 128 + 8 * rg, k0 = bk * 128 + 8 * g;
+
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = load_nt16(w + (n0 + i) * ld_w + k0);
+    const uint32_t mask = 0x7FFF7FFFu;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        m = pk_max_u16(m, pk_max_u16(pk_max_u16(v[i].x & mask, v[i].y & mask),
+                                     pk_max_u16(v[i].z & mask, v[i].w & mask)));
+    m = wave_max(umax32(m & 0xFFFFu, m >> 16));
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+    m = umax32(umax32(red[0], red[1]), umax32(red[2], red[3]));
+    const GroupScale gs = group_scale(m);
+
+    uint32_t code[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float a[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                      bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = quot_fast(__builtin_fabsf(a[e]), gs);
+        if (gs.slow) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qv[e] = quot_slow(__builtin_fabsf(a[e]), gs);
+        }
+        code[i][0] = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[i].x, v[i].y));
+        code[i][1] = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[i].z, v[i].w));
+        *reinterpret_cast<uint2*>(q + (n0 + i) * ld_q + k0) = make_uint2(code[i][0], code[i][1]);
+    }
+    if (t == 0) scale[bn * ld_s + bk] = gs.s;
+    if (q_t != nullptr) {
+        if (t == 0) scale_t[bk * ld_st + bn] = gs.s;
+        // Column kk of the 8x8 tile = byte (kk % 4) of word (kk / 4) of rows 0..7.
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int d = kk >> 2;
+            const uint32_t byte = (uint32_t)(kk & 3);
+            const uint32_t lo = gather_byte4(code[0][d], code[1][d], code[2][d], code[3][d], byte);
+            const uint32_t hi = gather_byte4(code[4][d], code[5][d], code[6][d], code[7][d], byte);
+            *reinterpret_cast<uint2*>(q_t + (k0 + kk) * ld_qt + bn * 128 + 8 * rg) = make_uint2(lo, hi);
+        }
+    }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ launch
+
+hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
+                                  uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                                  hipStream_t stream) {
+    const int64_t slabs = cols / 128;
+    const int64_t units = (rows + kActRowsPerWave - 1) / kActRowsPerWave * slabs;
+    const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
+    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
+                                  uint8_t* qt, int64_t ld_q, float* scale, int64_t ld_s,
+                                  hipStream_t stream) {
+    const int64_t cblocks = (cols + 127) / 128;
+    const int64_t blocks = tokens / 128 * cblocks;
+    hipLaunchKernelGGL(quant_act_128x1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, tokens, cols, ld_x, qt, ld_q, scale, ld_s, cblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                               uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                               uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
+                               hipStream_t stream) {
+    const int64_t kblocks = k / 128;
+    const int64_t blocks = n / 128 * kblocks;
+    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st);
+    return hipGetLastError();
+}
+
+}  // namespace fp8q

@@ -1,0 +1,199 @@
+/*
+ * fp8q.h -- C ABI of the fine-grained FP8 quantization and block-scaled FP8
+ * GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the FP8 mixed-precision scheme quoted on the pages:
+ *   - GEMM operands are E4M3 on all tensors (page "Deepseek Ai News Expert
+ *     Interview", passage adopting E4M3 on all tensors);
+ *   - activations are grouped and scaled per 1x128 tile (per token per 128
+ *     channels) and weights per 128x128 block (per 128 input channels per 128
+ *     output channels) (page dssusan.co.kr Q&A board, passage on Figure 7(a));
+ *   - the three GEMMs of a Linear operator -- Fprop, Dgrad and Wgrad -- all
+ *     consume FP8 (same page, passage on Figure 6);
+ *   - partial products are promoted to full FP32 accumulation once per
+ *     128-element interval along K, where the per-group scales are applied
+ *     (page "Deepseek Ai News Expert Interview", passage on copying partial
+ *     results to FP32 registers; page inprokorea.com free board, passage on
+ *     the 128-element, four-WGMMA accumulation interval; page "Is aI Hitting
+ *     a Wall?", passage on the dequantization overhead);
+ *   - the GEMMs take FP8 tensors and produce BF16 or FP32 (page "Deepseek Ai
+ *     News Expert Interview", passage on GEMM inputs and outputs);
+ *   - MoE activations are quantized before dispatch, compatible with the FP8
+ *     Fprop of the expert up-projections (page "Eliminate Deepseek Ai News For
+ *     Good", passage on quantizing before the MoE up-projections).
+ *
+ * Numeric contract (readings where the pages are silent):
+ *   E4M3 is OCP E4M3FN (bias 7, no infinities, largest finite 448). For each
+ *   group: amax = max |x| (exact), scale s = fl32(amax / 448) (IEEE binary32
+ *   division), code q = E4M3(fl32(x / s)) rounded to nearest, ties to the even
+ *   code, saturating to +-448; an all-zero group stores s = 0 and signed-zero
+ *   codes; the sign bit of q is the sign of x. Dequantized value = dec(q) * s.
+ *   bf16 and fp32 subnormals are honoured. NaN/Inf inputs are out of contract
+ *   (the kernels finish, the output is unspecified).
+ *
+ * Conventions for every entry point:
+ *   - all data pointers are device memory (HBM) owned by the caller; the
+ *     library never allocates, frees or synchronizes, and inputs are const;
+ *   - bf16 tensors are passed as their uint16 bit patterns; FP8 tensors as
+ *     uint8 E4M3 codes; matrices are row-major with a leading dimension (ld)
+ *     counted in elements;
+ *   - work is enqueued asynchronously on `stream` (NULL = the default stream);
+ *     the call returns once the launch is enqueued;
+ *   - arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched and nothing is written;
+ *   - calls are thread-safe and keep no state besides the last HIP error code.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+#define FP8Q_OK         0 /* launched (or nothing to do)                          */
+#define FP8Q_ERR_NULL   1 /* a required pointer is NULL                           */
+#define FP8Q_ERR_SHAPE  2 /* negative size, bad divisibility, ld below the width  */
+#define FP8Q_ERR_ALIGN  3 /* a pointer or leading dimension breaks the alignment  */
+#define FP8Q_ERR_ENUM   4 /* an enum argument is out of range                     */
+#define FP8Q_ERR_HIP    5 /* the HIP launch failed; see fp8q_last_hip_error()     */
+
+/* ---------------------------------------------------------------- enums */
+#define FP8Q_TILE_1x128       0 /* one scale per row per 128 consecutive columns  */
+#define FP8Q_TILE_128x1       1 /* one scale per column per 128 consecutive rows  */
+#define FP8Q_BSCALE_BLOCK128  0 /* B scales per 128x128 block: [ceil(n/128)][ld]  */
+#define FP8Q_BSCALE_ROW128    1 /* B scales per (128-slab, row): [k/128][ld]      */
+#define FP8Q_OUT_BF16         0 /* output rounded to bf16, nearest-even           */
+#define FP8Q_OUT_F32          1 /* output as fp32                                 */
+
+/*
+ * fp8_quantize_act -- fine-grained activation quantization.
+ *
+ * Tiles: page dssusan.co.kr Q&A board, passage on Figure 7(a) (1x128 tiles,
+ * per token per 128 channels); the 128x1 token tiles for the Wgrad operands
+ * are a reading (the Wgrad GEMM in FP8: same page, passage on Figure 6).
+ *
+ * x       bf16 input [rows][ld_x], ld_x >= cols.
+ * tiling  FP8Q_TILE_1x128: cols % 128 == 0. Writes codes q[rows][ld_q]
+ *           (ld_q >= cols, same layout as x) and scales scale[cols/128][ld_s]
+ *           with ld_s >= rows (slab-major: one row of scales per 128 columns).
+ *         FP8Q_TILE_128x1: rows % 128 == 0, cols % 8 == 0. Writes codes
+ *           TRANSPOSED, q[cols][ld_q] with ld_q >= rows (row c of q holds
+ *           column c of x, token-contiguous, ready to be a K-contiguous GEMM
+ *           operand), and scales scale[rows/128][ld_s] with ld_s >= cols.
+ * Alignment: x and q 16-byte aligned; ld_x % 8 == 0; ld_q % 16 == 0; scale
+ *         4-byte aligned.
+ * rows == 0 or cols == 0: returns FP8Q_OK without launching.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
+ *         FP8Q_ERR_HIP.
+ */
+int fp8_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, int tiling,
+                     uint8_t *q, int64_t ld_q, float *scale, int64_t ld_s, hipStream_t stream);
+
+/*
+ * fp8_quantize_weight -- 128x128 block weight quantization.
+ *
+ * Blocks: page dssusan.co.kr Q&A board, passage on Figure 7(a) (per 128 input
+ * channels per 128 output channels). The optional transposed copy feeds the
+ * Dgrad GEMM (same page, passage on Figure 6); block quantization commutes
+ * with transposition, so it is the exact transpose of q and scale.
+ *
+ * w        bf16 weight [n][ld_w] (n output channels x k input channels),
+ *          n % 128 == 0, k % 128 == 0, ld_w >= k.
+ * q        codes [n][ld_q], ld_q >= k; scale [n/128][ld_s], ld_s >= k/128.
+ * q_t      NULL, or the transposed codes [k][ld_qt] with ld_qt >= n; then
+ *          scale_t [k/128][ld_st] with ld_st >= n/128 must be non-NULL.
+ * Alignment: w, q, q_t 16-byte aligned; ld_w % 8 == 0; ld_q, ld_qt % 16 == 0.
+ * n == 0 or k == 0: returns FP8Q_OK without launching.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_HIP.
+ */
+int fp8_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                        uint8_t *q, int64_t ld_q, float *scale, int64_t ld_s,
+                        uint8_t *q_t, int64_t ld_qt, float *scale_t, int64_t ld_st,
+                        hipStream_t stream);
+
+/*
+ * fp8_gemm -- C = dequant(A) * dequant(B)^T with per-128-slab promotion.
+ *
+ * For each 128-element K slab j the FP8 products of the slab are summed into
+ * an FP32 partial P_j, and the FP32 accumulator takes acc += P_j * sA * sB,
+ * the scales of the slab's tiles/blocks (pages: see the file header).
+ *   Fprop:  A = X codes [m][k] (1x128),   B = W codes [n][k] (BLOCK128).
+ *   Dgrad:  A = dY codes [m][k] (1x128),  B = W^T codes [n][k] (BLOCK128,
+ *           the transposed copy of fp8_quantize_weight).
+ *   Wgrad:  A = dY^T codes [m][k], B = X^T codes [n][k], both from the 128x1
+ *           token tiling (ROW128); K is the token dimension.
+ *
+ * a        codes [m][lda], K contiguous, lda >= k.
+ * a_scale  [k/128][ld_as], ld_as >= m (slab-major, as written by
+ *          fp8_quantize_act in either tiling).
+ * b        codes [n][ldb], K contiguous, ldb >= k.
+ * b_scale  FP8Q_BSCALE_BLOCK128: [ceil(n/128)][ld_bs], ld_bs >= k/128.
+ *          FP8Q_BSCALE_ROW128:   [k/128][ld_bs], ld_bs >= n.
+ * c        [m][ldc], ldc >= n; out_dtype FP8Q_OUT_BF16 (uint16 bf16, rounded
+ *          to nearest even) or FP8Q_OUT_F32. Every element of the m x n
+ *          window is written; k == 0 writes zeros.
+ * Shapes:  m, n >= 0 (any value; ragged tiles are handled), k % 128 == 0.
+ * Alignment: a, b, c 16-byte aligned; lda, ldb % 16 == 0; ldc % 8 == 0;
+ *          scales 4-byte aligned.
+ * m == 0 or n == 0: returns FP8Q_OK without launching.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
+ *         FP8Q_ERR_HIP.
+ */
+int fp8_gemm(int64_t m, int64_t n, int64_t k,
+             const uint8_t *a, int64_t lda, const float *a_scale, int64_t ld_as,
+             const uint8_t *b, int64_t ldb, const float *b_scale, int64_t ld_bs, int b_scale_kind,
+             void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+
+/*
+ * fp8_grouped_gemm -- MoE expert Fprop over an expert-sorted row layout.
+ *
+ * Expert e owns rows [group_offsets[e], group_offsets[e+1]) of A and C; its
+ * first group_rows[e] rows are real tokens and the rest is padding. Real rows
+ * get C_e = dequant(A_e) * dequant(W_e)^T exactly as fp8_gemm with
+ * FP8Q_BSCALE_BLOCK128; padding rows of C are written as zeros. A is the FP8
+ * activation quantized once before dispatch (page "Eliminate Deepseek Ai News
+ * For Good", passage on quantizing before the MoE up-projections), with
+ * slab-major 1x128 scales.
+ *
+ * groups        number of experts, >= 0.
+ * group_offsets DEVICE int32[groups + 1]: non-decreasing multiples of 128,
+ *               group_offsets[0] == 0, group_offsets[groups] == m_total.
+ * group_rows    DEVICE int32[groups] real rows per expert,
+ *               0 <= group_rows[e] <= group_offsets[e+1] - group_offsets[e];
+ *               NULL means every row is real.
+ * m_total       rows of A and C (host copy of group_offsets[groups]),
+ *               m_total % 128 == 0.
+ * a, a_scale    codes [m_total][lda], scales [k/128][ld_as], ld_as >= m_total.
+ * b             expert weights: expert e at b + e * stride_b, codes [n][ldb].
+ * b_scale       expert e at b_scale + e * stride_bs, [n/128][ld_bs].
+ * c             [m_total][ldc]; out_dtype as in fp8_gemm.
+ * Shapes:       n % 128 == 0, k % 128 == 0.
+ * Alignment:    as fp8_gemm; stride_b % 16 == 0.
+ * The device arrays are trusted: offsets that break the contract give
+ * unspecified output (the kernels still stay within the m_total rows).
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
+ *         FP8Q_ERR_HIP.
+ */
+int fp8_grouped_gemm(int32_t groups, const int32_t *group_offsets, const int32_t *group_rows,
+                     int64_t m_total, int64_t n, int64_t k,
+                     const uint8_t *a, int64_t lda, const float *a_scale, int64_t ld_as,
+                     const uint8_t *b, int64_t ldb, int64_t stride_b,
+                     const float *b_scale, int64_t ld_bs, int64_t stride_bs,
+                     void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+
+/* Text for a status code (static storage; never NULL). */
+const char *fp8q_status_string(int status);
+
+/* hipError_t of the most recent FP8Q_ERR_HIP in this thread (0 if none). */
+int fp8q_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -1,0 +1,70 @@
+"""Helpers for the GPU parity tests: host <-> device marshalling and the pass
+criteria. Inputs come from ``workloads`` (seeded), expected values from
+``oracle`` only."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+NORM_TOL = 2e-3       # normwise ||C - ref||_F / ||ref||_F
+ELEM_TOL = 1e-2       # |C - ref| <= ELEM_TOL * (|ref| + rms(ref)) element-wise
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    """bf16 bit array (uint16) -> bf16 GPU tensor with the same bits."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def dev_codes(q: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(q)).cuda()
+
+
+def dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_codes(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.uint8).cpu().numpy()
+
+
+def host_f32(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy()
+
+
+def host_out(t: torch.Tensor) -> np.ndarray:
+    """GEMM output (bf16 or fp32) as float64."""
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str) -> None:
+    got = np.asarray(got)
+    ref = np.asarray(ref)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if got.dtype == np.float32:
+        got, ref = got.view(np.uint32), ref.view(np.uint32)
+    bad = np.nonzero(got != ref)
+    if len(bad[0]):
+        idx = tuple(b[:5] for b in bad)
+        raise AssertionError("%s: %d mismatches, first at %s: got %s ref %s" % (
+            what, len(bad[0]), [tuple(int(x) for x in i) for i in zip(*idx)],
+            got[idx], ref[idx]))
+
+
+def gemm_errors(got: np.ndarray, ref: np.ndarray) -> dict:
+    diff = got - ref
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    norm_ref = float(np.linalg.norm(ref))
+    normwise = float(np.linalg.norm(diff)) / norm_ref if norm_ref > 0 else float(np.linalg.norm(diff))
+    bound = ELEM_TOL * (np.abs(ref) + rms)
+    worst = float(np.max(np.abs(diff) / np.where(bound > 0, bound, 1.0))) if ref.size else 0.0
+    return {"normwise": normwise, "worst_elem_ratio": worst, "rms_ref": rms}
+
+
+def assert_gemm_close(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
+    """The pass criteria against the unrounded float64 oracle."""
+    e = gemm_errors(got, ref)
+    assert np.all(np.isfinite(got)), what + ": non-finite output"
+    assert e["normwise"] <= NORM_TOL, "%s: normwise %.3e > %.1e" % (what, e["normwise"], NORM_TOL)
+    assert e["worst_elem_ratio"] <= 1.0, "%s: element error %.3f x bound" % (what, e["worst_elem_ratio"])
+    return e

@@ -1,0 +1,192 @@
+"""CPU checks of the C ABI boundary (no GPU, no kernel launch).
+
+* the shared library loads and exports every function ``include/fp8q.h``
+  declares;
+* host-side validation returns the documented status code for NULL
+  pointers, bad shapes, misalignment and bad enums, before anything touches
+  the GPU (so these run without one);
+* the Python binding exposes the same names and refuses CPU tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8q.h")
+
+import fine_grained_fp8_quantize_amd as fq  # noqa: E402
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_ENUM, ERR_HIP = 0, 1, 2, 3, 4, 5
+
+
+def _declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fq.library_path()):
+        from fine_grained_fp8_quantize_amd import build
+        build.build(force=False)
+    return fq._load()
+
+
+def test_header_declares_the_four_entry_points():
+    names = _declared_functions()
+    for n in ("fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm", "fp8_grouped_gemm",
+              "fp8q_status_string", "fp8q_last_hip_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(fq.library_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_header_status_codes_match_binding():
+    text = open(HEADER).read()
+    codes = dict(re.findall(r"#define\s+(FP8Q_\w+)\s+(\d+)", text))
+    assert int(codes["FP8Q_OK"]) == OK
+    assert int(codes["FP8Q_ERR_NULL"]) == ERR_NULL
+    assert int(codes["FP8Q_ERR_SHAPE"]) == ERR_SHAPE
+    assert int(codes["FP8Q_ERR_ALIGN"]) == ERR_ALIGN
+    assert int(codes["FP8Q_ERR_ENUM"]) == ERR_ENUM
+    assert int(codes["FP8Q_ERR_HIP"]) == ERR_HIP
+    assert int(codes["FP8Q_TILE_1x128"]) == fq.TILE_1x128
+    assert int(codes["FP8Q_TILE_128x1"]) == fq.TILE_128x1
+    assert int(codes["FP8Q_BSCALE_BLOCK128"]) == fq.BSCALE_BLOCK128
+    assert int(codes["FP8Q_BSCALE_ROW128"]) == fq.BSCALE_ROW128
+    assert int(codes["FP8Q_OUT_BF16"]) == fq.OUT_BF16
+    assert int(codes["FP8Q_OUT_F32"]) == fq.OUT_F32
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert fq.fp8q_status_string(s)
+    assert fq.fp8q_status_string(99) == "unknown status"
+    assert fq.fp8q_last_hip_error() == 0
+
+
+# Fake, well-aligned device addresses: validation never dereferences them.
+# The default arguments of each helper below describe a VALID call; every
+# test call changes at least one argument so that validation rejects it (or
+# an empty size returns OK) before anything is launched.
+A16 = 0x10000
+A16b = 0x20000
+A16c = 0x30000
+A4 = 0x40000
+
+
+def _act(lib, x=A16, rows=256, cols=512, ld_x=512, tiling=0, q=A16b, ld_q=512, s=A4, ld_s=256):
+    return lib.fp8_quantize_act(x, rows, cols, ld_x, tiling, q, ld_q, s, ld_s, None)
+
+
+def test_quantize_act_validation(lib):
+    assert _act(lib, tiling=2) == ERR_ENUM
+    assert _act(lib, rows=-1) == ERR_SHAPE
+    assert _act(lib, rows=0) == OK                  # empty: nothing to do, no launch
+    assert _act(lib, cols=0) == OK
+    assert _act(lib, x=0) == ERR_NULL
+    assert _act(lib, q=0) == ERR_NULL
+    assert _act(lib, s=0) == ERR_NULL
+    assert _act(lib, cols=500, ld_x=512, ld_q=512) == ERR_SHAPE      # not a multiple of 128
+    assert _act(lib, ld_x=256) == ERR_SHAPE                           # ld below width
+    assert _act(lib, ld_s=255) == ERR_SHAPE                           # scale ld below rows
+    assert _act(lib, x=A16 + 8) == ERR_ALIGN
+    assert _act(lib, q=A16b + 4) == ERR_ALIGN
+    assert _act(lib, s=A4 + 2) == ERR_ALIGN
+    # 128x1: rows must be a multiple of 128, q is [cols][rows]
+    assert _act(lib, tiling=1, rows=200, ld_q=512, ld_s=512) == ERR_SHAPE
+    assert _act(lib, tiling=1, rows=256, cols=100, ld_x=512, ld_q=256, ld_s=512) == ERR_SHAPE
+    assert _act(lib, tiling=1, rows=256, ld_q=128, ld_s=512) == ERR_SHAPE   # ld_q < rows
+
+
+def test_quantize_act_ld_alignment_rule(lib):
+    # ld_x must be a multiple of 8 elements (16 bytes); ld_q a multiple of 16.
+    assert _act(lib, ld_x=516) == ERR_ALIGN
+    assert _act(lib, ld_q=520) == ERR_ALIGN
+
+
+def _w(lib, w=A16, n=256, k=384, ld_w=384, q=A16b, ld_q=384, s=A4, ld_s=3, qt=0, ld_qt=0, st=0, ld_st=0):
+    return lib.fp8_quantize_weight(w, n, k, ld_w, q, ld_q, s, ld_s, qt, ld_qt, st, ld_st, None)
+
+
+def test_quantize_weight_validation(lib):
+    assert _w(lib, n=0) == OK
+    assert _w(lib, n=-128) == ERR_SHAPE
+    assert _w(lib, w=0) == ERR_NULL
+    assert _w(lib, qt=A16c, st=0) == ERR_NULL          # transposed codes without scales
+    assert _w(lib, n=200) == ERR_SHAPE
+    assert _w(lib, k=200, ld_w=384, ld_q=384) == ERR_SHAPE
+    assert _w(lib, ld_s=2) == ERR_SHAPE
+    assert _w(lib, qt=A16c, ld_qt=128, st=A4, ld_st=2) == ERR_SHAPE   # ld_qt < n
+    assert _w(lib, qt=A16c, ld_qt=256, st=A4, ld_st=1) == ERR_SHAPE   # ld_st < n/128
+    assert _w(lib, w=A16 + 2) == ERR_ALIGN
+    assert _w(lib, qt=A16c + 8, ld_qt=256, st=A4, ld_st=2) == ERR_ALIGN
+
+
+def _g(lib, m=300, n=200, k=256, a=A16, lda=256, a_s=A4, ld_as=300, b=A16b, ldb=256, b_s=A4,
+       ld_bs=2, kind=0, c=A16c, ldc=200, out=0):
+    return lib.fp8_gemm(m, n, k, a, lda, a_s, ld_as, b, ldb, b_s, ld_bs, kind, c, ldc, out, None)
+
+
+def test_gemm_validation(lib):
+    assert _g(lib, kind=2) == ERR_ENUM
+    assert _g(lib, out=3) == ERR_ENUM
+    assert _g(lib, m=-1) == ERR_SHAPE
+    assert _g(lib, m=0) == OK
+    assert _g(lib, n=0) == OK
+    assert _g(lib, a=0) == ERR_NULL
+    assert _g(lib, c=0) == ERR_NULL
+    assert _g(lib, a_s=0) == ERR_NULL
+    assert _g(lib, k=200, lda=256, ldb=256) == ERR_SHAPE      # K not a multiple of 128
+    assert _g(lib, lda=128) == ERR_SHAPE
+    assert _g(lib, ldc=100) == ERR_SHAPE
+    assert _g(lib, ld_as=299) == ERR_SHAPE
+    assert _g(lib, ld_bs=1) == ERR_SHAPE                      # block scales need k/128 per row
+    assert _g(lib, kind=1, ld_bs=199) == ERR_SHAPE            # row scales need n per slab
+    assert _g(lib, a=A16 + 8) == ERR_ALIGN
+    assert _g(lib, lda=264) == ERR_ALIGN                      # 264 % 16 != 0
+    assert _g(lib, c=A16c + 4) == ERR_ALIGN
+    assert _g(lib, ldc=204) == ERR_ALIGN
+
+
+def _gg(lib, groups=4, off=A16, rows=0, m=512, n=256, k=256, a=A16b, lda=256, a_s=A4, ld_as=512,
+        b=A16c, ldb=256, sb=256 * 256, b_s=A4, ld_bs=2, sbs=4, c=A16, ldc=256, out=0):
+    return lib.fp8_grouped_gemm(groups, off, rows, m, n, k, a, lda, a_s, ld_as, b, ldb, sb,
+                                b_s, ld_bs, sbs, c, ldc, out, None)
+
+
+def test_grouped_gemm_validation(lib):
+    assert _gg(lib, groups=0) == OK
+    assert _gg(lib, m=0) == OK
+    assert _gg(lib, groups=-1) == ERR_SHAPE
+    assert _gg(lib, out=5) == ERR_ENUM
+    assert _gg(lib, off=0) == ERR_NULL
+    assert _gg(lib, m=500, ld_as=512) == ERR_SHAPE         # m_total not a multiple of 128
+    assert _gg(lib, n=200, ldc=256) == ERR_SHAPE           # n not a multiple of 128
+    assert _gg(lib, sb=100) == ERR_SHAPE                   # experts overlap
+    assert _gg(lib, sbs=1) == ERR_SHAPE
+    assert _gg(lib, sb=256 * 256 + 8) == ERR_ALIGN
+
+
+def test_binding_names_match_c_entry_points():
+    for name in ("fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm", "fp8_grouped_gemm"):
+        assert callable(getattr(fq, name))
+
+
+def test_binding_refuses_cpu_tensors():
+    x = torch.zeros((128, 128), dtype=torch.bfloat16)
+    with pytest.raises(fq.Fp8qError):
+        fq.fp8_quantize_act(x)
+    w = torch.zeros((128, 128), dtype=torch.bfloat16)
+    with pytest.raises(fq.Fp8qError):
+        fq.fp8_quantize_weight(w)

@@ -1,0 +1,260 @@
+"""GPU parity of the block-scaled FP8 GEMM (Fprop, Dgrad, Wgrad, grouped MoE).
+
+Both sides consume the same FP8 operands: the oracle quantizes the seeded
+bf16 inputs, the codes and scales are uploaded unchanged, and the GPU GEMM is
+compared with the oracle's unrounded float64 GEMM of the dequantized
+operands. Pass criteria: normwise error <= 2e-3 and every element within
+1e-2 * (|ref| + rms(ref)). At full size the comparison runs on sampled rows
+(every column of each sampled row), which the oracle computes directly; the
+small cases compare every element. An exact case (integer codes, power-of-two
+scales) must be bit-exact in FP32. End-to-end cases run the GPU quantizers
+too.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_fp8_quantize_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import (assert_bits_equal, assert_gemm_close, dev_bf16, dev_codes, dev_f32,
+                      host_codes, host_f32, host_out)
+
+pytestmark = pytest.mark.gpu
+
+OUT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _sample_rows(m: int, count: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 15, 16, 63, 64, 127, 128, 255, 256, m - 257, m - 256, m - 1]
+    fixed = [r for r in fixed if 0 <= r < m]
+    rand = rng.choice(m, size=min(count, m), replace=False)
+    return np.unique(np.concatenate([fixed, rand]).astype(np.int64))
+
+
+def _gpu_gemm(a_q, a_s, b_q, b_s, kind, out):
+    c = fq.fp8_gemm(dev_codes(a_q), dev_f32(a_s), dev_codes(b_q), dev_f32(b_s), kind, OUT[out])
+    torch.cuda.synchronize()
+    return host_out(c)
+
+
+def _check_full(a_q, a_s, b_q, b_s, kind, out, what):
+    got = _gpu_gemm(a_q, a_s, b_q, b_s, kind, out)
+    ref = oracle.gemm(a_q, a_s, b_q, b_s, kind)
+    return assert_gemm_close(got, ref, what)
+
+
+def _check_rows(a_q, a_s, b_q, b_s, kind, out, what, count=64, seed=0):
+    got = _gpu_gemm(a_q, a_s, b_q, b_s, kind, out)
+    rows = _sample_rows(a_q.shape[0], count, seed)
+    ref = oracle.gemm_rows(rows, a_q, a_s, b_q, b_s, kind)
+    return assert_gemm_close(got[rows], ref, what)
+
+
+# ------------------------------------------------------------ config shapes
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_tiny_fprop_all_elements(out):
+    d = wl.tiny_fprop()
+    a_q, a_s = oracle.quant_act_1x128(d["x"])
+    b_q, b_s = oracle.quant_weight_128x128(d["w"])
+    _check_full(a_q, a_s, b_q, b_s, "block", out, "tiny fprop " + out)
+
+
+def test_dense_fprop_full_size():
+    d = wl.dense_fprop()
+    a_q, a_s = oracle.quant_act_1x128(d["x"])
+    b_q, b_s = oracle.quant_weight_128x128(d["w"])
+    e = _check_rows(a_q, a_s, b_q, b_s, "block", "bf16", "dense fprop")
+    print("dense fprop errors", e)
+
+
+def test_dgrad_full_size():
+    d = wl.dgrad()
+    a_q, a_s = oracle.quant_act_1x128(d["dy"])               # [4096][2048]
+    w_q, w_s = oracle.quant_weight_128x128(d["w"])            # [2048][7168]
+    b_q = np.ascontiguousarray(w_q.T)                         # W^T codes [7168][2048]
+    b_s = np.ascontiguousarray(w_s.T)                         # [56][16]
+    e = _check_rows(a_q, a_s, b_q, b_s, "block", "bf16", "dgrad")
+    print("dgrad errors", e)
+
+
+def test_wgrad_full_size():
+    d = wl.wgrad()
+    a_q, a_s = oracle.quant_act_128x1(d["dy"])                # dY^T [2048][8192], [64][2048]
+    b_q, b_s = oracle.quant_act_128x1(d["x"])                 # X^T [7168][8192], [64][7168]
+    e = _check_rows(a_q, a_s, b_q, b_s, "row", "f32", "wgrad")
+    print("wgrad errors", e)
+
+
+# ------------------------------------------------------------ ragged / edge
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (17, 384, 384), (300, 256, 256), (257, 640, 640),
+                                   (513, 128, 1024)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_block_scaled_ragged(m, n, k, out):
+    x = wl.activation(2, "tiny_fprop", 30, m, k, 100.0)
+    w = wl.weight(2, "tiny_fprop", 31, n, k)
+    a_q, a_s = oracle.quant_act_1x128(x)
+    b_q, b_s = oracle.quant_weight_128x128(w)
+    _check_full(a_q, a_s, b_q, b_s, "block", out, "block m=%d n=%d k=%d %s" % (m, n, k, out))
+
+
+@pytest.mark.parametrize("m,n,tokens", [(1, 8, 128), (200, 72, 256), (130, 264, 384), (256, 512, 512)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_row_scaled_ragged(m, n, tokens, out):
+    dy = wl.activation(2, "wgrad", 32, tokens, m, None)
+    x = wl.activation(2, "wgrad", 33, tokens, n, 50.0)
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    b_q, b_s = oracle.quant_act_128x1(x)
+    _check_full(a_q, a_s, b_q, b_s, "row", out, "row m=%d n=%d k=%d %s" % (m, n, tokens, out))
+
+
+def test_k_zero_writes_zeros():
+    """K = 0: the product is the zero matrix; every element of the window is
+    written and nothing is read from the (unused) operands."""
+    lib = fq._load()
+    a = torch.zeros(16, dtype=torch.uint8, device="cuda")      # valid, never read
+    b = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = torch.full((40, 136), 3.0, dtype=torch.float32, device="cuda")
+    st = lib.fp8_gemm(40, 130, 0, a.data_ptr(), 16, None, 40, b.data_ptr(), 16, None, 1, 0,
+                      out.data_ptr(), 136, 1, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.all(out[:, :130] == 0)
+    assert torch.all(out[:, 130:] == 3.0)
+
+
+def test_exact_power_of_two_case():
+    """Integer codes (|q| <= 16) and scales in {1, 2}: every partial sum is an
+    integer below 2^24, so the FP32 result is exact and must equal the oracle
+    bit for bit; the bf16 output must be its nearest-even rounding."""
+    rng = np.random.default_rng(40)
+    m, n, k = 300, 384, 512
+    ints = list(range(17))
+    code = {v: oracle.e4m3_encode(float(v)) for v in ints}
+    va = rng.integers(-16, 17, (m, k))
+    vb = rng.integers(-16, 17, (n, k))
+    enc = np.vectorize(lambda t: code[abs(int(t))] | (0x80 if t < 0 else 0))
+    a_q = enc(va).astype(np.uint8)
+    b_q = enc(vb).astype(np.uint8)
+    a_s = rng.choice([1.0, 2.0], (k // 128, m)).astype(np.float32)
+    b_s = rng.choice([1.0, 2.0], (n // 128, k // 128)).astype(np.float32)
+    ref = oracle.gemm(a_q, a_s, b_q, b_s, "block")
+    got32 = _gpu_gemm(a_q, a_s, b_q, b_s, "block", "f32")
+    assert_bits_equal(got32.astype(np.float32), ref.astype(np.float32), "exact fp32")
+    assert np.array_equal(got32, ref)
+    got16 = _gpu_gemm(a_q, a_s, b_q, b_s, "block", "bf16")
+    assert np.array_equal(got16, oracle.bf16_round(ref))
+    # the row-scaled form on the same integers
+    a_r = rng.choice([1.0, 2.0], (k // 128, m)).astype(np.float32)
+    b_r = rng.choice([1.0, 2.0], (k // 128, n)).astype(np.float32)
+    ref_r = oracle.gemm(a_q, a_r, b_q, b_r, "row")
+    got_r = _gpu_gemm(a_q, a_r, b_q, b_r, "row", "f32")
+    assert np.array_equal(got_r, ref_r)
+
+
+# ------------------------------------------------------------------ grouped
+
+def _grouped_case(rows, n, k, seed=0, group_rows=True, out="bf16", sample=None, pad_extra=None):
+    rows = np.asarray(rows, dtype=np.int64)
+    g = wl.grouped_fprop(seed, n=n, k=k, experts=len(rows), rows=rows)
+    offsets = g["offsets"].copy()
+    if pad_extra is not None:   # enlarge some segments beyond the 128-padding
+        seg = np.diff(offsets) + np.asarray(pad_extra, dtype=np.int64)
+        offsets = np.concatenate([[0], np.cumsum(seg)])
+        x = np.zeros((int(offsets[-1]), k), np.uint16)
+        for e in range(len(rows)):
+            x[offsets[e]:offsets[e] + rows[e]] = g["x"][g["offsets"][e]:g["offsets"][e] + rows[e]]
+    else:
+        x = g["x"]
+    a_q, a_s = oracle.quant_act_1x128(x)
+    E = len(rows)
+    b_q = np.empty((E, n, k), np.uint8)
+    b_s = np.empty((E, n // 128, k // 128), np.float32)
+    for e in range(E):
+        b_q[e], b_s[e] = oracle.quant_weight_128x128(g["w"][e])
+    off_d = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    rows_d = torch.from_numpy(rows.astype(np.int32)).cuda() if group_rows else None
+    c = fq.fp8_grouped_gemm(off_d, rows_d, dev_codes(a_q), dev_f32(a_s), dev_codes(b_q),
+                            dev_f32(b_s), OUT[out])
+    torch.cuda.synchronize()
+    got = host_out(c)
+    real = rows if group_rows else np.diff(offsets)
+    for e in range(E):
+        r0, r = int(offsets[e]), int(real[e])
+        end = int(offsets[e + 1])
+        assert np.all(got[r0 + r:end] == 0), "expert %d padding rows not zero" % e
+        if r == 0:
+            continue
+        if sample is not None and r > sample:
+            idx = np.unique(np.concatenate([[0, r - 1], np.random.default_rng(e).choice(r, sample, replace=False)]))
+        else:
+            idx = np.arange(r)
+        ref = oracle.gemm_rows(r0 + idx, a_q, a_s, b_q[e], b_s[e], "block")
+        assert_gemm_close(got[r0 + idx], ref, "expert %d (rows %d)" % (e, r))
+    return got
+
+
+def test_grouped_edge_row_counts():
+    _grouped_case([0, 1, 127, 128, 129, 255, 256, 257, 3], n=256, k=384)
+
+
+def test_grouped_all_rows_real_and_f32():
+    _grouped_case([128, 256, 384], n=384, k=256, group_rows=False, out="f32")
+
+
+def test_grouped_wide_padding_segments():
+    # segments larger than the 128-rounding: real rows, then >= 128 padding rows
+    _grouped_case([5, 0, 300], n=256, k=256, pad_extra=[256, 128, 128])
+
+
+def test_grouped_moe_config_sampled():
+    """The MoE config: 32 experts, Zipf(1.1) routing of 8192 tokens, N=4096, K=7168."""
+    _grouped_case(wl.moe_rows(0), n=4096, k=7168, sample=6)
+
+
+# --------------------------------------------------------------- end to end
+
+@pytest.mark.parametrize("name", ["tiny_fprop", "dense_fprop"])
+def test_end_to_end_fprop(name):
+    """GPU quantizers + GPU GEMM against oracle quantizers + oracle GEMM."""
+    d = wl.tiny_fprop() if name == "tiny_fprop" else wl.dense_fprop()
+    xq, xs = fq.fp8_quantize_act(dev_bf16(d["x"]))
+    wq, ws = fq.fp8_quantize_weight(dev_bf16(d["w"]))
+    c = fq.fp8_gemm(xq, xs, wq, ws, "block", torch.bfloat16)
+    torch.cuda.synchronize()
+    got = host_out(c)
+    a_q, a_s = oracle.quant_act_1x128(d["x"])
+    b_q, b_s = oracle.quant_weight_128x128(d["w"])
+    rows = _sample_rows(a_q.shape[0], 48, 5)
+    ref = oracle.gemm_rows(rows, a_q, a_s, b_q, b_s, "block")
+    assert_gemm_close(got[rows], ref, name + " end to end")
+
+
+def test_end_to_end_dgrad_uses_transposed_copy():
+    d = wl.dgrad(m=512)
+    dq, ds = fq.fp8_quantize_act(dev_bf16(d["dy"]))
+    _, _, wqt, wst = fq.fp8_quantize_weight(dev_bf16(d["w"]), transposed=True)
+    c = fq.fp8_gemm(dq, ds, wqt, wst, "block", torch.bfloat16)
+    torch.cuda.synchronize()
+    a_q, a_s = oracle.quant_act_1x128(d["dy"])
+    w_q, w_s = oracle.quant_weight_128x128(d["w"])
+    ref = oracle.gemm(a_q, a_s, np.ascontiguousarray(w_q.T), np.ascontiguousarray(w_s.T), "block")
+    assert_gemm_close(host_out(c), ref, "dgrad end to end")
+
+
+def test_end_to_end_wgrad():
+    d = wl.wgrad(tokens=1024, n_out=384, k_in=640)
+    aq, as_ = fq.fp8_quantize_act(dev_bf16(d["dy"]), "128x1")
+    bq, bs = fq.fp8_quantize_act(dev_bf16(d["x"]), "128x1")
+    c = fq.fp8_gemm(aq, as_, bq, bs, "row", torch.float32)
+    torch.cuda.synchronize()
+    a_q, a_s = oracle.quant_act_128x1(d["dy"])
+    b_q, b_s = oracle.quant_act_128x1(d["x"])
+    assert_bits_equal(host_codes(aq), a_q, "wgrad dY^T codes")
+    assert_bits_equal(host_f32(bs), b_s, "wgrad X^T scales")
+    assert_gemm_close(host_out(c), oracle.gemm(a_q, a_s, b_q, b_s, "row"), "wgrad end to end")

@@ -1,0 +1,223 @@
+"""GPU parity of the quantization kernels: FP8 codes and FP32 scales must be
+bit-identical to the CPU oracle on the same seeded inputs.
+
+Covers every config's quantized operands at full size, ragged row counts,
+edge tiles (all-zero, signed zeros, bf16 subnormals, bf16 max, subnormal
+fp32 scales, single values, ties), padded leading dimensions, and the
+exhaustive sweep over every bf16 (x, amax) pair (both signs).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_fp8_quantize_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import assert_bits_equal, dev_bf16, host_codes, host_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_act(bits: np.ndarray, tiling: str = "1x128"):
+    x = dev_bf16(bits)
+    q, s = fq.fp8_quantize_act(x, tiling)
+    torch.cuda.synchronize()
+    return host_codes(q), host_f32(s)
+
+
+def _check_act_1x128(bits: np.ndarray, what: str):
+    q, s = _gpu_act(bits)
+    q_ref, s_ref = oracle.quant_act_1x128(bits)
+    assert_bits_equal(s, s_ref, what + " scales")
+    assert_bits_equal(q, q_ref, what + " codes")
+
+
+def _check_act_128x1(bits: np.ndarray, what: str):
+    q, s = _gpu_act(bits, "128x1")
+    q_ref, s_ref = oracle.quant_act_128x1(bits)
+    assert_bits_equal(s, s_ref, what + " scales")
+    assert_bits_equal(q, q_ref, what + " codes")
+
+
+def _edge_rows(rng) -> np.ndarray:
+    def bf(v):
+        return wl.f32_to_bf16_bits(np.asarray(v, dtype=np.float32))
+    rows = [bf(rng.standard_normal(128))]
+    z = np.zeros(128, np.uint16)
+    z[::3] = 0x8000
+    rows.append(z)                                            # all +-0: s = 0
+    r = bf(rng.standard_normal(128) * 1e-3)
+    r[17] = bf([1000.0])[0]
+    rows.append(r)                                            # one outlier
+    sub = rng.integers(1, 0x80, 128).astype(np.uint16)
+    sub[::2] |= 0x8000
+    rows.append(sub)                                          # bf16 subnormals only
+    big = bf(rng.standard_normal(128))
+    big[5] = 0x7F7F
+    rows.append(big)                                          # amax = bf16 max
+    rows.append(bf(rng.standard_normal(128) * 1e-38))         # subnormal fp32 scale
+    rows.append(bf(rng.standard_normal(128) * 1e-20))         # scale below 2^-60
+    one = np.zeros(128, np.uint16)
+    one[77] = bf([-3.0])[0]
+    rows.append(one)                                          # single nonzero value
+    ties = bf(np.full(128, 448.0 * 17 / 64))
+    ties[0] = bf([448.0])[0]
+    rows.append(ties)                                         # exact E4M3 ties
+    neg = bf(-np.abs(rng.standard_normal(128)) * 1e-6)
+    neg[3] = 0x8000
+    rows.append(neg)                                          # negatives rounding to -0
+    return np.stack(rows)
+
+
+# ------------------------------------------------------------------ 1x128
+
+@pytest.mark.parametrize("name", ["tiny_fprop", "dense_fprop", "dgrad", "grouped_fprop"])
+def test_act_1x128_configs_full_size(name):
+    if name == "tiny_fprop":
+        bits = wl.tiny_fprop()["x"]
+    elif name == "dense_fprop":
+        bits = wl.dense_fprop()["x"]
+    elif name == "dgrad":
+        bits = wl.dgrad()["dy"]
+    else:
+        bits = wl.grouped_fprop(with_weights=False)["x"]
+    _check_act_1x128(bits, name)
+
+
+@pytest.mark.parametrize("rows", [1, 3, 15, 16, 17, 63, 129, 1000])
+def test_act_1x128_ragged_rows(rows):
+    bits = wl.activation(1, "tiny_fprop", 20, rows, 384, 100.0)
+    _check_act_1x128(bits, "rows=%d" % rows)
+
+
+def test_act_1x128_edge_tiles():
+    rng = np.random.default_rng(11)
+    e = _edge_rows(rng)
+    # two slabs per row: edge tile in slab 0, a plain tile in slab 1, so every
+    # 16-lane group also sees its neighbours' special cases
+    bits = np.concatenate([e, wl.activation(1, "tiny_fprop", 21, e.shape[0], 128, None)], axis=1)
+    _check_act_1x128(bits, "edge tiles")
+
+
+def test_act_1x128_padded_leading_dimension():
+    bits = wl.activation(1, "tiny_fprop", 22, 70, 512, 100.0)
+    x_full = dev_bf16(np.concatenate([bits, np.zeros((70, 128), np.uint16)], axis=1))
+    x = x_full[:, :384]
+    q = torch.full((70, 400), 0x5A, dtype=torch.uint8, device="cuda")[:, :384]
+    s = torch.full((3, 80), 7.0, dtype=torch.float32, device="cuda")[:, :70]
+    fq.fp8_quantize_act(x, "1x128", q=q, scale=s)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act_1x128(bits[:, :384])
+    assert_bits_equal(host_codes(q.contiguous()), q_ref, "padded ld codes")
+    assert_bits_equal(host_f32(s.contiguous()), s_ref, "padded ld scales")
+    # bytes outside the logical window are untouched
+    assert torch.all(q.as_strided((70, 16), (400, 1), q.storage_offset() + 384) == 0x5A)
+
+
+def test_exhaustive_x_amax_sweep():
+    """Every bf16 amax A > 0 with every bf16 |x| <= A, both signs: A sits in
+    slot 0 of a 1x128 tile and 127 x values fill the rest. GPU codes must
+    equal the oracle's for all ~1.07e9 pairs."""
+    amax_bits = np.arange(1, 0x7F80, dtype=np.int64)          # positive finite bf16
+    counts = amax_bits + 1                                    # |x| bits 0..A
+    chunk_edges = np.searchsorted(np.cumsum(counts), np.linspace(0, counts.sum(), 17)[1:-1])
+    total_pairs = 0
+    for sign in (0, 0x8000):
+        for chunk in np.split(amax_bits, chunk_edges):
+            if chunk.size == 0:
+                continue
+            c = chunk + 1
+            tiles_per = (c + 126) // 127
+            n_tiles = int(tiles_per.sum())
+            tile_amax = np.repeat(chunk, tiles_per)
+            # x bit pattern for slot 1..127 of tile t: 127*(t - first tile of its A) + slot - 1
+            first = np.repeat(np.cumsum(tiles_per) - tiles_per, tiles_per)
+            local = (np.arange(n_tiles) - first)[:, None] * 127 + np.arange(127)[None, :]
+            xb = np.where(local <= tile_amax[:, None], local, 0).astype(np.uint16) | np.uint16(sign)
+            tiles = np.empty((n_tiles, 128), np.uint16)
+            tiles[:, 0] = tile_amax.astype(np.uint16)
+            tiles[:, 1:] = xb
+            total_pairs += int(c.sum())
+            _check_act_1x128(tiles, "sweep sign=%#x A in [%#x, %#x]" % (sign, chunk[0], chunk[-1]))
+    assert total_pairs == 2 * int(counts.sum())
+
+
+# ------------------------------------------------------------------ 128x1
+
+@pytest.mark.parametrize("which", ["dy", "x"])
+def test_act_128x1_wgrad_full_size(which):
+    d = wl.wgrad()
+    _check_act_128x1(d[which], "wgrad " + which)
+
+
+@pytest.mark.parametrize("cols", [8, 120, 200, 264])
+def test_act_128x1_ragged_columns(cols):
+    bits = wl.activation(1, "wgrad", 23, 384, cols, 50.0)
+    _check_act_128x1(bits, "cols=%d" % cols)
+
+
+def test_act_128x1_edge_tiles():
+    rng = np.random.default_rng(12)
+    e = _edge_rows(rng)                                       # [10][128]: one tile per row
+    bits = np.ascontiguousarray(np.concatenate([e, e[::-1]], axis=0)[:16].T)  # [128][16]
+    bits = np.concatenate([bits, bits[::-1]], axis=0)         # [256][16]
+    _check_act_128x1(bits, "edge tiles 128x1")
+
+
+# ---------------------------------------------------------------- 128x128
+
+@pytest.mark.parametrize("name", ["tiny_fprop", "dense_fprop", "dgrad"])
+def test_weight_configs_full_size(name):
+    w = {"tiny_fprop": wl.tiny_fprop, "dense_fprop": wl.dense_fprop, "dgrad": wl.dgrad}[name]()["w"]
+    q, s, qt, st = fq.fp8_quantize_weight(dev_bf16(w), transposed=True)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_weight_128x128(w)
+    assert_bits_equal(host_f32(s), s_ref, name + " weight scales")
+    assert_bits_equal(host_codes(q), q_ref, name + " weight codes")
+    assert_bits_equal(host_f32(st), np.ascontiguousarray(s_ref.T), name + " transposed scales")
+    assert_bits_equal(host_codes(qt), np.ascontiguousarray(q_ref.T), name + " transposed codes")
+
+
+def test_weight_grouped_experts_sampled():
+    """All 32 expert weights quantized on the GPU (the bench launch); experts
+    0, 13 and 31 compared in full with the oracle."""
+    g = wl.grouped_fprop()
+    w = g["w"]
+    E, n, k = w.shape
+    dw = dev_bf16(w.reshape(E * n, k))
+    q, s = fq.fp8_quantize_weight(dw)   # experts stacked along n: blocks never straddle
+    torch.cuda.synchronize()
+    q = host_codes(q).reshape(E, n, k)
+    s = host_f32(s).reshape(E, n // 128, k // 128)
+    for e in (0, 13, 31):
+        q_ref, s_ref = oracle.quant_weight_128x128(w[e])
+        assert_bits_equal(s[e], s_ref, "expert %d scales" % e)
+        assert_bits_equal(q[e], q_ref, "expert %d codes" % e)
+
+
+def test_weight_edge_blocks():
+    rng = np.random.default_rng(13)
+    w = wl.weight(1, "tiny_fprop", 24, 384, 256)
+    w[0:128, 0:128] = 0                                   # all-zero block
+    w[0:128:3, 0:128:5] = 0x8000                          # with signed zeros
+    w[128:256, 128:256] = rng.integers(1, 0x80, (128, 128)).astype(np.uint16)  # subnormals
+    w[256, 7] = 0x7F7F                                    # bf16 max
+    w[300:384, 128:256] = wl.f32_to_bf16_bits(rng.standard_normal((84, 128)).astype(np.float32) * 1e-39)
+    w[256:300, 128:256] = 0
+    q, s, qt, st = fq.fp8_quantize_weight(dev_bf16(w), transposed=True)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_weight_128x128(w)
+    assert_bits_equal(host_f32(s), s_ref, "edge weight scales")
+    assert_bits_equal(host_codes(q), q_ref, "edge weight codes")
+    assert_bits_equal(host_codes(qt), np.ascontiguousarray(q_ref.T), "edge transposed codes")
+
+
+def test_empty_inputs_are_noops():
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = fq.fp8_quantize_act(x)
+    assert q.shape == (0, 256) and s.shape == (2, 0)
+    w = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    q, s = fq.fp8_quantize_weight(w)
+    assert q.shape == (0, 128)
