@@ -16,18 +16,22 @@
 // accumulator to protect: the FP32 MFMA sum of a slab is already exact-ish,
 // and the interval is set by the scales, not by the hardware.
 //
-// Tiling: 256 (m) x 256 (n) block tile, 8 waves (4 along m x 2 along n),
-// 64 x 128 per wave. Each 128-byte K slab of the A and B tiles is copied
-// global -> LDS by the direct LDS-DMA load (global_load_lds_dwordx4), double
-// buffered, with 16-byte chunks XOR-swizzled by row so that fragment reads
-// are bank-conflict free. The MFMA computes the transposed tile: its row
-// operand is B (n), its column operand is A (m), so every lane holds four
-// consecutive n of one m -- one A scale per lane per m-subtile, and the B
-// block scale is wave-uniform.
+// Tiling: 256 (m) x BN (n) block tiles, BN = 256 or 224, 8 waves (4 along
+// m x 2 along n), 64 x BN/2 per wave. BN = 224 makes N = 7168 (Dgrad, Wgrad)
+// an exact multiple, so those grids are whole waves of the 256 CUs. Each
+// 128-byte K slab of the A and B tiles is copied global -> LDS by the direct
+// LDS-DMA load (global_load_lds_dwordx4), double buffered, with 16-byte
+// chunks XOR-swizzled by row so that fragment reads are bank-conflict free.
+// The MFMA computes the transposed tile: its row operand is B (n), its column
+// operand is A (m), so every lane holds four consecutive n of one m -- one A
+// scale per lane per m-subtile, and the B block scale is wave-uniform per
+// 16-column subtile. Waves whose rows are all past the real rows (grouped
+// padding, ragged M) skip their MFMAs.
 #include "fp8q_device.h"
 #include "launch.h"
 
 #include <type_traits>
+#include <utility>
 
 namespace fp8q {
 namespace {
@@ -38,12 +42,10 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kSlab = 128;  // K elements per promotion interval
 constexpr int kBM = 256;
-constexpr int kBN = 256;
+constexpr int kBNMax = 256;  // LDS is laid out for the widest n tile
 constexpr int kThreads = 512;
 constexpr int kWaveM = 64;
-constexpr int kWaveN = 128;
 constexpr int kMSub = kWaveM / 16;
-constexpr int kNSub = kWaveN / 16;
 
 // LDS map (bytes): A stage 0 | A stage 1 | B stage 0 | B stage 1 |
 //                  sA stage 0 | sA stage 1 | sB stage 0 | sB stage 1.
@@ -52,7 +54,7 @@ constexpr int kOffA = 0;
 constexpr int kOffB = 2 * kTileBytes;
 constexpr int kOffSA = 4 * kTileBytes;
 constexpr int kOffSB = kOffSA + 2 * kBM * 4;
-constexpr int kLdsBytes = kOffSB + 2 * kBN * 4;
+constexpr int kLdsBytes = kOffSB + 2 * kBNMax * 4;
 
 // Physical 16-byte chunk of logical chunk c in LDS row `row`.
 __device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ (row & 7); }
@@ -89,9 +91,10 @@ struct TileRows {
 // Dense tile order: block -> XCD x = block % 8 gets the contiguous slot
 // range [x*per, (x+1)*per); slots walk 4-row bands of tiles so the blocks
 // resident on one XCD share A and B panels in its L2.
+template <int BN>
 __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
     const int tiles_m = (int)((p.m + kBM - 1) / kBM);
-    const int tiles_n = (int)((p.n + kBN - 1) / kBN);
+    const int tiles_n = (int)((p.n + BN - 1) / BN);
     const int total = tiles_m * tiles_n;
     const int per = (total + 7) / 8;
     const int slot = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
@@ -106,7 +109,7 @@ __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
     t.m0 = (int64_t)tm * kBM;
     t.row_hi = p.m;
     t.real_end = p.m;
-    t.n0 = (int64_t)tn * kBN;
+    t.n0 = (int64_t)tn * BN;
     t.b = p.b;
     t.b_scale = p.b_scale;
     return true;
@@ -116,8 +119,9 @@ __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
 // 256-row m-tiles (the last may hold only 128 rows); slots run expert-major,
 // then n-tile, then m-tile, so consecutive slots on one XCD reuse the same
 // 256 x K panel of W_e.
+template <int BN>
 __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
-    const int tiles_n = (int)(p.n / kBN + (p.n % kBN != 0));
+    const int tiles_n = (int)((p.n + BN - 1) / BN);
     int total = 0;
     for (int e = 0; e < p.groups; ++e) {
         const int seg = p.group_offsets[e + 1] - p.group_offsets[e];
@@ -137,7 +141,7 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
             t.row_hi = min(min((int64_t)end, t.m0 + kBM), p.m);
             const int real = p.group_rows ? p.group_rows[e] : end - beg;
             t.real_end = beg + (int64_t)real;
-            t.n0 = (int64_t)tn * kBN;
+            t.n0 = (int64_t)tn * BN;
             t.b = p.b + e * p.stride_b;
             t.b_scale = p.b_scale + e * p.stride_bs;
             return true;
@@ -153,34 +157,36 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
 // of the next slab) before any LDS read, serialising load and compute. The
 // DMA of a stage is fenced explicitly (vmcnt(0) + barrier) before it is read.
 
-// A fragments of the four m-subtiles plus the lane's four A scales and the
-// wave's B block scale (or, with per-row B scales, an unused value).
+// A fragments of the four m-subtiles, the lane's four A scales, and the two
+// B block scales the wave can touch (with per-row B scaling: unused values).
 template <int ST>
 __device__ __forceinline__ void read_a_frags(uint32_t v0, uint32_t v1, uint32_t vs, uint32_t vsb,
-                                             v8i (&am)[kMSub], float (&sa)[kMSub], float& sb) {
+                                             v8i (&am)[kMSub], float (&sa)[kMSub], float& sb0,
+                                             float& sb1) {
     v4i l0, h0, l1, h1, l2, h2, l3, h3;
-    float f0, f1, f2, f3, fb;
+    float f0, f1, f2, f3, fb0, fb1;
     asm volatile(
-        "ds_read_b128 %0, %13 offset:%15\n\t"
-        "ds_read_b128 %1, %14 offset:%15\n\t"
-        "ds_read_b128 %2, %13 offset:%16\n\t"
-        "ds_read_b128 %3, %14 offset:%16\n\t"
-        "ds_read_b128 %4, %13 offset:%17\n\t"
-        "ds_read_b128 %5, %14 offset:%17\n\t"
-        "ds_read_b128 %6, %13 offset:%18\n\t"
-        "ds_read_b128 %7, %14 offset:%18\n\t"
-        "ds_read_b32 %8, %19 offset:%20\n\t"
-        "ds_read_b32 %9, %19 offset:%21\n\t"
-        "ds_read_b32 %10, %19 offset:%22\n\t"
-        "ds_read_b32 %11, %19 offset:%23\n\t"
-        "ds_read_b32 %12, %24 offset:%25\n\t"
+        "ds_read_b128 %0, %14 offset:%16\n\t"
+        "ds_read_b128 %1, %15 offset:%16\n\t"
+        "ds_read_b128 %2, %14 offset:%17\n\t"
+        "ds_read_b128 %3, %15 offset:%17\n\t"
+        "ds_read_b128 %4, %14 offset:%18\n\t"
+        "ds_read_b128 %5, %15 offset:%18\n\t"
+        "ds_read_b128 %6, %14 offset:%19\n\t"
+        "ds_read_b128 %7, %15 offset:%19\n\t"
+        "ds_read_b32 %8, %20 offset:%21\n\t"
+        "ds_read_b32 %9, %20 offset:%22\n\t"
+        "ds_read_b32 %10, %20 offset:%23\n\t"
+        "ds_read_b32 %11, %20 offset:%24\n\t"
+        "ds_read_b32 %12, %25 offset:%26\n\t"
+        "ds_read_b32 %13, %25 offset:%27\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3),
-          "=&v"(f0), "=&v"(f1), "=&v"(f2), "=&v"(f3), "=&v"(fb)
+          "=&v"(f0), "=&v"(f1), "=&v"(f2), "=&v"(f3), "=&v"(fb0), "=&v"(fb1)
         : "v"(v0), "v"(v1), "n"(ST * kTileBytes + 0 * 2048), "n"(ST * kTileBytes + 1 * 2048),
           "n"(ST * kTileBytes + 2 * 2048), "n"(ST * kTileBytes + 3 * 2048), "v"(vs),
           "n"(ST * kBM * 4 + 0), "n"(ST * kBM * 4 + 64), "n"(ST * kBM * 4 + 128),
-          "n"(ST * kBM * 4 + 192), "v"(vsb), "n"(ST * kBN * 4)
+          "n"(ST * kBM * 4 + 192), "v"(vsb), "n"(ST * kBNMax * 4), "n"(ST * kBNMax * 4 + 4)
         : "memory");
     am[0] = __builtin_shufflevector(l0, h0, 0, 1, 2, 3, 4, 5, 6, 7);
     am[1] = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -190,7 +196,8 @@ __device__ __forceinline__ void read_a_frags(uint32_t v0, uint32_t v1, uint32_t 
     sa[1] = f1;
     sa[2] = f2;
     sa[3] = f3;
-    sb = fb;
+    sb0 = fb0;
+    sb1 = fb1;
 }
 
 // A B fragment in flight: issued by issue_b_frag, completed by wait_b_frag.
@@ -203,13 +210,13 @@ struct BFrag {
 
 template <bool ROWSCALE, int ST, int T>
 __device__ __forceinline__ void issue_b_frag(uint32_t v0, uint32_t v1, uint32_t vs, BFrag& f) {
-    if (ROWSCALE) {
+    if constexpr (ROWSCALE) {
         asm volatile(
             "ds_read_b128 %0, %3 offset:%5\n\t"
             "ds_read_b128 %1, %4 offset:%5\n\t"
             "ds_read_b128 %2, %6 offset:%7"
             : "=&v"(f.lo), "=&v"(f.hi), "=&v"(f.sb)
-            : "v"(v0), "v"(v1), "n"(ST * kTileBytes + T * 2048), "v"(vs), "n"(ST * kBN * 4 + T * 64)
+            : "v"(v0), "v"(v1), "n"(ST * kTileBytes + T * 2048), "v"(vs), "n"(ST * kBNMax * 4 + T * 64)
             : "memory");
     } else {
         asm volatile(
@@ -223,7 +230,7 @@ __device__ __forceinline__ void issue_b_frag(uint32_t v0, uint32_t v1, uint32_t 
 
 template <bool ROWSCALE>
 __device__ __forceinline__ void wait_b_frag(BFrag& f) {
-    if (ROWSCALE)
+    if constexpr (ROWSCALE)
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.lo), "+v"(f.hi), "+v"(f.sb) : : "memory");
     else
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.lo), "+v"(f.hi) : : "memory");
@@ -233,27 +240,40 @@ __device__ __forceinline__ void wait_dma_and_barrier() {
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <int... Is, class F>
+__device__ __forceinline__ void unroll(std::integer_sequence<int, Is...>, F&& f) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+
 // ---------------------------------------------------------------- the kernel
 
-template <bool ROWSCALE, bool OUT_F32, bool GROUPED>
+template <int BN, bool ROWSCALE, bool OUT_F32, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
+    static_assert(BN == 256 || BN == 224, "n tile");
+    constexpr int WN = BN / 2;        // n extent of one wave
+    constexpr int NSUB = WN / 16;     // n-subtiles per wave
+    // With 224-wide tiles a wave's 112 columns can straddle two 128-wide
+    // weight blocks; each 16-column subtile still lies inside one block.
+    constexpr bool STRADDLE = !ROWSCALE && (WN % 128 != 0);
+
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
 
     TileRows tr;
-    if (GROUPED ? !grouped_tile(p, tr) : !dense_tile(p, tr)) return;
+    if (GROUPED ? !grouped_tile<BN>(p, tr) : !dense_tile<BN>(p, tr)) return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int slabs = (int)(p.k / kSlab);
-    const int64_t m_last = (GROUPED ? p.m : p.m) - 1;
+    const int64_t m_last = p.m - 1;
     const int64_t n_last = p.n - 1;
 
     // ---- LDS-DMA sources: wave w copies rows [32w, 32w+32) of both tiles,
     // 8 rows (1 KB) per instruction; lane l -> row 8i + l/8, chunk l%8.
-    // Addresses are a wave-uniform base (tile origin + slab) plus a 32-bit
-    // per-lane offset, which maps onto the saddr + voffset load form.
+    // Rows past the tile or the matrix are clamped to valid rows (loaded,
+    // never used). Addresses are a wave-uniform base (tile origin + slab) plus
+    // a 32-bit per-lane offset, which maps onto the saddr + voffset form.
     const uint8_t* const tileA = p.a + tr.m0 * p.lda;
     const uint8_t* const tileB = tr.b + tr.n0 * p.ldb;
     uint32_t offA[4], offB[4];
@@ -262,12 +282,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         const int row = 32 * wave + 8 * i + (lane >> 3);
         const int chunk = swz_chunk(lane & 7, row);
         offA[i] = (uint32_t)((min(tr.m0 + row, m_last) - tr.m0) * p.lda) + chunk * 16;
-        offB[i] = (uint32_t)((min(tr.n0 + row, n_last) - tr.n0) * p.ldb) + chunk * 16;
+        offB[i] = (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + chunk * 16;
     }
     // Scales: waves 0-3 copy the slab's 256 A scales (64 each) into the sA
     // area. Waves 4-7 copy B scales into the sB area: with per-row scaling the
-    // slab's 256 B scales (64 each); with 128x128 blocks, lane l copies the
-    // scale of n-block (n0/128 + l%2) (only wave 4's first two are read).
+    // slab's B scales (64 each); with 128x128 blocks, lane l copies the scale
+    // of n-block (n0/128 + l%4), the at most three blocks a tile touches.
     const float* scale_base;
     int64_t ld_s;
     uint32_t offS;
@@ -278,11 +298,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     } else if (ROWSCALE) {
         scale_base = tr.b_scale + tr.n0;
         ld_s = p.ld_bs;
-        offS = (uint32_t)(min(tr.n0 + 64 * (wave - 4) + lane, n_last) - tr.n0) * 4u;
+        offS = (uint32_t)(min(tr.n0 + min(64 * (wave - 4) + lane, BN - 1), n_last) - tr.n0) * 4u;
     } else {
         scale_base = tr.b_scale;
         ld_s = 1;
-        offS = (uint32_t)(min(tr.n0 / 128 + (lane & 1), n_last / 128) * p.ld_bs) * 4u;
+        offS = (uint32_t)(min(tr.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
     }
     const int lds_s = wave < 4 ? kOffSA + 64 * 4 * wave : kOffSB + 64 * 4 * (wave - 4);
 
@@ -308,120 +328,146 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     const uint32_t off1 = fi * kSlab + swz_chunk(2 * fg + 1, fi) * 16;
     const uint32_t vA0 = lds0 + kOffA + wm * kWaveM * kSlab + off0;
     const uint32_t vA1 = lds0 + kOffA + wm * kWaveM * kSlab + off1;
-    const uint32_t vB0 = lds0 + kOffB + wn * kWaveN * kSlab + off0;
-    const uint32_t vB1 = lds0 + kOffB + wn * kWaveN * kSlab + off1;
+    const uint32_t vB0 = lds0 + kOffB + wn * WN * kSlab + off0;
+    const uint32_t vB1 = lds0 + kOffB + wn * WN * kSlab + off1;
     const uint32_t vSA = lds0 + kOffSA + (wm * kWaveM + fi) * 4;
-    const uint32_t vSB = lds0 + kOffSB + (wn * kWaveN + 4 * fg) * 4;
-    // The wave's 128 n rows are exactly one 128x128 weight block (n-block wn
-    // of the tile), whose scale wave 4 copied to sB[wn].
-    const uint32_t vSBblk = lds0 + kOffSB + wn * 4;
+    const uint32_t vSB = lds0 + kOffSB + (wn * WN + 4 * fg) * 4;
+    // Block scales: the wave's first column lies in n-block nb0; sB holds the
+    // tile's blocks from n0/128 on. Subtiles T < split are in nb0, the rest in
+    // nb0 + 1 (only possible when STRADDLE).
+    const int64_t wcol = tr.n0 + wn * WN;
+    const int nb_rel = (int)(wcol / 128 - tr.n0 / 128);
+    const uint32_t vSBblk = lds0 + kOffSB + nb_rel * 4;
+    const int split = (int)((128 - (wcol & 127)) / 16);
 
-    v4f acc[kNSub][kMSub];
+    // Real rows of the wave (grouped padding, ragged M): m-subtiles past them
+    // skip their MFMAs. act is wave-uniform.
+    const int64_t wrow = tr.m0 + wm * kWaveM;
+    const int64_t live = min(tr.real_end, tr.row_hi) - wrow;
+    const int act = (int)max((int64_t)0, min((int64_t)kMSub, (live + 15) / 16));
+
+    v4f acc[NSUB][kMSub];
 #pragma unroll
-    for (int t = 0; t < kNSub; ++t)
+    for (int t = 0; t < NSUB; ++t)
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) acc[t][s] = v4f{0.f, 0.f, 0.f, 0.f};
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    auto step = [&](auto stage_tag, int j) {
+    // One slab of MFMAs + promotion for the first ACT m-subtiles of the wave.
+    auto compute = [&](auto stage_tag, auto act_tag) {
         constexpr int ST = decltype(stage_tag)::value;
-        wait_dma_and_barrier();
-        // Prefetch the next slab into the other stage. The last step re-loads
-        // its own slab there instead (never read), keeping the body branch-free.
-        issue(min(j + 1, slabs - 1), ST ^ 1);
+        constexpr int ACT = decltype(act_tag)::value;
         v8i am[kMSub];
-        float sa[kMSub], sb;
-        read_a_frags<ST>(vA0, vA1, vSA, vSBblk, am, sa, sb);
-        float sab[kMSub];
+        float sa[kMSub], sb0, sb1;
+        read_a_frags<ST>(vA0, vA1, vSA, vSBblk, am, sa, sb0, sb1);
+        float sab0[kMSub], sab1[kMSub];
 #pragma unroll
-        for (int s = 0; s < kMSub; ++s) sab[s] = sa[s] * sb;
-
-        // Software pipeline over the 8 n-subtiles: while the MFMAs of subtile
-        // T run, the fragment of T+1 is in flight and the partials of T-1 are
+        for (int s = 0; s < kMSub; ++s) {
+            sab0[s] = sa[s] * sb0;
+            if constexpr (STRADDLE) sab1[s] = sa[s] * sb1;
+        }
+        // Software pipeline over the n-subtiles: while the MFMAs of subtile T
+        // run, the fragment of T+1 is in flight and the partials of T-1 are
         // promoted (acc += P * sA * sB), one FMA group after each MFMA.
         BFrag fr[2];
         v4f pc[kMSub], pp[kMSub];
         v4f sbp;
+        auto promote = [&](auto t_tag, const v4f& sbn) {
+            constexpr int T = decltype(t_tag)::value;
+#pragma unroll
+            for (int s = 0; s < ACT; ++s) {
+                if constexpr (ROWSCALE) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        acc[T][s][r] = __builtin_fmaf(pp[s][r], sa[s] * sbn[r], acc[T][s][r]);
+                } else {
+                    float f = sab0[s];
+                    if constexpr (STRADDLE) f = T < split ? sab0[s] : sab1[s];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[T][s][r] = __builtin_fmaf(pp[s][r], f, acc[T][s][r]);
+                }
+            }
+        };
         issue_b_frag<ROWSCALE, ST, 0>(vB0, vB1, vSB, fr[0]);
-        auto tile = [&](auto t_tag) {
+        unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
             constexpr int T = decltype(t_tag)::value;
             BFrag& cur = fr[T & 1];
             wait_b_frag<ROWSCALE>(cur);
-            if (T + 1 < kNSub) issue_b_frag<ROWSCALE, ST, (T + 1) % kNSub>(vB0, vB1, vSB, fr[(T + 1) & 1]);
+            if constexpr (T + 1 < NSUB)
+                issue_b_frag<ROWSCALE, ST, T + 1>(vB0, vB1, vSB, fr[(T + 1) & 1]);
             const v8i bf = __builtin_shufflevector(cur.lo, cur.hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-            for (int s = 0; s < kMSub; ++s) {
+            for (int s = 0; s < ACT; ++s)
                 pc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], zero, 0, 0, 0, 0, 0, 0);
-                if constexpr (T > 0) {
-                    if (ROWSCALE) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[T - 1][s][r] = __builtin_fmaf(pp[s][r], sa[s] * sbp[r], acc[T - 1][s][r]);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[T - 1][s][r] = __builtin_fmaf(pp[s][r], sab[s], acc[T - 1][s][r]);
-                    }
-                }
-            }
             if constexpr (T > 0) {
-                // one MFMA, then the FMA group of one m-subtile, four times
+                promote(std::integral_constant<int, T - 1>{}, sbp);
+                // one MFMA, then the FMA group of one m-subtile, ACT times
 #pragma unroll
-                for (int s = 0; s < kMSub; ++s) {
+                for (int s = 0; s < ACT; ++s) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, ROWSCALE ? 8 : 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, ROWSCALE ? 8 : (STRADDLE ? 5 : 4), 0);
                 }
             }
 #pragma unroll
-            for (int s = 0; s < kMSub; ++s) pp[s] = pc[s];
+            for (int s = 0; s < ACT; ++s) pp[s] = pc[s];
             sbp = cur.sb;
             __builtin_amdgcn_sched_barrier(0);
-        };
-        tile(std::integral_constant<int, 0>{});
-        tile(std::integral_constant<int, 1>{});
-        tile(std::integral_constant<int, 2>{});
-        tile(std::integral_constant<int, 3>{});
-        tile(std::integral_constant<int, 4>{});
-        tile(std::integral_constant<int, 5>{});
-        tile(std::integral_constant<int, 6>{});
-        tile(std::integral_constant<int, 7>{});
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) {
-            if (ROWSCALE) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[kNSub - 1][s][r] = __builtin_fmaf(pp[s][r], sa[s] * sbp[r], acc[kNSub - 1][s][r]);
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[kNSub - 1][s][r] = __builtin_fmaf(pp[s][r], sab[s], acc[kNSub - 1][s][r]);
-            }
-        }
+        });
+        promote(std::integral_constant<int, NSUB - 1>{}, sbp);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (slabs > 0) issue(0, 0);
-    int j = 0;
-    for (; j + 2 <= slabs; j += 2) {
-        step(std::integral_constant<int, 0>{}, j);
-        step(std::integral_constant<int, 1>{}, j + 1);
+    // The K loop for a wave with ACT live m-subtiles (ACT = 0: the wave only
+    // does its share of the copies and the barriers).
+    auto mainloop = [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;
+        auto step = [&](auto stage_tag, int j) {
+            constexpr int ST = decltype(stage_tag)::value;
+            wait_dma_and_barrier();
+            // Prefetch the next slab into the other stage. The last step
+            // re-loads its own slab there instead (never read), keeping the
+            // body branch-free.
+            issue(min(j + 1, slabs - 1), ST ^ 1);
+            if constexpr (ACT > 0) compute(stage_tag, act_tag);
+        };
+        if (slabs > 0) issue(0, 0);
+        int j = 0;
+        for (; j + 2 <= slabs; j += 2) {
+            step(std::integral_constant<int, 0>{}, j);
+            step(std::integral_constant<int, 1>{}, j + 1);
+        }
+        if (j < slabs) step(std::integral_constant<int, 0>{}, j);
+    };
+    if constexpr (GROUPED) {
+        // expert tails: only the live m-subtiles do MFMA work
+        switch (act) {
+            case 4: mainloop(std::integral_constant<int, 4>{}); break;
+            case 3: mainloop(std::integral_constant<int, 3>{}); break;
+            case 2: mainloop(std::integral_constant<int, 2>{}); break;
+            case 1: mainloop(std::integral_constant<int, 1>{}); break;
+            default: mainloop(std::integral_constant<int, 0>{}); break;
+        }
+    } else if (act > 0) {
+        mainloop(std::integral_constant<int, 4>{});  // ragged-M rows are computed and dropped
+    } else {
+        mainloop(std::integral_constant<int, 0>{});
     }
-    if (j < slabs) step(std::integral_constant<int, 0>{}, j);
     // Drain the last (unused) prefetch before the block's LDS can be reused.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
 #pragma unroll
     for (int s = 0; s < kMSub; ++s) {
-        const int64_t m = tr.m0 + wm * kWaveM + s * 16 + fi;
+        const int64_t m = wrow + s * 16 + fi;
         if (m >= tr.row_hi) continue;
         const bool pad = m >= tr.real_end;
 #pragma unroll
-        for (int t = 0; t < kNSub; ++t) {
-            const int64_t n = tr.n0 + wn * kWaveN + t * 16 + 4 * fg;
+        for (int t = 0; t < NSUB; ++t) {
+            const int64_t n = wcol + t * 16 + 4 * fg;
+            if (n >= tr.n0 + BN) continue;
             v4f v = pad ? zero : acc[t][s];
-            if (OUT_F32) {
+            if constexpr (OUT_F32) {
                 float* dst = reinterpret_cast<float*>(p.c) + m * p.ldc + n;
                 if (n + 3 < p.n) {
                     *reinterpret_cast<v4f*>(dst) = v;
@@ -470,37 +516,50 @@ Params to_params(const GemmProblem& g) {
     return p;
 }
 
-template <bool GROUPED>
+template <int BN, bool GROUPED>
 hipError_t dispatch(const GemmProblem& g, int64_t slots, hipStream_t stream) {
     const Params p = to_params(g);
     const int64_t blocks = (slots + 7) / 8 * 8;
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (g.b_rowscale) {
         if (g.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<true, true, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, true, true, GROUPED>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<true, false, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, true, false, GROUPED>), grid, block, 0, stream, p);
     } else {
         if (g.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<false, true, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, false, true, GROUPED>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<false, false, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, false, false, GROUPED>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
+}
+
+// Time of a dense grid in units of one 256-wide tile's work: the number of
+// rounds of the 256 CUs times the tile width (all tiles share K and BM).
+int64_t grid_cost(int64_t m, int64_t n, int64_t bn) {
+    const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + bn - 1) / bn);
+    return (tiles + 255) / 256 * bn;
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem& g, hipStream_t stream) {
-    const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + kBN - 1) / kBN);
-    return dispatch<false>(g, tiles, stream);
+    // 224-wide n tiles when the grid then takes less time on the 256 CUs,
+    // e.g. N = 7168 = 32 x 224 (Dgrad, Wgrad); otherwise 256-wide.
+    if (grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256)) {
+        const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
+        return dispatch<224, false>(g, tiles, stream);
+    }
+    const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
+    return dispatch<256, false>(g, tiles, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& g, hipStream_t stream) {
     // Upper bound on the tile count: every 256-row m-tile of an expert holds at
     // least 128 of its rows, so there are at most m_total / 128 of them.
-    const int64_t tiles = (g.m / 128) * ((g.n + kBN - 1) / kBN);
-    return dispatch<true>(g, tiles, stream);
+    const int64_t tiles = (g.m / 128) * ((g.n + 255) / 256);
+    return dispatch<256, true>(g, tiles, stream);
 }
 
 }  // namespace fp8q

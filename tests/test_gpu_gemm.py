@@ -93,7 +93,7 @@ def test_wgrad_full_size():
 # ------------------------------------------------------------ ragged / edge
 
 @pytest.mark.parametrize("m,n,k", [(1, 128, 128), (17, 384, 384), (300, 256, 256), (257, 640, 640),
-                                   (513, 128, 1024)])
+                                   (513, 128, 1024), (4000, 3968, 256)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_block_scaled_ragged(m, n, k, out):
     x = wl.activation(2, "tiny_fprop", 30, m, k, 100.0)
@@ -103,7 +103,8 @@ def test_block_scaled_ragged(m, n, k, out):
     _check_full(a_q, a_s, b_q, b_s, "block", out, "block m=%d n=%d k=%d %s" % (m, n, k, out))
 
 
-@pytest.mark.parametrize("m,n,tokens", [(1, 8, 128), (200, 72, 256), (130, 264, 384), (256, 512, 512)])
+@pytest.mark.parametrize("m,n,tokens", [(1, 8, 128), (200, 72, 256), (130, 264, 384), (256, 512, 512),
+                                        (4000, 3992, 256)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_row_scaled_ragged(m, n, tokens, out):
     dy = wl.activation(2, "wgrad", 32, tokens, m, None)
