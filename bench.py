@@ -1,20 +1,32 @@
 """Benchmark of the fine-grained FP8 hot path on one MI355X.
 
 One step is one pass of the path over one batch of seeded synthetic input
-already resident in HBM: quantize the activations (1x128 tiles), quantize the
-weights (128x128 blocks), and run the block-scaled FP8 GEMM with bf16 output.
-The default workload is the dense Fprop layer X[4096][7168] x W[4096][7168]^T.
+already resident in HBM: quantize the operands (activations in 1x128 tiles,
+weights in 128x128 blocks, or both Wgrad operands in 128x1 tiles) and run the
+block-scaled FP8 GEMM. The default workload is the dense Fprop layer
+X[4096][7168] x W[4096][7168]^T with bf16 output.
 
-Prints ONE JSON line with the whole-step throughput in TFLOP/s (2*M*N*K per
-step), the GEMM kernel's roofline (its own launches timed with HIP events on
-the launch stream inside the timed region) and the CPU oracle timed on the
-host as a reported baseline.
+Prints ONE JSON line: the whole-step throughput in TFLOP/s (2*M*N*K per step),
+the GEMM kernel's roofline (its launches timed with HIP events on the launch
+stream inside the timed region), every kernel's own time and rate, and the CPU
+oracle timed on the host as a reported baseline.
 
-    python bench.py [--steps K] [--warmup W] [--config dense_fprop|dgrad|wgrad|grouped_fprop]
+    python bench.py [--steps K] [--warmup W]
+                    [--config dense_fprop|dgrad|wgrad|grouped_fprop|tiny_fprop]
+
+Counter runs (HBM traffic of each kernel, from rocprofv3 FETCH_SIZE and
+WRITE_SIZE; a plain copy of known size calibrates each counter):
+
+    rocprofv3 --pmc FETCH_SIZE -d OUT -o fetch --output-format csv -- \
+        python bench.py --steps 3 --warmup 1 --prewarm-s 0 --no-cpu-baseline --copy-probe-mib 256
+    (same with WRITE_SIZE and -o write)
+    python bench.py --pmc-summary OUT/fetch_counter_collection.csv OUT/write_counter_collection.csv
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -24,148 +36,201 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
-HBM_PEAK_GBS = 8000.0
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak (1 GPU)"
+CONFIGS = ["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "tiny_fprop"]
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+# Kernel name fragments (as rocprofv3 prints them) for each launch label.
+KERNEL_NAMES = {
+    "quant_act_1x128": "quant_act_1x128_kernel",
+    "quant_act_128x1": "quant_act_128x1_kernel",
+    "quant_weight": "quant_weight_kernel",
+    "gemm": "gemm_kernel",
+}
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources; stored counter figures are valid only for
+    the kernels they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fine_grained_fp8_quantize_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="dense_fprop",
-                    choices=["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "tiny_fprop"])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warmup steps (clock ramp)")
+    ap.add_argument("--config", default="dense_fprop", choices=CONFIGS)
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="bf16 input sets cycled over the steps, so that the inputs of one "
+                         "step are not left in the 256 MiB MALL by the step before")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
-                    help="HBM bytes per GEMM launch from rocprofv3 counters (see DESIGN.md)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one device copy of this size first (counter calibration)")
+    ap.add_argument("--traffic-json", default=TRAFFIC_JSON)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter CSVs of this script into --traffic-json")
     return ap.parse_args()
+
+
+class Launch:
+    """One kernel launch of the step with its algorithmic cost."""
+
+    def __init__(self, label, fn, nbytes, flops=0.0):
+        self.label, self.fn, self.bytes, self.flops = label, fn, float(nbytes), float(flops)
 
 
 class Workload:
     """Inputs on the GPU plus preallocated outputs; step() enqueues one pass."""
 
-    def __init__(self, name: str):
+    def __init__(self, name: str, rotate: int = 1):
         import numpy as np
         import torch
 
         import fine_grained_fp8_quantize_amd as fq
         import workloads as wl
 
-        self.fq, self.torch, self.name = fq, torch, name
+        self.torch, self.name = torch, name
+        u8, f32, bf16 = torch.uint8, torch.float32, torch.bfloat16
 
         def dev(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(bf16).cuda()
+
+        def empty(shape, dt):
+            return torch.empty(shape, dtype=dt, device="cuda")
+
+        def sets(bits):
+            # `rotate` device copies of one bf16 input; step i reads copy i % rotate
+            t = dev(bits)
+            return [t] + [t.clone() for _ in range(rotate - 1)]
+
+        def act_bytes(r, c):       # bf16 in, codes + one fp32 scale per 128 values out
+            return 2 * r * c + r * c + 4 * r * c // 128
+
+        def gemm_bytes(m_a, n, k, b_scale_count, out_elem, m_out):
+            return m_a * k + n * k + 4 * m_a * (k // 128) + 4 * b_scale_count + out_elem * m_out * n
 
         self.host = None
         if name in ("dense_fprop", "tiny_fprop"):
             d = wl.dense_fprop() if name == "dense_fprop" else wl.tiny_fprop()
             self.host = d
-            self.x, self.w = dev(d["x"]), dev(d["w"])
-            m, k = self.x.shape
-            n = self.w.shape[0]
-            self.m, self.n, self.k = m, n, k
+            X, W = sets(d["x"]), sets(d["w"])
+            m, k = X[0].shape
+            n = W[0].shape[0]
+            xq, xs = empty((m, k), u8), empty((k // 128, m), f32)
+            wq, ws = empty((n, k), u8), empty((n // 128, k // 128), f32)
+            y = empty((m, n), bf16)
             self.flops = 2.0 * m * n * k
-            self.xq = torch.empty((m, k), dtype=torch.uint8, device="cuda")
-            self.xs = torch.empty((k // 128, m), dtype=torch.float32, device="cuda")
-            self.wq = torch.empty((n, k), dtype=torch.uint8, device="cuda")
-            self.ws = torch.empty((n // 128, k // 128), dtype=torch.float32, device="cuda")
-            self.y = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
-            self.desc = {"workload": name, "m": m, "n": n, "k": k, "x": "bf16 1x128 tiles",
-                         "w": "bf16 128x128 blocks", "out": "bf16"}
+            self.launches = [
+                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(X[r], "1x128", q=xq, scale=xs),
+                       act_bytes(m, k)),
+                Launch("quant_weight", lambda r: fq.fp8_quantize_weight(W[r], q=wq, scale=ws),
+                       3 * n * k + 4 * (n // 128) * (k // 128)),
+                Launch("gemm", lambda r: fq.fp8_gemm(xq, xs, wq, ws, "block", bf16, out=y),
+                       gemm_bytes(m, n, k, (n // 128) * (k // 128), 2, m), self.flops),
+            ]
+            self.desc = {"workload": name, "m": m, "n": n, "k": k, "x": "bf16, 1x128 tiles",
+                         "w": "bf16, 128x128 blocks", "out": "bf16"}
         elif name == "dgrad":
             d = wl.dgrad()
-            self.dy, self.w = dev(d["dy"]), dev(d["w"])
-            m, n_out = self.dy.shape
-            k_in = self.w.shape[1]
-            self.m, self.n, self.k = m, k_in, n_out
+            DY, W = sets(d["dy"]), sets(d["w"])
+            m, n_out = DY[0].shape
+            k_in = W[0].shape[1]
+            dq, ds = empty((m, n_out), u8), empty((n_out // 128, m), f32)
+            wq, ws = empty((n_out, k_in), u8), empty((n_out // 128, k_in // 128), f32)
+            wqt, wst = empty((k_in, n_out), u8), empty((k_in // 128, n_out // 128), f32)
+            y = empty((m, k_in), bf16)
             self.flops = 2.0 * m * k_in * n_out
-            self.dq = torch.empty((m, n_out), dtype=torch.uint8, device="cuda")
-            self.ds = torch.empty((n_out // 128, m), dtype=torch.float32, device="cuda")
-            self.wq = torch.empty((n_out, k_in), dtype=torch.uint8, device="cuda")
-            self.ws = torch.empty((n_out // 128, k_in // 128), dtype=torch.float32, device="cuda")
-            self.wqt = torch.empty((k_in, n_out), dtype=torch.uint8, device="cuda")
-            self.wst = torch.empty((k_in // 128, n_out // 128), dtype=torch.float32, device="cuda")
-            self.y = torch.empty((m, k_in), dtype=torch.bfloat16, device="cuda")
-            self.desc = {"workload": name, "m": m, "n": k_in, "k": n_out, "out": "bf16"}
+            nb = (n_out // 128) * (k_in // 128)
+            self.launches = [
+                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(DY[r], "1x128", q=dq, scale=ds),
+                       act_bytes(m, n_out)),
+                Launch("quant_weight", lambda r: fq.fp8_quantize_weight(
+                    W[r], transposed=True, q=wq, scale=ws, q_t=wqt, scale_t=wst),
+                       4 * n_out * k_in + 8 * nb),
+                Launch("gemm", lambda r: fq.fp8_gemm(dq, ds, wqt, wst, "block", bf16, out=y),
+                       gemm_bytes(m, k_in, n_out, nb, 2, m), self.flops),
+            ]
+            self.desc = {"workload": name, "m": m, "n": k_in, "k": n_out,
+                         "dy": "bf16, 1x128 tiles", "w": "bf16, 128x128 blocks, transposed copy",
+                         "out": "bf16"}
         elif name == "wgrad":
             d = wl.wgrad()
-            self.dy, self.x = dev(d["dy"]), dev(d["x"])
-            t, n_out = self.dy.shape
-            k_in = self.x.shape[1]
-            self.m, self.n, self.k = n_out, k_in, t
+            DY, X = sets(d["dy"]), sets(d["x"])
+            t, n_out = DY[0].shape
+            k_in = X[0].shape[1]
+            aq, as_ = empty((n_out, t), u8), empty((t // 128, n_out), f32)
+            bq, bs = empty((k_in, t), u8), empty((t // 128, k_in), f32)
+            y = empty((n_out, k_in), f32)
             self.flops = 2.0 * n_out * k_in * t
-            self.aq = torch.empty((n_out, t), dtype=torch.uint8, device="cuda")
-            self.as_ = torch.empty((t // 128, n_out), dtype=torch.float32, device="cuda")
-            self.bq = torch.empty((k_in, t), dtype=torch.uint8, device="cuda")
-            self.bs = torch.empty((t // 128, k_in), dtype=torch.float32, device="cuda")
-            self.y = torch.empty((n_out, k_in), dtype=torch.float32, device="cuda")
-            self.desc = {"workload": name, "m": n_out, "n": k_in, "k": t, "out": "fp32"}
+            self.launches = [
+                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
+                       act_bytes(t, n_out)),
+                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(X[r], "128x1", q=bq, scale=bs),
+                       act_bytes(t, k_in)),
+                Launch("gemm", lambda r: fq.fp8_gemm(aq, as_, bq, bs, "row", f32, out=y),
+                       gemm_bytes(n_out, k_in, t, k_in * (t // 128), 4, n_out), self.flops),
+            ]
+            self.desc = {"workload": name, "m": n_out, "n": k_in, "k": t,
+                         "dy, x": "bf16, 128x1 tiles (along tokens)", "out": "fp32"}
         else:  # grouped_fprop
             g = wl.grouped_fprop()
             rows = g["rows"]
-            self.x = dev(g["x"])
+            X = sets(g["x"])
             E, n, k = g["w"].shape
-            self.w = dev(g["w"].reshape(E * n, k))
-            m_total = self.x.shape[0]
-            self.m, self.n, self.k = int(rows.sum()), n, k
-            self.flops = 2.0 * float(rows.sum()) * n * k   # real rows only
-            self.off = torch.from_numpy(g["offsets"].astype("int32")).cuda()
-            self.rows = torch.from_numpy(rows.astype("int32")).cuda()
-            self.xq = torch.empty((m_total, k), dtype=torch.uint8, device="cuda")
-            self.xs = torch.empty((k // 128, m_total), dtype=torch.float32, device="cuda")
-            self.wq = torch.empty((E * n, k), dtype=torch.uint8, device="cuda")
-            self.ws = torch.empty((E * n // 128, k // 128), dtype=torch.float32, device="cuda")
-            self.E = E
-            self.y = torch.empty((m_total, n), dtype=torch.bfloat16, device="cuda")
-            self.desc = {"workload": name, "experts": E, "rows_real": int(rows.sum()),
+            w = dev(g["w"].reshape(E * n, k))   # 1.8 GB: already far beyond the MALL
+            m_total = X[0].shape[0]
+            real = int(rows.sum())
+            off = torch.from_numpy(g["offsets"].astype("int32")).cuda()
+            rws = torch.from_numpy(rows.astype("int32")).cuda()
+            xq, xs = empty((m_total, k), u8), empty((k // 128, m_total), f32)
+            wq, ws = empty((E * n, k), u8), empty((E * n // 128, k // 128), f32)
+            y = empty((m_total, n), bf16)
+            self.flops = 2.0 * real * n * k   # real rows only
+            nb = E * (n // 128) * (k // 128)
+            self.launches = [
+                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(X[r], "1x128", q=xq, scale=xs),
+                       act_bytes(m_total, k)),
+                Launch("quant_weight", lambda r: fq.fp8_quantize_weight(w, q=wq, scale=ws),
+                       3 * E * n * k + 4 * nb),
+                # real rows of A read; every padded row of C written (padding rows are zeroed)
+                Launch("gemm", lambda r: fq.fp8_grouped_gemm(
+                    off, rws, xq, xs, wq.view(E, n, k), ws.view(E, n // 128, k // 128), bf16, out=y),
+                       gemm_bytes(real, E * n, k, nb, 2, 0) + 2 * m_total * n, self.flops),
+            ]
+            self.desc = {"workload": name, "experts": E, "rows_real": real,
                          "rows_padded": m_total, "n": n, "k": k, "out": "bf16"}
+        self.rotate, self.count = rotate, 0
+        self.desc["input_sets"] = rotate
         torch.cuda.synchronize()
 
     def step(self, ev=None):
-        fq, torch = self.fq, self.torch
-        if self.name in ("dense_fprop", "tiny_fprop"):
-            fq.fp8_quantize_act(self.x, "1x128", q=self.xq, scale=self.xs)
-            fq.fp8_quantize_weight(self.w, q=self.wq, scale=self.ws)
-            if ev is not None:
-                ev[0].record()
-            fq.fp8_gemm(self.xq, self.xs, self.wq, self.ws, "block", torch.bfloat16, out=self.y)
-            if ev is not None:
-                ev[1].record()
-        elif self.name == "dgrad":
-            fq.fp8_quantize_act(self.dy, "1x128", q=self.dq, scale=self.ds)
-            fq.fp8_quantize_weight(self.w, transposed=True, q=self.wq, scale=self.ws, q_t=self.wqt,
-                                   scale_t=self.wst)
-            if ev is not None:
-                ev[0].record()
-            fq.fp8_gemm(self.dq, self.ds, self.wqt, self.wst, "block", torch.bfloat16, out=self.y)
-            if ev is not None:
-                ev[1].record()
-        elif self.name == "wgrad":
-            fq.fp8_quantize_act(self.dy, "128x1", q=self.aq, scale=self.as_)
-            fq.fp8_quantize_act(self.x, "128x1", q=self.bq, scale=self.bs)
-            if ev is not None:
-                ev[0].record()
-            fq.fp8_gemm(self.aq, self.as_, self.bq, self.bs, "row", torch.float32, out=self.y)
-            if ev is not None:
-                ev[1].record()
-        else:
-            fq.fp8_quantize_act(self.x, "1x128", q=self.xq, scale=self.xs)
-            fq.fp8_quantize_weight(self.w, q=self.wq, scale=self.ws)
-            if ev is not None:
-                ev[0].record()
-            n, k = self.n, self.k
-            fq.fp8_grouped_gemm(self.off, self.rows, self.xq, self.xs,
-                                self.wq.view(self.E, n, k), self.ws.view(self.E, n // 128, k // 128),
-                                torch.bfloat16, out=self.y)
-            if ev is not None:
-                ev[1].record()
+        """One pass over the next input set; ev (len(launches)+1 events)
+        brackets every launch."""
+        r = self.count % self.rotate
+        self.count += 1
+        if ev is None:
+            for ln in self.launches:
+                ln.fn(r)
+            return
+        ev[0].record()
+        for i, ln in enumerate(self.launches):
+            ln.fn(r)
+            ev[i + 1].record()
 
 
-def cpu_baseline(wl_obj: Workload) -> dict:
+def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 200) -> dict:
     """The oracle, as it stands, on the same Dense Fprop inputs (the whole step)."""
-    import numpy as np
-
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -174,25 +239,100 @@ def cpu_baseline(wl_obj: Workload) -> dict:
         blas_threads = 1
     omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     d = wl_obj.host
-    t0 = time.perf_counter()
-    a_q, a_s = oracle.quant_act_1x128(d["x"])
-    b_q, b_s = oracle.quant_weight_128x128(d["w"])
-    c = oracle.gemm(a_q, a_s, b_q, b_s, "block")
-    dt = time.perf_counter() - t0
-    del c
     m, k = d["x"].shape
     n = d["w"].shape[0]
+    # Whole oracle steps (quantize X, quantize W, float64 GEMM) on the same
+    # inputs, repeated until at least min_seconds of CPU work.
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        a_q, a_s = oracle.quant_act_1x128(d["x"])
+        b_q, b_s = oracle.quant_weight_128x128(d["w"])
+        c = oracle.gemm(a_q, a_s, b_q, b_s, "block")
+        del c
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or steps >= max_steps:
+            break
     return {
-        "value": 2.0 * m * n * k / dt / 1e12,
+        "value": round(2.0 * m * n * k * steps / dt / 1e12, 4),
         "unit": "TFLOP/s",
         "cores": max(omp, blas_threads),
         "kind": "oracle",
         "seconds": round(dt, 3),
-        "sample": "one full step of the workload (X %dx%d 1x128 quantize, W %dx%d 128x128 "
-                  "quantize, float64 dequantize + GEMM), scalar C quantizers with OpenMP and "
-                  "numpy float64 matmul" % (m, k, n, k),
+        "steps": steps,
+        "sample": "%d full steps of the workload (X %dx%d 1x128 quantize, W %dx%d 128x128 "
+                  "quantize, float64 dequantize + GEMM): scalar C quantizers with OpenMP and "
+                  "numpy float64 matmul" % (steps, m, k, n, k),
     }
 
+
+# ---------------------------------------------------------------- counters
+
+def _read_counter_csv(path: str, counter: str):
+    """Dispatches of one rocprofv3 counter CSV: [(dispatch_id, kernel, KiB)]."""
+    rows = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            did = int(r["Dispatch_Id"])
+            name, val = r["Kernel_Name"], float(r["Counter_Value"])
+            rows[did] = (did, name, rows.get(did, (0, name, 0.0))[2] + val)
+    return [rows[d] for d in sorted(rows)]
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, config: str, probe_mib: int, out_json: str,
+                wl_obj: Workload) -> dict:
+    """Per-launch HBM bytes of every kernel of the step from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by the factor that maps what
+    the counter reads for the calibration copy onto the copy's true bytes."""
+    probe = probe_mib * (1 << 20)
+    res = {"kernel_source": kernel_source_digest(), "copy_probe_bytes": probe,
+           "fetch_csv": os.path.basename(fetch_csv), "write_csv": os.path.basename(write_csv)}
+    for counter, path, key in (("FETCH_SIZE", fetch_csv, "fetch"), ("WRITE_SIZE", write_csv, "write")):
+        rows = _read_counter_csv(path, counter)
+        copies = [r for r in rows if "copyBuffer" in r[1]]
+        if not copies:
+            raise SystemExit("no calibration copy in %s (run with --copy-probe-mib)" % path)
+        factor = probe / (copies[0][2] * 1024.0)
+        res[key + "_factor"] = round(factor, 4)
+        for label, frag in KERNEL_NAMES.items():
+            vals = [r[2] for r in rows if frag in r[1]]
+            if vals:
+                ent = res.setdefault("kernels", {}).setdefault(label, {})
+                ent[key + "_bytes"] = round(sum(vals) / len(vals) * 1024.0 * factor)
+                ent["dispatches"] = len(vals)
+    for label, ent in res.get("kernels", {}).items():
+        ent["traffic_bytes"] = ent.get("fetch_bytes", 0) + ent.get("write_bytes", 0)
+        alg = [ln.bytes for ln in wl_obj.launches if ln.label == label]
+        ent["algorithmic_bytes"] = round(sum(alg) / len(alg))
+        ent["ratio"] = round(ent["traffic_bytes"] / ent["algorithmic_bytes"], 3)
+    data = {}
+    try:
+        with open(out_json) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        pass
+    data[config] = res
+    with open(out_json, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return res
+
+
+def stored_traffic(path: str, config: str):
+    """Counter figures for this config, or None when absent or taken on other kernels."""
+    try:
+        with open(path) as f:
+            ent = json.load(f).get(config)
+    except (OSError, ValueError):
+        return None
+    if not ent or ent.get("kernel_source") != kernel_source_digest():
+        return None
+    return ent.get("kernels")
+
+
+# -------------------------------------------------------------------- main
 
 def main():
     args = parse()
@@ -202,14 +342,39 @@ def main():
         sys.exit(2)
     import torch
 
-    wl_obj = Workload(args.config)
+    if args.pmc_summary:
+        wl_obj = Workload(args.config, 1) if torch.cuda.is_available() else None
+        if wl_obj is None:
+            # the algorithmic bytes only need the shapes: build them on the CPU
+            raise SystemExit("--pmc-summary needs the workload shapes; run it on the GPU box")
+        print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config,
+                                     args.copy_probe_mib or 256, args.traffic_json, wl_obj)))
+        return
+
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl_obj = Workload(args.config, max(1, args.rotate))
     stream = torch.cuda.current_stream()
+    # Untimed pre-warm: the GPU ramps its clocks over the first tens of
+    # milliseconds of sustained work; run steps for a while before the W
+    # warmup steps so the timed steps see steady-state clocks.
+    t_pre = time.perf_counter()
+    while time.perf_counter() - t_pre < args.prewarm_s:
+        for _ in range(10):
+            wl_obj.step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         wl_obj.step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    nl = len(wl_obj.launches)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -217,20 +382,31 @@ def main():
     start.record(stream)
     for i in range(args.steps):
         wl_obj.step(evs[i])
+    t_host = time.perf_counter() - t_wall
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(stop) / args.steps
-    gemm_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    per_launch = [sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(nl)]
+    launch_ms = [sum(v) / len(v) for v in per_launch]
 
     value = wl_obj.flops / (ms * 1e-3) / 1e12
-    gemm_tflops = wl_obj.flops / (gemm_ms * 1e-3) / 1e12
-    traffic = None
-    try:
-        with open(args.traffic_json) as f:
-            traffic = json.load(f).get(args.config)
-    except (OSError, ValueError):
-        traffic = None
+    traffic = stored_traffic(args.traffic_json, args.config)
+    kernels = {}
+    for ln, t, v in zip(wl_obj.launches, launch_ms, per_launch):
+        key = ln.label if ln.label not in kernels else ln.label + "_b"
+        ent = {"ms": round(t, 4), "ms_median": round(v[len(v) // 2], 4), "ms_min": round(v[0], 4),
+               "algorithmic_bytes": int(ln.bytes),
+               "hbm_gbs": round(ln.bytes / (t * 1e-3) / 1e9, 1),
+               "hbm_frac": round(ln.bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if ln.flops:
+            ent["tflops"] = round(ln.flops / (t * 1e-3) / 1e12, 2)
+        single = sum(1 for o in wl_obj.launches if o.label == ln.label) == 1
+        if traffic and single and ln.label in traffic:
+            ent["traffic_bytes"] = traffic[ln.label]["traffic_bytes"]
+        kernels[key] = ent
+    gemm = [(ln, t) for ln, t in zip(wl_obj.launches, launch_ms) if ln.label == "gemm"][0]
+    gemm_tflops = gemm[0].flops / (gemm[1] * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -248,18 +424,19 @@ def main():
         "data": "synthetic (seeded; see workloads/)",
         "config": wl_obj.desc,
         "pct_of_fp8_peak": round(100.0 * value / FP8_DENSE_PEAK_TFLOPS, 2),
-        "gemm_ms": round(gemm_ms, 4),
-        "gemm_tflops": round(gemm_tflops, 2),
         "roofline": {
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": FP8_DENSE_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
-            "traffic": traffic,
-            "kernel": "gemm_kernel" if args.config != "grouped_fprop" else "gemm_kernel (grouped)",
+            "traffic": traffic["gemm"]["traffic_bytes"] if traffic and "gemm" in traffic else None,
+            "kernel": "gemm_kernel" + (" (grouped)" if args.config == "grouped_fprop" else ""),
+            "algorithmic_bytes": int(gemm[0].bytes),
         },
+        "kernels": kernels,
         "wall_s": round(t_wall, 3),
+        "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
     }
     if not args.no_cpu_baseline and wl_obj.host is not None:
         out["cpu_baseline"] = cpu_baseline(wl_obj)

@@ -306,19 +306,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     }
     const int lds_s = wave < 4 ? kOffSA + 64 * 4 * wave : kOffSB + 64 * 4 * (wave - 4);
 
-    auto issue = [&](int j, int st) {
+    // Part i (0..3) of this wave's copy of slab j into stage st: 8 rows of
+    // A and 8 rows of B; part 3 also carries the scales. Computing waves
+    // spread the parts over their first n-subtiles, which keeps the LDS-DMA
+    // writes from bunching up behind the barrier.
+    auto issue_part = [&](int j, int st, int i) {
         uint8_t* base_a = smem + kOffA + st * kTileBytes + 32 * wave * kSlab;
         uint8_t* base_b = smem + kOffB + st * kTileBytes + 32 * wave * kSlab;
         const uint8_t* ga = tileA + (int64_t)j * kSlab;
         const uint8_t* gb = tileB + (int64_t)j * kSlab;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_global_load_lds(ga + offA[i], (lds_void*)(base_a + i * 8 * kSlab), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(gb + offB[i], (lds_void*)(base_b + i * 8 * kSlab), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ga + offA[i], (lds_void*)(base_a + i * 8 * kSlab), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(gb + offB[i], (lds_void*)(base_b + i * 8 * kSlab), 16, 0, 0);
+        if (i == 3) {
+            const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
+            __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)(smem + lds_s + st * kBM * 4), 4, 0, 0);
         }
-        const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
-        __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)(smem + lds_s + st * kBM * 4), 4, 0, 0);
     };
+    auto issue = [&](int j, int st) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) issue_part(j, st, i);
+    };
+    int jnext = 0;  // slab the current step prefetches
 
     // ---- fragment addresses: lane (i = l%16, g = l/16) reads 32 bytes of
     // row i at logical chunks 2g and 2g+1 of every 16-row subtile.
@@ -396,6 +404,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             wait_b_frag<ROWSCALE>(cur);
             if constexpr (T + 1 < NSUB)
                 issue_b_frag<ROWSCALE, ST, T + 1>(vB0, vB1, vSB, fr[(T + 1) & 1]);
+            if constexpr (!GROUPED && T < 4) issue_part(jnext, ST ^ 1, T);
             const v8i bf = __builtin_shufflevector(cur.lo, cur.hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
             for (int s = 0; s < ACT; ++s)
@@ -425,10 +434,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         auto step = [&](auto stage_tag, int j) {
             constexpr int ST = decltype(stage_tag)::value;
             wait_dma_and_barrier();
-            // Prefetch the next slab into the other stage. The last step
-            // re-loads its own slab there instead (never read), keeping the
-            // body branch-free.
-            issue(min(j + 1, slabs - 1), ST ^ 1);
+            // Prefetch the next slab into the other stage: spread over the
+            // first n-subtiles for a dense tile, all at once for a grouped
+            // tile (whose operands miss L2 more often, so the copy needs the
+            // whole step to land) or for a wave without MFMA work. The last
+            // step re-loads its own slab there instead (never read), keeping
+            // the body branch-free.
+            jnext = min(j + 1, slabs - 1);
+            if constexpr (GROUPED || ACT == 0) issue(jnext, ST ^ 1);
             if constexpr (ACT > 0) compute(stage_tag, act_tag);
         };
         if (slabs > 0) issue(0, 0);

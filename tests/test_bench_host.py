@@ -1,0 +1,77 @@
+"""Host-side logic of bench.py: counter CSV parsing, calibration scaling and
+the guard that drops stored traffic taken on other kernel sources."""
+from __future__ import annotations
+
+import csv
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _write(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for did, name, val in rows:
+            w.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": val})
+
+
+class _Stub:
+    def __init__(self):
+        self.launches = [bench.Launch("quant_act_1x128", None, 3000.0),
+                         bench.Launch("gemm", None, 10000.0, 1.0)]
+
+
+def test_pmc_summary_scales_by_the_copy_calibration(tmp_path):
+    probe_mib = 1
+    fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    # the copy reads 1 MiB but the fetch counter shows half of it (KiB units)
+    _write(fetch, "FETCH_SIZE", [(1, "__amd_rocclr_copyBuffer", 512.0),
+                                 (2, "fp8q::quant_act_1x128_kernel(...)", 1.0),
+                                 (3, "void fp8q::gemm_kernel<256>(Params)", 4.0),
+                                 (4, "void fp8q::gemm_kernel<256>(Params)", 6.0),
+                                 (5, "at::native::other", 99.0)])
+    _write(write, "WRITE_SIZE", [(1, "__amd_rocclr_copyBuffer", 1024.0),
+                                 (2, "fp8q::quant_act_1x128_kernel(...)", 2.0),
+                                 (3, "void fp8q::gemm_kernel<256>(Params)", 3.0),
+                                 (4, "void fp8q::gemm_kernel<256>(Params)", 3.0)])
+    out = str(tmp_path / "t.json")
+    res = bench.pmc_summary(fetch, write, "dense_fprop", probe_mib, out, _Stub())
+    assert res["fetch_factor"] == 2.0 and res["write_factor"] == 1.0
+    g = res["kernels"]["gemm"]
+    assert g["fetch_bytes"] == 5 * 1024 * 2 and g["write_bytes"] == 3 * 1024
+    assert g["traffic_bytes"] == 13 * 1024 and g["dispatches"] == 2
+    assert g["algorithmic_bytes"] == 10000
+    q = res["kernels"]["quant_act_1x128"]
+    assert q["traffic_bytes"] == 1 * 2048 + 2 * 1024
+    with open(out) as f:
+        assert json.load(f)["dense_fprop"]["kernel_source"] == bench.kernel_source_digest()
+    assert bench.stored_traffic(out, "dense_fprop")["gemm"]["traffic_bytes"] == 13 * 1024
+
+
+def test_stored_traffic_dropped_for_other_kernel_source(tmp_path):
+    out = str(tmp_path / "t.json")
+    with open(out, "w") as f:
+        json.dump({"dense_fprop": {"kernel_source": "0" * 16, "kernels": {"gemm": {}}}}, f)
+    assert bench.stored_traffic(out, "dense_fprop") is None
+    assert bench.stored_traffic(out, "wgrad") is None
+    assert bench.stored_traffic(str(tmp_path / "missing.json"), "dense_fprop") is None
+
+
+def test_multi_gpu_request_exits_with_message(capsys, monkeypatch):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    try:
+        bench.main()
+    except SystemExit as e:
+        assert e.code == 2
+    else:
+        raise AssertionError("bench.main() accepted --gpus 2")
+    assert "one GPU" in capsys.readouterr().err
