@@ -345,8 +345,7 @@ def main():
     if args.pmc_summary:
         wl_obj = Workload(args.config, 1) if torch.cuda.is_available() else None
         if wl_obj is None:
-            # the algorithmic bytes only need the shapes: build them on the CPU
-            raise SystemExit("--pmc-summary needs the workload shapes; run it on the GPU box")
+            raise SystemExit("--pmc-summary needs the workload shapes, which are built on the GPU")
         print(json.dumps(pmc_summary(args.pmc_summary[0], args.pmc_summary[1], args.config,
                                      args.copy_probe_mib or 256, args.traffic_json, wl_obj)))
         return

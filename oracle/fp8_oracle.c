@@ -15,7 +15,7 @@
  *     dssusan.co.kr (Q&A board), passage on Figure 7(a);
  *   - each group shares one exponent through its scale -- page "Deepseek Ai
  *     News Expert Interview", passage on smaller element groups.
- * Readings where the pages are silent (each listed in the design doc):
+ * Readings where the pages are silent:
  *   - the E4M3 variant is OCP E4M3FN: bias 7, no infinities, 0x7F/0xFF are NaN,
  *     largest finite value 448;
  *   - scale s = fl32(amax / 448), an IEEE single-precision division;
