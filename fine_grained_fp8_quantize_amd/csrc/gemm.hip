@@ -47,14 +47,9 @@ constexpr int kThreads = 512;
 constexpr int kWaveM = 64;
 constexpr int kMSub = kWaveM / 16;
 
-// LDS map (bytes): A stage 0 | A stage 1 | B stage 0 | B stage 1 |
-//                  sA stage 0 | sA stage 1 | sB stage 0 | sB stage 1.
+// LDS per stage: one 256x128-byte tile of A, one of B, 256 A scales and up
+// to 256 B scales (two stages: 135168 bytes).
 constexpr int kTileBytes = kBM * kSlab;
-constexpr int kOffA = 0;
-constexpr int kOffB = 2 * kTileBytes;
-constexpr int kOffSA = 4 * kTileBytes;
-constexpr int kOffSB = kOffSA + 2 * kBM * 4;
-constexpr int kLdsBytes = kOffSB + 2 * kBNMax * 4;
 
 // Physical 16-byte chunk of logical chunk c in LDS row `row`.
 __device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ (row & 7); }
@@ -151,93 +146,25 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
     return false;
 }
 
-// ---------------------------------------------------------------- LDS reads
-// Fragment reads are inline asm with their own s_waitcnt: the compiler would
-// otherwise wait for every outstanding LDS-DMA load (including the prefetch
-// of the next slab) before any LDS read, serialising load and compute. The
-// DMA of a stage is fenced explicitly (vmcnt(0) + barrier) before it is read.
+// ---------------------------------------------------------------- LDS
+// Every stage of every operand is its own __shared__ array. The copy of slab
+// j+1 into one stage and the fragment reads of slab j from the other then
+// touch provably distinct objects, so the compiler's wait insertion lets the
+// reads proceed while the copy is in flight; a stage is fenced explicitly
+// (vmcnt(0) + barrier) before it is read.
 
-// A fragments of the four m-subtiles, the lane's four A scales, and the two
-// B block scales the wave can touch (with per-row B scaling: unused values).
-template <int ST>
-__device__ __forceinline__ void read_a_frags(uint32_t v0, uint32_t v1, uint32_t vs, uint32_t vsb,
-                                             v8i (&am)[kMSub], float (&sa)[kMSub], float& sb0,
-                                             float& sb1) {
-    v4i l0, h0, l1, h1, l2, h2, l3, h3;
-    float f0, f1, f2, f3, fb0, fb1;
-    asm volatile(
-        "ds_read_b128 %0, %14 offset:%16\n\t"
-        "ds_read_b128 %1, %15 offset:%16\n\t"
-        "ds_read_b128 %2, %14 offset:%17\n\t"
-        "ds_read_b128 %3, %15 offset:%17\n\t"
-        "ds_read_b128 %4, %14 offset:%18\n\t"
-        "ds_read_b128 %5, %15 offset:%18\n\t"
-        "ds_read_b128 %6, %14 offset:%19\n\t"
-        "ds_read_b128 %7, %15 offset:%19\n\t"
-        "ds_read_b32 %8, %20 offset:%21\n\t"
-        "ds_read_b32 %9, %20 offset:%22\n\t"
-        "ds_read_b32 %10, %20 offset:%23\n\t"
-        "ds_read_b32 %11, %20 offset:%24\n\t"
-        "ds_read_b32 %12, %25 offset:%26\n\t"
-        "ds_read_b32 %13, %25 offset:%27\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(l0), "=&v"(h0), "=&v"(l1), "=&v"(h1), "=&v"(l2), "=&v"(h2), "=&v"(l3), "=&v"(h3),
-          "=&v"(f0), "=&v"(f1), "=&v"(f2), "=&v"(f3), "=&v"(fb0), "=&v"(fb1)
-        : "v"(v0), "v"(v1), "n"(ST * kTileBytes + 0 * 2048), "n"(ST * kTileBytes + 1 * 2048),
-          "n"(ST * kTileBytes + 2 * 2048), "n"(ST * kTileBytes + 3 * 2048), "v"(vs),
-          "n"(ST * kBM * 4 + 0), "n"(ST * kBM * 4 + 64), "n"(ST * kBM * 4 + 128),
-          "n"(ST * kBM * 4 + 192), "v"(vsb), "n"(ST * kBNMax * 4), "n"(ST * kBNMax * 4 + 4)
-        : "memory");
-    am[0] = __builtin_shufflevector(l0, h0, 0, 1, 2, 3, 4, 5, 6, 7);
-    am[1] = __builtin_shufflevector(l1, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-    am[2] = __builtin_shufflevector(l2, h2, 0, 1, 2, 3, 4, 5, 6, 7);
-    am[3] = __builtin_shufflevector(l3, h3, 0, 1, 2, 3, 4, 5, 6, 7);
-    sa[0] = f0;
-    sa[1] = f1;
-    sa[2] = f2;
-    sa[3] = f3;
-    sb0 = fb0;
-    sb1 = fb1;
-}
-
-// A B fragment in flight: issued by issue_b_frag, completed by wait_b_frag.
-// The wait takes the destination registers as in/out operands, so nothing
-// can read them (and the compiler cannot reuse them) before the data landed.
-struct BFrag {
-    v4i lo, hi;
-    v4f sb;  // per-row B scales of the lane's four n (per-row scaling only)
-};
-
-template <bool ROWSCALE, int ST, int T>
-__device__ __forceinline__ void issue_b_frag(uint32_t v0, uint32_t v1, uint32_t vs, BFrag& f) {
-    if constexpr (ROWSCALE) {
-        asm volatile(
-            "ds_read_b128 %0, %3 offset:%5\n\t"
-            "ds_read_b128 %1, %4 offset:%5\n\t"
-            "ds_read_b128 %2, %6 offset:%7"
-            : "=&v"(f.lo), "=&v"(f.hi), "=&v"(f.sb)
-            : "v"(v0), "v"(v1), "n"(ST * kTileBytes + T * 2048), "v"(vs), "n"(ST * kBNMax * 4 + T * 64)
-            : "memory");
-    } else {
-        asm volatile(
-            "ds_read_b128 %0, %2 offset:%4\n\t"
-            "ds_read_b128 %1, %3 offset:%4"
-            : "=&v"(f.lo), "=&v"(f.hi)
-            : "v"(v0), "v"(v1), "n"(ST * kTileBytes + T * 2048)
-            : "memory");
-    }
-}
-
-template <bool ROWSCALE>
-__device__ __forceinline__ void wait_b_frag(BFrag& f) {
-    if constexpr (ROWSCALE)
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.lo), "+v"(f.hi), "+v"(f.sb) : : "memory");
-    else
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(f.lo), "+v"(f.hi) : : "memory");
-}
+// s_waitcnt with vmcnt = 0 and the other counters left at their maxima.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ void wait_dma_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_barrier();
+}
+
+__device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
+    const v4i lo = *reinterpret_cast<const v4i*>(p0);
+    const v4i hi = *reinterpret_cast<const v4i*>(p1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 template <int... Is, class F>
@@ -256,7 +183,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // weight blocks; each 16-column subtile still lies inside one block.
     constexpr bool STRADDLE = !ROWSCALE && (WN % 128 != 0);
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kTileBytes];
+    __shared__ __attribute__((aligned(16))) float lds_sa0[kBM];
+    __shared__ __attribute__((aligned(16))) float lds_sa1[kBM];
+    __shared__ __attribute__((aligned(16))) float lds_sb0[kBNMax];
+    __shared__ __attribute__((aligned(16))) float lds_sb1[kBNMax];
+    auto stage_a = [&](auto st) -> uint8_t* {
+        if constexpr (decltype(st)::value == 0) return lds_a0; else return lds_a1;
+    };
+    auto stage_b = [&](auto st) -> uint8_t* {
+        if constexpr (decltype(st)::value == 0) return lds_b0; else return lds_b1;
+    };
+    auto stage_sa = [&](auto st) -> float* {
+        if constexpr (decltype(st)::value == 0) return lds_sa0; else return lds_sa1;
+    };
+    auto stage_sb = [&](auto st) -> float* {
+        if constexpr (decltype(st)::value == 0) return lds_sb0; else return lds_sb1;
+    };
 
     TileRows tr;
     if (GROUPED ? !grouped_tile<BN>(p, tr) : !dense_tile<BN>(p, tr)) return;
@@ -304,25 +250,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         ld_s = 1;
         offS = (uint32_t)(min(tr.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
     }
-    const int lds_s = wave < 4 ? kOffSA + 64 * 4 * wave : kOffSB + 64 * 4 * (wave - 4);
 
     // Part i (0..3) of this wave's copy of slab j into stage st: 8 rows of
     // A and 8 rows of B; part 3 also carries the scales. Computing waves
     // spread the parts over their first n-subtiles, which keeps the LDS-DMA
     // writes from bunching up behind the barrier.
-    auto issue_part = [&](int j, int st, int i) {
-        uint8_t* base_a = smem + kOffA + st * kTileBytes + 32 * wave * kSlab;
-        uint8_t* base_b = smem + kOffB + st * kTileBytes + 32 * wave * kSlab;
+    auto issue_part = [&](int j, auto st, int i) {
+        uint8_t* base_a = stage_a(st) + 32 * wave * kSlab;
+        uint8_t* base_b = stage_b(st) + 32 * wave * kSlab;
         const uint8_t* ga = tileA + (int64_t)j * kSlab;
         const uint8_t* gb = tileB + (int64_t)j * kSlab;
         __builtin_amdgcn_global_load_lds(ga + offA[i], (lds_void*)(base_a + i * 8 * kSlab), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(gb + offB[i], (lds_void*)(base_b + i * 8 * kSlab), 16, 0, 0);
         if (i == 3) {
             const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
-            __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)(smem + lds_s + st * kBM * 4), 4, 0, 0);
+            float* dst = wave < 4 ? stage_sa(st) + 64 * wave : stage_sb(st) + 64 * (wave - 4);
+            __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)dst, 4, 0, 0);
         }
     };
-    auto issue = [&](int j, int st) {
+    auto issue = [&](int j, auto st) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) issue_part(j, st, i);
     };
@@ -331,21 +277,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // ---- fragment addresses: lane (i = l%16, g = l/16) reads 32 bytes of
     // row i at logical chunks 2g and 2g+1 of every 16-row subtile.
     const int fi = lane & 15, fg = lane >> 4;
-    const uint32_t lds0 = lds_addr(smem);
     const uint32_t off0 = fi * kSlab + swz_chunk(2 * fg, fi) * 16;
     const uint32_t off1 = fi * kSlab + swz_chunk(2 * fg + 1, fi) * 16;
-    const uint32_t vA0 = lds0 + kOffA + wm * kWaveM * kSlab + off0;
-    const uint32_t vA1 = lds0 + kOffA + wm * kWaveM * kSlab + off1;
-    const uint32_t vB0 = lds0 + kOffB + wn * WN * kSlab + off0;
-    const uint32_t vB1 = lds0 + kOffB + wn * WN * kSlab + off1;
-    const uint32_t vSA = lds0 + kOffSA + (wm * kWaveM + fi) * 4;
-    const uint32_t vSB = lds0 + kOffSB + (wn * WN + 4 * fg) * 4;
+    const uint32_t fragA = wm * kWaveM * kSlab;
+    const uint32_t fragB = wn * WN * kSlab;
     // Block scales: the wave's first column lies in n-block nb0; sB holds the
     // tile's blocks from n0/128 on. Subtiles T < split are in nb0, the rest in
     // nb0 + 1 (only possible when STRADDLE).
     const int64_t wcol = tr.n0 + wn * WN;
     const int nb_rel = (int)(wcol / 128 - tr.n0 / 128);
-    const uint32_t vSBblk = lds0 + kOffSB + nb_rel * 4;
     const int split = (int)((128 - (wcol & 127)) / 16);
 
     // Real rows of the wave (grouped padding, ragged M): m-subtiles past them
@@ -366,9 +306,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     auto compute = [&](auto stage_tag, auto act_tag) {
         constexpr int ST = decltype(stage_tag)::value;
         constexpr int ACT = decltype(act_tag)::value;
+        const uint8_t* const la = stage_a(stage_tag) + fragA;
+        const uint8_t* const lb = stage_b(stage_tag) + fragB;
+        const float* const lsa = stage_sa(stage_tag) + wm * kWaveM + fi;
+        const float* const lsb = stage_sb(stage_tag);
         v8i am[kMSub];
-        float sa[kMSub], sb0, sb1;
-        read_a_frags<ST>(vA0, vA1, vSA, vSBblk, am, sa, sb0, sb1);
+        float sa[kMSub];
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) {
+            am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
+            sa[s] = lsa[16 * s];
+        }
+        const float sb0 = ROWSCALE ? 0.f : lsb[nb_rel];
+        const float sb1 = ROWSCALE ? 0.f : lsb[nb_rel + 1];
         float sab0[kMSub], sab1[kMSub];
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) {
@@ -378,7 +328,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         // Software pipeline over the n-subtiles: while the MFMAs of subtile T
         // run, the fragment of T+1 is in flight and the partials of T-1 are
         // promoted (acc += P * sA * sB), one FMA group after each MFMA.
-        BFrag fr[2];
+        // B fragment of n-subtile T (and, with per-row B scales, the lane's
+        // four scales)
+        auto read_b = [&](auto t_tag, v8i& bf, v4f& sbv) {
+            constexpr int T = decltype(t_tag)::value;
+            bf = ld_frag(lb + T * 2048 + off0, lb + T * 2048 + off1);
+            if constexpr (ROWSCALE)
+                sbv = *reinterpret_cast<const v4f*>(lsb + wn * WN + 4 * fg + 16 * T);
+        };
+        v8i fr[2];
+        v4f fsb[2];
         v4f pc[kMSub], pp[kMSub];
         v4f sbp;
         auto promote = [&](auto t_tag, const v4f& sbn) {
@@ -397,30 +356,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
                 }
             }
         };
-        issue_b_frag<ROWSCALE, ST, 0>(vB0, vB1, vSB, fr[0]);
+        read_b(std::integral_constant<int, 0>{}, fr[0], fsb[0]);
+        __builtin_amdgcn_sched_barrier(0);
         unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
             constexpr int T = decltype(t_tag)::value;
-            BFrag& cur = fr[T & 1];
-            wait_b_frag<ROWSCALE>(cur);
+            constexpr int NEXT_READS = ROWSCALE ? 3 : 2;
+            const v8i bf = fr[T & 1];
             if constexpr (T + 1 < NSUB)
-                issue_b_frag<ROWSCALE, ST, T + 1>(vB0, vB1, vSB, fr[(T + 1) & 1]);
-            if constexpr (!GROUPED && T < 4) issue_part(jnext, ST ^ 1, T);
-            const v8i bf = __builtin_shufflevector(cur.lo, cur.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                read_b(std::integral_constant<int, T + 1>{}, fr[(T + 1) & 1], fsb[(T + 1) & 1]);
+            if constexpr (!GROUPED && T < 4)
+                issue_part(jnext, std::integral_constant<int, ST ^ 1>{}, T);
 #pragma unroll
             for (int s = 0; s < ACT; ++s)
                 pc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], zero, 0, 0, 0, 0, 0, 0);
-            if constexpr (T > 0) {
-                promote(std::integral_constant<int, T - 1>{}, sbp);
-                // one MFMA, then the FMA group of one m-subtile, ACT times
+            if constexpr (T > 0) promote(std::integral_constant<int, T - 1>{}, sbp);
+            // Order: the first MFMA (its wait covers only the fragment read
+            // one subtile earlier), the next fragment's reads, this subtile's
+            // copy part, then the FMA group of one m-subtile after each MFMA.
+            constexpr int FMAS = ROWSCALE ? 8 : (STRADDLE ? 5 : 4);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NEXT_READS, 0);
+            if constexpr (!GROUPED && T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
+            if constexpr (T > 0) __builtin_amdgcn_sched_group_barrier(0x002, FMAS, 0);
 #pragma unroll
-                for (int s = 0; s < ACT; ++s) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, ROWSCALE ? 8 : (STRADDLE ? 5 : 4), 0);
-                }
+            for (int s = 1; s < ACT; ++s) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (T > 0) __builtin_amdgcn_sched_group_barrier(0x002, FMAS, 0);
             }
 #pragma unroll
             for (int s = 0; s < ACT; ++s) pp[s] = pc[s];
-            sbp = cur.sb;
+            sbp = fsb[T & 1];
             __builtin_amdgcn_sched_barrier(0);
         });
         promote(std::integral_constant<int, NSUB - 1>{}, sbp);
@@ -441,10 +406,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             // step re-loads its own slab there instead (never read), keeping
             // the body branch-free.
             jnext = min(j + 1, slabs - 1);
-            if constexpr (GROUPED || ACT == 0) issue(jnext, ST ^ 1);
+            if constexpr (GROUPED || ACT == 0) issue(jnext, std::integral_constant<int, ST ^ 1>{});
             if constexpr (ACT > 0) compute(stage_tag, act_tag);
         };
-        if (slabs > 0) issue(0, 0);
+        if (slabs > 0) issue(0, std::integral_constant<int, 0>{});
         int j = 0;
         for (; j + 2 <= slabs; j += 2) {
             step(std::integral_constant<int, 0>{}, j);
@@ -467,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         mainloop(std::integral_constant<int, 0>{});
     }
     // Drain the last (unused) prefetch before the block's LDS can be reused.
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
 #pragma unroll
