@@ -103,7 +103,7 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
     if (st != FP8Q_OK) return st;
     if (k > 0 && b_scale_kind == FP8Q_BSCALE_BLOCK128 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
     if (k > 0 && b_scale_kind == FP8Q_BSCALE_ROW128 && ld_bs < n) return FP8Q_ERR_SHAPE;
-    if (!grid_ok(((m + 255) / 256) * ((n + 255) / 256) + 8)) return FP8Q_ERR_SHAPE;
+    if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) + 8)) return FP8Q_ERR_SHAPE;
     fp8q::GemmProblem g = {};
     g.m = m; g.n = n; g.k = k;
     g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;
@@ -129,7 +129,7 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     if (k > 0 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
     if (stride_b < n * ldb || (k > 0 && stride_bs < (n / 128) * ld_bs)) return FP8Q_ERR_SHAPE;
     if (stride_b % 16 != 0) return FP8Q_ERR_ALIGN;
-    if (!grid_ok((m_total / 128) * ((n + 255) / 256) + 8)) return FP8Q_ERR_SHAPE;
+    if (!grid_ok((m_total / 128) * ((n + 255) / 256) + 256)) return FP8Q_ERR_SHAPE;
     fp8q::GemmProblem g = {};
     g.m = m_total; g.n = n; g.k = k;
     g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;

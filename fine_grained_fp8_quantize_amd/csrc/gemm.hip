@@ -110,38 +110,93 @@ __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
     return true;
 }
 
-// Grouped tile order: expert e's segment [off[e], off[e+1]) is cut into
-// 256-row m-tiles (the last may hold only 128 rows); slots run expert-major,
-// then n-tile, then m-tile, so consecutive slots on one XCD reuse the same
-// 256 x K panel of W_e.
+// Grouped tiles. Expert e's segment [off[e], off[e+1]) is cut into 256-row
+// m-tiles. A tile's class is the number of its 64-row quarters that hold real
+// rows: 4 for a tile of real rows only, 1..4 for the tail tile, 0 for a tile
+// of padding only (which is still written, as zeros). Slots run class 4
+// first, then 3, 2, 1, 0 -- the longest tiles first, so the short ones fill
+// the last round -- and inside a class by expert, n-tile, m-tile, so m-tiles
+// that share a 256 x K panel of W_e are consecutive.
+struct ExpertSplit {
+    int beg;   // first row of the segment
+    int full;  // m-tiles of real rows only
+    int tail;  // class of the tail tile (0: no tail)
+    int pad;   // m-tiles of padding rows only
+};
+
+__device__ __forceinline__ ExpertSplit expert_split(const Params& p, int e) {
+    ExpertSplit x;
+    x.beg = p.group_offsets[e];
+    const int seg = max(p.group_offsets[e + 1] - x.beg, 0);
+    const int real = p.group_rows ? min(max(p.group_rows[e], 0), seg) : seg;
+    const int rest = real % kBM;
+    x.full = real / kBM;
+    x.tail = (rest + 63) / 64;
+    x.pad = (seg + kBM - 1) / kBM - x.full - (rest > 0 ? 1 : 0);
+    return x;
+}
+
+// m-tiles of expert split x in class c, and the first of them.
+__device__ __forceinline__ int class_tiles(const ExpertSplit& x, int c, int& first) {
+    if (c == 4) {
+        first = 0;
+        return x.full + (x.tail == 4 ? 1 : 0);
+    }
+    if (c == 0) {
+        first = x.full + (x.tail > 0 ? 1 : 0);
+        return x.pad;
+    }
+    first = x.full;
+    return x.tail == c ? 1 : 0;
+}
+
+// Block b runs on XCD b % 8; round r of that XCD's 32 CUs takes the 32
+// consecutive slots 256 r + 32 (b % 8) + [0, 32). Every round is then spread
+// evenly over the XCDs and panel reuse stays inside one L2. The grid is a
+// multiple of 256 blocks, so this is a bijection onto its slots.
 template <int BN>
 __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
     const int tiles_n = (int)((p.n + BN - 1) / BN);
-    int total = 0;
+    const int q = (int)(blockIdx.x >> 3);
+    int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
+    int cnt[5] = {0, 0, 0, 0, 0};
     for (int e = 0; e < p.groups; ++e) {
-        const int seg = p.group_offsets[e + 1] - p.group_offsets[e];
-        total += (seg + kBM - 1) / kBM * tiles_n;
+        const ExpertSplit x = expert_split(p, e);
+        cnt[4] += x.full + (x.tail == 4 ? 1 : 0);
+        cnt[3] += x.tail == 3 ? 1 : 0;
+        cnt[2] += x.tail == 2 ? 1 : 0;
+        cnt[1] += x.tail == 1 ? 1 : 0;
+        cnt[0] += x.pad;
     }
-    const int per = (total + 7) / 8;
-    int slot = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (slot >= total) return false;
+    int cls = -1;
+#pragma unroll
+    for (int c = 4; c >= 0; --c) {
+        if (cls < 0) {
+            if (slot < cnt[c] * tiles_n) cls = c;
+            else slot -= cnt[c] * tiles_n;
+        }
+    }
+    if (cls < 0) return false;
     for (int e = 0; e < p.groups; ++e) {
-        const int beg = p.group_offsets[e], end = p.group_offsets[e + 1];
-        const int cnt = (end - beg + kBM - 1) / kBM;
-        if (slot < cnt * tiles_n) {
-            const int tn = slot / cnt, mt = slot - tn * cnt;
-            t.m0 = beg + (int64_t)mt * kBM;
+        const ExpertSplit x = expert_split(p, e);
+        int first;
+        const int k = class_tiles(x, cls, first);
+        if (slot < k * tiles_n) {
+            const int tn = slot / k, mt = first + slot % k;
+            const int end = x.beg + max(p.group_offsets[e + 1] - x.beg, 0);
+            t.m0 = x.beg + (int64_t)mt * kBM;
             // offsets that break the contract must not move stores outside C
             if (t.m0 < 0 || t.m0 >= p.m) return false;
             t.row_hi = min(min((int64_t)end, t.m0 + kBM), p.m);
-            const int real = p.group_rows ? p.group_rows[e] : end - beg;
-            t.real_end = beg + (int64_t)real;
+            const int seg = end - x.beg;
+            const int real = p.group_rows ? min(max(p.group_rows[e], 0), seg) : seg;
+            t.real_end = x.beg + (int64_t)real;
             t.n0 = (int64_t)tn * BN;
             t.b = p.b + e * p.stride_b;
             t.b_scale = p.b_scale + e * p.stride_bs;
             return true;
         }
-        slot -= cnt * tiles_n;
+        slot -= k * tiles_n;
     }
     return false;
 }
@@ -494,10 +549,11 @@ Params to_params(const GemmProblem& g) {
     return p;
 }
 
+// blocks: a multiple of 8 (dense: slots rounded up; grouped: a multiple of
+// 256, see grouped_tile).
 template <int BN, bool GROUPED>
-hipError_t dispatch(const GemmProblem& g, int64_t slots, hipStream_t stream) {
+hipError_t dispatch(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
     const Params p = to_params(g);
-    const int64_t blocks = (slots + 7) / 8 * 8;
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (g.b_rowscale) {
         if (g.out_f32)
@@ -527,17 +583,17 @@ hipError_t launch_gemm(const GemmProblem& g, hipStream_t stream) {
     // e.g. N = 7168 = 32 x 224 (Dgrad, Wgrad); otherwise 256-wide.
     if (grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256)) {
         const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
-        return dispatch<224, false>(g, tiles, stream);
+        return dispatch<224, false>(g, (tiles + 7) / 8 * 8, stream);
     }
     const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
-    return dispatch<256, false>(g, tiles, stream);
+    return dispatch<256, false>(g, (tiles + 7) / 8 * 8, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& g, hipStream_t stream) {
     // Upper bound on the tile count: every 256-row m-tile of an expert holds at
     // least 128 of its rows, so there are at most m_total / 128 of them.
     const int64_t tiles = (g.m / 128) * ((g.n + 255) / 256);
-    return dispatch<256, true>(g, tiles, stream);
+    return dispatch<256, true>(g, (tiles + 255) / 256 * 256, stream);
 }
 
 }  // namespace fp8q
