@@ -277,12 +277,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // a 32-bit per-lane offset, which maps onto the saddr + voffset form.
     const uint8_t* const tileA = p.a + tr.m0 * p.lda;
     const uint8_t* const tileB = tr.b + tr.n0 * p.ldb;
+    // In a grouped tile, A rows past the tile's real rows only feed outputs
+    // that are written as zeros or not at all (an output row depends on its
+    // own A row only): every lane of such an 8-row chunk reads the same
+    // 128-byte line, so the copy costs one L2 line instead of 1 KB.
+    const int a_rows = (int)min((int64_t)kBM, min(tr.real_end, tr.row_hi) - tr.m0);
     uint32_t offA[4], offB[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 32 * wave + 8 * i + (lane >> 3);
         const int chunk = swz_chunk(lane & 7, row);
-        offA[i] = (uint32_t)((min(tr.m0 + row, m_last) - tr.m0) * p.lda) + chunk * 16;
+        const int src = (GROUPED && 32 * wave + 8 * i >= a_rows) ? max(a_rows - 1, 0) : row;
+        offA[i] = (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + chunk * 16;
         offB[i] = (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + chunk * 16;
     }
     // Scales: waves 0-3 copy the slab's 256 A scales (64 each) into the sA
