@@ -8,6 +8,7 @@ IEEE and denormals are kept.
 """
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 import sys
@@ -56,6 +57,13 @@ def build(force: bool = True, verbose: bool = False) -> str:
         print("\n".join(msgs), file=sys.stderr)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed with status %d" % res.returncode)
+    # A shared library links with unresolved symbols; bind every symbol now
+    # so that a missing kernel stub fails the build, not the first call.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        os.unlink(tmp)
+        raise RuntimeError("built library does not load: %s" % e) from None
     os.replace(tmp, LIB)
     return LIB
 

@@ -208,11 +208,45 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
 // reads proceed while the copy is in flight; a stage is fenced explicitly
 // (vmcnt(0) + barrier) before it is read.
 
-// s_waitcnt with vmcnt = 0 and the other counters left at their maxima.
-constexpr int kWaitVmcnt0 = 0x0F70;
+// The arrays live at namespace scope; a kernel's LDS holds only the ones
+// it uses. Two-stage kernels (dense): A, B, A scales and B scales in stages
+// 0 and 1 (135168 bytes). Three-stage kernels (grouped): A in stages 0 and
+// 1, B in stages 0, 1 and 2, scales in registers (163840 bytes).
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kTileBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t lds_b2[kTileBytes];
+__shared__ __attribute__((aligned(16))) float lds_sa0[kBM];
+__shared__ __attribute__((aligned(16))) float lds_sa1[kBM];
+__shared__ __attribute__((aligned(16))) float lds_sb0[kBNMax];
+__shared__ __attribute__((aligned(16))) float lds_sb1[kBNMax];
 
+template <int S>
+__device__ __forceinline__ uint8_t* stage_a() {
+    if constexpr (S == 0) return lds_a0; else return lds_a1;
+}
+template <int S>
+__device__ __forceinline__ uint8_t* stage_b() {
+    if constexpr (S == 0) return lds_b0;
+    else if constexpr (S == 1) return lds_b1;
+    else return lds_b2;
+}
+template <int S>
+__device__ __forceinline__ float* stage_sa() {
+    if constexpr (S == 0) return lds_sa0; else return lds_sa1;
+}
+template <int S>
+__device__ __forceinline__ float* stage_sb() {
+    if constexpr (S == 0) return lds_sb0; else return lds_sb1;
+}
+
+// s_waitcnt with vmcnt = N and the other counters left at their maxima.
+constexpr int waitcnt_vm(int n) { return 0x0F70 | n; }
+
+template <int N>
 __device__ __forceinline__ void wait_dma_and_barrier() {
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
     __builtin_amdgcn_s_barrier();
 }
 
@@ -238,26 +272,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // weight blocks; each 16-column subtile still lies inside one block.
     constexpr bool STRADDLE = !ROWSCALE && (WN % 128 != 0);
 
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_a0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_a1[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_b0[kTileBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds_b1[kTileBytes];
-    __shared__ __attribute__((aligned(16))) float lds_sa0[kBM];
-    __shared__ __attribute__((aligned(16))) float lds_sa1[kBM];
-    __shared__ __attribute__((aligned(16))) float lds_sb0[kBNMax];
-    __shared__ __attribute__((aligned(16))) float lds_sb1[kBNMax];
-    auto stage_a = [&](auto st) -> uint8_t* {
-        if constexpr (decltype(st)::value == 0) return lds_a0; else return lds_a1;
-    };
-    auto stage_b = [&](auto st) -> uint8_t* {
-        if constexpr (decltype(st)::value == 0) return lds_b0; else return lds_b1;
-    };
-    auto stage_sa = [&](auto st) -> float* {
-        if constexpr (decltype(st)::value == 0) return lds_sa0; else return lds_sa1;
-    };
-    auto stage_sb = [&](auto st) -> float* {
-        if constexpr (decltype(st)::value == 0) return lds_sb0; else return lds_sb1;
-    };
+    // Grouped tiles stream each expert's weights from HBM once: they keep two
+    // B slabs in flight (three B stages) and take their scales through
+    // registers; dense tiles, whose operands mostly hit L2, use two stages.
+    constexpr bool DEEP = GROUPED;
+    static_assert(!DEEP || (!ROWSCALE && BN == 256), "three-stage tiles: block scales, 256 wide");
 
     TileRows tr;
     if (GROUPED ? !grouped_tile<BN>(p, tr) : !dense_tile<BN>(p, tr)) return;
@@ -316,17 +335,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // A and 8 rows of B; part 3 also carries the scales. Computing waves
     // spread the parts over their first n-subtiles, which keeps the LDS-DMA
     // writes from bunching up behind the barrier.
-    auto issue_part = [&](int j, auto st, int i) {
-        uint8_t* base_a = stage_a(st) + 32 * wave * kSlab;
-        uint8_t* base_b = stage_b(st) + 32 * wave * kSlab;
+    // Three-stage kernels recompute the offsets of each copy (a few VALU
+    // operations at the step boundary) instead of holding eight registers
+    // through the MFMA loop. The swizzled chunk depends on row & 7 only, the
+    // same for all four parts of a wave.
+    const uint32_t chunk16 = swz_chunk(lane & 7, lane >> 3) * 16;
+    auto a_off = [&](int i) -> uint32_t {
+        if constexpr (!DEEP) return offA[i];
+        const int row = 32 * wave + 8 * i + (lane >> 3);
+        const int src = 32 * wave + 8 * i >= a_rows ? max(a_rows - 1, 0) : row;
+        return (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + chunk16;
+    };
+    auto b_off = [&](int i) -> uint32_t {
+        if constexpr (!DEEP) return offB[i];
+        const int row = 32 * wave + 8 * i + (lane >> 3);
+        return (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + chunk16;
+    };
+    auto copy_a = [&](int j, auto st, int i) {
+        uint8_t* base = stage_a<decltype(st)::value>() + 32 * wave * kSlab;
         const uint8_t* ga = tileA + (int64_t)j * kSlab;
+        // (offset computed outside the builtin's argument list: a lambda
+        // call there keeps the host pass from emitting the kernel's stub)
+        const uint32_t off = a_off(i);
+        __builtin_amdgcn_global_load_lds(ga + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, 0);
+    };
+    auto copy_b = [&](int j, auto st, int i) {
+        uint8_t* base = stage_b<decltype(st)::value>() + 32 * wave * kSlab;
         const uint8_t* gb = tileB + (int64_t)j * kSlab;
-        __builtin_amdgcn_global_load_lds(ga + offA[i], (lds_void*)(base_a + i * 8 * kSlab), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(gb + offB[i], (lds_void*)(base_b + i * 8 * kSlab), 16, 0, 0);
-        if (i == 3) {
-            const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
-            float* dst = wave < 4 ? stage_sa(st) + 64 * wave : stage_sb(st) + 64 * (wave - 4);
-            __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)dst, 4, 0, 0);
+        const uint32_t off = b_off(i);
+        __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, 0);
+    };
+    auto issue_part = [&](int j, auto st, int i) {
+        copy_a(j, st, i);
+        copy_b(j, st, i);
+        if constexpr (!DEEP) {
+            if (i == 3) {
+                constexpr int S = decltype(st)::value;
+                const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
+                float* dst = wave < 4 ? stage_sa<S>() + 64 * wave : stage_sb<S>() + 64 * (wave - 4);
+                __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)dst, 4, 0, 0);
+            }
         }
     };
     auto issue = [&](int j, auto st) {
@@ -363,27 +411,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
 
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    // One slab of MFMAs + promotion for the first ACT m-subtiles of the wave.
-    auto compute = [&](auto stage_tag, auto act_tag) {
-        constexpr int ST = decltype(stage_tag)::value;
+    // Three-stage kernel: the lane's four A scales and the wave's B block
+    // scale of slab j, loaded into registers one step ahead.
+    const int row_a0 = (int)(wrow - tr.m0) + fi;       // the lane's row in m-subtile 0
+    const int row_a_last = (int)(m_last - tr.m0);
+    const float* const bscale_row = tr.b_scale + min(wcol, n_last) / 128 * p.ld_bs;
+    auto load_scales = [&](int j, float (&sa)[kMSub], float& sb) {
+        const float* as = p.a_scale + tr.m0 + (int64_t)j * p.ld_as;
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) sa[s] = as[min(row_a0 + 16 * s, row_a_last)];
+        sb = bscale_row[j];
+    };
+
+    // One slab of MFMAs + promotion for the first ACT m-subtiles of the wave,
+    // on A stage AS and B stage BS (two-stage kernels: AS = BS, scales from
+    // LDS; three-stage kernels: the products sA * sB come in sab_in).
+    auto compute = [&](auto a_tag, auto b_tag, auto act_tag, const float (&sab_in)[kMSub]) {
+        constexpr int ST = decltype(a_tag)::value;
+        constexpr int BS = decltype(b_tag)::value;
         constexpr int ACT = decltype(act_tag)::value;
-        const uint8_t* const la = stage_a(stage_tag) + fragA;
-        const uint8_t* const lb = stage_b(stage_tag) + fragB;
-        const float* const lsa = stage_sa(stage_tag) + wm * kWaveM + fi;
-        const float* const lsb = stage_sb(stage_tag);
+        const uint8_t* const la = stage_a<ST>() + fragA;
+        const uint8_t* const lb = stage_b<BS>() + fragB;
+        const float* const lsa = stage_sa<ST % 2>() + wm * kWaveM + fi;
+        const float* const lsb = stage_sb<ST % 2>();
         v8i am[kMSub];
         float sa[kMSub];
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) {
             am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
-            sa[s] = lsa[16 * s];
+            sa[s] = DEEP ? 0.f : lsa[16 * s];
         }
-        const float sb0 = ROWSCALE ? 0.f : lsb[nb_rel];
-        const float sb1 = ROWSCALE ? 0.f : lsb[nb_rel + 1];
+        const float sb0 = (ROWSCALE || DEEP) ? 0.f : lsb[nb_rel];
+        const float sb1 = (ROWSCALE || !STRADDLE) ? 0.f : lsb[nb_rel + 1];
         float sab0[kMSub], sab1[kMSub];
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) {
-            sab0[s] = sa[s] * sb0;
+            sab0[s] = DEEP ? sab_in[s] : sa[s] * sb0;
             if constexpr (STRADDLE) sab1[s] = sa[s] * sb1;
         }
         // Software pipeline over the n-subtiles: while the MFMAs of subtile T
@@ -457,18 +520,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // does its share of the copies and the barriers).
     auto mainloop = [&](auto act_tag) {
         constexpr int ACT = decltype(act_tag)::value;
+        const float no_sab[kMSub] = {0.f, 0.f, 0.f, 0.f};
         auto step = [&](auto stage_tag, int j) {
             constexpr int ST = decltype(stage_tag)::value;
-            wait_dma_and_barrier();
+            wait_dma_and_barrier<0>();
             // Prefetch the next slab into the other stage: spread over the
-            // first n-subtiles for a dense tile, all at once for a grouped
-            // tile (whose operands miss L2 more often, so the copy needs the
-            // whole step to land) or for a wave without MFMA work. The last
-            // step re-loads its own slab there instead (never read), keeping
-            // the body branch-free.
+            // first n-subtiles, or all at once for a wave without MFMA work.
+            // The last step re-loads its own slab there instead (never read),
+            // keeping the body branch-free.
             jnext = min(j + 1, slabs - 1);
-            if constexpr (GROUPED || ACT == 0) issue(jnext, std::integral_constant<int, ST ^ 1>{});
-            if constexpr (ACT > 0) compute(stage_tag, act_tag);
+            if constexpr (ACT == 0) issue(jnext, std::integral_constant<int, ST ^ 1>{});
+            if constexpr (ACT > 0) compute(stage_tag, stage_tag, act_tag, no_sab);
         };
         if (slabs > 0) issue(0, std::integral_constant<int, 0>{});
         int j = 0;
@@ -478,22 +540,80 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         }
         if (j < slabs) step(std::integral_constant<int, 0>{}, j);
     };
+
+    // Three-stage K loop: slab j lives in A stage j % 2 and B stage j % 3.
+    // Step j waits until only this wave's youngest copy (the 4 B parts of
+    // slab j + 1) may still be in flight, then prefetches the scales and A of
+    // slab j + 1 and the B of slab j + 2, in that order (the wait count
+    // relies on it). Clamped slab indices keep the tail branch-free.
+    auto mainloop_deep = [&](auto act_tag) {
+        constexpr int ACT = decltype(act_tag)::value;
+        float sa_nx[kMSub], sb_nx;
+        auto copy_all_a = [&](int jj, auto st) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) copy_a(jj, st, i);
+        };
+        auto copy_all_b = [&](int jj, auto st) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) copy_b(jj, st, i);
+        };
+        auto step = [&](auto a_tag, auto b_tag, int j) {
+            constexpr int AS = decltype(a_tag)::value;
+            constexpr int BS = decltype(b_tag)::value;
+            wait_dma_and_barrier<4>();
+            float sab[kMSub];
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) sab[s] = sa_nx[s] * sb_nx;
+            load_scales(min(j + 1, slabs - 1), sa_nx, sb_nx);
+            copy_all_a(min(j + 1, slabs - 1), std::integral_constant<int, AS ^ 1>{});
+            __builtin_amdgcn_sched_barrier(0);
+            copy_all_b(min(j + 2, slabs - 1), std::integral_constant<int, (BS + 2) % 3>{});
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (ACT > 0) compute(a_tag, b_tag, act_tag, sab);
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        if (slabs == 0) return;
+        load_scales(0, sa_nx, sb_nx);
+        copy_all_a(0, I0{});
+        __builtin_amdgcn_sched_barrier(0);
+        copy_all_b(0, I0{});
+        __builtin_amdgcn_sched_barrier(0);
+        copy_all_b(min(1, slabs - 1), I1{});
+        __builtin_amdgcn_sched_barrier(0);
+        int j = 0;
+        for (; j + 6 <= slabs; j += 6) {
+            step(I0{}, I0{}, j);
+            step(I1{}, I1{}, j + 1);
+            step(I0{}, I2{}, j + 2);
+            step(I1{}, I0{}, j + 3);
+            step(I0{}, I1{}, j + 4);
+            step(I1{}, I2{}, j + 5);
+        }
+        const int rem = slabs - j;
+        if (rem > 0) step(I0{}, I0{}, j);
+        if (rem > 1) step(I1{}, I1{}, j + 1);
+        if (rem > 2) step(I0{}, I2{}, j + 2);
+        if (rem > 3) step(I1{}, I0{}, j + 3);
+        if (rem > 4) step(I0{}, I1{}, j + 4);
+    };
     if constexpr (GROUPED) {
         // expert tails: only the live m-subtiles do MFMA work
         switch (act) {
-            case 4: mainloop(std::integral_constant<int, 4>{}); break;
-            case 3: mainloop(std::integral_constant<int, 3>{}); break;
-            case 2: mainloop(std::integral_constant<int, 2>{}); break;
-            case 1: mainloop(std::integral_constant<int, 1>{}); break;
-            default: mainloop(std::integral_constant<int, 0>{}); break;
+            case 4: mainloop_deep(std::integral_constant<int, 4>{}); break;
+            case 3: mainloop_deep(std::integral_constant<int, 3>{}); break;
+            case 2: mainloop_deep(std::integral_constant<int, 2>{}); break;
+            case 1: mainloop_deep(std::integral_constant<int, 1>{}); break;
+            default: mainloop_deep(std::integral_constant<int, 0>{}); break;
         }
     } else if (act > 0) {
         mainloop(std::integral_constant<int, 4>{});  // ragged-M rows are computed and dropped
     } else {
         mainloop(std::integral_constant<int, 0>{});
     }
-    // Drain the last (unused) prefetch before the block's LDS can be reused.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Drain the last (unused) prefetches before the block's LDS can be reused.
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
     // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
 #pragma unroll
@@ -555,23 +675,34 @@ Params to_params(const GemmProblem& g) {
     return p;
 }
 
-// blocks: a multiple of 8 (dense: slots rounded up; grouped: a multiple of
-// 256, see grouped_tile).
-template <int BN, bool GROUPED>
-hipError_t dispatch(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
+// blocks: the dense slots rounded up to a multiple of 8.
+template <int BN>
+hipError_t dispatch_dense(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
     const Params p = to_params(g);
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (g.b_rowscale) {
         if (g.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<BN, true, true, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, true, true, false>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<BN, true, false, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, true, false, false>), grid, block, 0, stream, p);
     } else {
         if (g.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<BN, false, true, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, false, true, false>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<BN, false, false, GROUPED>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, false, false, false>), grid, block, 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+// blocks: a multiple of 256 (see grouped_tile). Grouped GEMMs take 128x128
+// block scales only.
+hipError_t dispatch_grouped(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
+    const Params p = to_params(g);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (g.out_f32)
+        hipLaunchKernelGGL((gemm_kernel<256, false, true, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<256, false, false, true>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
@@ -589,17 +720,17 @@ hipError_t launch_gemm(const GemmProblem& g, hipStream_t stream) {
     // e.g. N = 7168 = 32 x 224 (Dgrad, Wgrad); otherwise 256-wide.
     if (grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256)) {
         const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
-        return dispatch<224, false>(g, (tiles + 7) / 8 * 8, stream);
+        return dispatch_dense<224>(g, (tiles + 7) / 8 * 8, stream);
     }
     const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
-    return dispatch<256, false>(g, (tiles + 7) / 8 * 8, stream);
+    return dispatch_dense<256>(g, (tiles + 7) / 8 * 8, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& g, hipStream_t stream) {
     // Upper bound on the tile count: every 256-row m-tile of an expert holds at
     // least 128 of its rows, so there are at most m_total / 128 of them.
     const int64_t tiles = (g.m / 128) * ((g.n + 255) / 256);
-    return dispatch<256, true>(g, (tiles + 255) / 256 * 256, stream);
+    return dispatch_grouped(g, (tiles + 255) / 256 * 256, stream);
 }
 
 }  // namespace fp8q
