@@ -100,6 +100,27 @@ def quant_act_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return q, s
 
 
+def quant_act_scatter(x: np.ndarray, dst_rows: np.ndarray, m_total: int):
+    """Quantize before dispatch (page "Eliminate Deepseek Ai News For Good",
+    passage on quantizing activations before the MoE dispatch): every token
+    row of bf16 X[tokens][cols] gets its 1x128 quantization, and the codes and
+    scales of token t go to each destination row dst_rows[t][k] in
+    [0, m_total). Returns (Q uint8[m_total][cols], S float32[cols/128][m_total],
+    written bool[m_total]); unwritten rows hold zeros."""
+    q_tok, s_tok = quant_act_1x128(x)
+    dst = np.asarray(dst_rows, dtype=np.int64)
+    tokens, cols = q_tok.shape
+    q = np.zeros((m_total, cols), dtype=np.uint8)
+    s = np.zeros((cols // 128, m_total), dtype=np.float32)
+    written = np.zeros(m_total, dtype=bool)
+    t_idx, k_idx = np.nonzero((dst >= 0) & (dst < m_total))
+    d = dst[t_idx, k_idx]
+    q[d] = q_tok[t_idx]
+    s[:, d] = s_tok[:, t_idx]
+    written[d] = True
+    return q, s, written
+
+
 def quant_act_128x1(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """bf16 bits X[tokens][cols] -> (QT uint8[cols][tokens], S float32[tokens/128][cols])."""
     x = np.ascontiguousarray(x, dtype=np.uint16)

@@ -436,3 +436,50 @@ def test_128x128_scale_placement_closed_form():
             blk = xf[128 * bn:128 * bn + 128, 128 * bk:128 * bk + 128].reshape(-1)[::37]
             got = q[128 * bn:128 * bn + 128, 128 * bk:128 * bk + 128].reshape(-1)[::37]
             assert list(got) == [oracle.e4m3_encode(float(v) * 2.0 ** -p[bn, bk]) for v in blk]
+
+
+def test_scatter_identity_route_is_the_tile_quantizer():
+    """Special case: one route per token to its own row is plain 1x128 quantization."""
+    x = wl.activation(0, "grouped_fprop", 50, 37, 256, 50.0)
+    dst = np.arange(37, dtype=np.int32)[:, None]
+    q, s, written = oracle.quant_act_scatter(x, dst, 37)
+    q_ref, s_ref = oracle.quant_act_1x128(x)
+    assert written.all()
+    assert np.array_equal(q, q_ref) and np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_scatter_rows_are_quantized_source_rows():
+    """Invariant (quantization commutes with row moves): each destination row
+    equals the 1x128 quantization of the bf16 row of its source token; a token
+    routed twice gives two identical rows; -1 and out-of-range routes write
+    nothing. Checked against quantizing the gathered bf16 rows directly."""
+    x = wl.activation(0, "grouped_fprop", 51, 6, 384, 50.0)
+    dst = np.array([[4, -1], [0, 7], [-1, -1], [2, 99], [5, 1], [-1, 3]], dtype=np.int32)
+    m_total = 9
+    q, s, written = oracle.quant_act_scatter(x, dst, m_total)
+    src = {4: 0, 0: 1, 7: 1, 2: 3, 5: 4, 1: 4, 3: 5}
+    assert sorted(np.nonzero(written)[0].tolist()) == sorted(src)
+    rows = sorted(src)
+    q_g, s_g = oracle.quant_act_1x128(np.stack([x[src[r]] for r in rows]))
+    assert np.array_equal(q[rows], q_g)
+    assert np.array_equal(s[:, rows].view(np.uint32), s_g.view(np.uint32))
+    assert np.array_equal(q[0], q[7]) and not q[6].any() and not q[8].any()
+
+
+def test_moe_dispatch_map_is_a_valid_layout():
+    """The seeded routing fills every real row of every expert segment exactly
+    once, in token order, with at most top_k routes per token."""
+    d = wl.moe_dispatch(0, k=128)
+    dst, rows, off = d["dst_rows"], d["rows"], d["offsets"]
+    v = dst[dst >= 0]
+    assert len(v) == rows.sum() and len(np.unique(v)) == len(v)
+    real = np.concatenate([np.arange(off[e], off[e] + rows[e]) for e in range(len(rows))])
+    assert np.array_equal(np.sort(v), real)
+    assert (dst >= 0).sum(axis=1).max() <= dst.shape[1]
+    t_idx, k_idx = np.nonzero(dst >= 0)
+    d = dst[t_idx, k_idx]
+    order = np.argsort(d)
+    tok_by_row, row_sorted = t_idx[order], d[order]
+    seg = np.searchsorted(off, row_sorted, side="right") - 1
+    same = seg[1:] == seg[:-1]
+    assert np.all(np.diff(tok_by_row)[same] > 0)      # token order inside each segment

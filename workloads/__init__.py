@@ -164,3 +164,37 @@ def grouped_fprop(seed: int = 0, n: int = 4096, k: int = 7168, experts: int = 32
     if with_weights:
         out["w"] = weight(seed, "grouped_fprop", 1, len(rows), n, k)
     return out
+
+
+def moe_dispatch(seed: int = 0, k: int = 7168, tokens: int = 8192, top_k: int = 8,
+                 rows: np.ndarray | None = None) -> dict:
+    """Token activations and their routes into the expert-sorted layout.
+
+    Expert e's rows (moe_rows) are r_e distinct tokens drawn uniformly without
+    replacement, kept in token order inside the expert's 128-padded segment.
+    dst_rows[t] lists token t's destination rows in increasing expert order,
+    -1 past its last route; a draw that gives some token more than top_k
+    routes is redrawn (next stream of the same seed).
+    """
+    if rows is None:
+        rows = moe_rows(seed, tokens=tokens, top_k=top_k)
+    rows = np.asarray(rows, dtype=np.int64)
+    offsets = pad_offsets(rows)
+    for attempt in range(64):
+        rng = _rng(seed, "grouped_fprop", 3 + attempt)
+        dst = np.full((tokens, top_k), -1, dtype=np.int32)
+        fill = np.zeros(tokens, dtype=np.int64)
+        ok = True
+        for e in range(len(rows)):
+            toks = np.sort(rng.choice(tokens, size=int(rows[e]), replace=False))
+            if np.any(fill[toks] >= top_k):
+                ok = False
+                break
+            dst[toks, fill[toks]] = offsets[e] + np.arange(len(toks), dtype=np.int64)
+            fill[toks] += 1
+        if ok:
+            break
+    else:  # pragma: no cover - needs an absurd routing skew
+        raise RuntimeError("no routing with at most top_k routes per token")
+    x = activation(seed, "grouped_fprop", 2, tokens, k, 50.0)
+    return {"x": x, "dst_rows": dst, "rows": rows, "offsets": offsets}
