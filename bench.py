@@ -44,7 +44,8 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Kernel name fragments (as rocprofv3 prints them) for each launch label.
 KERNEL_NAMES = {
-    "quant_act_1x128": "quant_act_1x128_kernel",
+    "quant_act_1x128": "quant_act_1x128_kernel<false>",
+    "quant_act_scatter": "quant_act_1x128_kernel<true>",
     "quant_act_128x1": "quant_act_128x1_kernel",
     "quant_weight": "quant_weight_kernel",
     "gemm": "gemm_kernel",
@@ -183,24 +184,29 @@ class Workload:
             ]
             self.desc = {"workload": name, "m": n_out, "n": k_in, "k": t,
                          "dy, x": "bf16, 128x1 tiles (along tokens)", "out": "fp32"}
-        else:  # grouped_fprop
-            g = wl.grouped_fprop()
-            rows = g["rows"]
-            X = sets(g["x"])
-            E, n, k = g["w"].shape
-            w = dev(g["w"].reshape(E * n, k))   # 1.8 GB: already far beyond the MALL
-            m_total = X[0].shape[0]
+        else:  # grouped_fprop: quantize the tokens before dispatch, then the expert GEMM
+            d = wl.moe_dispatch()
+            rows = d["rows"]
+            X = sets(d["x"])
+            E, n, k = len(rows), 4096, X[0].shape[1]
+            # the expert weights of the grouped MoE config (1.9 GB: far beyond the MALL)
+            w = dev(wl.weight(0, "grouped_fprop", 1, E, n, k).reshape(E * n, k))
+            tokens = X[0].shape[0]
+            m_total = int(d["offsets"][-1])
             real = int(rows.sum())
-            off = torch.from_numpy(g["offsets"].astype("int32")).cuda()
+            off = torch.from_numpy(d["offsets"].astype("int32")).cuda()
             rws = torch.from_numpy(rows.astype("int32")).cuda()
+            dst = torch.from_numpy(d["dst_rows"]).cuda()
             xq, xs = empty((m_total, k), u8), empty((k // 128, m_total), f32)
             wq, ws = empty((E * n, k), u8), empty((E * n // 128, k // 128), f32)
             y = empty((m_total, n), bf16)
             self.flops = 2.0 * real * n * k   # real rows only
             nb = E * (n // 128) * (k // 128)
             self.launches = [
-                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(X[r], "1x128", q=xq, scale=xs),
-                       act_bytes(m_total, k)),
+                # tokens read once; every route writes its codes and scales
+                Launch("quant_act_scatter", lambda r: fq.fp8_quantize_act_scatter(
+                    X[r], dst, m_total, q=xq, scale=xs),
+                       2 * tokens * k + real * (k + 4 * k // 128)),
                 Launch("quant_weight", lambda r: fq.fp8_quantize_weight(w, q=wq, scale=ws),
                        3 * E * n * k + 4 * nb),
                 # real rows of A read; every padded row of C written (padding rows are zeroed)
@@ -208,8 +214,9 @@ class Workload:
                     off, rws, xq, xs, wq.view(E, n, k), ws.view(E, n // 128, k // 128), bf16, out=y),
                        gemm_bytes(real, E * n, k, nb, 2, 0) + 2 * m_total * n, self.flops),
             ]
-            self.desc = {"workload": name, "experts": E, "rows_real": real,
-                         "rows_padded": m_total, "n": n, "k": k, "out": "bf16"}
+            self.desc = {"workload": name, "experts": E, "tokens": tokens, "top_k": 8,
+                         "rows_real": real, "rows_padded": m_total, "n": n, "k": k,
+                         "x": "bf16 tokens, quantized 1x128 before dispatch", "out": "bf16"}
         self.rotate, self.count = rotate, 0
         self.desc["input_sets"] = rotate
         torch.cuda.synchronize()

@@ -33,6 +33,7 @@ import torch
 
 __all__ = [
     "fp8_quantize_act",
+    "fp8_quantize_act_scatter",
     "fp8_quantize_weight",
     "fp8_gemm",
     "fp8_grouped_gemm",
@@ -74,6 +75,7 @@ def _load() -> ctypes.CDLL:
     L = ctypes.CDLL(_LIB_PATH)
     p, i64, i32, cint = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     L.fp8_quantize_act.argtypes = [p, i64, i64, i64, cint, p, i64, p, i64, p]
+    L.fp8_quantize_act_scatter.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, cint, p, i64, cint, p]
     L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
@@ -167,6 +169,41 @@ def fp8_quantize_act(x: torch.Tensor, tiling: str = "1x128", q: torch.Tensor | N
     st = _load().fp8_quantize_act(_ptr(x), rows, cols, x.stride(0), t, _ptr(q), q.stride(0),
                                   _ptr(scale), scale.stride(0), _stream(stream))
     _check(st, "fp8_quantize_act")
+    return q, scale
+
+
+def fp8_quantize_act_scatter(x: torch.Tensor, dst_rows: torch.Tensor, m_total: int,
+                             q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                             stream=None):
+    """Quantize bf16 token rows once (1x128 tiles) and scatter codes and
+    scales to their expert-sorted destination rows.
+
+    ``dst_rows`` is an int32 device tensor ``[tokens][topk]`` (topk 1..8) of
+    destination rows in ``q``, -1 for routes outside this layout. Returns
+    ``q[m_total][cols]`` and ``scale[cols/128][m_total]``; rows no route names
+    (segment padding) are left as they were.
+    """
+    _need_gpu(x, dst_rows)
+    _rowmajor(x, "x")
+    if not dst_rows.is_contiguous():
+        raise Fp8qError("dst_rows must be contiguous [tokens][topk]")
+    if x.dtype != torch.bfloat16:
+        raise Fp8qError("x must be bfloat16")
+    if dst_rows.dtype != torch.int32 or dst_rows.dim() != 2 or dst_rows.shape[0] != x.shape[0]:
+        raise Fp8qError("dst_rows must be int32 [tokens][topk]")
+    tokens, cols = x.shape
+    topk = dst_rows.shape[1]
+    dev = x.device
+    if q is None:
+        q = torch.empty((m_total, cols), dtype=torch.float8_e4m3fn, device=dev)
+    if scale is None:
+        scale = torch.empty((cols // 128, m_total), dtype=torch.float32, device=dev)
+    _need_gpu(q, scale)
+    _codes(q, "q")
+    st = _load().fp8_quantize_act_scatter(_ptr(x), tokens, cols, x.stride(0), topk, _ptr(dst_rows),
+                                          m_total, _ptr(q), q.stride(0), _ptr(scale),
+                                          scale.stride(0), _stream(stream))
+    _check(st, "fp8_quantize_act_scatter")
     return q, scale
 
 

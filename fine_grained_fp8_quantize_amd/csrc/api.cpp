@@ -62,6 +62,21 @@ int fp8_quantize_act(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x
     return hip_status(fp8q::launch_quant_act_128x1(x, rows, cols, ld_x, q, ld_q, scale, ld_s, stream));
 }
 
+int fp8_quantize_act_scatter(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
+                             int32_t topk, const int32_t* dst_rows, int64_t m_total, uint8_t* q,
+                             int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream) {
+    if (tokens < 0 || cols < 0 || m_total < 0 || topk < 1 || topk > 8) return FP8Q_ERR_SHAPE;
+    if (tokens == 0 || cols == 0 || m_total == 0) return FP8Q_OK;
+    if (!x || !dst_rows || !q || !scale) return FP8Q_ERR_NULL;
+    if (cols % 128 != 0 || ld_x < cols || ld_q < cols || ld_s < m_total) return FP8Q_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || !aligned(dst_rows, 4) ||
+        ld_x % 8 != 0 || ld_q % 16 != 0)
+        return FP8Q_ERR_ALIGN;
+    if (!grid_ok((tokens + 15) / 16 * (cols / 128) / 4 + 1)) return FP8Q_ERR_SHAPE;
+    return hip_status(fp8q::launch_quant_act_scatter(x, tokens, cols, ld_x, topk, dst_rows, m_total, q,
+                                                     ld_q, scale, ld_s, stream));
+}
+
 int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
                         uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                         uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,

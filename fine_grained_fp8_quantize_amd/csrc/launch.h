@@ -11,6 +11,10 @@ hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols,
                                   uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                                   hipStream_t stream);
 
+hipError_t launch_quant_act_scatter(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
+                                    int topk, const int32_t* dst_rows, int64_t m_total, uint8_t* q,
+                                    int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream);
+
 hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
                                   uint8_t* qt, int64_t ld_q, float* scale, int64_t ld_s,
                                   hipStream_t stream);

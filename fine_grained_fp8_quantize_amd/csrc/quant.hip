@@ -19,13 +19,20 @@ namespace {
 // One wave quantizes 16 rows of one 128-column slab (16 tiles). Lane
 // 16*rr + c holds the 16-byte chunk c (8 bf16) of rows 4u + rr, u = 0..3, so
 // each 1x128 tile is one DPP row of 16 lanes and its amax reduces in-row.
+//
+// SCATTER (quantize before dispatch): source row t is quantized once and
+// its codes and scale are stored to every destination row dst[t][k] >= 0,
+// k < topk, of the expert-sorted layout (page "Eliminate Deepseek Ai News For
+// Good", passage on quantizing activations before the MoE dispatch).
 constexpr int kActRowsPerWave = 16;
 constexpr int kActWavesPerBlock = 4;
+constexpr int kMaxTopk = 8;  // destinations per source row (scatter)
 
+template <bool SCATTER>
 __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
-    int64_t units) {
+    int64_t units, const int32_t* __restrict__ dst, int topk, int64_t m_total) {
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * kActWavesPerBlock + (threadIdx.x >> 6);
     if (unit >= units) return;  // whole wave
@@ -41,6 +48,15 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
         v[u] = make_uint4(0, 0, 0, 0);
         if (row[u] < rows)
             v[u] = load_nt16(x + row[u] * ld_x + j * 128 + c * 8);
+    }
+    // destinations of the lane's four rows, loaded alongside the data
+    int32_t d[SCATTER ? 4 : 1][SCATTER ? kMaxTopk : 1];
+    if constexpr (SCATTER) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < kMaxTopk; ++k)
+                d[u][k] = (row[u] < rows && k < topk) ? dst[row[u] * topk + k] : -1;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -62,8 +78,18 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
         const uint32_t w0 = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[u].x, v[u].y));
         const uint32_t w1 = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[u].z, v[u].w));
         if (row[u] < rows) {
-            *reinterpret_cast<uint2*>(q + row[u] * ld_q + j * 128 + c * 8) = make_uint2(w0, w1);
-            if (c == 0) scale[j * ld_s + row[u]] = g.s;
+            if constexpr (SCATTER) {
+#pragma unroll
+                for (int k = 0; k < kMaxTopk; ++k) {
+                    const int64_t dk = d[u][k];
+                    if (dk < 0 || dk >= m_total) continue;  // not routed here (or out of contract)
+                    *reinterpret_cast<uint2*>(q + dk * ld_q + j * 128 + c * 8) = make_uint2(w0, w1);
+                    if (c == 0) scale[j * ld_s + dk] = g.s;
+                }
+            } else {
+                *reinterpret_cast<uint2*>(q + row[u] * ld_q + j * 128 + c * 8) = make_uint2(w0, w1);
+                if (c == 0) scale[j * ld_s + row[u]] = g.s;
+            }
         }
     }
 }
@@ -250,8 +276,19 @@ hipError_t launch_quant_act_1x128(const uint16_t* x, int64_t rows, int64_t cols,
     const int64_t slabs = cols / 128;
     const int64_t units = (rows + kActRowsPerWave - 1) / kActRowsPerWave * slabs;
     const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
-    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units);
+    hipLaunchKernelGGL(quant_act_1x128_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units, nullptr, 0, (int64_t)0);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_scatter(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
+                                    int topk, const int32_t* dst_rows, int64_t m_total, uint8_t* q,
+                                    int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream) {
+    const int64_t slabs = cols / 128;
+    const int64_t units = (tokens + kActRowsPerWave - 1) / kActRowsPerWave * slabs;
+    const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
+    hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, tokens, slabs, ld_x, q, ld_q, scale, ld_s, units, dst_rows, topk, m_total);
     return hipGetLastError();
 }
 

@@ -95,6 +95,37 @@ int fp8_quantize_act(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x
                      uint8_t *q, int64_t ld_q, float *scale, int64_t ld_s, hipStream_t stream);
 
 /*
+ * fp8_quantize_act_scatter -- quantize before the MoE dispatch.
+ *
+ * Page "Eliminate Deepseek Ai News For Good", passage on quantizing the
+ * activations into FP8 before the MoE dispatch, compatible with the FP8 Fprop
+ * of the expert up-projections; 1x128 tiles as in fp8_quantize_act. Each
+ * token row of x is quantized once; its codes and scales are stored to every
+ * row of the expert-sorted layout (the A operand of fp8_grouped_gemm) that
+ * the routing sends it to. Row r of q then equals what fp8_quantize_act
+ * writes for the token routed to r (quantization commutes with row moves).
+ *
+ * x        bf16 tokens [tokens][ld_x], ld_x >= cols, cols % 128 == 0.
+ * topk     destinations per token, 1..8.
+ * dst_rows device int32 [tokens][topk]: the destination row in q of token t's
+ *          k-th route, or -1 (not routed to this layout). Values >= m_total
+ *          are ignored. Each destination row should be named once; a row
+ *          named by several tokens ends up with one of their codes.
+ * q        codes [m_total][ld_q], ld_q >= cols. scale [cols/128][ld_s] with
+ *          ld_s >= m_total. Rows named by no route (the 128-row padding of
+ *          each expert segment) are not written; fp8_grouped_gemm never lets
+ *          their contents reach a stored output.
+ * Alignment: x and q 16-byte aligned; ld_x % 8 == 0; ld_q % 16 == 0; scale
+ *          and dst_rows 4-byte aligned.
+ * tokens, cols or m_total == 0: returns FP8Q_OK without launching.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE (also topk outside 1..8),
+ *         FP8Q_ERR_ALIGN, FP8Q_ERR_HIP.
+ */
+int fp8_quantize_act_scatter(const uint16_t *x, int64_t tokens, int64_t cols, int64_t ld_x,
+                             int32_t topk, const int32_t *dst_rows, int64_t m_total, uint8_t *q,
+                             int64_t ld_q, float *scale, int64_t ld_s, hipStream_t stream);
+
+/*
  * fp8_quantize_weight -- 128x128 block weight quantization.
  *
  * Blocks: page dssusan.co.kr Q&A board, passage on Figure 7(a) (per 128 input
@@ -169,6 +200,8 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
  * m_total       rows of A and C (host copy of group_offsets[groups]),
  *               m_total % 128 == 0.
  * a, a_scale    codes [m_total][lda], scales [k/128][ld_as], ld_as >= m_total.
+ *               The codes and scales of padding rows may hold any bytes: they
+ *               feed only padding rows of C, which are written as zeros.
  * b             expert weights: expert e at b + e * stride_b, codes [n][ldb].
  * b_scale       expert e at b_scale + e * stride_bs, [n/128][ld_bs].
  * c             [m_total][ldc]; out_dtype as in fp8_gemm.

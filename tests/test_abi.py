@@ -115,6 +115,26 @@ def test_quantize_act_ld_alignment_rule(lib):
     assert _act(lib, ld_q=520) == ERR_ALIGN
 
 
+def _sc(lib, x=A16, tokens=100, cols=512, ld_x=512, topk=8, dst=A4, m_total=256, q=A16b, ld_q=512,
+        s=A4, ld_s=256):
+    return lib.fp8_quantize_act_scatter(x, tokens, cols, ld_x, topk, dst, m_total, q, ld_q, s, ld_s, None)
+
+
+def test_quantize_act_scatter_validation(lib):
+    assert _sc(lib, tokens=0) == OK
+    assert _sc(lib, m_total=0) == OK
+    assert _sc(lib, tokens=-1) == ERR_SHAPE
+    assert _sc(lib, topk=0) == ERR_SHAPE                  # 1..8 routes per token
+    assert _sc(lib, topk=9) == ERR_SHAPE
+    assert _sc(lib, dst=0) == ERR_NULL
+    assert _sc(lib, x=0) == ERR_NULL
+    assert _sc(lib, cols=500, ld_x=512, ld_q=512) == ERR_SHAPE
+    assert _sc(lib, ld_s=255) == ERR_SHAPE                # scale ld below m_total
+    assert _sc(lib, ld_q=256) == ERR_SHAPE
+    assert _sc(lib, dst=A4 + 2) == ERR_ALIGN
+    assert _sc(lib, q=A16b + 8) == ERR_ALIGN
+
+
 def _w(lib, w=A16, n=256, k=384, ld_w=384, q=A16b, ld_q=384, s=A4, ld_s=3, qt=0, ld_qt=0, st=0, ld_st=0):
     return lib.fp8_quantize_weight(w, n, k, ld_w, q, ld_q, s, ld_s, qt, ld_qt, st, ld_st, None)
 
@@ -179,7 +199,8 @@ def test_grouped_gemm_validation(lib):
 
 
 def test_binding_names_match_c_entry_points():
-    for name in ("fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm", "fp8_grouped_gemm"):
+    for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
+                 "fp8_grouped_gemm"):
         assert callable(getattr(fq, name))
 
 

@@ -35,12 +35,12 @@ def test_pmc_summary_scales_by_the_copy_calibration(tmp_path):
     fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
     # the copy reads 1 MiB but the fetch counter shows half of it (KiB units)
     _write(fetch, "FETCH_SIZE", [(1, "__amd_rocclr_copyBuffer", 512.0),
-                                 (2, "fp8q::quant_act_1x128_kernel(...)", 1.0),
+                                 (2, "void fp8q::quant_act_1x128_kernel<false>(...)", 1.0),
                                  (3, "void fp8q::gemm_kernel<256>(Params)", 4.0),
                                  (4, "void fp8q::gemm_kernel<256>(Params)", 6.0),
                                  (5, "at::native::other", 99.0)])
     _write(write, "WRITE_SIZE", [(1, "__amd_rocclr_copyBuffer", 1024.0),
-                                 (2, "fp8q::quant_act_1x128_kernel(...)", 2.0),
+                                 (2, "void fp8q::quant_act_1x128_kernel<false>(...)", 2.0),
                                  (3, "void fp8q::gemm_kernel<256>(Params)", 3.0),
                                  (4, "void fp8q::gemm_kernel<256>(Params)", 3.0)])
     out = str(tmp_path / "t.json")
