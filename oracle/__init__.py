@@ -230,6 +230,25 @@ def grouped_gemm(offsets: np.ndarray, rows: np.ndarray, a_q: np.ndarray, a_s: np
     return out
 
 
+def grouped_gemm_wgrad(offsets: np.ndarray, a_q: np.ndarray, a_s: np.ndarray, b_q: np.ndarray,
+                       b_s: np.ndarray) -> np.ndarray:
+    """MoE expert Wgrad: dW_e = GEMM over expert e's token slice [off_e, off_e+1)
+    of A = dY^T codes [m][k_total] and B = X^T codes [n][k_total], both with
+    per-(slab, row) scales [k_total/128][rows] (the Wgrad GEMM of page
+    dssusan.co.kr Q&A board, Figure 6, per expert). Returns float64 [E][m][n]."""
+    m, n = a_q.shape[0], b_q.shape[0]
+    E = len(offsets) - 1
+    out = np.zeros((E, m, n), dtype=np.float64)
+    for e in range(E):
+        t0, t1 = int(offsets[e]), int(offsets[e + 1])
+        if t1 == t0:
+            continue
+        out[e] = gemm(np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
+                      np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]),
+                      "row")
+    return out
+
+
 def bf16_round(a: np.ndarray) -> np.ndarray:
     """Round float64 values to bf16 (via float32, nearest-even each step) as float64.
 

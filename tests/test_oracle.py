@@ -483,3 +483,43 @@ def test_moe_dispatch_map_is_a_valid_layout():
     seg = np.searchsorted(off, row_sorted, side="right") - 1
     same = seg[1:] == seg[:-1]
     assert np.all(np.diff(tok_by_row)[same] > 0)      # token order inside each segment
+
+
+def _packed_tokens(rows, cols, tensor_id, grad=False):
+    """Expert-sorted bf16 rows (128-padded segments, zero padding rows)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    off = wl.pad_offsets(rows)
+    real = (wl.grad_rowscaled(0, "grouped_fprop", tensor_id, int(rows.sum()), cols) if grad
+            else wl.activation(0, "grouped_fprop", tensor_id, int(rows.sum()), cols, 50.0))
+    out = np.zeros((int(off[-1]), cols), np.uint16)
+    src = 0
+    for e in range(len(rows)):
+        out[off[e]:off[e] + rows[e]] = real[src:src + rows[e]]
+        src += int(rows[e])
+    return out, off
+
+
+def test_grouped_wgrad_sums_to_dense_wgrad():
+    """Invariant: with zero padding tokens, the expert gradients add up to the
+    dense Wgrad over all tokens (the pinned row-scale GEMM): every 128-token
+    slab belongs to one expert, so the sum regroups the same slab terms."""
+    rows = [5, 0, 130, 128, 1]
+    dy, off = _packed_tokens(rows, 256, 90, grad=True)
+    x, _ = _packed_tokens(rows, 384, 91)
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    b_q, b_s = oracle.quant_act_128x1(x)
+    per = oracle.grouped_gemm_wgrad(off, a_q, a_s, b_q, b_s)
+    dense = oracle.gemm(a_q, a_s, b_q, b_s, "row")
+    assert per.shape == (5, 256, 384)
+    assert not per[1].any()                                  # empty segment: zero gradient
+    np.testing.assert_allclose(per.sum(axis=0), dense, rtol=1e-12, atol=1e-12 * np.abs(dense).max())
+
+
+def test_grouped_wgrad_single_expert_is_dense_wgrad():
+    """Special case: one expert owning every token is the dense Wgrad GEMM."""
+    dy, off = _packed_tokens([256], 128, 92, grad=True)
+    x, _ = _packed_tokens([256], 256, 93)
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    b_q, b_s = oracle.quant_act_128x1(x)
+    per = oracle.grouped_gemm_wgrad(off, a_q, a_s, b_q, b_s)
+    assert np.array_equal(per[0], oracle.gemm(a_q, a_s, b_q, b_s, "row"))
