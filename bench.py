@@ -39,7 +39,8 @@ FP8_DENSE_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 MFMA (no sparsity)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak (1 GPU)"
-CONFIGS = ["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "tiny_fprop"]
+CONFIGS = ["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "grouped_dgrad", "grouped_wgrad",
+           "tiny_fprop"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Kernel name fragments (as rocprofv3 prints them) for each launch label.
@@ -121,7 +122,17 @@ class Workload:
         def gemm_bytes(m_a, n, k, b_scale_count, out_elem, m_out):
             return m_a * k + n * k + 4 * m_a * (k // 128) + 4 * b_scale_count + out_elem * m_out * n
 
+        def packed(real_bits, off, rows):
+            # expert-sorted rows, 128-padded segments, zero padding rows
+            out = np.zeros((int(off[-1]), real_bits.shape[1]), np.uint16)
+            src = 0
+            for e in range(len(rows)):
+                out[off[e]:off[e] + rows[e]] = real_bits[src:src + rows[e]]
+                src += int(rows[e])
+            return out
+
         self.host = None
+        self.bound = "mfma"
         if name in ("dense_fprop", "tiny_fprop"):
             d = wl.dense_fprop() if name == "dense_fprop" else wl.tiny_fprop()
             self.host = d
@@ -184,6 +195,64 @@ class Workload:
             ]
             self.desc = {"workload": name, "m": n_out, "n": k_in, "k": t,
                          "dy, x": "bf16, 128x1 tiles (along tokens)", "out": "fp32"}
+        elif name == "grouped_dgrad":
+            # MoE up-projection Dgrad: dX_e = dY_e W_e with each expert's transposed copy
+            rows = wl.moe_rows(0)
+            off = wl.pad_offsets(rows)
+            E, n_out, k_in = len(rows), 4096, 7168
+            real = int(rows.sum())
+            m_total = int(off[-1])
+            DY = sets(packed(wl.grad_rowscaled(0, "grouped_fprop", 4, real, n_out), off, rows))
+            w = dev(wl.weight(0, "grouped_fprop", 1, E, n_out, k_in))
+            offd = torch.from_numpy(off.astype("int32")).cuda()
+            rws = torch.from_numpy(rows.astype("int32")).cuda()
+            dq, ds = empty((m_total, n_out), u8), empty((n_out // 128, m_total), f32)
+            wq, ws = empty((E, n_out, k_in), u8), empty((E, n_out // 128, k_in // 128), f32)
+            wqt, wst = empty((E, k_in, n_out), u8), empty((E, k_in // 128, n_out // 128), f32)
+            y = empty((m_total, k_in), bf16)
+            self.flops = 2.0 * real * k_in * n_out
+            nb = E * (n_out // 128) * (k_in // 128)
+
+            def quant_w(r):
+                for e in range(E):
+                    fq.fp8_quantize_weight(w[e], transposed=True, q=wq[e], scale=ws[e], q_t=wqt[e],
+                                           scale_t=wst[e])
+            self.launches = [
+                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(DY[r], "1x128", q=dq, scale=ds),
+                       act_bytes(m_total, n_out)),
+                Launch("quant_weight", quant_w, 4 * E * n_out * k_in + 8 * nb),
+                Launch("gemm", lambda r: fq.fp8_grouped_gemm(offd, rws, dq, ds, wqt, wst, bf16, out=y),
+                       gemm_bytes(real, E * k_in, n_out, nb, 2, 0) + 2 * m_total * k_in, self.flops),
+            ]
+            self.desc = {"workload": name, "experts": E, "rows_real": real, "rows_padded": m_total,
+                         "n": k_in, "k": n_out, "dy": "bf16, 1x128 tiles",
+                         "w": "bf16, 128x128 blocks, transposed copy per expert", "out": "bf16"}
+        elif name == "grouped_wgrad":
+            # MoE up-projection Wgrad: dW_e = dY_e^T X_e over each expert's tokens
+            rows = wl.moe_rows(0)
+            off = wl.pad_offsets(rows)
+            E, n_out, k_in = len(rows), 4096, 7168
+            real = int(rows.sum())
+            m_total = int(off[-1])
+            DY = sets(packed(wl.grad_rowscaled(0, "grouped_fprop", 4, real, n_out), off, rows))
+            X = sets(packed(wl.activation(0, "grouped_fprop", 5, real, k_in, 50.0), off, rows))
+            offd = torch.from_numpy(off.astype("int32")).cuda()
+            aq, as_ = empty((n_out, m_total), u8), empty((m_total // 128, n_out), f32)
+            bq, bs = empty((k_in, m_total), u8), empty((m_total // 128, k_in), f32)
+            y = empty((E, n_out, k_in), f32)
+            self.flops = 2.0 * real * n_out * k_in   # real tokens only
+            self.bound = "hbm"                        # 3.8 GB of fp32 gradients written
+            self.launches = [
+                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
+                       act_bytes(m_total, n_out)),
+                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(X[r], "128x1", q=bq, scale=bs),
+                       act_bytes(m_total, k_in)),
+                Launch("gemm", lambda r: fq.fp8_grouped_gemm_wgrad(offd, aq, as_, bq, bs, f32, out=y),
+                       (n_out + k_in) * m_total * (1 + 4 / 128) + 4 * E * n_out * k_in, self.flops),
+            ]
+            self.desc = {"workload": name, "experts": E, "tokens_real": real, "tokens_padded": m_total,
+                         "m": n_out, "n": k_in, "dy, x": "bf16, 128x1 tiles (along tokens)",
+                         "out": "fp32 [experts][m][n]"}
         else:  # grouped_fprop: quantize the tokens before dispatch, then the expert GEMM
             d = wl.moe_dispatch()
             rows = d["rows"]
@@ -413,6 +482,7 @@ def main():
         kernels[key] = ent
     gemm = [(ln, t) for ln, t in zip(wl_obj.launches, launch_ms) if ln.label == "gemm"][0]
     gemm_tflops = gemm[0].flops / (gemm[1] * 1e-3) / 1e12
+    gemm_gbs = gemm[0].bytes / (gemm[1] * 1e-3) / 1e9
 
     out = {
         "metric": METRIC,
@@ -430,16 +500,26 @@ def main():
         "data": "synthetic (seeded; see workloads/)",
         "config": wl_obj.desc,
         "pct_of_fp8_peak": round(100.0 * value / FP8_DENSE_PEAK_TFLOPS, 2),
-        "roofline": {
+        "roofline": dict(({
             "bound": "mfma",
             "achieved": round(gemm_tflops, 2),
             "peak": FP8_DENSE_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / FP8_DENSE_PEAK_TFLOPS, 4),
+        } if wl_obj.bound == "mfma" else {
+            "bound": "hbm",
+            "achieved": round(gemm_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
+        }), **{
             "traffic": traffic["gemm"]["traffic_bytes"] if traffic and "gemm" in traffic else None,
-            "kernel": "gemm_kernel" + (" (grouped)" if args.config == "grouped_fprop" else ""),
+            "kernel": "gemm_kernel" + ({"grouped_fprop": " (grouped over M)",
+                                        "grouped_dgrad": " (grouped over M)",
+                                        "grouped_wgrad": " (grouped over K)"}.get(args.config, "")),
             "algorithmic_bytes": int(gemm[0].bytes),
-        },
+            "tflops": round(gemm_tflops, 2),
+        }),
         "kernels": kernels,
         "wall_s": round(t_wall, 3),
         "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),

@@ -37,6 +37,7 @@ __all__ = [
     "fp8_quantize_weight",
     "fp8_gemm",
     "fp8_grouped_gemm",
+    "fp8_grouped_gemm_wgrad",
     "fp8q_status_string",
     "fp8q_last_hip_error",
     "Fp8qError",
@@ -78,9 +79,12 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_act_scatter.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, cint, p, i64, cint, p]
+    L.fp8_grouped_gemm_wgrad.argtypes = [i32, p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64,
+                                         p, i64, i64, cint, p]
     L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
                                    i64, p, i64, cint, p]
-    for name in ("fp8_quantize_act", "fp8_quantize_weight", "fp8_gemm", "fp8_grouped_gemm"):
+    for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
+                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad"):
         getattr(L, name).restype = cint
     L.fp8q_status_string.argtypes = [cint]
     L.fp8q_status_string.restype = ctypes.c_char_p
@@ -123,7 +127,8 @@ def _need_gpu(*ts: torch.Tensor) -> None:
 
 
 def _rowmajor(t: torch.Tensor, name: str) -> None:
-    if t.dim() != 2 or t.stride(1) != 1:
+    # an empty matrix has no layout to check (numpy hands out zero strides)
+    if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
         raise Fp8qError("%s must be a 2-D tensor with unit column stride" % name)
 
 
@@ -316,4 +321,41 @@ def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | Non
         _ptr(b), b.stride(1), b.stride(0), _ptr(b_scale), b_scale.stride(1), b_scale.stride(0),
         _ptr(out), out.stride(0), oc, _stream(stream))
     _check(st, "fp8_grouped_gemm")
+    return out
+
+
+def fp8_grouped_gemm_wgrad(group_offsets: torch.Tensor, a: torch.Tensor, a_scale: torch.Tensor,
+                           b: torch.Tensor, b_scale: torch.Tensor, out_dtype=torch.float32,
+                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """MoE expert Wgrad: ``out[e] = sum over e's tokens t of A[:, t] B[:, t]^T``.
+
+    ``a``: dY^T codes ``[m][k_total]`` and ``a_scale[k_total/128][m]`` (from
+    ``fp8_quantize_act(dY, "128x1")`` on the expert-sorted layout); ``b``: X^T
+    codes ``[n][k_total]``, ``b_scale[k_total/128][n]``; ``group_offsets``:
+    int32 GPU tensor ``[E+1]`` of token offsets (multiples of 128). Returns
+    ``out[E][m][n]``.
+    """
+    _need_gpu(group_offsets, a, a_scale, b, b_scale, out)
+    _rowmajor(a, "a")
+    _rowmajor(b, "b")
+    _codes(a, "a")
+    _codes(b, "b")
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1:
+        raise Fp8qError("group_offsets must be a 1-D int32 tensor")
+    groups = group_offsets.numel() - 1
+    m, k_total = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k_total:
+        raise Fp8qError("a and b must cover the same tokens")
+    oc = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((groups, m, n), dtype=out_dtype, device=a.device)
+    if out.dim() != 3 or out.stride(2) != 1:
+        raise Fp8qError("out must be [E][m][n] with unit column stride")
+    st = _load().fp8_grouped_gemm_wgrad(
+        groups, _ptr(group_offsets), k_total, m, n,
+        _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
+        _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0),
+        _ptr(out), out.stride(1), out.stride(0), oc, _stream(stream))
+    _check(st, "fp8_grouped_gemm_wgrad")
     return out

@@ -99,10 +99,12 @@ static int check_gemm_common(int64_t m, int64_t n, int64_t k, const uint8_t* a, 
                              const float* a_scale, int64_t ld_as, const uint8_t* b, int64_t ldb,
                              const float* b_scale, void* c, int64_t ldc, int out_dtype) {
     if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
-    if (!a || !b || !c || (k > 0 && (!a_scale || !b_scale))) return FP8Q_ERR_NULL;
-    if (k % 128 != 0 || lda < k || ldb < k || ldc < n || (k > 0 && ld_as < m)) return FP8Q_ERR_SHAPE;
-    if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16) || !aligned(a_scale, 4) ||
-        !aligned(b_scale, 4) || lda % 16 != 0 || ldb % 16 != 0 || ldc % 8 != 0)
+    // k == 0: C is all zeros; A, B and their scales are not read (may be NULL)
+    if (!c || (k > 0 && (!a || !b || !a_scale || !b_scale))) return FP8Q_ERR_NULL;
+    if (k % 128 != 0 || ldc < n || (k > 0 && (lda < k || ldb < k || ld_as < m))) return FP8Q_ERR_SHAPE;
+    if (!aligned(c, 16) || ldc % 8 != 0) return FP8Q_ERR_ALIGN;
+    if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
+                  lda % 16 != 0 || ldb % 16 != 0))
         return FP8Q_ERR_ALIGN;
     return FP8Q_OK;
 }
@@ -154,6 +156,31 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     g.groups = groups; g.group_offsets = group_offsets; g.group_rows = group_rows;
     g.stride_b = stride_b; g.stride_bs = stride_bs;
     return hip_status(fp8q::launch_grouped_gemm(g, stream));
+}
+
+int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t* group_offsets, int64_t k_total,
+                           int64_t m, int64_t n,
+                           const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
+                           const uint8_t* b, int64_t ldb, const float* b_scale, int64_t ld_bs,
+                           void* c, int64_t ldc, int64_t stride_c, int out_dtype, hipStream_t stream) {
+    if (groups < 0 || k_total < 0 || m < 0 || n < 0) return FP8Q_ERR_SHAPE;
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
+    if (groups == 0 || m == 0 || n == 0) return FP8Q_OK;
+    if (!group_offsets) return FP8Q_ERR_NULL;
+    int st = check_gemm_common(m, n, k_total, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
+    if (st != FP8Q_OK) return st;
+    if (k_total > 0x7FFFFFFFLL || (k_total > 0 && ld_bs < n) || stride_c < m * ldc) return FP8Q_ERR_SHAPE;
+    if (stride_c % 8 != 0) return FP8Q_ERR_ALIGN;
+    if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) * groups + 256)) return FP8Q_ERR_SHAPE;
+    fp8q::GemmProblem g = {};
+    g.m = m; g.n = n; g.k = k_total;
+    g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;
+    g.b = b; g.ldb = ldb; g.b_scale = b_scale; g.ld_bs = ld_bs;
+    g.b_rowscale = true;
+    g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
+    g.groups = groups; g.group_offsets = group_offsets;
+    g.stride_c = stride_c;
+    return hip_status(fp8q::launch_grouped_k_gemm(g, stream));
 }
 
 }  // extern "C"

@@ -71,6 +71,7 @@ struct Params {
     const int32_t* group_rows;
     int64_t stride_b;
     int64_t stride_bs;
+    int64_t stride_c_bytes;  // grouped over K: distance between expert outputs
 };
 
 // Which rows of the output a block tile owns.
@@ -81,7 +82,17 @@ struct TileRows {
     int64_t n0;
     const uint8_t* b;
     const float* b_scale;
+    int slab0;         // first K slab of the tile's contraction
+    int slabs;         // number of K slabs
+    void* c;           // output matrix the tile belongs to
 };
+
+// Kernel modes: one GEMM; grouped over M (MoE Fprop/Dgrad: experts own row
+// segments, one weight each); grouped over K (MoE Wgrad: experts own token
+// segments of the contraction, one output each).
+constexpr int kDense = 0;
+constexpr int kGroupedM = 1;
+constexpr int kGroupedK = 2;
 
 // Dense tile order: block -> XCD x = block % 8 gets the contiguous slot
 // range [x*per, (x+1)*per); slots walk 4-row bands of tiles so the blocks
@@ -107,6 +118,9 @@ __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
     t.n0 = (int64_t)tn * BN;
     t.b = p.b;
     t.b_scale = p.b_scale;
+    t.slab0 = 0;
+    t.slabs = (int)(p.k / kSlab);
+    t.c = p.c;
     return true;
 }
 
@@ -194,11 +208,52 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
             t.n0 = (int64_t)tn * BN;
             t.b = p.b + e * p.stride_b;
             t.b_scale = p.b_scale + e * p.stride_bs;
+            t.slab0 = 0;
+            t.slabs = (int)(p.k / kSlab);
+            t.c = p.c;
             return true;
         }
         slot -= k * tiles_n;
     }
     return false;
+}
+
+// Grouped-over-K tiles (MoE Wgrad): expert e contracts over its token segment
+// [off[e], off[e+1]) (a multiple of 128: whole slabs) and owns the output
+// matrix c + e * stride_c. Every expert has the same tiles_m x tiles_n tiles;
+// slots run expert by expert, inside an expert in the dense order (bands of
+// 4 m-tiles). Blocks take slots in XCD rounds as grouped_tile does, so the
+// 32 tiles an XCD runs together share the expert's A and B panels in L2.
+// An expert without rows still writes its (zero) output.
+template <int BN>
+__device__ __forceinline__ bool grouped_k_tile(const Params& p, TileRows& t) {
+    const int tiles_m = (int)((p.m + kBM - 1) / kBM);
+    const int tiles_n = (int)((p.n + BN - 1) / BN);
+    const int per = tiles_m * tiles_n;
+    const int q = (int)(blockIdx.x >> 3);
+    const int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
+    if (slot >= per * p.groups) return false;
+    const int e = slot / per;
+    const int within_e = slot - e * per;
+    constexpr int G = 4;
+    const int group = within_e / (G * tiles_n);
+    const int first_m = group * G;
+    const int gm = min(tiles_m - first_m, G);
+    const int within = within_e - group * G * tiles_n;
+    const int beg = p.group_offsets[e];
+    const int seg = max(p.group_offsets[e + 1] - beg, 0);
+    // offsets that break the contract must not move reads outside A and B
+    if (beg < 0 || (int64_t)beg + seg > p.k) return false;
+    t.m0 = (int64_t)(first_m + within % gm) * kBM;
+    t.row_hi = p.m;
+    t.real_end = p.m;
+    t.n0 = (int64_t)(within / gm) * BN;
+    t.b = p.b;
+    t.b_scale = p.b_scale;
+    t.slab0 = beg / kSlab;
+    t.slabs = seg / kSlab;
+    t.c = static_cast<char*>(p.c) + (int64_t)e * p.stride_c_bytes;
+    return true;
 }
 
 // ---------------------------------------------------------------- LDS
@@ -263,8 +318,9 @@ __device__ __forceinline__ void unroll(std::integer_sequence<int, Is...>, F&& f)
 
 // ---------------------------------------------------------------- the kernel
 
-template <int BN, bool ROWSCALE, bool OUT_F32, bool GROUPED>
+template <int BN, bool ROWSCALE, bool OUT_F32, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
+    constexpr bool GROUPED = MODE == kGroupedM;
     static_assert(BN == 256 || BN == 224, "n tile");
     constexpr int WN = BN / 2;        // n extent of one wave
     constexpr int NSUB = WN / 16;     // n-subtiles per wave
@@ -279,13 +335,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     static_assert(!DEEP || (!ROWSCALE && BN == 256), "three-stage tiles: block scales, 256 wide");
 
     TileRows tr;
-    if (GROUPED ? !grouped_tile<BN>(p, tr) : !dense_tile<BN>(p, tr)) return;
+    if constexpr (MODE == kGroupedM) {
+        if (!grouped_tile<BN>(p, tr)) return;
+    } else if constexpr (MODE == kGroupedK) {
+        if (!grouped_k_tile<BN>(p, tr)) return;
+    } else {
+        if (!dense_tile<BN>(p, tr)) return;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int slabs = (int)(p.k / kSlab);
+    const int slabs = tr.slabs;
     const int64_t m_last = p.m - 1;
     const int64_t n_last = p.n - 1;
 
@@ -294,8 +356,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // Rows past the tile or the matrix are clamped to valid rows (loaded,
     // never used). Addresses are a wave-uniform base (tile origin + slab) plus
     // a 32-bit per-lane offset, which maps onto the saddr + voffset form.
-    const uint8_t* const tileA = p.a + tr.m0 * p.lda;
-    const uint8_t* const tileB = tr.b + tr.n0 * p.ldb;
+    const uint8_t* const tileA = p.a + tr.m0 * p.lda + (int64_t)tr.slab0 * kSlab;
+    const uint8_t* const tileB = tr.b + tr.n0 * p.ldb + (int64_t)tr.slab0 * kSlab;
     // In a grouped tile, A rows past the tile's real rows only feed outputs
     // that are written as zeros or not at all (an output row depends on its
     // own A row only): every lane of such an 8-row chunk reads the same
@@ -330,6 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         ld_s = 1;
         offS = (uint32_t)(min(tr.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
     }
+    scale_base += (int64_t)tr.slab0 * ld_s;  // the tile's first slab
 
     // Part i (0..3) of this wave's copy of slab j into stage st: 8 rows of
     // A and 8 rows of B; part 3 also carries the scales. Computing waves
@@ -627,7 +690,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             if (n >= tr.n0 + BN) continue;
             v4f v = pad ? zero : acc[t][s];
             if constexpr (OUT_F32) {
-                float* dst = reinterpret_cast<float*>(p.c) + m * p.ldc + n;
+                float* dst = reinterpret_cast<float*>(tr.c) + m * p.ldc + n;
                 if (n + 3 < p.n) {
                     *reinterpret_cast<v4f*>(dst) = v;
                 } else {
@@ -636,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
                         if (n + r < p.n) dst[r] = v[r];
                 }
             } else {
-                uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n;
+                uint16_t* dst = reinterpret_cast<uint16_t*>(tr.c) + m * p.ldc + n;
                 const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
                 if (n + 3 < p.n) {
                     *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
@@ -672,6 +735,7 @@ Params to_params(const GemmProblem& g) {
     p.group_rows = g.group_rows;
     p.stride_b = g.stride_b;
     p.stride_bs = g.stride_bs;
+    p.stride_c_bytes = g.stride_c * (g.out_f32 ? 4 : 2);
     return p;
 }
 
@@ -682,14 +746,14 @@ hipError_t dispatch_dense(const GemmProblem& g, int64_t blocks, hipStream_t stre
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (g.b_rowscale) {
         if (g.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<BN, true, true, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, true, true, kDense>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<BN, true, false, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, true, false, kDense>), grid, block, 0, stream, p);
     } else {
         if (g.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<BN, false, true, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, false, true, kDense>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((gemm_kernel<BN, false, false, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((gemm_kernel<BN, false, false, kDense>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -700,9 +764,22 @@ hipError_t dispatch_grouped(const GemmProblem& g, int64_t blocks, hipStream_t st
     const Params p = to_params(g);
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (g.out_f32)
-        hipLaunchKernelGGL((gemm_kernel<256, false, true, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_kernel<256, false, true, kGroupedM>), grid, block, 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_kernel<256, false, false, true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((gemm_kernel<256, false, false, kGroupedM>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
+// blocks: a multiple of 256 (see grouped_k_tile). Grouped-over-K GEMMs take
+// per-row (128x1) scales on both operands, as Wgrad does.
+template <int BN>
+hipError_t dispatch_grouped_k(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
+    const Params p = to_params(g);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (g.out_f32)
+        hipLaunchKernelGGL((gemm_kernel<BN, true, true, kGroupedK>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BN, true, false, kGroupedK>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
@@ -731,6 +808,16 @@ hipError_t launch_grouped_gemm(const GemmProblem& g, hipStream_t stream) {
     // least 128 of its rows, so there are at most m_total / 128 of them.
     const int64_t tiles = (g.m / 128) * ((g.n + 255) / 256);
     return dispatch_grouped(g, (tiles + 255) / 256 * 256, stream);
+}
+
+hipError_t launch_grouped_k_gemm(const GemmProblem& g, hipStream_t stream) {
+    // Every expert has the same output tiles; 224-wide when that tiles N
+    // better (N = 7168), as for a dense GEMM.
+    const int bn = grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256) ? 224 : 256;
+    const int64_t per = ((g.m + kBM - 1) / kBM) * ((g.n + bn - 1) / bn);
+    const int64_t blocks = (per * g.groups + 255) / 256 * 256;
+    return bn == 224 ? dispatch_grouped_k<224>(g, blocks, stream)
+                     : dispatch_grouped_k<256>(g, blocks, stream);
 }
 
 }  // namespace fp8q

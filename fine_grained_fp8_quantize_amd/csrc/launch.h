@@ -44,9 +44,11 @@ struct GemmProblem {
     const int32_t* group_rows;
     int64_t stride_b;
     int64_t stride_bs;
+    int64_t stride_c;  // grouped over K: elements between expert outputs
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_grouped_k_gemm(const GemmProblem& p, hipStream_t stream);
 
 }  // namespace fp8q

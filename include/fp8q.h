@@ -167,7 +167,8 @@ int fp8_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
  *          FP8Q_BSCALE_ROW128:   [k/128][ld_bs], ld_bs >= n.
  * c        [m][ldc], ldc >= n; out_dtype FP8Q_OUT_BF16 (uint16 bf16, rounded
  *          to nearest even) or FP8Q_OUT_F32. Every element of the m x n
- *          window is written; k == 0 writes zeros.
+ *          window is written; k == 0 writes zeros (A, B and their scales
+ *          are then not read and may be NULL).
  * Shapes:  m, n >= 0 (any value; ragged tiles are handled), k % 128 == 0.
  * Alignment: a, b, c 16-byte aligned; lda, ldb % 16 == 0; ldc % 8 == 0;
  *          scales 4-byte aligned.
@@ -218,6 +219,47 @@ int fp8_grouped_gemm(int32_t groups, const int32_t *group_offsets, const int32_t
                      const uint8_t *b, int64_t ldb, int64_t stride_b,
                      const float *b_scale, int64_t ld_bs, int64_t stride_bs,
                      void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+
+/*
+ * fp8_grouped_gemm_wgrad -- MoE expert Wgrad: one weight gradient per expert,
+ * each contracting over that expert's own token segment.
+ *
+ * The Wgrad GEMM in FP8 (page dssusan.co.kr Q&A board, passage on Figure 6)
+ * applied to every expert of a MoE layer; the per-(slab, row) scales come
+ * from 128x1 token tiles, as for fp8_gemm with FP8Q_BSCALE_ROW128.
+ *   dW_e[i][j] = sum over tokens t in [group_offsets[e], group_offsets[e+1])
+ *                of dequant(A)[i][t] * dequant(B)[j][t],
+ * with the same per-slab promotion as fp8_gemm: A = dY^T codes, B = X^T codes
+ * of the expert-sorted token layout, both quantized with FP8Q_TILE_128x1 over
+ * all k_total tokens. Segments are multiples of 128 tokens, so no 128-token
+ * tile straddles two experts; padding tokens must be zero in the bf16 inputs
+ * (their codes are then zero and add nothing).
+ *
+ * groups        number of experts, >= 0.
+ * group_offsets DEVICE int32[groups + 1]: non-decreasing multiples of 128,
+ *               group_offsets[0] == 0, group_offsets[groups] == k_total.
+ * k_total       tokens of the layout (host copy of group_offsets[groups]).
+ * m, n          rows and columns of each dW_e (n_out x k_in).
+ * a, a_scale    codes [m][lda], lda >= k_total; scales [k_total/128][ld_as],
+ *               ld_as >= m.
+ * b, b_scale    codes [n][ldb], ldb >= k_total; scales [k_total/128][ld_bs],
+ *               ld_bs >= n.
+ * c             dW_e at c + e * stride_c (elements of out_dtype), [m][ldc],
+ *               ldc >= n, stride_c >= m * ldc, stride_c % 8 == 0. An expert
+ *               with an empty segment gets dW_e = 0 (k_total == 0: all are
+ *               zero, and A, B and their scales may be NULL).
+ * Alignment:    as fp8_gemm.
+ * The device array is trusted: segments outside [0, k_total] are skipped
+ * (their dW_e is not written).
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
+ *         FP8Q_ERR_HIP.
+ */
+int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t *group_offsets, int64_t k_total,
+                           int64_t m, int64_t n,
+                           const uint8_t *a, int64_t lda, const float *a_scale, int64_t ld_as,
+                           const uint8_t *b, int64_t ldb, const float *b_scale, int64_t ld_bs,
+                           void *c, int64_t ldc, int64_t stride_c, int out_dtype,
+                           hipStream_t stream);
 
 /* Text for a status code (static storage; never NULL). */
 const char *fp8q_status_string(int status);

@@ -198,9 +198,30 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, sb=256 * 256 + 8) == ERR_ALIGN
 
 
+def _gw(lib, groups=4, off=A16, kt=512, m=256, n=384, a=A16b, lda=512, a_s=A4, ld_as=256,
+        b=A16c, ldb=512, b_s=A4, ld_bs=384, c=A16, ldc=384, sc=256 * 384, out=1):
+    return lib.fp8_grouped_gemm_wgrad(groups, off, kt, m, n, a, lda, a_s, ld_as, b, ldb, b_s, ld_bs,
+                                      c, ldc, sc, out, None)
+
+
+def test_grouped_gemm_wgrad_validation(lib):
+    assert _gw(lib, groups=0) == OK
+    assert _gw(lib, m=0) == OK
+    assert _gw(lib, groups=-1) == ERR_SHAPE
+    assert _gw(lib, out=7) == ERR_ENUM
+    assert _gw(lib, off=0) == ERR_NULL
+    assert _gw(lib, b_s=0) == ERR_NULL
+    assert _gw(lib, kt=500, lda=512, ldb=512) == ERR_SHAPE     # tokens not a multiple of 128
+    assert _gw(lib, lda=256) == ERR_SHAPE                      # lda below k_total
+    assert _gw(lib, ld_bs=383) == ERR_SHAPE                    # row scales need n per slab
+    assert _gw(lib, sc=256 * 384 - 8) == ERR_SHAPE             # expert outputs overlap
+    assert _gw(lib, sc=256 * 384 + 4) == ERR_ALIGN
+    assert _gw(lib, c=A16 + 4) == ERR_ALIGN
+
+
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
-                 "fp8_grouped_gemm"):
+                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad"):
         assert callable(getattr(fq, name))
 
 

@@ -259,3 +259,54 @@ def test_end_to_end_wgrad():
     assert_bits_equal(host_codes(aq), a_q, "wgrad dY^T codes")
     assert_bits_equal(host_f32(bs), b_s, "wgrad X^T scales")
     assert_gemm_close(host_out(c), oracle.gemm(a_q, a_s, b_q, b_s, "row"), "wgrad end to end")
+
+
+# ------------------------------------------------------------ grouped Dgrad
+
+def _grouped_dgrad_case(rows, n_out, k_in, sample=None):
+    """dX_e = dY_e W_e for every expert: the grouped GEMM with each expert's
+    transposed weight copy (W_e^T codes [k_in][n_out], transposed block
+    scales) as B; dY in the expert-sorted layout, quantized 1x128."""
+    rows = np.asarray(rows, dtype=np.int64)
+    off = wl.pad_offsets(rows)
+    m_total = int(off[-1])
+    E = len(rows)
+    dy = np.zeros((m_total, n_out), np.uint16)
+    real = wl.grad_rowscaled(0, "grouped_fprop", 80, int(rows.sum()), n_out)
+    src = 0
+    for e in range(E):
+        dy[off[e]:off[e] + rows[e]] = real[src:src + rows[e]]
+        src += int(rows[e])
+    w = wl.weight(0, "grouped_fprop", 81, E, n_out, k_in)
+    wt_q = torch.empty((E, k_in, n_out), dtype=torch.uint8, device="cuda")
+    wt_s = torch.empty((E, k_in // 128, n_out // 128), dtype=torch.float32, device="cuda")
+    for e in range(E):   # one launch per expert: codes, scales and the transposed copy
+        fq.fp8_quantize_weight(dev_bf16(w[e]), transposed=True, q_t=wt_q[e], scale_t=wt_s[e])
+    dq, ds = fq.fp8_quantize_act(dev_bf16(dy))
+    c = fq.fp8_grouped_gemm(torch.from_numpy(off.astype(np.int32)).cuda(),
+                            torch.from_numpy(rows.astype(np.int32)).cuda(), dq, ds, wt_q, wt_s,
+                            torch.bfloat16)
+    torch.cuda.synchronize()
+    got = host_out(c)
+    a_q, a_s = oracle.quant_act_1x128(dy)
+    for e in range(E):
+        r0, r, end = int(off[e]), int(rows[e]), int(off[e + 1])
+        assert np.all(got[r0 + r:end] == 0), "expert %d padding rows not zero" % e
+        if r == 0:
+            continue
+        w_q, w_s = oracle.quant_weight_128x128(w[e])
+        bt_q, bt_s = np.ascontiguousarray(w_q.T), np.ascontiguousarray(w_s.T)
+        assert_bits_equal(host_codes(wt_q[e]), bt_q, "expert %d transposed codes" % e)
+        idx = np.arange(r) if sample is None or r <= sample else np.unique(
+            np.concatenate([[0, r - 1], np.random.default_rng(e).choice(r, sample, replace=False)]))
+        ref = oracle.gemm_rows(r0 + idx, a_q, a_s, bt_q, bt_s, "block")
+        assert_gemm_close(got[r0 + idx], ref, "dgrad expert %d (rows %d)" % (e, r))
+
+
+def test_grouped_dgrad_edge_rows():
+    _grouped_dgrad_case([0, 1, 129, 256, 3], n_out=256, k_in=384)
+
+
+def test_grouped_dgrad_moe_config_sampled():
+    """MoE up-projection Dgrad: 32 experts, dY [rows][4096] -> dX [rows][7168]."""
+    _grouped_dgrad_case(wl.moe_rows(0), n_out=4096, k_in=7168, sample=4)

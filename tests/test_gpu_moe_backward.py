@@ -1,0 +1,82 @@
+"""GPU parity of the MoE expert Wgrad (fp8_grouped_gemm_wgrad).
+
+dY and X in the expert-sorted layout (128-padded segments, zero padding
+rows) are quantized on the GPU in 128x1 token tiles; each expert's gradient
+contracts over its own token segment. Compared with the oracle's per-expert
+row-scale GEMM on the oracle's codes.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_fp8_quantize_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import assert_bits_equal, assert_gemm_close, dev_bf16, host_codes, host_f32, host_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _packed(rows, cols, tensor_id, grad):
+    rows = np.asarray(rows, dtype=np.int64)
+    off = wl.pad_offsets(rows)
+    real = (wl.grad_rowscaled(1, "grouped_fprop", tensor_id, int(rows.sum()), cols) if grad
+            else wl.activation(1, "grouped_fprop", tensor_id, int(rows.sum()), cols, 50.0))
+    out = np.zeros((int(off[-1]), cols), np.uint16)
+    src = 0
+    for e in range(len(rows)):
+        out[off[e]:off[e] + rows[e]] = real[src:src + rows[e]]
+        src += int(rows[e])
+    return out, off
+
+
+def _wgrad_case(rows, m, n, out_dtype=torch.float32, sample_experts=None, sample_rows=None):
+    dy, off = _packed(rows, m, 100, grad=True)
+    x, _ = _packed(rows, n, 101, grad=False)
+    aq, as_ = fq.fp8_quantize_act(dev_bf16(dy), "128x1")
+    bq, bs = fq.fp8_quantize_act(dev_bf16(x), "128x1")
+    off_d = torch.from_numpy(off.astype(np.int32)).cuda()
+    out = fq.fp8_grouped_gemm_wgrad(off_d, aq, as_, bq, bs, out_dtype)
+    torch.cuda.synchronize()
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    b_q, b_s = oracle.quant_act_128x1(x)
+    assert_bits_equal(host_codes(aq), a_q, "dY^T codes")
+    assert_bits_equal(host_f32(as_), a_s, "dY^T scales")
+    experts = range(len(rows)) if sample_experts is None else sample_experts
+    for e in experts:
+        t0, t1 = int(off[e]), int(off[e + 1])
+        got_e = out[e]
+        idx = np.arange(m) if sample_rows is None else np.unique(np.concatenate(
+            [[0, m - 1], np.random.default_rng(e).choice(m, sample_rows, replace=False)]))
+        got = host_out(got_e[torch.from_numpy(idx).cuda()])
+        if t1 == t0:
+            assert np.all(got == 0), "expert %d: empty segment must give zeros" % e
+            continue
+        ref = oracle.gemm_rows(idx, np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
+                               np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]),
+                               "row")
+        assert_gemm_close(got, ref, "wgrad expert %d (%d tokens)" % (e, rows[e]))
+
+
+def test_grouped_wgrad_edge_segments():
+    # empty expert, 1 token, exact 128, 129 (two slabs), a 2-slab expert
+    _wgrad_case([0, 1, 128, 129, 256], m=256, n=384)
+
+
+def test_grouped_wgrad_ragged_output_and_bf16():
+    _wgrad_case([3, 200, 64], m=320, n=200, out_dtype=torch.bfloat16)
+
+
+def test_grouped_wgrad_all_empty():
+    _wgrad_case([0, 0, 0], m=256, n=256)
+
+
+def test_grouped_wgrad_moe_config_sampled():
+    """MoE up-projection Wgrad: 32 experts, dW_e [4096][7168] over each expert's
+    tokens (8192 routed rows, 10112 padded); 4 experts and rows sampled."""
+    rows = wl.moe_rows(0)
+    big = int(np.argmax(rows))
+    small = int(np.argmin(rows))
+    _wgrad_case(rows, m=4096, n=7168, sample_experts=[0, big, small, 31], sample_rows=12)
