@@ -51,8 +51,14 @@ constexpr int kMSub = kWaveM / 16;
 // to 256 B scales (two stages: 135168 bytes).
 constexpr int kTileBytes = kBM * kSlab;
 
-// Physical 16-byte chunk of logical chunk c in LDS row `row`.
-__device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ (row & 7); }
+// Physical 16-byte chunk of logical chunk c in LDS row `row` (rows are 128
+// bytes). A fragment read has each 16-lane quarter of the wave fetch one
+// chunk from 16 consecutive rows; XOR with (row >> 1) & 7 sends those 16
+// reads to 16 different 16-byte bank groups (rows 2r and 2r+1 already sit
+// in opposite halves of the 64 banks), so the read is conflict-free. Tiles
+// and subtiles start at multiples of 16 rows, so tile-relative and
+// subtile-relative rows give the same chunk.
+__device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ ((row >> 1) & 7); }
 
 struct Params {
     int64_t m, n, k;
@@ -400,19 +406,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // writes from bunching up behind the barrier.
     // Three-stage kernels recompute the offsets of each copy (a few VALU
     // operations at the step boundary) instead of holding eight registers
-    // through the MFMA loop. The swizzled chunk depends on row & 7 only, the
-    // same for all four parts of a wave.
-    const uint32_t chunk16 = swz_chunk(lane & 7, lane >> 3) * 16;
+    // through the MFMA loop.
     auto a_off = [&](int i) -> uint32_t {
         if constexpr (!DEEP) return offA[i];
         const int row = 32 * wave + 8 * i + (lane >> 3);
         const int src = 32 * wave + 8 * i >= a_rows ? max(a_rows - 1, 0) : row;
-        return (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + chunk16;
+        return (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + swz_chunk(lane & 7, row) * 16;
     };
     auto b_off = [&](int i) -> uint32_t {
         if constexpr (!DEEP) return offB[i];
         const int row = 32 * wave + 8 * i + (lane >> 3);
-        return (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + chunk16;
+        return (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + swz_chunk(lane & 7, row) * 16;
     };
     auto copy_a = [&](int j, auto st, int i) {
         uint8_t* base = stage_a<decltype(st)::value>() + 32 * wave * kSlab;
