@@ -490,6 +490,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         sb = bscale_row[j];
     };
 
+    // Block-scale dense kernels defer the promotion of each slab's last
+    // subtile into the next slab (carry_p * carry_f; zero before the first).
+    constexpr bool DEFER = !ROWSCALE && !DEEP;
+    v4f carry_p[kMSub];
+    float carry_f[kMSub];
+#pragma unroll
+    for (int s = 0; s < kMSub; ++s) {
+        carry_p[s] = zero;
+        carry_f[s] = 0.f;
+    }
+
     // One slab of MFMAs + promotion for the first ACT m-subtiles of the wave,
     // on A stage AS and B stage BS (two-stage kernels: AS = BS, scales from
     // LDS; three-stage kernels: the products sA * sB come in sab_in).
@@ -501,24 +512,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         const uint8_t* const lb = stage_b<BS>() + fragB;
         const float* const lsa = stage_sa<ST % 2>() + wm * kWaveM + fi;
         const float* const lsb = stage_sb<ST % 2>();
-        v8i am[kMSub];
-        float sa[kMSub];
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) {
-            am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
-            sa[s] = DEEP ? 0.f : lsa[16 * s];
-        }
-        const float sb0 = (ROWSCALE || DEEP) ? 0.f : lsb[nb_rel];
-        const float sb1 = (ROWSCALE || !STRADDLE) ? 0.f : lsb[nb_rel + 1];
-        float sab0[kMSub], sab1[kMSub];
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) {
-            sab0[s] = DEEP ? sab_in[s] : sa[s] * sb0;
-            if constexpr (STRADDLE) sab1[s] = sa[s] * sb1;
-        }
-        // Software pipeline over the n-subtiles: while the MFMAs of subtile T
-        // run, the fragment of T+1 is in flight and the partials of T-1 are
-        // promoted (acc += P * sA * sB), one FMA group after each MFMA.
         // B fragment of n-subtile T (and, with per-row B scales, the lane's
         // four scales)
         auto read_b = [&](auto t_tag, v8i& bf, v4f& sbv) {
@@ -531,6 +524,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         v4f fsb[2];
         v4f pc[kMSub], pp[kMSub];
         v4f sbp;
+        // Reads in the order the first MFMAs use them -- B fragment 0, A
+        // fragments 0..3, then the scales (first needed by the promotion in
+        // subtile 1) -- so the first MFMA waits for four reads, not all.
+        read_b(std::integral_constant<int, 0>{}, fr[0], fsb[0]);
+        v8i am[kMSub];
+        float sa[kMSub];
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) sa[s] = DEEP ? 0.f : lsa[16 * s];
+        const float sb0 = (ROWSCALE || DEEP) ? 0.f : lsb[nb_rel];
+        const float sb1 = (ROWSCALE || !STRADDLE) ? 0.f : lsb[nb_rel + 1];
+        float sab0[kMSub], sab1[kMSub];
+        // Software pipeline over the n-subtiles: while the MFMAs of subtile T
+        // run, the fragment of T+1 is in flight and the partials of T-1 are
+        // promoted (acc += P * sA * sB), one FMA group after each MFMA.
         auto promote = [&](auto t_tag, const v4f& sbn) {
             constexpr int T = decltype(t_tag)::value;
 #pragma unroll
@@ -547,7 +556,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
                 }
             }
         };
-        read_b(std::integral_constant<int, 0>{}, fr[0], fsb[0]);
         __builtin_amdgcn_sched_barrier(0);
         unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
             constexpr int T = decltype(t_tag)::value;
@@ -560,26 +568,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
 #pragma unroll
             for (int s = 0; s < ACT; ++s)
                 pc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], zero, 0, 0, 0, 0, 0, 0);
-            if constexpr (T > 0) promote(std::integral_constant<int, T - 1>{}, sbp);
+            if constexpr (T == 0) {
+                // the previous slab's last subtile (deferred), then this
+                // slab's scale products
+                if constexpr (DEFER) {
+#pragma unroll
+                    for (int s = 0; s < ACT; ++s)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[NSUB - 1][s][r] = __builtin_fmaf(carry_p[s][r], carry_f[s], acc[NSUB - 1][s][r]);
+                }
+#pragma unroll
+                for (int s = 0; s < kMSub; ++s) {
+                    sab0[s] = DEEP ? sab_in[s] : sa[s] * sb0;
+                    if constexpr (STRADDLE) sab1[s] = sa[s] * sb1;
+                }
+            } else {
+                promote(std::integral_constant<int, T - 1>{}, sbp);
+            }
             // Order: the first MFMA (its wait covers only the fragment read
             // one subtile earlier), the next fragment's reads, this subtile's
             // copy part, then the FMA group of one m-subtile after each MFMA.
             constexpr int FMAS = ROWSCALE ? 8 : (STRADDLE ? 5 : 4);
+            constexpr bool HAS_FMAS = T > 0 || DEFER;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NEXT_READS, 0);
             if constexpr (!GROUPED && T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
-            if constexpr (T > 0) __builtin_amdgcn_sched_group_barrier(0x002, FMAS, 0);
+            if constexpr (HAS_FMAS) __builtin_amdgcn_sched_group_barrier(0x002, T > 0 ? FMAS : 4, 0);
 #pragma unroll
             for (int s = 1; s < ACT; ++s) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if constexpr (T > 0) __builtin_amdgcn_sched_group_barrier(0x002, FMAS, 0);
+                if constexpr (HAS_FMAS) __builtin_amdgcn_sched_group_barrier(0x002, T > 0 ? FMAS : 4, 0);
             }
 #pragma unroll
             for (int s = 0; s < ACT; ++s) pp[s] = pc[s];
             sbp = fsb[T & 1];
             __builtin_amdgcn_sched_barrier(0);
         });
-        promote(std::integral_constant<int, NSUB - 1>{}, sbp);
+        if constexpr (DEFER) {
+            // the last subtile is promoted at the start of the next slab,
+            // where the VALU otherwise waits for the fragment reads
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) {
+                carry_p[s] = pp[s];
+                carry_f[s] = (!STRADDLE || NSUB - 1 < split) ? sab0[s] : sab1[s];
+            }
+        } else {
+            promote(std::integral_constant<int, NSUB - 1>{}, sbp);
+        }
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -606,6 +642,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             step(std::integral_constant<int, 1>{}, j + 1);
         }
         if (j < slabs) step(std::integral_constant<int, 0>{}, j);
+        if constexpr (DEFER && ACT > 0) {
+#pragma unroll
+            for (int s = 0; s < ACT; ++s)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[NSUB - 1][s][r] = __builtin_fmaf(carry_p[s][r], carry_f[s], acc[NSUB - 1][s][r]);
+        }
     };
 
     // Three-stage K loop: slab j lives in A stage j % 2 and B stage j % 3.
