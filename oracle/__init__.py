@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_encoders_disagree.restype = ctypes.c_int64
         L.oracle_quant_pairs.argtypes = [u16p, u16p, i64, u8p]
         L.oracle_quant_pairs.restype = None
+        L.oracle_quant_mx_1x32.argtypes = [u16p, i64, i64, i64, u8p, i64, u8p, i64]
+        L.oracle_quant_mx_1x32.restype = None
         _LIB = L
     return _LIB
 
@@ -119,6 +121,32 @@ def quant_act_scatter(x: np.ndarray, dst_rows: np.ndarray, m_total: int):
     s[:, d] = s_tok[:, t_idx]
     written[d] = True
     return q, s, written
+
+
+def quant_mx_1x32(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Microscaling (OCP MX, E4M3 elements): bf16 bits X[rows][cols] ->
+    (Q uint8[rows][cols], E uint8[rows][cols/32] E8M0 exponent bytes)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    rows, cols = x.shape
+    assert cols % 32 == 0
+    q = np.empty((rows, cols), dtype=np.uint8)
+    e = np.empty((rows, cols // 32), dtype=np.uint8)
+    lib().oracle_quant_mx_1x32(_p(x, ctypes.c_uint16), rows, cols, cols,
+                               _p(q, ctypes.c_uint8), cols, _p(e, ctypes.c_uint8), cols // 32)
+    return q, e
+
+
+def dequant_mx(q: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """float64 value of MX codes: dec(q) * 2^(E - 127) per 32-element block."""
+    rows, cols = q.shape
+    scale = np.ldexp(1.0, e.astype(np.int64) - 127)
+    return _dec()[q] * np.repeat(scale, 32, axis=1)
+
+
+def gemm_mx(a_q: np.ndarray, a_e: np.ndarray, b_q: np.ndarray, b_e: np.ndarray) -> np.ndarray:
+    """float64 C[m][n] = deq_mx(A)[m][:] . deq_mx(B)[n][:], unrounded (both
+    operands K-contiguous, 32-element blocks along K)."""
+    return dequant_mx(a_q, a_e) @ dequant_mx(b_q, b_e).T
 
 
 def quant_act_128x1(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

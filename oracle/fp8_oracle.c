@@ -227,3 +227,47 @@ void oracle_quant_pairs(const uint16_t *x, const uint16_t *amax, int64_t count, 
         q[i] = quantize_value(oracle_bf16_to_f32(x[i]), a, group_scale(a));
     }
 }
+
+/* ------------------------------------------------------------ microscaling */
+
+/* The microscaling variant (page "Deepseek Ai News Expert Interview", passage
+ * likening the fine-grained groups to microscaling formats with smaller
+ * quantization granularity): blocks of 32 consecutive elements along a row
+ * share one power-of-two scale X = 2^e, stored as an E8M0 byte e + 127.
+ * Readings (OCP MX, FP8 E4M3 elements): e = floor(log2(amax)) - 8, where 8
+ * is the exponent of E4M3's largest normal (448 = 1.75 * 2^8), clamped to
+ * [-127, 127]; an all-zero block takes e = -127. Each element is
+ * E4M3_RNE_sat(x / X); the division by a power of two is done exactly (in
+ * double) before the single rounding to E4M3. */
+static int mx_exponent(float amax) {
+    if (amax == 0.0f) return -127;
+    int ex;
+    (void)frexp((double)amax, &ex);   /* amax = m * 2^ex, m in [0.5, 1) */
+    int e = (ex - 1) - 8;             /* floor(log2(amax)) - 8 */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/* x[rows][ldx] bf16, cols % 32 == 0 -> q[rows][ldq], e8m0[rows][lde]
+ * (byte b of row r is the exponent byte of columns [32b, 32b + 32)). */
+void oracle_quant_mx_1x32(const uint16_t *x, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *q, int64_t ldq, uint8_t *e8m0, int64_t lde) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++) {
+        for (int64_t b = 0; b < cols / 32; b++) {
+            const uint16_t *blk = x + r * ldx + b * 32;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; i++) {
+                float a = fabsf(oracle_bf16_to_f32(blk[i]));
+                if (a > amax) amax = a;
+            }
+            int e = mx_exponent(amax);
+            e8m0[r * lde + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; i++) {
+                float v = (float)ldexp((double)oracle_bf16_to_f32(blk[i]), -e);
+                q[r * ldq + b * 32 + i] = oracle_e4m3_encode_bits(v);
+            }
+        }
+    }
+}

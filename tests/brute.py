@@ -127,3 +127,15 @@ def gemm_exact(a_codes, a_scales, b_codes, b_scales) -> list[list[Fraction]]:
             row.append(acc)
         out.append(row)
     return out
+
+
+def quantize_mx_block(bits: list[int]) -> tuple[int, list[int]]:
+    """One microscaling block (OCP MX, E4M3 elements): e = floor(log2(amax)) - 8
+    clamped to [-127, 127] (all-zero block: -127); q = nearest E4M3 of x / 2^e
+    (exact rational, ties to the even code, largest finite code beyond 448).
+    Returns (e, codes)."""
+    vals = [bf16_value(b) for b in bits]
+    amax = max(abs(v) for v in vals)
+    e = -127 if amax == 0 else max(-127, min(127, _floor_log2(amax) - 8))
+    scale = Fraction(2) ** e
+    return e, [e4m3_nearest(v / scale, bf16_is_negative(b)) for b, v in zip(bits, vals)]

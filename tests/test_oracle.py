@@ -523,3 +523,78 @@ def test_grouped_wgrad_single_expert_is_dense_wgrad():
     b_q, b_s = oracle.quant_act_128x1(x)
     per = oracle.grouped_gemm_wgrad(off, a_q, a_s, b_q, b_s)
     assert np.array_equal(per[0], oracle.gemm(a_q, a_s, b_q, b_s, "row"))
+
+
+# ------------------------------------------------------------- microscaling
+
+def test_mx_hand_worked_block():
+    """A block worked by hand under the OCP-MX reading: amax = 3 gives
+    floor(log2 3) - 8 = -7 (E8M0 byte 120, X = 2^-7); 3 -> 384 = 1.5 * 2^8
+    (0x7C); 1 -> 128 = 2^7 (0x70); bf16(0.1) = 0.10009765625 -> 12.8125,
+    rounded to 13 = 1.625 * 2^3 (0x55); bf16(-0.001) -> -0.12805..., rounded
+    to -0.125 = -2^-3 (0xA0); zeros stay +0."""
+    bits = np.zeros(32, np.uint16)
+    bits[:4] = wl.f32_to_bf16_bits(np.array([3.0, 1.0, 0.1, -0.001], np.float32))
+    q, e = oracle.quant_mx_1x32(bits[None, :])
+    assert e[0, 0] == 120
+    assert list(q[0, :4]) == [0x7C, 0x70, 0x55, 0xA0]
+    assert not q[0, 4:].any()
+
+
+def _mx_special_rows(rng):
+    rows = [wl.f32_to_bf16_bits(rng.standard_normal(64).astype(np.float32))]
+    z = np.zeros(64, np.uint16)
+    z[::5] = 0x8000
+    rows.append(z)                                                    # zero blocks, signed zeros
+    rows.append(rng.integers(1, 0x80, 64).astype(np.uint16) | np.uint16(0x8000))  # bf16 subnormals
+    big = wl.f32_to_bf16_bits(rng.standard_normal(64).astype(np.float32) * 1e37)
+    big[3] = 0x7F7F                                                   # bf16 max: e = 127 - 8
+    rows.append(big)
+    rows.append(wl.f32_to_bf16_bits(rng.standard_normal(64).astype(np.float32) * 1e-37))  # e below -127 -> clamp
+    ties = wl.f32_to_bf16_bits(np.full(64, 448.0 * 17 / 64, np.float32))
+    rows.append(ties)
+    return np.stack(rows)
+
+
+def test_mx_matches_exact_rational_brute_force():
+    """Pin: every 32-element block equals the exact-rational MX quantization."""
+    rng = np.random.default_rng(21)
+    x = _mx_special_rows(rng)
+    q, e = oracle.quant_mx_1x32(x)
+    for r in range(x.shape[0]):
+        for b in range(x.shape[1] // 32):
+            be, bq = brute.quantize_mx_block([int(v) for v in x[r, 32 * b:32 * b + 32]])
+            assert e[r, b] == be + 127, (r, b)
+            assert list(q[r, 32 * b:32 * b + 32]) == bq, (r, b)
+
+
+def test_mx_invariants():
+    """Invariants: a nonzero block with an unclamped exponent has max |q| in
+    [256, 448] (amax / 2^e lies in [256, 512)); scaling X by 2^p keeps the
+    codes and adds p to every exponent; negation flips sign bits only."""
+    x = wl.activation(0, "tiny_fprop", 91, 64, 256, 50.0)
+    q, e = oracle.quant_mx_1x32(x)
+    dec = np.abs(oracle.e4m3_decode_table()[q]).reshape(64, 8, 32).max(axis=2)
+    assert np.all((dec >= 256) & (dec <= 448))
+    xf = wl.bf16_bits_to_f32(x)
+    for p in (-5, 3):
+        q2, e2 = oracle.quant_mx_1x32(wl.f32_to_bf16_bits(xf * np.float32(2.0 ** p)))
+        assert np.array_equal(q2, q) and np.array_equal(e2.astype(int), e.astype(int) + p)
+    qn, en = oracle.quant_mx_1x32(x ^ np.uint16(0x8000))
+    assert np.array_equal(en, e) and np.array_equal(qn, q ^ np.uint8(0x80))
+
+
+def test_gemm_mx_matches_exact_rational_brute_force():
+    """Pin: tiny MX GEMM (M, N <= 5, K = 96) equals the exact rational sum."""
+    rng = np.random.default_rng(22)
+    a = wl.f32_to_bf16_bits(rng.standard_normal((4, 96)).astype(np.float32) * 3)
+    b = wl.f32_to_bf16_bits(rng.standard_normal((5, 96)).astype(np.float32) * 0.02)
+    aq, ae = oracle.quant_mx_1x32(a)
+    bq, be = oracle.quant_mx_1x32(b)
+    got = oracle.gemm_mx(aq, ae, bq, be)
+    exp_a = [[2.0 ** (int(ae[m, k // 32]) - 127) for k in range(96)] for m in range(4)]
+    exp_b = [[2.0 ** (int(be[n, k // 32]) - 127) for k in range(96)] for n in range(5)]
+    ref = brute.gemm_exact(aq.tolist(), exp_a, bq.tolist(), exp_b)
+    for m in range(4):
+        for n in range(5):
+            assert got[m, n] == float(ref[m][n])
