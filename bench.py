@@ -12,7 +12,8 @@ stream inside the timed region), every kernel's own time and rate, and the CPU
 oracle timed on the host as a reported baseline.
 
     python bench.py [--steps K] [--warmup W]
-                    [--config dense_fprop|dgrad|wgrad|grouped_fprop|tiny_fprop]
+                    [--config dense_fprop|dgrad|wgrad|grouped_fprop|grouped_dgrad|
+                              grouped_wgrad|mx_fprop|tiny_fprop]
 
 Counter runs (HBM traffic of each kernel, from rocprofv3 FETCH_SIZE and
 WRITE_SIZE; a plain copy of known size calibrates each counter):
@@ -40,7 +41,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak (1 GPU)"
 CONFIGS = ["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "grouped_dgrad", "grouped_wgrad",
-           "tiny_fprop"]
+           "mx_fprop", "tiny_fprop"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Kernel name fragments (as rocprofv3 prints them) for each launch label.
@@ -49,6 +50,7 @@ KERNEL_NAMES = {
     "quant_act_scatter": "quant_act_1x128_kernel<true>",
     "quant_act_128x1": "quant_act_128x1_kernel",
     "quant_weight": "quant_weight_kernel",
+    "quant_mx": "quant_mx_1x32_kernel",
     "gemm": "gemm_kernel",
 }
 
@@ -153,6 +155,28 @@ class Workload:
             ]
             self.desc = {"workload": name, "m": m, "n": n, "k": k, "x": "bf16, 1x128 tiles",
                          "w": "bf16, 128x128 blocks", "out": "bf16"}
+        elif name == "mx_fprop":
+            # the Dense Fprop shapes with microscaling: both operands in 1x32
+            # blocks along K with E8M0 scales, scaled-MFMA GEMM
+            d = wl.dense_fprop()
+            X, W = sets(d["x"]), sets(d["w"])
+            m, k = X[0].shape
+            n = W[0].shape[0]
+            xq, xs = empty((m, k), u8), empty((k // 128, m), torch.int32)
+            wq, ws = empty((n, k), u8), empty((k // 128, n), torch.int32)
+            y = empty((m, n), bf16)
+            self.flops = 2.0 * m * n * k
+
+            def mx_bytes(r, c):   # bf16 in, codes + one byte per 32 values out
+                return 2 * r * c + r * c + r * c // 32
+            self.launches = [
+                Launch("quant_mx", lambda r: fq.fp8_quantize_mx(X[r], q=xq, scale=xs), mx_bytes(m, k)),
+                Launch("quant_mx", lambda r: fq.fp8_quantize_mx(W[r], q=wq, scale=ws), mx_bytes(n, k)),
+                Launch("gemm", lambda r: fq.fp8_gemm_mx(xq, xs, wq, ws, bf16, out=y),
+                       m * k + n * k + (m + n) * k // 32 + 2 * m * n, self.flops),
+            ]
+            self.desc = {"workload": name, "m": m, "n": n, "k": k,
+                         "x, w": "bf16, 1x32 blocks along K, E8M0 scales (OCP MX)", "out": "bf16"}
         elif name == "dgrad":
             d = wl.dgrad()
             DY, W = sets(d["dy"]), sets(d["w"])
@@ -516,7 +540,8 @@ def main():
             "traffic": traffic["gemm"]["traffic_bytes"] if traffic and "gemm" in traffic else None,
             "kernel": "gemm_kernel" + ({"grouped_fprop": " (grouped over M)",
                                         "grouped_dgrad": " (grouped over M)",
-                                        "grouped_wgrad": " (grouped over K)"}.get(args.config, "")),
+                                        "grouped_wgrad": " (grouped over K)",
+                                        "mx_fprop": " (microscaling)"}.get(args.config, "")),
             "algorithmic_bytes": int(gemm[0].bytes),
             "tflops": round(gemm_tflops, 2),
         }),

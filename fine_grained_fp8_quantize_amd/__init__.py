@@ -38,6 +38,8 @@ __all__ = [
     "fp8_gemm",
     "fp8_grouped_gemm",
     "fp8_grouped_gemm_wgrad",
+    "fp8_quantize_mx",
+    "fp8_gemm_mx",
     "fp8q_status_string",
     "fp8q_last_hip_error",
     "Fp8qError",
@@ -78,13 +80,15 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_act.argtypes = [p, i64, i64, i64, cint, p, i64, p, i64, p]
     L.fp8_quantize_act_scatter.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+    L.fp8_quantize_mx.argtypes = [p, i64, i64, i64, p, i64, p, i64, p]
+    L.fp8_gemm_mx.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64, cint, p]
     L.fp8_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, cint, p, i64, cint, p]
     L.fp8_grouped_gemm_wgrad.argtypes = [i32, p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64,
                                          p, i64, i64, cint, p]
     L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
                                    i64, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
-                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad"):
+                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx"):
         getattr(L, name).restype = cint
     L.fp8q_status_string.argtypes = [cint]
     L.fp8q_status_string.restype = ctypes.c_char_p
@@ -358,4 +362,49 @@ def fp8_grouped_gemm_wgrad(group_offsets: torch.Tensor, a: torch.Tensor, a_scale
         _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0),
         _ptr(out), out.stride(1), out.stride(0), oc, _stream(stream))
     _check(st, "fp8_grouped_gemm_wgrad")
+    return out
+
+
+# ------------------------------------------------------------- microscaling
+
+def fp8_quantize_mx(x: torch.Tensor, q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                    stream=None):
+    """Microscaling quantization (32-element blocks along each row, E8M0
+    power-of-two scales, E4M3 codes). Returns ``q[rows][cols]`` and the scale
+    words ``scale[cols/128][rows]`` (int32 tensor of 4 E8M0 bytes each)."""
+    _need_gpu(x)
+    _rowmajor(x, "x")
+    if x.dtype != torch.bfloat16:
+        raise Fp8qError("x must be bfloat16")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=x.device)
+    if scale is None:
+        scale = torch.empty((cols // 128, rows), dtype=torch.int32, device=x.device)
+    _need_gpu(q, scale)
+    _codes(q, "q")
+    st = _load().fp8_quantize_mx(_ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0), _ptr(scale),
+                                 scale.stride(0), _stream(stream))
+    _check(st, "fp8_quantize_mx")
+    return q, scale
+
+
+def fp8_gemm_mx(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
+                out_dtype=torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """``C = dequant_mx(A) @ dequant_mx(B)^T`` with both operands from
+    :func:`fp8_quantize_mx` along K."""
+    _need_gpu(a, a_scale, b, b_scale, out)
+    _rowmajor(a, "a")
+    _rowmajor(b, "b")
+    _codes(a, "a")
+    _codes(b, "b")
+    m, k = a.shape
+    n = b.shape[0]
+    oc = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    st = _load().fp8_gemm_mx(m, n, k, _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
+                             _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0),
+                             _ptr(out), out.stride(0), oc, _stream(stream))
+    _check(st, "fp8_gemm_mx")
     return out

@@ -183,4 +183,38 @@ int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t* group_offsets, int64_t
     return hip_status(fp8q::launch_grouped_k_gemm(g, stream));
 }
 
+int fp8_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                    int64_t ld_q, uint32_t* scale, int64_t ld_s, hipStream_t stream) {
+    if (rows < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!x || !q || !scale) return FP8Q_ERR_NULL;
+    if (cols % 128 != 0 || ld_x < cols || ld_q < cols || ld_s < rows) return FP8Q_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || ld_x % 8 != 0 || ld_q % 16 != 0)
+        return FP8Q_ERR_ALIGN;
+    if (!grid_ok((rows + 15) / 16 * (cols / 128) / 4 + 1)) return FP8Q_ERR_SHAPE;
+    return hip_status(fp8q::launch_quant_mx(x, rows, cols, ld_x, q, ld_q, scale, ld_s, stream));
+}
+
+int fp8_gemm_mx(int64_t m, int64_t n, int64_t k,
+                const uint8_t* a, int64_t lda, const uint32_t* a_scale, int64_t ld_as,
+                const uint8_t* b, int64_t ldb, const uint32_t* b_scale, int64_t ld_bs,
+                void* c, int64_t ldc, int out_dtype, hipStream_t stream) {
+    if (m < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
+    if (m == 0 || n == 0) return FP8Q_OK;
+    const float* as = reinterpret_cast<const float*>(a_scale);
+    const float* bs = reinterpret_cast<const float*>(b_scale);
+    int st = check_gemm_common(m, n, k, a, lda, as, ld_as, b, ldb, bs, c, ldc, out_dtype);
+    if (st != FP8Q_OK) return st;
+    if (k > 0 && ld_bs < n) return FP8Q_ERR_SHAPE;
+    if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) + 8)) return FP8Q_ERR_SHAPE;
+    fp8q::GemmProblem g = {};
+    g.m = m; g.n = n; g.k = k;
+    g.a = a; g.lda = lda; g.a_scale = as; g.ld_as = ld_as;
+    g.b = b; g.ldb = ldb; g.b_scale = bs; g.ld_bs = ld_bs;
+    g.b_rowscale = true;
+    g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
+    return hip_status(fp8q::launch_gemm_mx(g, stream));
+}
+
 }  // extern "C"

@@ -51,6 +51,13 @@ __device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > 
 // Max over each DPP row of 16 lanes; every lane of the row gets the result.
 // quad_perm [1,0,3,2] and [2,3,0,1] reduce each quad, row_half_mirror joins
 // the two quads of each half-row, row_mirror joins the two half-rows.
+// Max over each quad of lanes (DPP quad permutations).
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    return v;
+}
+
 __device__ __forceinline__ uint32_t row16_max(uint32_t v) {
     v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
     v = umax32(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));

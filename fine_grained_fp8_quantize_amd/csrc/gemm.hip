@@ -324,9 +324,14 @@ __device__ __forceinline__ void unroll(std::integer_sequence<int, Is...>, F&& f)
 
 // ---------------------------------------------------------------- the kernel
 
-template <int BN, bool ROWSCALE, bool OUT_F32, int MODE>
+// MX: microscaling operands (OCP MX, E4M3 elements): each row's 32-element
+// K blocks carry E8M0 scales, one uint32 per row and slab (byte b = block
+// 4j + b); the scaled MFMA applies them and accumulates in place, with no
+// promotion step. Copies and scale staging are those of per-row scales.
+template <int BN, bool ROWSCALE, bool OUT_F32, int MODE, bool MX = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     constexpr bool GROUPED = MODE == kGroupedM;
+    static_assert(!MX || (ROWSCALE && MODE == kDense), "microscaling: dense, per-row staging");
     static_assert(BN == 256 || BN == 224, "n tile");
     constexpr int WN = BN / 2;        // n extent of one wave
     constexpr int NSUB = WN / 16;     // n-subtiles per wave
@@ -619,6 +624,57 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // One slab of the microscaling GEMM: the scaled MFMA takes each lane's
+    // E8M0 byte and accumulates into acc directly. In the 16x16x128 FP8 MFMA,
+    // the 32 bytes of lane group g are K[16g, 16g+16) and K[64+16g, 64+16g+16)
+    // of the slab, and the scale of K block b (32 elements) comes from lane
+    // group b (measured on gfx950). So lane group g reads 16-byte chunks g and
+    // g + 4: block b then consists of chunks 2b and 2b+1 -- the quantizer's
+    // block b -- and lane group g supplies block g's byte. (The unscaled MFMA
+    // is blind to this order: any K permutation shared by A and B gives the
+    // same sum.)
+    const uint32_t moff0 = fi * kSlab + swz_chunk(fg, fi) * 16;
+    const uint32_t moff1 = fi * kSlab + swz_chunk(fg + 4, fi) * 16;
+    auto compute_mx = [&](auto a_tag, auto act_tag) {
+        constexpr int ST = decltype(a_tag)::value;
+        constexpr int ACT = decltype(act_tag)::value;
+        const uint8_t* const la = stage_a<ST>() + fragA;
+        const uint8_t* const lb = stage_b<ST>() + fragB;
+        const uint32_t* const lsa = reinterpret_cast<const uint32_t*>(stage_sa<ST>()) + wm * kWaveM + fi;
+        const uint32_t* const lsb = reinterpret_cast<const uint32_t*>(stage_sb<ST>()) + wn * WN + fi;
+        const int shift = 8 * fg;
+        v8i fr[2];
+        uint32_t sbw[2];
+        fr[0] = ld_frag(lb + moff0, lb + moff1);
+        sbw[0] = lsb[0];
+        v8i am[kMSub];
+        int sae[kMSub];
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + moff0, la + s * 2048 + moff1);
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) sae[s] = (int)((lsa[16 * s] >> shift) & 0xFFu);
+        __builtin_amdgcn_sched_barrier(0);
+        unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
+            constexpr int T = decltype(t_tag)::value;
+            const v8i bf = fr[T & 1];
+            const int sbe = (int)((sbw[T & 1] >> shift) & 0xFFu);
+            if constexpr (T + 1 < NSUB) {
+                fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + moff0, lb + (T + 1) * 2048 + moff1);
+                sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
+            }
+            if constexpr (T < 4) issue_part(jnext, std::integral_constant<int, ST ^ 1>{}, T);
+#pragma unroll
+            for (int s = 0; s < ACT; ++s)
+                acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
+                                                                            0, sbe, 0, sae[s]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            if constexpr (T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, ACT - 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
     // The K loop for a wave with ACT live m-subtiles (ACT = 0: the wave only
     // does its share of the copies and the barriers).
     auto mainloop = [&](auto act_tag) {
@@ -633,7 +689,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             // keeping the body branch-free.
             jnext = min(j + 1, slabs - 1);
             if constexpr (ACT == 0) issue(jnext, std::integral_constant<int, ST ^ 1>{});
-            if constexpr (ACT > 0) compute(stage_tag, stage_tag, act_tag, no_sab);
+            if constexpr (ACT > 0) {
+                if constexpr (MX)
+                    compute_mx(stage_tag, act_tag);
+                else
+                    compute(stage_tag, stage_tag, act_tag, no_sab);
+            }
         };
         if (slabs > 0) issue(0, std::integral_constant<int, 0>{});
         int j = 0;
@@ -805,6 +866,18 @@ hipError_t dispatch_dense(const GemmProblem& g, int64_t blocks, hipStream_t stre
     return hipGetLastError();
 }
 
+// Microscaling dense GEMM (per-row E8M0 scale words on both operands).
+template <int BN>
+hipError_t dispatch_mx(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
+    const Params p = to_params(g);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (g.out_f32)
+        hipLaunchKernelGGL((gemm_kernel<BN, true, true, kDense, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BN, true, false, kDense, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 // blocks: a multiple of 256 (see grouped_tile). Grouped GEMMs take 128x128
 // block scales only.
 hipError_t dispatch_grouped(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
@@ -865,6 +938,15 @@ hipError_t launch_grouped_k_gemm(const GemmProblem& g, hipStream_t stream) {
     const int64_t blocks = (per * g.groups + 255) / 256 * 256;
     return bn == 224 ? dispatch_grouped_k<224>(g, blocks, stream)
                      : dispatch_grouped_k<256>(g, blocks, stream);
+}
+
+hipError_t launch_gemm_mx(const GemmProblem& g, hipStream_t stream) {
+    if (grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256)) {
+        const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
+        return dispatch_mx<224>(g, (tiles + 7) / 8 * 8, stream);
+    }
+    const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
+    return dispatch_mx<256>(g, (tiles + 7) / 8 * 8, stream);
 }
 
 }  // namespace fp8q

@@ -15,6 +15,9 @@ hipError_t launch_quant_act_scatter(const uint16_t* x, int64_t tokens, int64_t c
                                     int topk, const int32_t* dst_rows, int64_t m_total, uint8_t* q,
                                     int64_t ld_q, float* scale, int64_t ld_s, hipStream_t stream);
 
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                           int64_t ld_q, uint32_t* scale, int64_t ld_s, hipStream_t stream);
+
 hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
                                   uint8_t* qt, int64_t ld_q, float* scale, int64_t ld_s,
                                   hipStream_t stream);
@@ -50,5 +53,6 @@ struct GemmProblem {
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_grouped_k_gemm(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_gemm_mx(const GemmProblem& p, hipStream_t stream);
 
 }  // namespace fp8q

@@ -94,6 +94,64 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
     }
 }
 
+// ------------------------------------------------------------ MX (1x32)
+
+// Microscaling variant (page "Deepseek Ai News Expert Interview", passage
+// likening the fine-grained groups to microscaling formats): 32 consecutive
+// elements of a row share an E8M0 power-of-two scale 2^e with
+// e = floor(log2(amax)) - 8 (8: exponent of E4M3's largest normal), clamped
+// to [-127, 127], -127 for an all-zero block; codes are E4M3_RNE_sat(x / 2^e).
+// Same wave layout as the 1x128 kernel; a 32-element block is one quad of
+// lanes. The scale of row r, slab j is one uint32: byte b = block 4j + b.
+__global__ __launch_bounds__(256) void quant_mx_1x32_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, uint32_t* __restrict__ scale, int64_t ld_s,
+    int64_t units) {
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * kActWavesPerBlock + (threadIdx.x >> 6);
+    if (unit >= units) return;  // whole wave
+    const int64_t rg = unit / slabs;
+    const int64_t j = unit - rg * slabs;
+    const int rr = lane >> 4, c = lane & 15;
+
+    uint4 v[4];
+    int64_t row[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        row[u] = rg * kActRowsPerWave + u * 4 + rr;
+        v[u] = make_uint4(0, 0, 0, 0);
+        if (row[u] < rows)
+            v[u] = load_nt16(x + row[u] * ld_x + j * 128 + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t mask = 0x7FFF7FFFu;
+        uint32_t m = pk_max_u16(pk_max_u16(v[u].x & mask, v[u].y & mask),
+                                pk_max_u16(v[u].z & mask, v[u].w & mask));
+        m = quad_max(umax32(m & 0xFFFFu, m >> 16));  // amax bits of the lane's block
+        // floor(log2(amax)) from the bf16 bits: the unbiased exponent of a
+        // normal, or the top mantissa bit of a subnormal (value mant * 2^-133)
+        const int ebits = (int)(m >> 7);
+        const int fl2 = ebits != 0 ? ebits - 127 : (31 - __builtin_clz(m | 1u)) - 133;
+        int e = m == 0 ? -127 : fl2 - 8;
+        e = e < -127 ? -127 : (e > 127 ? 127 : e);
+        // 2^-e as a float: normal for -e >= -126, else the subnormal 2^-127
+        const float factor = __builtin_bit_cast(float, -e >= -126 ? (uint32_t)(127 - e) << 23 : 0x00400000u);
+        float a[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                      bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+        float qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = __builtin_fabsf(a[i]) * factor;  // exact
+        const uint32_t w0 = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[u].x, v[u].y));
+        const uint32_t w1 = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[u].z, v[u].w));
+        if (row[u] < rows) {
+            *reinterpret_cast<uint2*>(q + row[u] * ld_q + j * 128 + c * 8) = make_uint2(w0, w1);
+            if ((c & 3) == 0)
+                reinterpret_cast<uint8_t*>(scale + j * ld_s + row[u])[c >> 2] = (uint8_t)(e + 127);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ 128x1
 
 // One 256-thread block quantizes a 128-token x 128-channel panel: thread
@@ -289,6 +347,16 @@ hipError_t launch_quant_act_scatter(const uint16_t* x, int64_t tokens, int64_t c
     const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
     hipLaunchKernelGGL(quant_act_1x128_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
                        x, tokens, slabs, ld_x, q, ld_q, scale, ld_s, units, dst_rows, topk, m_total);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                           int64_t ld_q, uint32_t* scale, int64_t ld_s, hipStream_t stream) {
+    const int64_t slabs = cols / 128;
+    const int64_t units = (rows + kActRowsPerWave - 1) / kActRowsPerWave * slabs;
+    const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
+    hipLaunchKernelGGL(quant_mx_1x32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units);
     return hipGetLastError();
 }
 

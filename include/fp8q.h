@@ -261,6 +261,49 @@ int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t *group_offsets, int64_t
                            void *c, int64_t ldc, int64_t stride_c, int out_dtype,
                            hipStream_t stream);
 
+/*
+ * fp8_quantize_mx -- microscaling (OCP MX) quantization with E4M3 elements.
+ *
+ * The variant the pages liken their fine-grained groups to (page "Deepseek
+ * Ai News Expert Interview", passage on microscaling formats with smaller
+ * quantization granularity). A different numeric contract from
+ * fp8_quantize_act: every 32 consecutive elements of a row share a power-
+ * of-two scale 2^e, e = floor(log2(amax)) - 8 clamped to [-127, 127] (-127
+ * for an all-zero block), stored as the E8M0 byte e + 127; each code is
+ * E4M3(x / 2^e) rounded to nearest, ties to the even code, saturating to
+ * +-448. Dequantized value = dec(q) * 2^e.
+ *
+ * x      bf16 [rows][ld_x], ld_x >= cols, cols % 128 == 0.
+ * q      codes [rows][ld_q], ld_q >= cols (the layout of x).
+ * scale  uint32 [cols/128][ld_s], ld_s >= rows: word (j, r) holds the four
+ *        E8M0 bytes of row r's blocks 4j .. 4j+3, byte b for block 4j + b.
+ * Alignment: x and q 16-byte aligned; ld_x % 8 == 0; ld_q % 16 == 0; scale
+ *        4-byte aligned. rows == 0 or cols == 0: returns FP8Q_OK.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_HIP.
+ */
+int fp8_quantize_mx(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *q,
+                    int64_t ld_q, uint32_t *scale, int64_t ld_s, hipStream_t stream);
+
+/*
+ * fp8_gemm_mx -- C = dequant_mx(A) * dequant_mx(B)^T.
+ *
+ * Both operands are K-contiguous MX codes with their scale words (as written
+ * by fp8_quantize_mx along K). The gfx950 scaled MFMA applies every 32-element
+ * block's two power-of-two scales and accumulates in FP32 inside the matrix
+ * core; there is no separate promotion step.
+ * a, a_scale  [m][lda], lda >= k; words [k/128][ld_as], ld_as >= m.
+ * b, b_scale  [n][ldb], ldb >= k; words [k/128][ld_bs], ld_bs >= n.
+ * c           [m][ldc], ldc >= n; out_dtype FP8Q_OUT_BF16 or FP8Q_OUT_F32.
+ * Shapes:     m, n >= 0, k % 128 == 0 (k == 0 writes zeros).
+ * Alignment:  as fp8_gemm.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
+ *         FP8Q_ERR_HIP.
+ */
+int fp8_gemm_mx(int64_t m, int64_t n, int64_t k,
+                const uint8_t *a, int64_t lda, const uint32_t *a_scale, int64_t ld_as,
+                const uint8_t *b, int64_t ldb, const uint32_t *b_scale, int64_t ld_bs,
+                void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+
 /* Text for a status code (static storage; never NULL). */
 const char *fp8q_status_string(int status);
 

@@ -219,9 +219,33 @@ def test_grouped_gemm_wgrad_validation(lib):
     assert _gw(lib, c=A16 + 4) == ERR_ALIGN
 
 
+def _mxq(lib, x=A16, rows=256, cols=512, ld_x=512, q=A16b, ld_q=512, s=A4, ld_s=256):
+    return lib.fp8_quantize_mx(x, rows, cols, ld_x, q, ld_q, s, ld_s, None)
+
+
+def _mxg(lib, m=300, n=200, k=256, a=A16, lda=256, a_s=A4, ld_as=300, b=A16b, ldb=256, b_s=A4,
+         ld_bs=200, c=A16c, ldc=200, out=0):
+    return lib.fp8_gemm_mx(m, n, k, a, lda, a_s, ld_as, b, ldb, b_s, ld_bs, c, ldc, out, None)
+
+
+def test_mx_validation(lib):
+    assert _mxq(lib, rows=0) == OK
+    assert _mxq(lib, rows=-1) == ERR_SHAPE
+    assert _mxq(lib, x=0) == ERR_NULL
+    assert _mxq(lib, cols=480, ld_x=512, ld_q=512) == ERR_SHAPE   # whole 128-column slabs only
+    assert _mxq(lib, ld_s=255) == ERR_SHAPE
+    assert _mxq(lib, q=A16b + 8) == ERR_ALIGN
+    assert _mxg(lib, m=0) == OK
+    assert _mxg(lib, out=2) == ERR_ENUM
+    assert _mxg(lib, b_s=0) == ERR_NULL
+    assert _mxg(lib, k=200, lda=256, ldb=256) == ERR_SHAPE
+    assert _mxg(lib, ld_bs=199) == ERR_SHAPE                    # one scale word per B row
+    assert _mxg(lib, lda=264) == ERR_ALIGN
+
+
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
-                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad"):
+                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx"):
         assert callable(getattr(fq, name))
 
 

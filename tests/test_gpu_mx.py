@@ -1,0 +1,102 @@
+"""GPU parity of the microscaling variant (fp8_quantize_mx, fp8_gemm_mx).
+
+Codes and E8M0 exponent bytes must equal the oracle's bit for bit; the
+scaled-MFMA GEMM must match the unrounded float64 oracle GEMM of the same MX
+operands to the same tolerance as the block-scaled GEMM.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_fp8_quantize_amd as fq
+import oracle
+import workloads as wl
+from gpu_util import assert_bits_equal, assert_gemm_close, dev_bf16, host_codes, host_out
+
+pytestmark = pytest.mark.gpu
+
+
+def _words_to_bytes(words: torch.Tensor, rows: int) -> np.ndarray:
+    """GPU scale words [cols/128][rows] (byte b = block 4j + b) -> [rows][cols/32]."""
+    w = words.contiguous().cpu().numpy().view(np.uint8).reshape(words.shape[0], words.shape[1], 4)
+    return np.ascontiguousarray(w[:, :rows].transpose(1, 0, 2).reshape(rows, -1))
+
+
+def _check_quant(bits: np.ndarray, what: str):
+    q, s = fq.fp8_quantize_mx(dev_bf16(bits))
+    torch.cuda.synchronize()
+    q_ref, e_ref = oracle.quant_mx_1x32(bits)
+    assert_bits_equal(_words_to_bytes(s, bits.shape[0]), e_ref, what + " E8M0 bytes")
+    assert_bits_equal(host_codes(q), q_ref, what + " codes")
+
+
+@pytest.mark.parametrize("which", ["x", "w"])
+def test_mx_quant_dense_full_size(which):
+    _check_quant(wl.dense_fprop()[which], "dense " + which)
+
+
+@pytest.mark.parametrize("rows", [1, 15, 17, 129])
+def test_mx_quant_ragged_rows(rows):
+    _check_quant(wl.activation(2, "tiny_fprop", 95, rows, 384, 50.0), "rows=%d" % rows)
+
+
+def test_mx_quant_special_blocks():
+    rng = np.random.default_rng(31)
+    rows = []
+    z = np.zeros(128, np.uint16)
+    z[::7] = 0x8000
+    rows.append(z)                                                               # all zero
+    rows.append(rng.integers(1, 0x80, 128).astype(np.uint16))                   # bf16 subnormals
+    big = wl.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32) * 1e37)
+    big[9] = 0x7F7F
+    rows.append(big)                                                             # largest exponents
+    rows.append(wl.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32) * 1e-37))  # clamp at -127
+    rows.append(wl.f32_to_bf16_bits(np.full(128, 448.0 * 17 / 64, np.float32)))   # ties
+    one = np.zeros(128, np.uint16)
+    one[40] = wl.f32_to_bf16_bits(np.array([-5.0], np.float32))[0]
+    rows.append(one)                                                             # single value
+    mixed = wl.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32))
+    mixed[32:64] = 0                                                             # one zero block among others
+    rows.append(mixed)
+    _check_quant(np.stack(rows), "special blocks")
+
+
+def _gemm_case(m, n, k, out_dtype=torch.bfloat16, sample=None, seed=0):
+    a = wl.activation(seed, "tiny_fprop", 96, m, k, 50.0)
+    b = wl.weight(seed, "tiny_fprop", 97, n, k)
+    aq, asc = fq.fp8_quantize_mx(dev_bf16(a))
+    bq, bsc = fq.fp8_quantize_mx(dev_bf16(b))
+    c = fq.fp8_gemm_mx(aq, asc, bq, bsc, out_dtype)
+    torch.cuda.synchronize()
+    got = host_out(c)
+    a_q, a_e = oracle.quant_mx_1x32(a)
+    b_q, b_e = oracle.quant_mx_1x32(b)
+    rows = np.arange(m) if sample is None else np.unique(np.concatenate(
+        [[0, 1, m - 1], np.random.default_rng(seed).choice(m, sample, replace=False)]))
+    ref = oracle.gemm_mx(a_q[rows], a_e[rows], b_q, b_e)
+    assert_gemm_close(got[rows], ref, "mx gemm %dx%dx%d" % (m, n, k))
+
+
+def test_mx_gemm_tiny_all_elements():
+    _gemm_case(128, 256, 512)
+
+
+def test_mx_gemm_ragged_and_f32():
+    _gemm_case(300, 200, 384, out_dtype=torch.float32)
+
+
+def test_mx_gemm_dense_fprop_sampled():
+    _gemm_case(4096, 4096, 7168, sample=40)
+
+
+def test_mx_gemm_k0_writes_zeros():
+    a = torch.empty((64, 0), dtype=torch.uint8, device="cuda")
+    s = torch.empty((0, 64), dtype=torch.int32, device="cuda")
+    c = torch.full((64, 128), 3.0, dtype=torch.float32, device="cuda")
+    b = torch.empty((128, 0), dtype=torch.uint8, device="cuda")
+    sb = torch.empty((0, 128), dtype=torch.int32, device="cuda")
+    fq.fp8_gemm_mx(a, s, b, sb, torch.float32, out=c)
+    torch.cuda.synchronize()
+    assert torch.all(c == 0)
