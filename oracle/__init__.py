@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_quant_pairs.restype = None
         L.oracle_quant_mx_1x32.argtypes = [u16p, i64, i64, i64, u8p, i64, u8p, i64]
         L.oracle_quant_mx_1x32.restype = None
+        L.oracle_retile_128x1.argtypes = [u8p, i64, i64, i64, f32p, i64, u8p, i64, f32p, i64]
+        L.oracle_retile_128x1.restype = None
         _LIB = L
     return _LIB
 
@@ -161,6 +163,25 @@ def quant_act_128x1(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return qt, s
 
 
+def retile_128x1(q: np.ndarray, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Cached FP8 activation re-tiled for Wgrad: 1x128 codes Q uint8[tokens][cols]
+    with scales S float32[cols/128][tokens] -> (QT uint8[cols][tokens],
+    ST float32[tokens/128][cols]). Every value is dequantized to binary32,
+    v = fl32(dec(q) * s), and quantized again in 128x1 tiles along tokens
+    (page "Is aI Hitting a Wall?", passage on keeping activations in FP8 for
+    the backward pass)."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    rows, cols = q.shape
+    assert rows % 128 == 0 and cols % 128 == 0
+    s = np.ascontiguousarray(s[:, :rows], dtype=np.float32)
+    assert s.shape == (cols // 128, rows)
+    qt = np.empty((cols, rows), dtype=np.uint8)
+    st = np.empty((rows // 128, cols), dtype=np.float32)
+    lib().oracle_retile_128x1(_p(q, ctypes.c_uint8), rows, cols, cols, _p(s, ctypes.c_float), rows,
+                              _p(qt, ctypes.c_uint8), rows, _p(st, ctypes.c_float), cols)
+    return qt, st
+
+
 def quant_weight_128x128(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """bf16 bits W[n][k] -> (Q uint8[n][k], S float32[n/128][k/128])."""
     w = np.ascontiguousarray(w, dtype=np.uint16)
@@ -238,6 +259,22 @@ def gemm_rows(row_idx: np.ndarray, a_q: np.ndarray, a_s: np.ndarray, b_q: np.nda
     row_idx = np.asarray(row_idx)
     return gemm(np.ascontiguousarray(a_q[row_idx]), np.ascontiguousarray(a_s[:, row_idx]),
                 b_q, b_s, b_scale_kind)
+
+
+def gemm_tensor(a_q: np.ndarray, a_s: float, b_q: np.ndarray, b_s: float) -> np.ndarray:
+    """Per-tensor scaled FP8 GEMM, the accumulation-study arm whose whole K
+    sum stays inside the matrix core (page "Eliminate Deepseek Ai News For
+    Good", passage on limited accumulation precision at K = 4096):
+
+        C[m][n] = sA * sB * sum_k dec(qA[m,k]) * dec(qB[n,k])
+
+    E4M3 values are multiples of 2^-9 below 2^9, so every product is a
+    multiple of 2^-18 below 2^18 and, for K <= 131072, every partial sum is
+    exact in float64 in any order: the matmul is the exact sum, and the one
+    rounding is the final multiplication by sA * sB (itself exact)."""
+    assert a_q.shape[1] <= 131072
+    d = _dec()
+    return (float(a_s) * float(b_s)) * (d[a_q] @ d[b_q].T)
 
 
 def grouped_gemm(offsets: np.ndarray, rows: np.ndarray, a_q: np.ndarray, a_s: np.ndarray,

@@ -191,6 +191,40 @@ void oracle_quant_weight_128x128(const uint16_t *w, int64_t n, int64_t k, int64_
     }
 }
 
+/* ------------------------------------------------ FP8 activation cache */
+
+/* A cached FP8 activation re-tiled for Wgrad. The FP8 Wgrad GEMM lets the
+ * forward activations be kept in FP8 for the backward pass (page "Is aI
+ * Hitting a Wall?", passage on storing activations in FP8 for the backward
+ * pass), but Wgrad wants 128x1 tiles along tokens while the forward pass
+ * made 1x128 tiles. Reading: each cached value is dequantized to binary32,
+ * v = fl32(dec(q) * s), and the values are quantized again in 128x1 tiles
+ * exactly as oracle_quant_act_128x1 quantizes bf16 input.
+ * q[rows=tokens][ldq] with scale[cols/128][lds] (1x128, slab-major) ->
+ * qt[cols][ldqt] (token-contiguous) with scale_t[rows/128][ldst].
+ * rows and cols must be multiples of 128. */
+void oracle_retile_128x1(const uint8_t *q, int64_t rows, int64_t cols, int64_t ldq,
+                         const float *scale, int64_t lds, uint8_t *qt, int64_t ldqt,
+                         float *scale_t, int64_t ldst) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; c++) {
+        float v[128];
+        for (int64_t j = 0; j < rows / 128; j++) {
+            float amax = 0.0f;
+            for (int i = 0; i < 128; i++) {
+                int64_t r = j * 128 + i;
+                float d = (float)oracle_e4m3_decode(q[r * ldq + c]); /* exact in binary32 */
+                v[i] = d * scale[(c / 128) * lds + r];
+                float a = fabsf(v[i]);
+                if (a > amax) amax = a;
+            }
+            float s = group_scale(amax);
+            scale_t[j * ldst + c] = s;
+            for (int i = 0; i < 128; i++) qt[c * ldqt + j * 128 + i] = quantize_value(v[i], amax, s);
+        }
+    }
+}
+
 /* ------------------------------------------------------- self-check helpers */
 
 /* Agreement of the two encoders over the binary32 bit patterns lo_bits,

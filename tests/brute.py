@@ -139,3 +139,20 @@ def quantize_mx_block(bits: list[int]) -> tuple[int, list[int]]:
     e = -127 if amax == 0 else max(-127, min(127, _floor_log2(amax) - 8))
     scale = Fraction(2) ** e
     return e, [e4m3_nearest(v / scale, bf16_is_negative(b)) for b, v in zip(bits, vals)]
+
+
+def retile_group(codes: list[int], scales: list[Fraction]) -> tuple[Fraction, list[int]]:
+    """One 128x1 group of a cached 1x128 activation: v = rn32(dec(q) * s) per
+    element (s: the element's 1x128 scale), then the group quantization of
+    :func:`quantize_group` on the v (sign of each code = sign of its q)."""
+    vals = [round_binary32(e4m3_value(c) * s) for c, s in zip(codes, scales)]
+    neg = [bool(c & 0x80) for c in codes]
+    amax = max(abs(v) for v in vals)
+    s_new = round_binary32(amax / 448)
+    out = []
+    for v, ng in zip(vals, neg):
+        if amax == 0:
+            out.append(0x80 if ng else 0x00)
+        else:
+            out.append(e4m3_nearest(round_binary32(v / s_new), ng))
+    return s_new, out

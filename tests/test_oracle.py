@@ -598,3 +598,134 @@ def test_gemm_mx_matches_exact_rational_brute_force():
     for m in range(4):
         for n in range(5):
             assert got[m, n] == float(ref[m][n])
+
+
+# ------------------------------------------------- FP8 activation cache re-tile
+
+def _cached_activation(rng, tokens, cols):
+    """1x128 codes and scales of a bf16 activation with special token rows:
+    zero rows (scale 0), a row with only signed zeros, rows of tiny values
+    (subnormal fp32 scales), an outlier row and negative-only rows."""
+    x = wl.f32_to_bf16_bits(rng.standard_normal((tokens, cols)).astype(np.float32))
+    x[3] = 0
+    x[4] = 0x8000
+    x[5] = wl.f32_to_bf16_bits(rng.standard_normal(cols).astype(np.float32) * 1e-39)
+    x[6] = wl.f32_to_bf16_bits(rng.standard_normal(cols).astype(np.float32) * 3e3)
+    x[7] = wl.f32_to_bf16_bits(-np.abs(rng.standard_normal(cols)).astype(np.float32))
+    if tokens > 128:
+        x[128:256, 5] = 0                                  # an all-zero 128x1 group
+    return oracle.quant_act_1x128(x)
+
+
+def test_retile_matches_exact_rational_brute_force():
+    """Pin: sampled 128x1 groups of the re-tiled cache equal the exact-rational
+    dequantize (rn32(dec(q) * s)) and requantize of brute force."""
+    rng = np.random.default_rng(31)
+    q, s = _cached_activation(rng, 256, 256)
+    qt, st = oracle.retile_128x1(q, s)
+    for c in (0, 1, 5, 127, 128, 200, 255):
+        for j in range(2):
+            toks = range(128 * j, 128 * j + 128)
+            codes = [int(q[t, c]) for t in toks]
+            scales = [Fraction(float(s[c // 128, t])) for t in toks]
+            bs, bq = brute.retile_group(codes, scales)
+            assert Fraction(float(st[j, c])) == bs, (c, j)
+            assert list(qt[c, 128 * j:128 * j + 128]) == bq, (c, j)
+
+
+def test_retile_power_of_two_rows_reproduce_the_codes():
+    """Closed form: when every token's 1x128 scale is the same 2^p and every
+    128x1 group holds the code 448, v = dec(q) * 2^p exactly, the new scale is
+    448 * 2^p / 448 = 2^p and each code comes back unchanged (transposed)."""
+    rng = np.random.default_rng(32)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    q = rng.choice(finite, size=(256, 384)).astype(np.uint8)
+    q[rng.integers(0, 128, 384), np.arange(384)] = 0x7E         # +448 in every group
+    q[128 + rng.integers(0, 128, 384), np.arange(384)] = 0xFE   # -448
+    for p in (-20, 0, 7):
+        s = np.full((3, 256), 2.0 ** p, np.float32)
+        qt, st = oracle.retile_128x1(q, s)
+        assert np.array_equal(qt, q.T)
+        assert np.all(st == np.float32(2.0 ** p))
+
+
+def test_retile_error_within_one_half_e4m3_step():
+    """Bound: each re-tiled value differs from the cached value v by at most
+    half an E4M3 step at the new scale (rounding v / s' to nearest), plus the
+    binary32 rounding of the quotient."""
+    rng = np.random.default_rng(33)
+    q, s = _cached_activation(rng, 256, 512)
+    qt, st = oracle.retile_128x1(q, s)
+    dec = oracle.e4m3_decode_table()
+    v = (dec[q].astype(np.float32) * np.repeat(s.T, 128, axis=1)).astype(np.float64)   # [t][c]
+    back = dec[qt].T * np.repeat(st.astype(np.float64), 128, axis=0)
+    y = np.abs(v) / np.repeat(np.where(st == 0, 1, st).astype(np.float64), 128, axis=0)
+    expo = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+    step = 2.0 ** (expo - 3)                                  # E4M3 spacing at y (2^-9 below 2^-6)
+    bound = (0.5 * step * (1 + 2 ** -20) + y * 2 ** -24) * np.repeat(st.astype(np.float64), 128, axis=0)
+    assert np.all(np.abs(back - v) <= bound)
+
+
+def test_retile_sign_and_zero_groups():
+    """Special cases: an all-zero group stores scale 0 and keeps signed zeros;
+    negating the cache flips only the sign bits of the re-tiled codes."""
+    rng = np.random.default_rng(34)
+    q, s = _cached_activation(rng, 256, 256)
+    qt, st = oracle.retile_128x1(q, s)
+    assert st[1, 5] == 0 and np.all((qt[5, 128:256] & 0x7F) == 0)
+    qn, stn = oracle.retile_128x1(q ^ np.uint8(0x80), s)
+    assert np.array_equal(stn, st)
+    assert np.array_equal(qn, qt ^ np.uint8(0x80))
+
+
+# ---------------------------------------------- per-tensor GEMM (study arm)
+
+def test_gemm_tensor_matches_exact_rational_brute_force():
+    """Pin: tiny per-tensor GEMM equals the exact rational sum times sA * sB."""
+    rng = np.random.default_rng(35)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    a = rng.choice(finite, size=(3, 160)).astype(np.uint8)
+    b = rng.choice(finite, size=(4, 160)).astype(np.uint8)
+    sa, sb = np.float32(0.375), np.float32(3.1e-3)
+    c = oracle.gemm_tensor(a, sa, b, sb)
+    ex = brute.gemm_exact([[int(v) for v in r] for r in a], [[Fraction(float(sa))] * 160] * 3,
+                          [[int(v) for v in r] for r in b], [[Fraction(float(sb))] * 160] * 4)
+    for i in range(3):
+        for j in range(4):
+            assert c[i, j] == float(ex[i][j])
+
+
+def test_gemm_tensor_is_exact_at_k4096():
+    """Pin: at the study's K = 4096 the oracle sum is exact: it equals the
+    integer GEMM of the codes' values times 2^9 (exact in int64), scaled by
+    2^-18, bit for bit."""
+    rng = np.random.default_rng(36)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    a = rng.choice(finite, size=(24, 4096)).astype(np.uint8)
+    b = rng.choice(finite, size=(20, 4096)).astype(np.uint8)
+    ints = np.array([int(brute.e4m3_value(c) * 512) if (c & 0x7F) != 0x7F else 0
+                     for c in range(256)], np.int64)
+    exact = ints[a] @ ints[b].T                                # int64, no rounding
+    c = oracle.gemm_tensor(a, 1.0, b, 1.0)
+    assert np.array_equal(c * 2.0 ** 18, exact.astype(np.float64))
+    assert np.all(np.abs(exact) < 2 ** 53)
+
+
+def test_retile_dequantizes_to_binary32_before_requantizing():
+    """Pin of the reading that the cached value is first rounded to binary32:
+    token 0 holds 448 at scale 1 (so the new scale is exactly 1) and token 1
+    holds 1.125 at scale s = the smallest binary32 above 17/18. The exact
+    product lies just above the E4M3 tie 1.0625 (-> 1.125, code 0x39), but
+    rn32 of it is the tie itself, which goes to the even code 1.0 (0x38)."""
+    s1 = np.float32(17 / 18)
+    if Fraction(float(s1)) <= Fraction(17, 18):
+        s1 = np.nextafter(s1, np.float32(1))
+    assert np.float32(1.125) * s1 == np.float32(1.0625)
+    assert Fraction(9, 8) * Fraction(float(s1)) > Fraction(17, 16)
+    q = np.zeros((128, 128), np.uint8)
+    s = np.ones((1, 128), np.float32)
+    q[0, 0], q[1, 0], s[0, 1] = 0x7E, 0x39, s1
+    qt, st = oracle.retile_128x1(q, s)
+    assert st[0, 0] == 1.0 and qt[0, 0] == 0x7E and qt[0, 1] == 0x38
+    bs, bq = brute.retile_group([int(v) for v in q[:, 0]], [Fraction(float(v)) for v in s[0]])
+    assert bs == 1 and bq[:2] == [0x7E, 0x38]
