@@ -40,6 +40,8 @@ __all__ = [
     "fp8_grouped_gemm_wgrad",
     "fp8_quantize_mx",
     "fp8_gemm_mx",
+    "fp8_retile_act_128x1",
+    "fp8_gemm_tensor",
     "fp8q_status_string",
     "fp8q_last_hip_error",
     "Fp8qError",
@@ -87,8 +89,11 @@ def _load() -> ctypes.CDLL:
                                          p, i64, i64, cint, p]
     L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
                                    i64, p, i64, cint, p]
+    L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
+    L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
-                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx"):
+                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
+                 "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
     L.fp8q_status_string.argtypes = [cint]
     L.fp8q_status_string.restype = ctypes.c_char_p
@@ -407,4 +412,57 @@ def fp8_gemm_mx(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale
                              _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0),
                              _ptr(out), out.stride(0), oc, _stream(stream))
     _check(st, "fp8_gemm_mx")
+    return out
+
+
+def fp8_retile_act_128x1(q: torch.Tensor, scale: torch.Tensor, q_t: torch.Tensor | None = None,
+                         scale_t: torch.Tensor | None = None, stream=None):
+    """Cached 1x128 FP8 activation (codes ``q[tokens][cols]``, scales
+    ``scale[cols/128][tokens]``) -> 128x1 token tiles for Wgrad: codes
+    ``q_t[cols][tokens]`` and scales ``scale_t[tokens/128][cols]``."""
+    _need_gpu(q, scale, q_t, scale_t)
+    _rowmajor(q, "q")
+    _rowmajor(scale, "scale")
+    _codes(q, "q")
+    if scale.dtype != torch.float32:
+        raise Fp8qError("scale must be float32")
+    tokens, cols = q.shape
+    if q_t is None:
+        q_t = torch.empty((cols, tokens), dtype=torch.float8_e4m3fn, device=q.device)
+    if scale_t is None:
+        scale_t = torch.empty((tokens // 128, cols), dtype=torch.float32, device=q.device)
+    _codes(q_t, "q_t")
+    st = _load().fp8_retile_act_128x1(_ptr(q), tokens, cols, q.stride(0), _ptr(scale), scale.stride(0),
+                                      _ptr(q_t), q_t.stride(0), _ptr(scale_t), scale_t.stride(0),
+                                      _stream(stream))
+    _check(st, "fp8_retile_act_128x1")
+    return q_t, scale_t
+
+
+def fp8_gemm_tensor(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
+                    out_dtype=torch.bfloat16, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """``C = sA * sB * sum_k dec(A)[m][k] dec(B)[n][k]`` with one scale per
+    operand (one-element float32 tensors) and the whole K sum accumulated in
+    the MFMA accumulators (no per-slab promotion)."""
+    _need_gpu(a, a_scale, b, b_scale, out)
+    _rowmajor(a, "a")
+    _rowmajor(b, "b")
+    _codes(a, "a")
+    _codes(b, "b")
+    m, k = a.shape
+    n, kb = b.shape
+    if kb != k:
+        raise Fp8qError("a and b disagree on K (%d vs %d)" % (k, kb))
+    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
+        raise Fp8qError("scales must be float32")
+    if a_scale.numel() != 1 or b_scale.numel() != 1:
+        raise Fp8qError("per-tensor scales hold one element each")
+    oc = _out_code(out_dtype)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    elif out.dtype != out_dtype:
+        raise Fp8qError("out has dtype %s, expected %s" % (out.dtype, out_dtype))
+    st = _load().fp8_gemm_tensor(m, n, k, _ptr(a), a.stride(0), _ptr(a_scale), _ptr(b), b.stride(0),
+                                 _ptr(b_scale), _ptr(out), out.stride(0), oc, _stream(stream))
+    _check(st, "fp8_gemm_tensor")
     return out

@@ -217,4 +217,40 @@ int fp8_gemm_mx(int64_t m, int64_t n, int64_t k,
     return hip_status(fp8q::launch_gemm_mx(g, stream));
 }
 
+int fp8_retile_act_128x1(const uint8_t* q, int64_t tokens, int64_t cols, int64_t ld_q,
+                         const float* scale, int64_t ld_s, uint8_t* q_t, int64_t ld_qt,
+                         float* scale_t, int64_t ld_st, hipStream_t stream) {
+    if (tokens < 0 || cols < 0) return FP8Q_ERR_SHAPE;
+    if (tokens == 0 || cols == 0) return FP8Q_OK;
+    if (!q || !scale || !q_t || !scale_t) return FP8Q_ERR_NULL;
+    if (tokens % 128 != 0 || cols % 128 != 0 || ld_q < cols || ld_s < tokens || ld_qt < tokens ||
+        ld_st < cols)
+        return FP8Q_ERR_SHAPE;
+    if (!aligned(q, 16) || !aligned(scale, 16) || !aligned(q_t, 16) || !aligned(scale_t, 4) ||
+        ld_q % 16 != 0 || ld_s % 4 != 0 || ld_qt % 16 != 0)
+        return FP8Q_ERR_ALIGN;
+    if (!grid_ok(tokens / 128 * (cols / 128))) return FP8Q_ERR_SHAPE;
+    return hip_status(fp8q::launch_retile_128x1(q, tokens, cols, ld_q, scale, ld_s, q_t, ld_qt, scale_t,
+                                                ld_st, stream));
+}
+
+int fp8_gemm_tensor(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda, const float* a_scale,
+                    const uint8_t* b, int64_t ldb, const float* b_scale, void* c, int64_t ldc,
+                    int out_dtype, hipStream_t stream) {
+    if (m < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
+    if (m == 0 || n == 0) return FP8Q_OK;
+    // one scale per operand: the slab-major scale checks see a leading dimension of m
+    int st = check_gemm_common(m, n, k, a, lda, a_scale, m, b, ldb, b_scale, c, ldc, out_dtype);
+    if (st != FP8Q_OK) return st;
+    if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) + 8)) return FP8Q_ERR_SHAPE;
+    fp8q::GemmProblem g = {};
+    g.m = m; g.n = n; g.k = k;
+    g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = 0;
+    g.b = b; g.ldb = ldb; g.b_scale = b_scale; g.ld_bs = 0;
+    g.b_rowscale = true;
+    g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
+    return hip_status(fp8q::launch_gemm_tensor(g, stream));
+}
+
 }  // extern "C"

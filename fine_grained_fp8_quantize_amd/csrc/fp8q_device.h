@@ -89,16 +89,24 @@ struct GroupScale {
     bool slow;
 };
 
-__device__ __forceinline__ GroupScale group_scale(uint32_t amax_bf16_bits) {
+__device__ __forceinline__ GroupScale group_scale_f32(float amax) {
     GroupScale g;
-    float amax = __uint_as_float(amax_bf16_bits << 16);
     g.s = amax / kE4M3Max;
     g.slow = !(g.s >= kSmallScale);
     g.y = g.slow ? 0.0f : 1.0f / g.s;
     return g;
 }
 
-// fl32(|x| / s), clamped to 448 (saturation), for a magnitude ax >= 0.
+__device__ __forceinline__ GroupScale group_scale(uint32_t amax_bf16_bits) {
+    return group_scale_f32(__uint_as_float(amax_bf16_bits << 16));
+}
+
+// fl32(|x| / s) for a magnitude ax >= 0 (the caller clamps to 448). For
+// binary32 numerators in general (not only bf16 ones) this is Markstein's
+// correction: with y the correctly rounded 1/s and q0 within one ulp of
+// ax/s, the residual r is exact and fl32(q0 + r*y) is the correctly rounded
+// quotient, barring underflow, which s >= 2^-60 rules out where a code can
+// be nonzero.
 __device__ __forceinline__ float quot_fast(float ax, const GroupScale& g) {
     float q0 = ax * g.y;
     float r = __builtin_fmaf(-q0, g.s, ax);

@@ -328,10 +328,14 @@ __device__ __forceinline__ void unroll(std::integer_sequence<int, Is...>, F&& f)
 // K blocks carry E8M0 scales, one uint32 per row and slab (byte b = block
 // 4j + b); the scaled MFMA applies them and accumulates in place, with no
 // promotion step. Copies and scale staging are those of per-row scales.
-template <int BN, bool ROWSCALE, bool OUT_F32, int MODE, bool MX = false>
+// TENSOR: one scale per operand (a_scale[0], b_scale[0]); the whole K sum is
+// accumulated inside the MFMA accumulators and scaled once in the epilogue.
+template <int BN, bool ROWSCALE, bool OUT_F32, int MODE, bool MX = false, bool TENSOR = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     constexpr bool GROUPED = MODE == kGroupedM;
     static_assert(!MX || (ROWSCALE && MODE == kDense), "microscaling: dense, per-row staging");
+    static_assert(!TENSOR || (ROWSCALE && MODE == kDense && !MX), "per-tensor: dense, no staged scales");
+    constexpr bool INPLACE = MX || TENSOR;  // MFMA accumulates across slabs
     static_assert(BN == 256 || BN == 224, "n tile");
     constexpr int WN = BN / 2;        // n extent of one wave
     constexpr int NSUB = WN / 16;     // n-subtiles per wave
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     auto issue_part = [&](int j, auto st, int i) {
         copy_a(j, st, i);
         copy_b(j, st, i);
-        if constexpr (!DEEP) {
+        if constexpr (!DEEP && !TENSOR) {
             if (i == 3) {
                 constexpr int S = decltype(st)::value;
                 const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
@@ -624,8 +628,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // One slab of the microscaling GEMM: the scaled MFMA takes each lane's
-    // E8M0 byte and accumulates into acc directly. In the 16x16x128 FP8 MFMA,
+    // One slab of the in-place GEMMs. Microscaling: the scaled MFMA takes
+    // each lane's E8M0 byte and accumulates into acc directly. Per-tensor:
+    // the plain MFMA accumulates into acc directly. In the 16x16x128 FP8 MFMA,
     // the 32 bytes of lane group g are K[16g, 16g+16) and K[64+16g, 64+16g+16)
     // of the slab, and the scale of K block b (32 elements) comes from lane
     // group b (measured on gfx950). So lane group g reads 16-byte chunks g and
@@ -635,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // same sum.)
     const uint32_t moff0 = fi * kSlab + swz_chunk(fg, fi) * 16;
     const uint32_t moff1 = fi * kSlab + swz_chunk(fg + 4, fi) * 16;
-    auto compute_mx = [&](auto a_tag, auto act_tag) {
+    auto compute_inplace = [&](auto a_tag, auto act_tag) {
         constexpr int ST = decltype(a_tag)::value;
         constexpr int ACT = decltype(act_tag)::value;
         const uint8_t* const la = stage_a<ST>() + fragA;
@@ -646,29 +651,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         v8i fr[2];
         uint32_t sbw[2];
         fr[0] = ld_frag(lb + moff0, lb + moff1);
-        sbw[0] = lsb[0];
+        sbw[0] = MX ? lsb[0] : 0u;
         v8i am[kMSub];
         int sae[kMSub];
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + moff0, la + s * 2048 + moff1);
 #pragma unroll
-        for (int s = 0; s < kMSub; ++s) sae[s] = (int)((lsa[16 * s] >> shift) & 0xFFu);
+        for (int s = 0; s < kMSub; ++s) sae[s] = MX ? (int)((lsa[16 * s] >> shift) & 0xFFu) : 0;
         __builtin_amdgcn_sched_barrier(0);
         unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
             constexpr int T = decltype(t_tag)::value;
             const v8i bf = fr[T & 1];
-            const int sbe = (int)((sbw[T & 1] >> shift) & 0xFFu);
+            const int sbe = MX ? (int)((sbw[T & 1] >> shift) & 0xFFu) : 0;
             if constexpr (T + 1 < NSUB) {
                 fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + moff0, lb + (T + 1) * 2048 + moff1);
-                sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
+                if constexpr (MX) sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
             }
             if constexpr (T < 4) issue_part(jnext, std::integral_constant<int, ST ^ 1>{}, T);
 #pragma unroll
-            for (int s = 0; s < ACT; ++s)
-                acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
-                                                                            0, sbe, 0, sae[s]);
+            for (int s = 0; s < ACT; ++s) {
+                // (zero scale operands select the unscaled instruction)
+                if constexpr (MX)
+                    acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
+                                                                                0, sbe, 0, sae[s]);
+                else
+                    acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
+                                                                                0, 0, 0, 0);
+            }
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, MX ? 3 : 2, 0);
             if constexpr (T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, ACT - 1, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -690,8 +701,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             jnext = min(j + 1, slabs - 1);
             if constexpr (ACT == 0) issue(jnext, std::integral_constant<int, ST ^ 1>{});
             if constexpr (ACT > 0) {
-                if constexpr (MX)
-                    compute_mx(stage_tag, act_tag);
+                if constexpr (INPLACE)
+                    compute_inplace(stage_tag, act_tag);
                 else
                     compute(stage_tag, stage_tag, act_tag, no_sab);
             }
@@ -787,6 +798,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
     // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
+    // (k == 0: the scales may be NULL and are not read; C is zero)
+    const float alpha = (TENSOR && p.k > 0) ? p.a_scale[0] * p.b_scale[0] : 1.0f;
 #pragma unroll
     for (int s = 0; s < kMSub; ++s) {
         const int64_t m = wrow + s * 16 + fi;
@@ -797,6 +810,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             const int64_t n = wcol + t * 16 + 4 * fg;
             if (n >= tr.n0 + BN) continue;
             v4f v = pad ? zero : acc[t][s];
+            if constexpr (TENSOR) v = v * alpha;
             if constexpr (OUT_F32) {
                 float* dst = reinterpret_cast<float*>(tr.c) + m * p.ldc + n;
                 if (n + 3 < p.n) {
@@ -878,6 +892,18 @@ hipError_t dispatch_mx(const GemmProblem& g, int64_t blocks, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Per-tensor scaled dense GEMM (whole-K accumulation in the MFMA).
+template <int BN>
+hipError_t dispatch_tensor(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
+    const Params p = to_params(g);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (g.out_f32)
+        hipLaunchKernelGGL((gemm_kernel<BN, true, true, kDense, false, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((gemm_kernel<BN, true, false, kDense, false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
+
 // blocks: a multiple of 256 (see grouped_tile). Grouped GEMMs take 128x128
 // block scales only.
 hipError_t dispatch_grouped(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
@@ -947,6 +973,15 @@ hipError_t launch_gemm_mx(const GemmProblem& g, hipStream_t stream) {
     }
     const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
     return dispatch_mx<256>(g, (tiles + 7) / 8 * 8, stream);
+}
+
+hipError_t launch_gemm_tensor(const GemmProblem& g, hipStream_t stream) {
+    if (grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256)) {
+        const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
+        return dispatch_tensor<224>(g, (tiles + 7) / 8 * 8, stream);
+    }
+    const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
+    return dispatch_tensor<256>(g, (tiles + 7) / 8 * 8, stream);
 }
 
 }  // namespace fp8q

@@ -22,6 +22,10 @@ hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t col
                                   uint8_t* qt, int64_t ld_q, float* scale, int64_t ld_s,
                                   hipStream_t stream);
 
+hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, int64_t ld_q,
+                               const float* scale, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
+                               float* scale_t, int64_t ld_st, hipStream_t stream);
+
 hipError_t launch_quant_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
                                uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                                uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
@@ -54,5 +58,6 @@ hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_grouped_k_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_gemm_tensor(const GemmProblem& p, hipStream_t stream);
 
 }  // namespace fp8q

@@ -261,6 +261,118 @@ __global__ __launch_bounds__(256) void quant_act_128x1_kernel(
     }
 }
 
+// ------------------------------------------------- cached activation re-tile
+
+// A cached FP8 activation (1x128 codes and scales from the forward pass)
+// re-tiled into the 128x1 token tiles Wgrad takes (page "Is aI Hitting a
+// Wall?", passage on keeping activations in FP8 for the backward pass): each
+// value is dequantized to binary32, v = fl32(dec(q) * s_token), and the v are
+// quantized in 128x1 tiles exactly as quant_act_128x1_kernel quantizes bf16.
+// One 256-thread block takes a 128-token x 128-channel panel; thread (token
+// group r = t/16, channel chunk g = t%16) loads 8 tokens x 8 channels of
+// codes (one 8-byte load per token) and the 8 tokens' scales. The code of an
+// output element keeps the sign bit of the input code (s_token >= 0).
+__global__ __launch_bounds__(256) void retile_128x1_kernel(
+    const uint8_t* __restrict__ q, int64_t ld_q, const float* __restrict__ scale, int64_t ld_s,
+    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
+    int64_t cblocks) {
+    __shared__ uint32_t red[4][16][8];
+    __shared__ float s_sh[128];
+    __shared__ float y_sh[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int g = t & 15, r = t >> 4;
+    const int64_t tb = blockIdx.x / cblocks, cb = blockIdx.x - tb * cblocks;
+    const int64_t t0 = tb * 128, c0 = cb * 128;
+
+    uint2 code[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 c = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2*>(q + (t0 + 8 * r + i) * ld_q + c0 + 8 * g));
+        code[i] = make_uint2(c.x, c.y);
+    }
+    // scale[slab cb][token]: the thread's 8 tokens are 32 contiguous bytes
+    const float4* sp = reinterpret_cast<const float4*>(scale + cb * ld_s + t0 + 8 * r);
+    const float4 s_lo = sp[0], s_hi = sp[1];
+    const float st[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
+
+    float v[8][8];  // [token][channel]
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].x, false);
+        const f2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].x, true);
+        const f2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].y, false);
+        const f2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].y, true);
+        const float d[8] = {d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[i][k] = d[k] * st[i];
+    }
+    // Column amax: over the thread's 8 tokens, the wave's 4 token groups
+    // (lanes 16 and 32 apart), then the 4 waves through LDS. Magnitudes of
+    // finite floats order as their bit patterns.
+    uint32_t m[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        uint32_t mm = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mm = umax32(mm, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+        mm = umax32(mm, (uint32_t)__shfl_xor((int)mm, 16));
+        mm = umax32(mm, (uint32_t)__shfl_xor((int)mm, 32));
+        m[k] = mm;
+    }
+    if ((lane >> 4) == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) red[w][g][k] = m[k];
+    }
+    __syncthreads();
+    if (t < 128) {
+        const int chunk = t >> 3, kk = t & 7;
+        uint32_t mm = 0;
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) mm = umax32(mm, red[ww][chunk][kk]);
+        const GroupScale gs = group_scale_f32(__uint_as_float(mm));
+        s_sh[t] = gs.s;
+        y_sh[t] = gs.y;
+        scale_t[tb * ld_st + c0 + t] = gs.s;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        GroupScale gs;
+        gs.s = s_sh[8 * g + k];
+        gs.y = y_sh[8 * g + k];
+        gs.slow = !(gs.s >= kSmallScale);
+        float qv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qv[i] = quot_fast(__builtin_fabsf(v[i][k]), gs);
+        if (gs.slow) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) qv[i] = quot_slow(__builtin_fabsf(v[i][k]), gs);
+        }
+        uint32_t wd[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) wd[i] = k < 4 ? code[i].x : code[i].y;
+        const uint32_t byte = (uint32_t)(k & 3);
+        const uint32_t s0 = gather_byte4(wd[0], wd[1], wd[2], wd[3], byte);
+        const uint32_t s1 = gather_byte4(wd[4], wd[5], wd[6], wd[7], byte);
+        const uint32_t w0 = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], s0);
+        const uint32_t w1 = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], s1);
+        *reinterpret_cast<uint2*>(&tr[(8 * g + k) * kTrStride + 8 * r]) = make_uint2(w0, w1);
+    }
+    __syncthreads();
+    const int cc = t >> 1, h = t & 1;
+    uint8_t* dst = qt + (c0 + cc) * ld_qt + t0 + 64 * h;
+    const uint8_t* src = &tr[cc * kTrStride + 64 * h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(src + 16 * i);
+}
+
 // ---------------------------------------------------------------- 128x128
 
 // One 256-thread block quantizes one 128x128 weight block: thread (row group
@@ -367,6 +479,16 @@ hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t col
     const int64_t blocks = tokens / 128 * cblocks;
     hipLaunchKernelGGL(quant_act_128x1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        x, tokens, cols, ld_x, qt, ld_q, scale, ld_s, cblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, int64_t ld_q,
+                               const float* scale, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
+                               float* scale_t, int64_t ld_st, hipStream_t stream) {
+    const int64_t cblocks = cols / 128;
+    const int64_t blocks = tokens / 128 * cblocks;
+    hipLaunchKernelGGL(retile_128x1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       q, ld_q, scale, ld_s, qt, ld_qt, scale_t, ld_st, cblocks);
     return hipGetLastError();
 }
 

@@ -304,6 +304,56 @@ int fp8_gemm_mx(int64_t m, int64_t n, int64_t k,
                 const uint8_t *b, int64_t ldb, const uint32_t *b_scale, int64_t ld_bs,
                 void *c, int64_t ldc, int out_dtype, hipStream_t stream);
 
+/*
+ * fp8_retile_act_128x1 -- a cached FP8 activation re-tiled for Wgrad.
+ *
+ * The FP8 Wgrad GEMM lets the forward activations be kept in FP8 for the
+ * backward pass (page "Is aI Hitting a Wall?", passage on storing
+ * activations in FP8 for the backward pass). The forward pass holds them as
+ * 1x128 codes and scales (fp8_quantize_act, FP8Q_TILE_1x128); Wgrad takes
+ * 128x1 token tiles. Each value is dequantized to binary32,
+ * v = fl32(dec(q) * s), and the v are quantized in 128x1 tiles exactly as
+ * FP8Q_TILE_128x1 quantizes bf16 input (s' = fl32(amax / 448),
+ * q' = E4M3(fl32(v / s')), RNE, saturating; all-zero tile: s' = 0). The
+ * result is bit-identical to that definition; it is not, in general, the
+ * 128x1 quantization of the original bf16 activation.
+ *
+ * q        codes [tokens][ld_q], ld_q >= cols (1x128 layout).
+ * scale    fp32 [cols/128][ld_s], ld_s >= tokens (slab-major 1x128 scales).
+ * q_t      codes [cols][ld_qt], ld_qt >= tokens (token-contiguous).
+ * scale_t  fp32 [tokens/128][ld_st], ld_st >= cols.
+ * Shapes: tokens % 128 == 0, cols % 128 == 0; either 0: returns FP8Q_OK.
+ * Alignment: q, q_t and scale 16-byte aligned; ld_q % 16 == 0,
+ *         ld_qt % 16 == 0, ld_s % 4 == 0; scale_t 4-byte aligned.
+ * Codes 0x7F / 0xFF (NaN) are outside the contract.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_HIP.
+ */
+int fp8_retile_act_128x1(const uint8_t *q, int64_t tokens, int64_t cols, int64_t ld_q,
+                         const float *scale, int64_t ld_s, uint8_t *q_t, int64_t ld_qt,
+                         float *scale_t, int64_t ld_st, hipStream_t stream);
+
+/*
+ * fp8_gemm_tensor -- C = sA * sB * sum_k dec(A[m][k]) * dec(B[n][k]), with one
+ * scale per operand and the whole K sum accumulated inside the matrix core.
+ *
+ * The arm of the accumulation study (page "Eliminate Deepseek Ai News For
+ * Good", passage on limited accumulation precision in a K = 4096 GEMM of
+ * random matrices): no per-interval promotion, the MFMA accumulators carry
+ * the sum over all K, and fl32(sA * sB) scales the result once. Compare
+ * fp8_gemm, which promotes every 128-element slab.
+ * a        codes [m][lda], lda >= k.    a_scale  one fp32 (device).
+ * b        codes [n][ldb], ldb >= k.    b_scale  one fp32 (device).
+ * c        [m][ldc], ldc >= n; out_dtype FP8Q_OUT_BF16 or FP8Q_OUT_F32.
+ * Shapes:  m, n >= 0, k % 128 == 0 (k == 0 writes zeros; a, b and the
+ *          scales are then not read and may be NULL).
+ * Alignment: as fp8_gemm.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
+ *         FP8Q_ERR_HIP.
+ */
+int fp8_gemm_tensor(int64_t m, int64_t n, int64_t k, const uint8_t *a, int64_t lda,
+                    const float *a_scale, const uint8_t *b, int64_t ldb, const float *b_scale,
+                    void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+
 /* Text for a status code (static storage; never NULL). */
 const char *fp8q_status_string(int status);
 

@@ -243,9 +243,49 @@ def test_mx_validation(lib):
     assert _mxg(lib, lda=264) == ERR_ALIGN
 
 
+def _rt(lib, q=A16, tokens=256, cols=384, ld_q=384, s=A4, ld_s=256, qt=A16b, ld_qt=256, st=A4 + 0x1000,
+        ld_st=384):
+    return lib.fp8_retile_act_128x1(q, tokens, cols, ld_q, s, ld_s, qt, ld_qt, st, ld_st, None)
+
+
+def test_retile_validation(lib):
+    assert _rt(lib, tokens=0) == OK
+    assert _rt(lib, cols=-128) == ERR_SHAPE
+    assert _rt(lib, qt=0) == ERR_NULL
+    assert _rt(lib, st=0) == ERR_NULL
+    assert _rt(lib, tokens=200, ld_s=256, ld_qt=256) == ERR_SHAPE   # whole 128-token tiles
+    assert _rt(lib, cols=320, ld_q=320, ld_st=320) == ERR_SHAPE     # whole 128-channel tiles
+    assert _rt(lib, ld_q=256) == ERR_SHAPE
+    assert _rt(lib, ld_s=128) == ERR_SHAPE
+    assert _rt(lib, ld_qt=128) == ERR_SHAPE
+    assert _rt(lib, ld_st=256) == ERR_SHAPE
+    assert _rt(lib, s=A4 + 4) == ERR_ALIGN                         # 16-byte scale reads
+    assert _rt(lib, ld_s=258) == ERR_ALIGN
+    assert _rt(lib, ld_q=392) == ERR_ALIGN
+    assert _rt(lib, qt=A16b + 8) == ERR_ALIGN
+
+
+def _tg(lib, m=300, n=200, k=256, a=A16, lda=256, a_s=A4, b=A16b, ldb=256, b_s=A4, c=A16c, ldc=200, out=1):
+    return lib.fp8_gemm_tensor(m, n, k, a, lda, a_s, b, ldb, b_s, c, ldc, out, None)
+
+
+def test_gemm_tensor_validation(lib):
+    assert _tg(lib, m=0) == OK
+    assert _tg(lib, k=-128) == ERR_SHAPE
+    assert _tg(lib, out=3) == ERR_ENUM
+    assert _tg(lib, a_s=0) == ERR_NULL
+    assert _tg(lib, b=0) == ERR_NULL
+    assert _tg(lib, k=200, lda=256, ldb=256) == ERR_SHAPE
+    assert _tg(lib, lda=128) == ERR_SHAPE
+    assert _tg(lib, ldc=100) == ERR_SHAPE
+    assert _tg(lib, ldb=264) == ERR_ALIGN
+    assert _tg(lib, c=A16c + 4) == ERR_ALIGN
+
+
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
-                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx"):
+                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
+                 "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))
 
 
