@@ -13,7 +13,7 @@ oracle timed on the host as a reported baseline.
 
     python bench.py [--steps K] [--warmup W]
                     [--config dense_fprop|dgrad|wgrad|grouped_fprop|grouped_dgrad|
-                              grouped_wgrad|mx_fprop|tiny_fprop]
+                              grouped_wgrad|mx_fprop|wgrad_cached|tiny_fprop]
 
 Counter runs (HBM traffic of each kernel, from rocprofv3 FETCH_SIZE and
 WRITE_SIZE; a plain copy of known size calibrates each counter):
@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak (1 GPU)"
 CONFIGS = ["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "grouped_dgrad", "grouped_wgrad",
-           "mx_fprop", "tiny_fprop"]
+           "mx_fprop", "wgrad_cached", "tiny_fprop"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Kernel name fragments (as rocprofv3 prints them) for each launch label.
@@ -51,6 +51,7 @@ KERNEL_NAMES = {
     "quant_act_128x1": "quant_act_128x1_kernel",
     "quant_weight": "quant_weight_kernel",
     "quant_mx": "quant_mx_1x32_kernel",
+    "retile_128x1": "retile_128x1_kernel",
     "gemm": "gemm_kernel",
 }
 
@@ -219,6 +220,37 @@ class Workload:
             ]
             self.desc = {"workload": name, "m": n_out, "n": k_in, "k": t,
                          "dy, x": "bf16, 128x1 tiles (along tokens)", "out": "fp32"}
+        elif name == "wgrad_cached":
+            # Wgrad with X taken from its forward-pass FP8 cache (1x128 codes
+            # and scales, written by the forward quantizer before the step):
+            # dY quantized 128x1, the cache re-tiled to 128x1, then the GEMM
+            d = wl.wgrad()
+            DY = sets(d["dy"])
+            t, n_out = DY[0].shape
+            k_in = d["x"].shape[1]
+            x_dev = dev(d["x"])
+            XQ, XS = [], []
+            for _ in range(rotate):
+                xq_, xs_ = fq.fp8_quantize_act(x_dev, "1x128")
+                XQ.append(xq_)
+                XS.append(xs_)
+            del x_dev
+            aq, as_ = empty((n_out, t), u8), empty((t // 128, n_out), f32)
+            bq, bs = empty((k_in, t), u8), empty((t // 128, k_in), f32)
+            y = empty((n_out, k_in), f32)
+            self.flops = 2.0 * n_out * k_in * t
+            self.launches = [
+                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
+                       act_bytes(t, n_out)),
+                # codes + 1x128 scales in, codes + 128x1 scales out
+                Launch("retile_128x1", lambda r: fq.fp8_retile_act_128x1(XQ[r], XS[r], q_t=bq, scale_t=bs),
+                       2 * t * k_in + 8 * t * k_in // 128),
+                Launch("gemm", lambda r: fq.fp8_gemm(aq, as_, bq, bs, "row", f32, out=y),
+                       gemm_bytes(n_out, k_in, t, k_in * (t // 128), 4, n_out), self.flops),
+            ]
+            self.desc = {"workload": name, "m": n_out, "n": k_in, "k": t,
+                         "dy": "bf16, 128x1 tiles (along tokens)",
+                         "x": "FP8 cache (1x128 codes + scales) re-tiled to 128x1", "out": "fp32"}
         elif name == "grouped_dgrad":
             # MoE up-projection Dgrad: dX_e = dY_e W_e with each expert's transposed copy
             rows = wl.moe_rows(0)
@@ -519,8 +551,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 accumulate, bf16 out" if args.config != "wgrad"
-                 else "fp8-e4m3 x fp8-e4m3 -> fp32 accumulate, fp32 out",
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 accumulate, " + (
+            "fp32 out" if args.config in ("wgrad", "wgrad_cached", "grouped_wgrad") else "bf16 out"),
         "data": "synthetic (seeded; see workloads/)",
         "config": wl_obj.desc,
         "pct_of_fp8_peak": round(100.0 * value / FP8_DENSE_PEAK_TFLOPS, 2),
