@@ -91,8 +91,9 @@ def parse():
 class Launch:
     """One kernel launch of the step with its algorithmic cost."""
 
-    def __init__(self, label, fn, nbytes, flops=0.0):
+    def __init__(self, label, fn, nbytes, flops=0.0, dispatches=1):
         self.label, self.fn, self.bytes, self.flops = label, fn, float(nbytes), float(flops)
+        self.dispatches = dispatches  # kernel dispatches the launch makes
 
 
 class Workload:
@@ -276,7 +277,7 @@ class Workload:
             self.launches = [
                 Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(DY[r], "1x128", q=dq, scale=ds),
                        act_bytes(m_total, n_out)),
-                Launch("quant_weight", quant_w, 4 * E * n_out * k_in + 8 * nb),
+                Launch("quant_weight", quant_w, 4 * E * n_out * k_in + 8 * nb, dispatches=E),
                 Launch("gemm", lambda r: fq.fp8_grouped_gemm(offd, rws, dq, ds, wqt, wst, bf16, out=y),
                        gemm_bytes(real, E * k_in, n_out, nb, 2, 0) + 2 * m_total * k_in, self.flops),
             ]
@@ -428,11 +429,16 @@ def pmc_summary(fetch_csv: str, write_csv: str, config: str, probe_mib: int, out
             raise SystemExit("no calibration copy in %s (run with --copy-probe-mib)" % path)
         factor = probe / (copies[0][2] * 1024.0)
         res[key + "_factor"] = round(factor, 4)
+        step_labels = {ln.label for ln in wl_obj.launches}
         for label, frag in KERNEL_NAMES.items():
+            if label not in step_labels:
+                continue  # e.g. set-up dispatches outside the step (the FP8 cache)
             vals = [r[2] for r in rows if frag in r[1]]
             if vals:
+                per = max(ln.dispatches for ln in wl_obj.launches if ln.label == label)
                 ent = res.setdefault("kernels", {}).setdefault(label, {})
-                ent[key + "_bytes"] = round(sum(vals) / len(vals) * 1024.0 * factor)
+                # per launch: the dispatch average times the dispatches one launch makes
+                ent[key + "_bytes"] = round(sum(vals) / len(vals) * per * 1024.0 * factor)
                 ent["dispatches"] = len(vals)
     for label, ent in res.get("kernels", {}).items():
         ent["traffic_bytes"] = ent.get("fetch_bytes", 0) + ent.get("write_bytes", 0)
@@ -462,6 +468,33 @@ def stored_traffic(path: str, config: str):
     if not ent or ent.get("kernel_source") != kernel_source_digest():
         return None
     return ent.get("kernels")
+
+
+# ------------------------------------------------------------------ device
+
+HIP_ATTR_CLOCK_RATE_KHZ = 5        # hipDeviceAttributeClockRate
+FP8_FLOP_PER_CLK_PER_CU = 8192     # dense FP8 MFMA: 4 SIMDs x 2048 FLOP per clock
+
+
+def device_info() -> dict:
+    """CU count, peak engine clock and the dense FP8 peak they imply (the
+    reported roofline peak stays the published 5.0 PFLOP/s)."""
+    import ctypes
+
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), HIP_ATTR_CLOCK_RATE_KHZ,
+                                     torch.cuda.current_device()) == 0:
+            info["max_sclk_mhz"] = val.value / 1000.0
+            info["fp8_peak_from_clock_tflops"] = round(
+                info["cus"] * val.value * 1e3 * FP8_FLOP_PER_CLK_PER_CU / 1e12, 1)
+    except OSError:
+        pass
+    return info
 
 
 # -------------------------------------------------------------------- main
@@ -578,6 +611,7 @@ def main():
             "tflops": round(gemm_tflops, 2),
         }),
         "kernels": kernels,
+        "device": device_info(),
         "wall_s": round(t_wall, 3),
         "host_enqueue_ms_per_step": round(t_host * 1e3 / args.steps, 4),
     }

@@ -12,9 +12,10 @@
 // gfx950 mapping: one v_mfma_f32_16x16x128_f8f6f4 consumes exactly one slab
 // for a 16x16 subtile and returns P_j in fresh registers (C operand 0); the
 // promotion is one v_fma_f32 per output element per slab on the vector ALU,
-// overlapped with the next subtile's MFMA. There is no limited-precision
-// accumulator to protect: the FP32 MFMA sum of a slab is already exact-ish,
-// and the interval is set by the scales, not by the hardware.
+// overlapped with the next subtile's MFMA. The interval is set by the
+// scales: measured on gfx950, chaining the MFMA accumulator across slabs
+// gives the same error as promoting each slab, and what precision is lost
+// is lost inside the instruction's own 128-product sum.
 //
 // Tiling: 256 (m) x BN (n) block tiles, BN = 256 or 224, 8 waves (4 along
 // m x 2 along n), 64 x BN/2 per wave. BN = 224 makes N = 7168 (Dgrad, Wgrad)

@@ -75,3 +75,20 @@ def test_multi_gpu_request_exits_with_message(capsys, monkeypatch):
     else:
         raise AssertionError("bench.main() accepted --gpus 2")
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_pmc_summary_ignores_kernels_outside_the_step(tmp_path):
+    """Set-up dispatches (say the 1x128 quantizer making an FP8 cache) whose
+    label is not one of the step's launches are not summarized."""
+    fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    _write(fetch, "FETCH_SIZE", [(1, "__amd_rocclr_copyBuffer", 1024.0),
+                                 (2, "void fp8q::quant_act_1x128_kernel<false>(...)", 9.0),
+                                 (3, "void fp8q::gemm_kernel<256>(Params)", 4.0)])
+    _write(write, "WRITE_SIZE", [(1, "__amd_rocclr_copyBuffer", 1024.0),
+                                 (2, "void fp8q::quant_act_1x128_kernel<false>(...)", 9.0),
+                                 (3, "void fp8q::gemm_kernel<256>(Params)", 3.0)])
+
+    class OnlyGemm:
+        launches = [bench.Launch("gemm", None, 100.0, 1.0)]
+    res = bench.pmc_summary(fetch, write, "x", 1, str(tmp_path / "t.json"), OnlyGemm())
+    assert set(res["kernels"]) == {"gemm"}
