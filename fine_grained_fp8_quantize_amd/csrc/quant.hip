@@ -299,27 +299,34 @@ __global__ __launch_bounds__(256) void retile_128x1_kernel(
     const float4 s_lo = sp[0], s_hi = sp[1];
     const float st[8] = {s_lo.x, s_lo.y, s_lo.z, s_lo.w, s_hi.x, s_hi.y, s_hi.z, s_hi.w};
 
-    float v[8][8];  // [token][channel]
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    // v = fl32(dec(q) * s_token) for token i, channels 4h..4h+3 (h = 0, 1).
+    // The values are made twice (amax pass, quotient pass) rather than held
+    // across the barrier: fewer registers, more blocks and loads in flight.
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    auto dequant4 = [&](int i, int h) -> f4 {
         typedef float f2 __attribute__((ext_vector_type(2)));
-        const f2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].x, false);
-        const f2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].x, true);
-        const f2 d2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].y, false);
-        const f2 d3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)code[i].y, true);
-        const float d[8] = {d0.x, d0.y, d1.x, d1.y, d2.x, d2.y, d3.x, d3.y};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[i][k] = d[k] * st[i];
-    }
+        const uint32_t word = h ? code[i].y : code[i].x;
+        const f2 d0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+        const f2 d1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+        return f4{d0.x * st[i], d0.y * st[i], d1.x * st[i], d1.y * st[i]};
+    };
     // Column amax: over the thread's 8 tokens, the wave's 4 token groups
     // (lanes 16 and 32 apart), then the 4 waves through LDS. Magnitudes of
-    // finite floats order as their bit patterns.
+    // finite non-negative floats order as their bit patterns.
+    float mf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f4 v = dequant4(i, h);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) mf[4 * h + c] = __builtin_fmaxf(mf[4 * h + c], __builtin_fabsf(v[c]));
+        }
+    }
     uint32_t m[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-        uint32_t mm = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) mm = umax32(mm, __float_as_uint(v[i][k]) & 0x7FFFFFFFu);
+        uint32_t mm = __float_as_uint(mf[k]);
         mm = umax32(mm, (uint32_t)__shfl_xor((int)mm, 16));
         mm = umax32(mm, (uint32_t)__shfl_xor((int)mm, 32));
         m[k] = mm;
@@ -340,6 +347,10 @@ __global__ __launch_bounds__(256) void retile_128x1_kernel(
         scale_t[tb * ld_st + c0 + t] = gs.s;
     }
     __syncthreads();
+    // (an empty asm marks the code words as changed, so the compiler makes
+    // the values again here instead of keeping 64 of them live)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(code[i].x), "+v"(code[i].y));
 
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -347,12 +358,15 @@ __global__ __launch_bounds__(256) void retile_128x1_kernel(
         gs.s = s_sh[8 * g + k];
         gs.y = y_sh[8 * g + k];
         gs.slow = !(gs.s >= kSmallScale);
+        float av[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) av[i] = __builtin_fabsf(dequant4(i, k >> 2)[k & 3]);
         float qv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qv[i] = quot_fast(__builtin_fabsf(v[i][k]), gs);
+        for (int i = 0; i < 8; ++i) qv[i] = quot_fast(av[i], gs);
         if (gs.slow) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qv[i] = quot_slow(__builtin_fabsf(v[i][k]), gs);
+            for (int i = 0; i < 8; ++i) qv[i] = quot_slow(av[i], gs);
         }
         uint32_t wd[8];
 #pragma unroll
