@@ -3,7 +3,9 @@
 One step is one pass of the path over one batch of seeded synthetic input
 already resident in HBM: quantize the operands (activations in 1x128 tiles,
 weights in 128x128 blocks, or both Wgrad operands in 128x1 tiles) and run the
-block-scaled FP8 GEMM. The default workload is the dense Fprop layer
+block-scaled FP8 GEMM, in that order on one stream (``--streams 2`` puts the
+two independent quantizations on two streams; that measures slower). The
+default workload is the dense Fprop layer
 X[4096][7168] x W[4096][7168]^T with bf16 output.
 
 Prints ONE JSON line: the whole-step throughput in TFLOP/s (2*M*N*K per step),
@@ -11,7 +13,7 @@ the GEMM kernel's roofline (its launches timed with HIP events on the launch
 stream inside the timed region), every kernel's own time and rate, and the CPU
 oracle timed on the host as a reported baseline.
 
-    python bench.py [--steps K] [--warmup W]
+    python bench.py [--steps K] [--warmup W] [--streams 1|2]
                     [--config dense_fprop|dgrad|wgrad|grouped_fprop|grouped_dgrad|
                               grouped_wgrad|mx_fprop|wgrad_cached|tiny_fprop]
 
@@ -79,6 +81,10 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3,
                     help="bf16 input sets cycled over the steps, so that the inputs of one "
                          "step are not left in the 256 MiB MALL by the step before")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="2: the two independent operand quantizations run on two streams "
+                         "(measured slower: both are HBM-bound, and the cross-stream wait "
+                         "before the GEMM costs more than the overlap saves)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
@@ -99,7 +105,7 @@ class Launch:
 class Workload:
     """Inputs on the GPU plus preallocated outputs; step() enqueues one pass."""
 
-    def __init__(self, name: str, rotate: int = 1):
+    def __init__(self, name: str, rotate: int = 1, streams: int = 1):
         import numpy as np
         import torch
 
@@ -345,21 +351,40 @@ class Workload:
                          "x": "bf16 tokens, quantized 1x128 before dispatch", "out": "bf16"}
         self.rotate, self.count = rotate, 0
         self.desc["input_sets"] = rotate
+        # streams == 2: the two operand quantizations are independent, so the
+        # second can run on a side stream (default priority) beside the first;
+        # the GEMM waits for both. The side stream's work of a step starts
+        # after everything the main stream enqueued before it (the previous
+        # step's GEMM included), so no buffer is overwritten while in use.
+        assert [ln.label for ln in self.launches][-1] == "gemm" and len(self.launches) == 3
+        self.side = torch.cuda.Stream() if streams == 2 else None
+        self.mark = torch.cuda.Event()
+        self.done = torch.cuda.Event()
+        self.desc["streams"] = streams
         torch.cuda.synchronize()
 
     def step(self, ev=None):
-        """One pass over the next input set; ev (len(launches)+1 events)
-        brackets every launch."""
+        """One pass over the next input set; ev (one (begin, end) event pair
+        per launch) brackets every launch on the stream it runs on."""
+        torch = self.torch
         r = self.count % self.rotate
         self.count += 1
-        if ev is None:
-            for ln in self.launches:
-                ln.fn(r)
-            return
-        ev[0].record()
+        main = torch.cuda.current_stream()
+        if self.side is not None:
+            self.mark.record(main)
+            self.side.wait_event(self.mark)
         for i, ln in enumerate(self.launches):
-            ln.fn(r)
-            ev[i + 1].record()
+            s = self.side if (self.side is not None and i == 1) else main
+            if ln.label == "gemm" and self.side is not None:
+                main.wait_event(self.done)
+            with torch.cuda.stream(s):
+                if ev is not None:
+                    ev[i][0].record(s)
+                ln.fn(r)
+                if ev is not None:
+                    ev[i][1].record(s)
+            if s is not main:
+                self.done.record(s)
 
 
 def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 200) -> dict:
@@ -523,7 +548,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    wl_obj = Workload(args.config, max(1, args.rotate))
+    wl_obj = Workload(args.config, max(1, args.rotate), args.streams)
     stream = torch.cuda.current_stream()
     # Untimed pre-warm: the GPU ramps its clocks over the first tens of
     # milliseconds of sustained work; run steps for a while before the W
@@ -538,7 +563,8 @@ def main():
     torch.cuda.synchronize()
 
     nl = len(wl_obj.launches)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nl + 1)] for _ in range(args.steps)]
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
+           for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -551,7 +577,7 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = start.elapsed_time(stop) / args.steps
-    per_launch = [sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i in range(nl)]
+    per_launch = [sorted(e[i][0].elapsed_time(e[i][1]) for e in evs) for i in range(nl)]
     launch_ms = [sum(v) / len(v) for v in per_launch]
 
     value = wl_obj.flops / (ms * 1e-3) / 1e12
