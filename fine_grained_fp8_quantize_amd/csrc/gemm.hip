@@ -132,43 +132,25 @@ __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
 }
 
 // Grouped tiles. Expert e's segment [off[e], off[e+1]) is cut into 256-row
-// m-tiles. A tile's class is the number of its 64-row quarters that hold real
-// rows: 4 for a tile of real rows only, 1..4 for the tail tile, 0 for a tile
-// of padding only (which is still written, as zeros). Slots run class 4
-// first, then 3, 2, 1, 0 -- the longest tiles first, so the short ones fill
-// the last round -- and inside a class by expert, n-tile, m-tile, so m-tiles
-// that share a 256 x K panel of W_e are consecutive.
+// m-tiles: whole tiles of real rows, then a tail tile whose first 1-4 64-row
+// quarters hold real rows, then tiles of padding only (written as zeros).
+// Slots run expert by expert, inside an expert by n-tile and then m-tile, so
+// the m-tiles that share a 256 x K panel of W_e -- the tail included -- are
+// consecutive and run together on one XCD, where the panel is fetched into
+// L2 once. (Every tile streams the same K x 256 weight panel, so tiles with
+// few real rows take about as long as full ones: ordering by tile size buys
+// no balance, and measured ~5% slower than this order.)
 struct ExpertSplit {
-    int beg;   // first row of the segment
-    int full;  // m-tiles of real rows only
-    int tail;  // class of the tail tile (0: no tail)
-    int pad;   // m-tiles of padding rows only
+    int beg;    // first row of the segment
+    int tiles;  // m-tiles of the segment
 };
 
 __device__ __forceinline__ ExpertSplit expert_split(const Params& p, int e) {
     ExpertSplit x;
     x.beg = p.group_offsets[e];
     const int seg = max(p.group_offsets[e + 1] - x.beg, 0);
-    const int real = p.group_rows ? min(max(p.group_rows[e], 0), seg) : seg;
-    const int rest = real % kBM;
-    x.full = real / kBM;
-    x.tail = (rest + 63) / 64;
-    x.pad = (seg + kBM - 1) / kBM - x.full - (rest > 0 ? 1 : 0);
+    x.tiles = (seg + kBM - 1) / kBM;
     return x;
-}
-
-// m-tiles of expert split x in class c, and the first of them.
-__device__ __forceinline__ int class_tiles(const ExpertSplit& x, int c, int& first) {
-    if (c == 4) {
-        first = 0;
-        return x.full + (x.tail == 4 ? 1 : 0);
-    }
-    if (c == 0) {
-        first = x.full + (x.tail > 0 ? 1 : 0);
-        return x.pad;
-    }
-    first = x.full;
-    return x.tail == c ? 1 : 0;
 }
 
 // Block b runs on XCD b % 8; round r of that XCD's 32 CUs takes the 32
@@ -180,30 +162,11 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
     const int tiles_n = (int)((p.n + BN - 1) / BN);
     const int q = (int)(blockIdx.x >> 3);
     int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
-    int cnt[5] = {0, 0, 0, 0, 0};
     for (int e = 0; e < p.groups; ++e) {
         const ExpertSplit x = expert_split(p, e);
-        cnt[4] += x.full + (x.tail == 4 ? 1 : 0);
-        cnt[3] += x.tail == 3 ? 1 : 0;
-        cnt[2] += x.tail == 2 ? 1 : 0;
-        cnt[1] += x.tail == 1 ? 1 : 0;
-        cnt[0] += x.pad;
-    }
-    int cls = -1;
-#pragma unroll
-    for (int c = 4; c >= 0; --c) {
-        if (cls < 0) {
-            if (slot < cnt[c] * tiles_n) cls = c;
-            else slot -= cnt[c] * tiles_n;
-        }
-    }
-    if (cls < 0) return false;
-    for (int e = 0; e < p.groups; ++e) {
-        const ExpertSplit x = expert_split(p, e);
-        int first;
-        const int k = class_tiles(x, cls, first);
+        const int k = x.tiles;
         if (slot < k * tiles_n) {
-            const int tn = slot / k, mt = first + slot % k;
+            const int tn = slot / k, mt = slot % k;
             const int end = x.beg + max(p.group_offsets[e + 1] - x.beg, 0);
             t.m0 = x.beg + (int64_t)mt * kBM;
             // offsets that break the contract must not move stores outside C
