@@ -73,3 +73,13 @@ def test_accumulation_study_k4096(positive):
     # promotion every slab buys nothing over chaining the MFMA accumulator
     chain, slab = r["arms"]["mfma_chain"]["normwise"], r["arms"]["slab_promotion"]["normwise"]
     assert abs(chain - slab) <= 0.1 * slab, (chain, slab)
+
+
+def test_gemm_tensor_224_wide_tiles():
+    """N = 7168 makes the launcher pick 224-wide n tiles (32 x 224)."""
+    qa, qb = _codes(11, 512, 256), _codes(12, 7168, 256)
+    c = fq.fp8_gemm_tensor(dev_codes(qa), torch.tensor([0.75], device="cuda"), dev_codes(qb),
+                           torch.tensor([1.5], device="cuda"), torch.float32)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(13).choice(512, 32, replace=False)
+    assert_gemm_close(host_out(c)[rows], oracle.gemm_tensor(qa[rows], 0.75, qb, 1.5), "tensor 224-wide")

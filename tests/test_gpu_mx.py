@@ -100,3 +100,29 @@ def test_mx_gemm_k0_writes_zeros():
     fq.fp8_gemm_mx(a, s, b, sb, torch.float32, out=c)
     torch.cuda.synchronize()
     assert torch.all(c == 0)
+
+
+def test_mx_gemm_224_wide_tiles():
+    """N = 7168 makes the launcher pick 224-wide n tiles (32 x 224)."""
+    _gemm_case(512, 7168, 256, sample=24, seed=3)
+
+
+def test_mx_gemm_padded_leading_dims():
+    """Operands and output as row-padded views (lda, ldb > k; ldc > n)."""
+    m, n, k = 200, 136, 256
+    a = wl.activation(4, "tiny_fprop", 98, m, k, 50.0)
+    b = wl.weight(4, "tiny_fprop", 99, n, k)
+    aq, asc = fq.fp8_quantize_mx(dev_bf16(a))
+    bq, bsc = fq.fp8_quantize_mx(dev_bf16(b))
+    ap = torch.zeros((m, k + 32), dtype=torch.uint8, device="cuda")
+    bp = torch.zeros((n, k + 64), dtype=torch.uint8, device="cuda")
+    ap[:, :k] = aq.view(torch.uint8)
+    bp[:, :k] = bq.view(torch.uint8)
+    c = torch.full((m, n + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fq.fp8_gemm_mx(ap[:, :k], asc, bp[:, :k], bsc, torch.bfloat16, out=c[:, :n])
+    torch.cuda.synchronize()
+    got = host_out(c)
+    assert np.all(np.isnan(got[:, n:])), "columns past n written"
+    a_q, a_e = oracle.quant_mx_1x32(a)
+    b_q, b_e = oracle.quant_mx_1x32(b)
+    assert_gemm_close(got[:, :n], oracle.gemm_mx(a_q, a_e, b_q, b_e), "mx gemm padded")
