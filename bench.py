@@ -272,26 +272,26 @@ class Workload:
             offd = torch.from_numpy(off.astype("int32")).cuda()
             rws = torch.from_numpy(rows.astype("int32")).cuda()
             dq, ds = empty((m_total, n_out), u8), empty((n_out // 128, m_total), f32)
+            # all experts' weights in one grouped-quantizer launch, with each
+            # expert's transposed copy contiguous (the Dgrad B operand)
             wq, ws = empty((E, n_out, k_in), u8), empty((E, n_out // 128, k_in // 128), f32)
             wqt, wst = empty((E, k_in, n_out), u8), empty((E, k_in // 128, n_out // 128), f32)
             y = empty((m_total, k_in), bf16)
             self.flops = 2.0 * real * k_in * n_out
             nb = E * (n_out // 128) * (k_in // 128)
-
-            def quant_w(r):
-                for e in range(E):
-                    fq.fp8_quantize_weight(w[e], transposed=True, q=wq[e], scale=ws[e], q_t=wqt[e],
-                                           scale_t=wst[e])
             self.launches = [
                 Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(DY[r], "1x128", q=dq, scale=ds),
                        act_bytes(m_total, n_out)),
-                Launch("quant_weight", quant_w, 4 * E * n_out * k_in + 8 * nb, dispatches=E),
+                Launch("quant_weight", lambda r: fq.fp8_quantize_weight_grouped(
+                    w, transposed=True, q=wq, scale=ws, q_t=wqt, scale_t=wst),
+                       4 * E * n_out * k_in + 8 * nb),
                 Launch("gemm", lambda r: fq.fp8_grouped_gemm(offd, rws, dq, ds, wqt, wst, bf16, out=y),
                        gemm_bytes(real, E * k_in, n_out, nb, 2, 0) + 2 * m_total * k_in, self.flops),
             ]
             self.desc = {"workload": name, "experts": E, "rows_real": real, "rows_padded": m_total,
                          "n": k_in, "k": n_out, "dy": "bf16, 1x128 tiles",
-                         "w": "bf16, 128x128 blocks, transposed copy per expert", "out": "bf16"}
+                         "w": "bf16, 128x128 blocks, all experts in one launch with per-expert transposed copies",
+                         "out": "bf16"}
         elif name == "grouped_wgrad":
             # MoE up-projection Wgrad: dW_e = dY_e^T X_e over each expert's tokens
             rows = wl.moe_rows(0)

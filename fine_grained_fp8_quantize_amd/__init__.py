@@ -35,6 +35,7 @@ __all__ = [
     "fp8_quantize_act",
     "fp8_quantize_act_scatter",
     "fp8_quantize_weight",
+    "fp8_quantize_weight_grouped",
     "fp8_gemm",
     "fp8_grouped_gemm",
     "fp8_grouped_gemm_wgrad",
@@ -82,6 +83,8 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_act.argtypes = [p, i64, i64, i64, cint, p, i64, p, i64, p]
     L.fp8_quantize_act_scatter.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+    L.fp8_quantize_weight_grouped.argtypes = [i32, p, i64, i64, i64, i64, p, i64, i64, p, i64, i64,
+                                              p, i64, i64, p, i64, i64, p]
     L.fp8_quantize_mx.argtypes = [p, i64, i64, i64, p, i64, p, i64, p]
     L.fp8_gemm_mx.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p, i64, cint, p]
     L.fp8_gemm.argtypes = [i64, i64, i64, p, i64, p, i64, p, i64, p, i64, cint, p, i64, cint, p]
@@ -91,7 +94,8 @@ def _load() -> ctypes.CDLL:
                                    i64, p, i64, cint, p]
     L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
-    for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
+    for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
+                 "fp8_quantize_weight_grouped", "fp8_gemm",
                  "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
                  "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
@@ -251,6 +255,48 @@ def fp8_quantize_weight(w: torch.Tensor, transposed: bool = False, q: torch.Tens
         _ptr(scale_t if transposed else None), scale_t.stride(0) if transposed else 0,
         _stream(stream))
     _check(st, "fp8_quantize_weight")
+    return (q, scale, q_t, scale_t) if transposed else (q, scale)
+
+
+def fp8_quantize_weight_grouped(w: torch.Tensor, transposed: bool = False, q: torch.Tensor | None = None,
+                                scale: torch.Tensor | None = None, q_t: torch.Tensor | None = None,
+                                scale_t: torch.Tensor | None = None, stream=None):
+    """Quantize ``E`` bf16 weights ``w[E][n][k]`` (say the experts of an MoE
+    layer) in 128x128 blocks with one launch.
+
+    Returns ``(q[E][n][k], scale[E][n/128][k/128])``, or with ``transposed``
+    also ``q_t[E][k][n]`` and ``scale_t[E][k/128][n/128]`` (each expert's exact
+    transpose, contiguous per expert, for Dgrad).
+    """
+    _need_gpu(w)
+    if w.dtype != torch.bfloat16:
+        raise Fp8qError("w must be bfloat16")
+    if w.dim() != 3 or w.stride(2) != 1:
+        raise Fp8qError("w must be [E][n][k] with k contiguous")
+    groups, n, k = w.shape
+    dev = w.device
+    if q is None:
+        q = torch.empty((groups, n, k), dtype=torch.float8_e4m3fn, device=dev)
+    if scale is None:
+        scale = torch.empty((groups, n // 128, k // 128), dtype=torch.float32, device=dev)
+    if transposed:
+        if q_t is None:
+            q_t = torch.empty((groups, k, n), dtype=torch.float8_e4m3fn, device=dev)
+        if scale_t is None:
+            scale_t = torch.empty((groups, k // 128, n // 128), dtype=torch.float32, device=dev)
+    _need_gpu(q, scale, q_t, scale_t)
+    for name, t in (("q", q), ("scale", scale)) + ((("q_t", q_t), ("scale_t", scale_t)) if transposed else ()):
+        if t.dim() != 3 or t.stride(2) != 1:
+            raise Fp8qError("%s must be a 3-d tensor with a contiguous last dimension" % name)
+    _codes(q, "q")
+    st = _load().fp8_quantize_weight_grouped(
+        groups, _ptr(w), n, k, w.stride(1), w.stride(0),
+        _ptr(q), q.stride(1), q.stride(0), _ptr(scale), scale.stride(1), scale.stride(0),
+        _ptr(q_t if transposed else None), q_t.stride(1) if transposed else 0,
+        q_t.stride(0) if transposed else 0,
+        _ptr(scale_t if transposed else None), scale_t.stride(1) if transposed else 0,
+        scale_t.stride(0) if transposed else 0, _stream(stream))
+    _check(st, "fp8_quantize_weight_grouped")
     return (q, scale, q_t, scale_t) if transposed else (q, scale)
 
 

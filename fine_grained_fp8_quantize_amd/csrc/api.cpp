@@ -77,22 +77,38 @@ int fp8_quantize_act_scatter(const uint16_t* x, int64_t tokens, int64_t cols, in
                                                      ld_q, scale, ld_s, stream));
 }
 
-int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
-                        uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
-                        uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
-                        hipStream_t stream) {
-    if (n < 0 || k < 0) return FP8Q_ERR_SHAPE;
-    if (n == 0 || k == 0) return FP8Q_OK;
+int fp8_quantize_weight_grouped(int32_t groups, const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                                int64_t stride_w, uint8_t* q, int64_t ld_q, int64_t stride_q, float* scale,
+                                int64_t ld_s, int64_t stride_s, uint8_t* q_t, int64_t ld_qt,
+                                int64_t stride_qt, float* scale_t, int64_t ld_st, int64_t stride_st,
+                                hipStream_t stream) {
+    if (groups < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    if (groups == 0 || n == 0 || k == 0) return FP8Q_OK;
     if (!w || !q || !scale) return FP8Q_ERR_NULL;
     if (q_t && !scale_t) return FP8Q_ERR_NULL;
     if (n % 128 != 0 || k % 128 != 0 || ld_w < k || ld_q < k || ld_s < k / 128) return FP8Q_ERR_SHAPE;
     if (q_t && (ld_qt < n || ld_st < n / 128)) return FP8Q_ERR_SHAPE;
-    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4) || ld_w % 8 != 0 || ld_q % 16 != 0)
+    if (stride_w < 0) return FP8Q_ERR_SHAPE;  // inputs are only read: they may overlap
+    // outputs of different groups must not overlap
+    if (groups > 1 && (stride_q < n * ld_q || stride_s < (n / 128) * ld_s)) return FP8Q_ERR_SHAPE;
+    if (groups > 1 && q_t && (stride_qt < k * ld_qt || stride_st < (k / 128) * ld_st)) return FP8Q_ERR_SHAPE;
+    if (!aligned(w, 16) || !aligned(q, 16) || !aligned(scale, 4) || ld_w % 8 != 0 || ld_q % 16 != 0 ||
+        stride_w % 8 != 0 || stride_q % 16 != 0)
         return FP8Q_ERR_ALIGN;
-    if (q_t && (!aligned(q_t, 16) || !aligned(scale_t, 4) || ld_qt % 16 != 0)) return FP8Q_ERR_ALIGN;
-    if (!grid_ok(n / 128 * (k / 128))) return FP8Q_ERR_SHAPE;
-    return hip_status(fp8q::launch_quant_weight(w, n, k, ld_w, q, ld_q, scale, ld_s,
-                                                q_t, ld_qt, scale_t, ld_st, stream));
+    if (q_t && (!aligned(q_t, 16) || !aligned(scale_t, 4) || ld_qt % 16 != 0 || stride_qt % 16 != 0))
+        return FP8Q_ERR_ALIGN;
+    if (!grid_ok((int64_t)groups * (n / 128) * (k / 128))) return FP8Q_ERR_SHAPE;
+    return hip_status(fp8q::launch_quant_weight(groups, w, n, k, ld_w, stride_w, q, ld_q, stride_q, scale,
+                                                ld_s, stride_s, q_t, ld_qt, stride_qt, scale_t, ld_st,
+                                                stride_st, stream));
+}
+
+int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                        uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
+                        uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
+                        hipStream_t stream) {
+    return fp8_quantize_weight_grouped(1, w, n, k, ld_w, 0, q, ld_q, 0, scale, ld_s, 0, q_t, ld_qt, 0,
+                                       scale_t, ld_st, 0, stream);
 }
 
 static int check_gemm_common(int64_t m, int64_t n, int64_t k, const uint8_t* a, int64_t lda,
@@ -144,7 +160,8 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     if (st != FP8Q_OK) return st;
     if (m_total % 128 != 0 || n % 128 != 0 || m_total > 0x7FFFFFFFLL) return FP8Q_ERR_SHAPE;
     if (k > 0 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
-    if (stride_b < n * ldb || (k > 0 && stride_bs < (n / 128) * ld_bs)) return FP8Q_ERR_SHAPE;
+    // the experts' weights are only read: their rows may interleave
+    if (stride_b < 0 || stride_bs < 0) return FP8Q_ERR_SHAPE;
     if (stride_b % 16 != 0) return FP8Q_ERR_ALIGN;
     if (!grid_ok((m_total / 128) * ((n + 255) / 256) + 256)) return FP8Q_ERR_SHAPE;
     fp8q::GemmProblem g = {};

@@ -26,10 +26,12 @@ hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, i
                                const float* scale, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
                                float* scale_t, int64_t ld_st, hipStream_t stream);
 
-hipError_t launch_quant_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
-                               uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
-                               uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
-                               hipStream_t stream);
+// groups weight matrices, group e at each base pointer + e * its stride
+// (elements); groups == 1 with zero strides is one matrix.
+hipError_t launch_quant_weight(int64_t groups, const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                               int64_t stride_w, uint8_t* q, int64_t ld_q, int64_t stride_q, float* scale,
+                               int64_t ld_s, int64_t stride_s, uint8_t* q_t, int64_t ld_qt, int64_t stride_qt,
+                               float* scale_t, int64_t ld_st, int64_t stride_st, hipStream_t stream);
 
 struct GemmProblem {
     int64_t m, n, k;

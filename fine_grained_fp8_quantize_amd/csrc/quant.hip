@@ -389,6 +389,13 @@ __global__ __launch_bounds__(256) void retile_128x1_kernel(
 
 // ---------------------------------------------------------------- 128x128
 
+// Several weight matrices (experts) in one launch: group e starts at the
+// base pointers plus e times these strides (elements); blocks per group.
+struct WeightGroups {
+    int64_t blocks;
+    int64_t w, q, s, qt, st;
+};
+
 // One 256-thread block quantizes one 128x128 weight block: thread (row group
 // rg = t/16, chunk g = t%16) holds rows 8rg..8rg+7 x columns 8g..8g+7. The
 // optional transposed copy is produced from the thread's 8x8 byte tile with
@@ -396,11 +403,21 @@ __global__ __launch_bounds__(256) void retile_128x1_kernel(
 __global__ __launch_bounds__(256) void quant_weight_kernel(
     const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
-    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st) {
+    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
+    WeightGroups grp) {
     __shared__ uint32_t red[4];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int g = t & 15, rg = t >> 4;
-    const int64_t bn = blockIdx.x / kblocks, bk = blockIdx.x - bn * kblocks;
+    // group (expert) of this block, then its block (bn, bk)
+    const int64_t e = blockIdx.x / grp.blocks, local = blockIdx.x - e * grp.blocks;
+    w += e * grp.w;
+    q += e * grp.q;
+    scale += e * grp.s;
+    if (q_t != nullptr) {
+        q_t += e * grp.qt;
+        scale_t += e * grp.st;
+    }
+    const int64_t bn = local / kblocks, bk = local - bn * kblocks;
     const int64_t n0 = bn * 128 + 8 * rg, k0 = bk * 128 + 8 * g;
 
     uint4 v[8];
@@ -506,14 +523,20 @@ hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, i
     return hipGetLastError();
 }
 
-hipError_t launch_quant_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
-                               uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
-                               uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,
-                               hipStream_t stream) {
+hipError_t launch_quant_weight(int64_t groups, const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
+                               int64_t stride_w, uint8_t* q, int64_t ld_q, int64_t stride_q, float* scale,
+                               int64_t ld_s, int64_t stride_s, uint8_t* q_t, int64_t ld_qt, int64_t stride_qt,
+                               float* scale_t, int64_t ld_st, int64_t stride_st, hipStream_t stream) {
     const int64_t kblocks = k / 128;
-    const int64_t blocks = n / 128 * kblocks;
-    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st);
+    WeightGroups grp;
+    grp.blocks = n / 128 * kblocks;
+    grp.w = stride_w;
+    grp.q = stride_q;
+    grp.s = stride_s;
+    grp.qt = stride_qt;
+    grp.st = stride_st;
+    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)(groups * grp.blocks)), dim3(256), 0, stream,
+                       w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp);
     return hipGetLastError();
 }
 

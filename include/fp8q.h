@@ -148,6 +148,32 @@ int fp8_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
                         hipStream_t stream);
 
 /*
+ * fp8_quantize_weight_grouped -- fp8_quantize_weight over several weight
+ * matrices of one shape (say the experts of an MoE layer) in one launch.
+ *
+ * Group e reads w + e*stride_w and writes q + e*stride_q, scale +
+ * e*stride_s and, when q_t is given, q_t + e*stride_qt and scale_t +
+ * e*stride_st (strides in elements), each exactly as fp8_quantize_weight
+ * with the same n, k and leading dimensions. One launch for all experts
+ * instead of one each; the per-expert transposed copies (Dgrad's B) come out
+ * contiguous. Blocks and passages as fp8_quantize_weight.
+ *
+ * groups   number of matrices, >= 0 (0: returns FP8Q_OK).
+ * Strides: all >= 0. The inputs may overlap (they are only read); for
+ *          groups > 1 the outputs may not: stride_q >= n*ld_q,
+ *          stride_s >= (n/128)*ld_s and, with q_t, stride_qt >= k*ld_qt,
+ *          stride_st >= (k/128)*ld_st.
+ * Alignment: as fp8_quantize_weight, and stride_w % 8 == 0,
+ *          stride_q % 16 == 0, stride_qt % 16 == 0.
+ * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_HIP.
+ */
+int fp8_quantize_weight_grouped(int32_t groups, const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
+                                int64_t stride_w, uint8_t *q, int64_t ld_q, int64_t stride_q,
+                                float *scale, int64_t ld_s, int64_t stride_s, uint8_t *q_t,
+                                int64_t ld_qt, int64_t stride_qt, float *scale_t, int64_t ld_st,
+                                int64_t stride_st, hipStream_t stream);
+
+/*
  * fp8_gemm -- C = dequant(A) * dequant(B)^T with per-128-slab promotion.
  *
  * For each 128-element K slab j the FP8 products of the slab are summed into
@@ -205,6 +231,12 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
  *               feed only padding rows of C, which are written as zeros.
  * b             expert weights: expert e at b + e * stride_b, codes [n][ldb].
  * b_scale       expert e at b_scale + e * stride_bs, [n/128][ld_bs].
+ *               The experts' weights are only read, so their rows may
+ *               interleave: stride_b and stride_bs need only be >= 0. For
+ *               Dgrad, quantizing all experts' W as one [E*N][K] matrix
+ *               gives the transposed copy [K][E*N]; expert e's W_e^T is
+ *               then b + e*N with ldb = E*N (stride_b = N), and its block
+ *               scales b_scale + e*N/128 with ld_bs = E*N/128.
  * c             [m_total][ldc]; out_dtype as in fp8_gemm.
  * Shapes:       n % 128 == 0, k % 128 == 0.
  * Alignment:    as fp8_gemm; stride_b % 16 == 0.

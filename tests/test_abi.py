@@ -193,9 +193,18 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, off=0) == ERR_NULL
     assert _gg(lib, m=500, ld_as=512) == ERR_SHAPE         # m_total not a multiple of 128
     assert _gg(lib, n=200, ldc=256) == ERR_SHAPE           # n not a multiple of 128
-    assert _gg(lib, sb=100) == ERR_SHAPE                   # experts overlap
-    assert _gg(lib, sbs=1) == ERR_SHAPE
+    assert _gg(lib, sb=-256) == ERR_SHAPE
+    assert _gg(lib, sbs=-1) == ERR_SHAPE
     assert _gg(lib, sb=256 * 256 + 8) == ERR_ALIGN
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="would launch on the fake pointers")
+def test_grouped_gemm_accepts_interleaved_expert_weights(lib):
+    """The weights are only read, so experts' rows may interleave: the
+    transposed copy of all experts quantized as one matrix has stride_b = k
+    and ldb = groups * k. Without a GPU the call gets past validation and
+    fails only at the launch (FP8Q_ERR_HIP), never with a shape error."""
+    assert _gg(lib, sb=256, ldb=4 * 256, sbs=2, ld_bs=8) == ERR_HIP
 
 
 def _gw(lib, groups=4, off=A16, kt=512, m=256, n=384, a=A16b, lda=512, a_s=A4, ld_as=256,
@@ -282,10 +291,33 @@ def test_gemm_tensor_validation(lib):
     assert _tg(lib, c=A16c + 4) == ERR_ALIGN
 
 
+def _wg(lib, groups=3, w=A16, n=256, k=384, ld_w=384, sw=256 * 384, q=A16b, ld_q=384, sq=256 * 384,
+        s=A4, ld_s=3, ss=6, qt=A16c, ld_qt=256, sqt=384 * 256, st=A4 + 0x1000, ld_st=2, sst=6):
+    return lib.fp8_quantize_weight_grouped(groups, w, n, k, ld_w, sw, q, ld_q, sq, s, ld_s, ss,
+                                           qt, ld_qt, sqt, st, ld_st, sst, None)
+
+
+def test_quantize_weight_grouped_validation(lib):
+    assert _wg(lib, groups=0) == OK
+    assert _wg(lib, n=0) == OK
+    assert _wg(lib, groups=-1) == ERR_SHAPE
+    assert _wg(lib, w=0) == ERR_NULL
+    assert _wg(lib, st=0) == ERR_NULL                            # q_t without scale_t
+    assert _wg(lib, n=200) == ERR_SHAPE
+    assert _wg(lib, sq=256 * 384 - 16) == ERR_SHAPE              # output groups overlap
+    assert _wg(lib, ss=5) == ERR_SHAPE
+    assert _wg(lib, sqt=384 * 256 - 16) == ERR_SHAPE
+    assert _wg(lib, sst=5) == ERR_SHAPE
+    assert _wg(lib, sw=-8) == ERR_SHAPE
+    assert _wg(lib, sw=256 * 384 + 4) == ERR_ALIGN               # 16-byte bf16 rows
+    assert _wg(lib, sq=256 * 384 + 8) == ERR_ALIGN
+    assert _wg(lib, sqt=384 * 256 + 8) == ERR_ALIGN
+
+
 def test_binding_names_match_c_entry_points():
-    for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight", "fp8_gemm",
-                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
-                 "fp8_retile_act_128x1", "fp8_gemm_tensor"):
+    for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
+                 "fp8_quantize_weight_grouped", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
+                 "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))
 
 

@@ -263,10 +263,13 @@ def test_end_to_end_wgrad():
 
 # ------------------------------------------------------------ grouped Dgrad
 
-def _grouped_dgrad_case(rows, n_out, k_in, sample=None):
+def _grouped_dgrad_case(rows, n_out, k_in, sample=None, one_launch=False):
     """dX_e = dY_e W_e for every expert: the grouped GEMM with each expert's
     transposed weight copy (W_e^T codes [k_in][n_out], transposed block
-    scales) as B; dY in the expert-sorted layout, quantized 1x128."""
+    scales) as B; dY in the expert-sorted layout, quantized 1x128.
+    one_launch: all experts' W quantized as one [E*n_out][k_in] matrix; the
+    transposed copy [k_in][E*n_out] is read in place, expert e at column
+    e*n_out (interleaved rows: stride_b = n_out, ldb = E*n_out)."""
     rows = np.asarray(rows, dtype=np.int64)
     off = wl.pad_offsets(rows)
     m_total = int(off[-1])
@@ -278,10 +281,18 @@ def _grouped_dgrad_case(rows, n_out, k_in, sample=None):
         dy[off[e]:off[e] + rows[e]] = real[src:src + rows[e]]
         src += int(rows[e])
     w = wl.weight(0, "grouped_fprop", 81, E, n_out, k_in)
-    wt_q = torch.empty((E, k_in, n_out), dtype=torch.uint8, device="cuda")
-    wt_s = torch.empty((E, k_in // 128, n_out // 128), dtype=torch.float32, device="cuda")
-    for e in range(E):   # one launch per expert: codes, scales and the transposed copy
-        fq.fp8_quantize_weight(dev_bf16(w[e]), transposed=True, q_t=wt_q[e], scale_t=wt_s[e])
+    if one_launch:
+        flat_q = torch.empty((k_in, E * n_out), dtype=torch.uint8, device="cuda")
+        flat_s = torch.empty((k_in // 128, E * n_out // 128), dtype=torch.float32, device="cuda")
+        fq.fp8_quantize_weight(dev_bf16(w.reshape(E * n_out, k_in)), transposed=True, q_t=flat_q,
+                               scale_t=flat_s)
+        wt_q = flat_q.view(k_in, E, n_out).permute(1, 0, 2)            # strides (n_out, E*n_out, 1)
+        wt_s = flat_s.view(k_in // 128, E, n_out // 128).permute(1, 0, 2)
+    else:
+        wt_q = torch.empty((E, k_in, n_out), dtype=torch.uint8, device="cuda")
+        wt_s = torch.empty((E, k_in // 128, n_out // 128), dtype=torch.float32, device="cuda")
+        for e in range(E):   # one launch per expert: codes, scales and the transposed copy
+            fq.fp8_quantize_weight(dev_bf16(w[e]), transposed=True, q_t=wt_q[e], scale_t=wt_s[e])
     dq, ds = fq.fp8_quantize_act(dev_bf16(dy))
     c = fq.fp8_grouped_gemm(torch.from_numpy(off.astype(np.int32)).cuda(),
                             torch.from_numpy(rows.astype(np.int32)).cuda(), dq, ds, wt_q, wt_s,
@@ -296,7 +307,8 @@ def _grouped_dgrad_case(rows, n_out, k_in, sample=None):
             continue
         w_q, w_s = oracle.quant_weight_128x128(w[e])
         bt_q, bt_s = np.ascontiguousarray(w_q.T), np.ascontiguousarray(w_s.T)
-        assert_bits_equal(host_codes(wt_q[e]), bt_q, "expert %d transposed codes" % e)
+        assert_bits_equal(host_codes(wt_q[e].contiguous()), bt_q, "expert %d transposed codes" % e)
+        assert_bits_equal(host_f32(wt_s[e].contiguous()), bt_s, "expert %d transposed scales" % e)
         idx = np.arange(r) if sample is None or r <= sample else np.unique(
             np.concatenate([[0, r - 1], np.random.default_rng(e).choice(r, sample, replace=False)]))
         ref = oracle.gemm_rows(r0 + idx, a_q, a_s, bt_q, bt_s, "block")
@@ -305,6 +317,16 @@ def _grouped_dgrad_case(rows, n_out, k_in, sample=None):
 
 def test_grouped_dgrad_edge_rows():
     _grouped_dgrad_case([0, 1, 129, 256, 3], n_out=256, k_in=384)
+
+
+def test_grouped_dgrad_edge_rows_one_weight_launch():
+    _grouped_dgrad_case([0, 1, 129, 256, 3], n_out=256, k_in=384, one_launch=True)
+
+
+def test_grouped_dgrad_moe_config_one_weight_launch_sampled():
+    """The MoE Dgrad with all 32 experts' weights quantized in one launch and
+    their transposed copies read in place (interleaved rows)."""
+    _grouped_dgrad_case(wl.moe_rows(0), n_out=4096, k_in=7168, sample=4, one_launch=True)
 
 
 def test_grouped_dgrad_moe_config_sampled():

@@ -221,3 +221,59 @@ def test_empty_inputs_are_noops():
     w = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
     q, s = fq.fp8_quantize_weight(w)
     assert q.shape == (0, 128)
+
+
+# ------------------------------------------------ grouped weight quantization
+
+def _check_grouped_weights(w, what, experts=None, pad=False):
+    """fp8_quantize_weight_grouped of w[E][n][k] (transposed copies too):
+    every checked expert equals the oracle's 128x128 quantization bit for bit.
+    pad: every operand has padded leading dimensions and group strides."""
+    E, n, k = w.shape
+    if pad:
+        wd = torch.zeros((E, n + 3, k + 8), dtype=torch.bfloat16, device="cuda")
+        wd[:, :n, :k] = dev_bf16(w)
+        wd = wd[:, :n, :k]
+        bufs = [torch.full((E, n + 1, k + 16), 0x5A, dtype=torch.uint8, device="cuda"),
+                torch.full((E, n // 128 + 1, k // 128 + 2), 7.0, device="cuda"),
+                torch.full((E, k + 2, n + 32), 0x5A, dtype=torch.uint8, device="cuda"),
+                torch.full((E, k // 128 + 1, n // 128 + 3), 7.0, device="cuda")]
+        q, s = bufs[0][:, :n, :k], bufs[1][:, :n // 128, :k // 128]
+        qt, st = bufs[2][:, :k, :n], bufs[3][:, :k // 128, :n // 128]
+        fq.fp8_quantize_weight_grouped(wd, transposed=True, q=q, scale=s, q_t=qt, scale_t=st)
+    else:
+        q, s, qt, st = fq.fp8_quantize_weight_grouped(dev_bf16(w), transposed=True)
+    torch.cuda.synchronize()
+    for e in (range(E) if experts is None else experts):
+        q_ref, s_ref = oracle.quant_weight_128x128(w[e])
+        tag = "%s expert %d" % (what, e)
+        assert_bits_equal(host_f32(s[e].contiguous()), s_ref, tag + " scales")
+        assert_bits_equal(host_codes(q[e].contiguous()), q_ref, tag + " codes")
+        assert_bits_equal(host_f32(st[e].contiguous()), np.ascontiguousarray(s_ref.T), tag + " transposed scales")
+        assert_bits_equal(host_codes(qt[e].contiguous()), np.ascontiguousarray(q_ref.T), tag + " transposed codes")
+    if pad:   # nothing outside the windows written
+        assert torch.all(bufs[0][:, n:, :] == 0x5A) and torch.all(bufs[0][:, :, k:] == 0x5A)
+        assert torch.all(bufs[2][:, k:, :] == 0x5A) and torch.all(bufs[2][:, :, n:] == 0x5A)
+        assert torch.all(bufs[1][:, n // 128:, :] == 7.0) and torch.all(bufs[1][:, :, k // 128:] == 7.0)
+        assert torch.all(bufs[3][:, k // 128:, :] == 7.0) and torch.all(bufs[3][:, :, n // 128:] == 7.0)
+
+
+def test_weight_grouped_small_experts_edge_blocks():
+    rng = np.random.default_rng(14)
+    w = np.stack([wl.weight(1, "tiny_fprop", 40 + e, 256, 384) for e in range(5)])
+    w[1, 0:128, 0:128] = 0                                                        # all-zero block
+    w[2, 128:256, 128:256] = rng.integers(1, 0x80, (128, 128)).astype(np.uint16)  # subnormals
+    w[3, 17, 300] = 0x7F7F                                                        # bf16 max
+    w[4] = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(w[4]) * np.float32(1e-30))    # tiny scales
+    _check_grouped_weights(w, "small experts")
+
+
+def test_weight_grouped_padded_strides():
+    w = np.stack([wl.weight(2, "tiny_fprop", 50 + e, 384, 256) for e in range(3)])
+    _check_grouped_weights(w, "padded", pad=True)
+
+
+def test_weight_grouped_moe_experts_sampled():
+    """The 32 MoE expert weights [32][4096][7168] in one launch, with their
+    transposed copies (the grouped Dgrad operand); experts 0, 17, 31 checked."""
+    _check_grouped_weights(wl.grouped_fprop()["w"], "MoE", experts=(0, 17, 31))
