@@ -17,7 +17,8 @@ reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--streams 1|2]
                     [--config dense_fprop|dgrad|wgrad|grouped_fprop|grouped_dgrad|
-                              grouped_wgrad|mx_fprop|wgrad_cached|tiny_fprop]
+                              grouped_wgrad|mx_fprop|wgrad_cached|
+                              grouped_wgrad_cached|tiny_fprop]
 
 Counter runs (HBM traffic of each kernel, from rocprofv3 FETCH_SIZE and
 WRITE_SIZE; a plain copy of known size calibrates each counter):
@@ -45,7 +46,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 
 METRIC = "FP8 block-scaled GEMM TFLOP/s and % of MI355X FP8 MFMA peak (1 GPU)"
 CONFIGS = ["dense_fprop", "dgrad", "wgrad", "grouped_fprop", "grouped_dgrad", "grouped_wgrad",
-           "mx_fprop", "wgrad_cached", "tiny_fprop"]
+           "mx_fprop", "wgrad_cached", "grouped_wgrad_cached", "tiny_fprop"]
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Kernel name fragments (as rocprofv3 prints them) for each launch label.
@@ -292,6 +293,45 @@ class Workload:
                          "n": k_in, "k": n_out, "dy": "bf16, 1x128 tiles",
                          "w": "bf16, 128x128 blocks, all experts in one launch with per-expert transposed copies",
                          "out": "bf16"}
+        elif name == "grouped_wgrad_cached":
+            # MoE Wgrad with X taken from the FP8 cache the dispatch quantizer
+            # wrote in the forward pass (expert-sorted 1x128 codes + scales,
+            # padding rows zero): dY quantized 128x1, the cache re-tiled to
+            # 128x1 (128-aligned segments: no tile straddles experts), GEMM
+            d = wl.moe_dispatch()
+            rows, off = d["rows"], d["offsets"]
+            E, n_out, k_in = len(rows), 4096, 7168
+            real = int(rows.sum())
+            m_total = int(off[-1])
+            DY = sets(packed(wl.grad_rowscaled(0, "grouped_fprop", 4, real, n_out), off, rows))
+            x_dev = dev(d["x"])
+            dst = torch.from_numpy(d["dst_rows"]).cuda()
+            XQ, XS = [], []
+            for _ in range(rotate):
+                xq_ = torch.zeros((m_total, k_in), dtype=u8, device="cuda")
+                xs_ = torch.zeros((k_in // 128, m_total), dtype=f32, device="cuda")
+                fq.fp8_quantize_act_scatter(x_dev, dst, m_total, q=xq_, scale=xs_)
+                XQ.append(xq_)
+                XS.append(xs_)
+            del x_dev
+            offd = torch.from_numpy(off.astype("int32")).cuda()
+            aq, as_ = empty((n_out, m_total), u8), empty((m_total // 128, n_out), f32)
+            bq, bs = empty((k_in, m_total), u8), empty((m_total // 128, k_in), f32)
+            y = empty((E, n_out, k_in), f32)
+            self.flops = 2.0 * real * n_out * k_in   # real tokens only
+            self.bound = "hbm"                        # 3.8 GB of fp32 gradients written
+            self.launches = [
+                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
+                       act_bytes(m_total, n_out)),
+                Launch("retile_128x1", lambda r: fq.fp8_retile_act_128x1(XQ[r], XS[r], q_t=bq, scale_t=bs),
+                       2 * m_total * k_in + 8 * m_total * k_in // 128),
+                Launch("gemm", lambda r: fq.fp8_grouped_gemm_wgrad(offd, aq, as_, bq, bs, f32, out=y),
+                       (n_out + k_in) * m_total * (1 + 4 / 128) + 4 * E * n_out * k_in, self.flops),
+            ]
+            self.desc = {"workload": name, "experts": E, "tokens_real": real, "tokens_padded": m_total,
+                         "m": n_out, "n": k_in, "dy": "bf16, 128x1 tiles (along tokens)",
+                         "x": "FP8 dispatch cache (expert-sorted 1x128 codes + scales) re-tiled to 128x1",
+                         "out": "fp32 [experts][m][n]"}
         elif name == "grouped_wgrad":
             # MoE up-projection Wgrad: dW_e = dY_e^T X_e over each expert's tokens
             rows = wl.moe_rows(0)
@@ -631,7 +671,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32 accumulate, " + (
-            "fp32 out" if args.config in ("wgrad", "wgrad_cached", "grouped_wgrad") else "bf16 out"),
+            "fp32 out" if args.config in ("wgrad", "wgrad_cached", "grouped_wgrad", "grouped_wgrad_cached")
+            else "bf16 out"),
         "data": "synthetic (seeded; see workloads/)",
         "config": wl_obj.desc,
         "pct_of_fp8_peak": round(100.0 * value / FP8_DENSE_PEAK_TFLOPS, 2),
@@ -652,6 +693,7 @@ def main():
             "kernel": "gemm_kernel" + ({"grouped_fprop": " (grouped over M)",
                                         "grouped_dgrad": " (grouped over M)",
                                         "grouped_wgrad": " (grouped over K)",
+                                        "grouped_wgrad_cached": " (grouped over K)",
                                         "mx_fprop": " (microscaling)"}.get(args.config, "")),
             "algorithmic_bytes": int(gemm[0].bytes),
             "tflops": round(gemm_tflops, 2),

@@ -80,3 +80,52 @@ def test_grouped_wgrad_moe_config_sampled():
     big = int(np.argmax(rows))
     small = int(np.argmin(rows))
     _wgrad_case(rows, m=4096, n=7168, sample_experts=[0, big, small, 31], sample_rows=12)
+
+
+def _wgrad_from_dispatch_cache(rows, m, k, tokens, top_k, sample_experts=None, sample_rows=None):
+    """MoE Wgrad with X taken from the FP8 cache the dispatch quantizer wrote:
+    the expert-sorted 1x128 codes and scales (padding rows zeroed before the
+    scatter) re-tiled to 128x1 token tiles, then the grouped-over-K GEMM.
+    Segments are 128-aligned, so no 128-token tile straddles two experts."""
+    rows = np.asarray(rows, dtype=np.int64)
+    d = wl.moe_dispatch(0, k=k, tokens=tokens, top_k=top_k, rows=rows)
+    off = d["offsets"]
+    m_total = int(off[-1])
+    q = torch.zeros((m_total, k), dtype=torch.uint8, device="cuda")         # padding rows stay zero
+    s = torch.zeros((k // 128, m_total), dtype=torch.float32, device="cuda")
+    fq.fp8_quantize_act_scatter(dev_bf16(d["x"]), torch.from_numpy(d["dst_rows"]).cuda(), m_total, q=q, scale=s)
+    bq, bs = fq.fp8_retile_act_128x1(q, s)
+    dy, _ = _packed(rows, m, 102, grad=True)
+    aq, as_ = fq.fp8_quantize_act(dev_bf16(dy), "128x1")
+    off_d = torch.from_numpy(off.astype(np.int32)).cuda()
+    out = fq.fp8_grouped_gemm_wgrad(off_d, aq, as_, bq, bs, torch.float32)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref, _ = oracle.quant_act_scatter(d["x"], d["dst_rows"], m_total)
+    b_q, b_s = oracle.retile_128x1(xq_ref, xs_ref)
+    assert_bits_equal(host_codes(bq), b_q, "re-tiled cache codes")
+    assert_bits_equal(host_f32(bs), b_s, "re-tiled cache scales")
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    experts = range(len(rows)) if sample_experts is None else sample_experts
+    for e in experts:
+        t0, t1 = int(off[e]), int(off[e + 1])
+        idx = np.arange(m) if sample_rows is None else np.unique(np.concatenate(
+            [[0, m - 1], np.random.default_rng(e).choice(m, sample_rows, replace=False)]))
+        got = host_out(out[e][torch.from_numpy(idx).cuda()])
+        if t1 == t0:
+            assert np.all(got == 0), "expert %d: empty segment must give zeros" % e
+            continue
+        ref = oracle.gemm_rows(idx, np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
+                               np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]),
+                               "row")
+        assert_gemm_close(got, ref, "cached-X wgrad expert %d (%d tokens)" % (e, rows[e]))
+
+
+def test_grouped_wgrad_from_dispatch_cache_small():
+    _wgrad_from_dispatch_cache([5, 0, 130, 64, 1], m=256, k=384, tokens=200, top_k=2)
+
+
+def test_grouped_wgrad_from_dispatch_cache_moe_sampled():
+    """The MoE config: 8192 tokens x 7168, top-8 routes into 32 local experts,
+    dW [32][4096][7168]; experts 0, 9 and 31, 24 rows each."""
+    _wgrad_from_dispatch_cache(wl.moe_rows(0), m=4096, k=7168, tokens=8192, top_k=8,
+                               sample_experts=(0, 9, 31), sample_rows=24)
