@@ -64,6 +64,27 @@ def lib() -> ctypes.CDLL:
     return _LIB
 
 
+class OutOfContract(ValueError):
+    """A non-finite input (NaN/Inf bf16 value, NaN E4M3 code 0x7F/0xFF, NaN
+    E8M0 byte 0xFF, or a non-finite scale): the method's numbers are defined
+    for finite values only, so the oracle refuses rather than guess."""
+
+
+def _finite_bf16(x: np.ndarray, what: str) -> None:
+    if np.any((np.asarray(x, dtype=np.uint16) & 0x7F80) == 0x7F80):
+        raise OutOfContract("%s holds a NaN or infinite bf16 value" % what)
+
+
+def _finite_codes(q: np.ndarray, what: str) -> None:
+    if np.any((np.asarray(q, dtype=np.uint8) & 0x7F) == 0x7F):
+        raise OutOfContract("%s holds a NaN E4M3 code" % what)
+
+
+def _finite_scales(s, what: str) -> None:
+    if not np.all(np.isfinite(np.asarray(s, dtype=np.float64))):
+        raise OutOfContract("%s holds a non-finite scale" % what)
+
+
 def _p(a: np.ndarray, ctype):
     assert a.flags["C_CONTIGUOUS"]
     return a.ctypes.data_as(ctypes.POINTER(ctype))
@@ -95,6 +116,7 @@ def encoders_disagree(lo_bits: int, hi_bits: int, stride: int = 1) -> tuple[int,
 def quant_act_1x128(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """bf16 bits X[rows][cols] -> (Q uint8[rows][cols], S float32[cols/128][rows])."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
+    _finite_bf16(x, "x")
     rows, cols = x.shape
     assert cols % 128 == 0
     q = np.empty((rows, cols), dtype=np.uint8)
@@ -129,6 +151,7 @@ def quant_mx_1x32(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Microscaling (OCP MX, E4M3 elements): bf16 bits X[rows][cols] ->
     (Q uint8[rows][cols], E uint8[rows][cols/32] E8M0 exponent bytes)."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
+    _finite_bf16(x, "x")
     rows, cols = x.shape
     assert cols % 32 == 0
     q = np.empty((rows, cols), dtype=np.uint8)
@@ -148,12 +171,17 @@ def dequant_mx(q: np.ndarray, e: np.ndarray) -> np.ndarray:
 def gemm_mx(a_q: np.ndarray, a_e: np.ndarray, b_q: np.ndarray, b_e: np.ndarray) -> np.ndarray:
     """float64 C[m][n] = deq_mx(A)[m][:] . deq_mx(B)[n][:], unrounded (both
     operands K-contiguous, 32-element blocks along K)."""
+    for q, e, what in ((a_q, a_e, "a"), (b_q, b_e, "b")):
+        _finite_codes(q, what)
+        if np.any(np.asarray(e, dtype=np.uint8) == 0xFF):
+            raise OutOfContract("%s holds the NaN E8M0 byte 0xFF" % what)
     return dequant_mx(a_q, a_e) @ dequant_mx(b_q, b_e).T
 
 
 def quant_act_128x1(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """bf16 bits X[tokens][cols] -> (QT uint8[cols][tokens], S float32[tokens/128][cols])."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
+    _finite_bf16(x, "x")
     rows, cols = x.shape
     assert rows % 128 == 0
     qt = np.empty((cols, rows), dtype=np.uint8)
@@ -174,6 +202,8 @@ def retile_128x1(q: np.ndarray, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     rows, cols = q.shape
     assert rows % 128 == 0 and cols % 128 == 0
     s = np.ascontiguousarray(s[:, :rows], dtype=np.float32)
+    _finite_codes(q, "q")
+    _finite_scales(s, "scale")
     assert s.shape == (cols // 128, rows)
     qt = np.empty((cols, rows), dtype=np.uint8)
     st = np.empty((rows // 128, cols), dtype=np.float32)
@@ -185,6 +215,7 @@ def retile_128x1(q: np.ndarray, s: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
 def quant_weight_128x128(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """bf16 bits W[n][k] -> (Q uint8[n][k], S float32[n/128][k/128])."""
     w = np.ascontiguousarray(w, dtype=np.uint16)
+    _finite_bf16(w, "w")
     n, k = w.shape
     assert n % 128 == 0 and k % 128 == 0
     q = np.empty((n, k), dtype=np.uint8)
@@ -198,6 +229,8 @@ def quant_pairs(x: np.ndarray, amax: np.ndarray) -> np.ndarray:
     """E4M3(fl32(x / fl32(|amax| / 448))) element-wise on bf16 bit arrays."""
     x = np.ascontiguousarray(x, dtype=np.uint16)
     amax = np.ascontiguousarray(amax, dtype=np.uint16)
+    _finite_bf16(x, "x")
+    _finite_bf16(amax, "amax")
     assert x.shape == amax.shape
     q = np.empty(x.shape, dtype=np.uint8)
     lib().oracle_quant_pairs(_p(x, ctypes.c_uint16), _p(amax, ctypes.c_uint16), x.size,
@@ -243,6 +276,10 @@ def gemm(a_q: np.ndarray, a_s: np.ndarray, b_q: np.ndarray, b_s: np.ndarray,
     [n/128][k/128] (``"block"``) or one per (slab, row) [k/128][n] (``"row"``,
     the Wgrad case where both operands were quantized in 128x1 token tiles).
     """
+    _finite_codes(a_q, "a")
+    _finite_codes(b_q, "b")
+    _finite_scales(a_s, "a_scale")
+    _finite_scales(b_s, "b_scale")
     A = dequant_rows_1x128(a_q, a_s)
     if b_scale_kind == "block":
         B = dequant_block_128x128(b_q, b_s)
@@ -273,6 +310,9 @@ def gemm_tensor(a_q: np.ndarray, a_s: float, b_q: np.ndarray, b_s: float) -> np.
     exact in float64 in any order: the matmul is the exact sum, and the one
     rounding is the final multiplication by sA * sB (itself exact)."""
     assert a_q.shape[1] <= 131072
+    _finite_codes(a_q, "a")
+    _finite_codes(b_q, "b")
+    _finite_scales([a_s, b_s], "per-tensor scale")
     d = _dec()
     return (float(a_s) * float(b_s)) * (d[a_q] @ d[b_q].T)
 

@@ -729,3 +729,29 @@ def test_retile_dequantizes_to_binary32_before_requantizing():
     assert st[0, 0] == 1.0 and qt[0, 0] == 0x7E and qt[0, 1] == 0x38
     bs, bq = brute.retile_group([int(v) for v in q[:, 0]], [Fraction(float(v)) for v in s[0]])
     assert bs == 1 and bq[:2] == [0x7E, 0x38]
+
+
+def test_oracle_refuses_non_finite_inputs():
+    """Non-finite inputs are outside the method's contract: every oracle entry
+    that reads bf16 values, E4M3 codes or scales refuses them."""
+    x = wl.activation(0, "tiny_fprop", 99, 128, 256, 50.0)
+    q, s = oracle.quant_act_1x128(x)
+    for bad in (0x7F80, 0xFF80, 0x7FC1):                       # +Inf, -Inf, a NaN
+        xb = x.copy()
+        xb[5, 200] = bad
+        for fn in (oracle.quant_act_1x128, oracle.quant_act_128x1, oracle.quant_weight_128x128,
+                   oracle.quant_mx_1x32):
+            with pytest.raises(oracle.OutOfContract):
+                fn(xb)
+    qn = q.copy()
+    qn[3, 3] = 0xFF                                            # E4M3 NaN
+    with pytest.raises(oracle.OutOfContract):
+        oracle.retile_128x1(qn, s)
+    with pytest.raises(oracle.OutOfContract):
+        oracle.gemm(qn, s, q[:128], np.ones((1, 2), np.float32), "block")
+    sn = s.copy()
+    sn[1, 7] = np.inf
+    with pytest.raises(oracle.OutOfContract):
+        oracle.retile_128x1(q, sn)
+    with pytest.raises(oracle.OutOfContract):
+        oracle.gemm_tensor(q, np.float32("nan"), q, 1.0)
