@@ -52,13 +52,20 @@ def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str) -> None:
 
 
 def gemm_errors(got: np.ndarray, ref: np.ndarray) -> dict:
+    """The pass metrics against the unrounded float64 oracle, plus (a
+    diagnostic only) the normwise error against the oracle rounded to bf16
+    nearest-even: for bf16 output that isolates the GEMM's own error."""
+    import oracle
     diff = got - ref
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
     norm_ref = float(np.linalg.norm(ref))
     normwise = float(np.linalg.norm(diff)) / norm_ref if norm_ref > 0 else float(np.linalg.norm(diff))
     bound = ELEM_TOL * (np.abs(ref) + rms)
     worst = float(np.max(np.abs(diff) / np.where(bound > 0, bound, 1.0))) if ref.size else 0.0
-    return {"normwise": normwise, "worst_elem_ratio": worst, "rms_ref": rms}
+    diff16 = got - oracle.bf16_round(ref)
+    normwise16 = float(np.linalg.norm(diff16)) / norm_ref if norm_ref > 0 else float(np.linalg.norm(diff16))
+    return {"normwise": normwise, "worst_elem_ratio": worst, "rms_ref": rms,
+            "normwise_vs_bf16_rounded_ref": normwise16}
 
 
 def assert_gemm_close(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
