@@ -424,10 +424,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     int jnext = 0;  // slab the current step prefetches
 
     // ---- fragment addresses: lane (i = l%16, g = l/16) reads 32 bytes of
-    // row i at logical chunks 2g and 2g+1 of every 16-row subtile.
+    // row i, the 16-byte chunks g and g + 4 of every 16-row subtile. In the
+    // 16x16x128 FP8 MFMA the 32 bytes of lane group g are K[16g, 16g+16) and
+    // K[64+16g, 64+16g+16) of the slab, and the scale of K block b (32
+    // elements) comes from lane group b (measured on gfx950); with chunks g
+    // and g + 4, block b is chunks 2b and 2b+1 -- the microscaling
+    // quantizer's block b. The unscaled MFMA is blind to the order (A and B
+    // share it), and this order reads LDS without bank conflicts (counted:
+    // chunks 2g and 2g+1 cost ~11M conflict cycles per Dense Fprop GEMM).
     const int fi = lane & 15, fg = lane >> 4;
-    const uint32_t off0 = fi * kSlab + swz_chunk(2 * fg, fi) * 16;
-    const uint32_t off1 = fi * kSlab + swz_chunk(2 * fg + 1, fi) * 16;
+    const uint32_t off0 = fi * kSlab + swz_chunk(fg, fi) * 16;
+    const uint32_t off1 = fi * kSlab + swz_chunk(fg + 4, fi) * 16;
     const uint32_t fragA = wm * kWaveM * kSlab;
     const uint32_t fragB = wn * WN * kSlab;
     // Block scales: the wave's first column lies in n-block nb0; sB holds the
@@ -593,17 +600,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     };
 
     // One slab of the in-place GEMMs. Microscaling: the scaled MFMA takes
-    // each lane's E8M0 byte and accumulates into acc directly. Per-tensor:
-    // the plain MFMA accumulates into acc directly. In the 16x16x128 FP8 MFMA,
-    // the 32 bytes of lane group g are K[16g, 16g+16) and K[64+16g, 64+16g+16)
-    // of the slab, and the scale of K block b (32 elements) comes from lane
-    // group b (measured on gfx950). So lane group g reads 16-byte chunks g and
-    // g + 4: block b then consists of chunks 2b and 2b+1 -- the quantizer's
-    // block b -- and lane group g supplies block g's byte. (The unscaled MFMA
-    // is blind to this order: any K permutation shared by A and B gives the
-    // same sum.)
-    const uint32_t moff0 = fi * kSlab + swz_chunk(fg, fi) * 16;
-    const uint32_t moff1 = fi * kSlab + swz_chunk(fg + 4, fi) * 16;
+    // each lane's E8M0 byte (lane group g supplies block g's byte, see the
+    // fragment addresses) and accumulates into acc directly. Per-tensor: the
+    // plain MFMA accumulates into acc directly.
     auto compute_inplace = [&](auto a_tag, auto act_tag) {
         constexpr int ST = decltype(a_tag)::value;
         constexpr int ACT = decltype(act_tag)::value;
@@ -614,12 +613,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         const int shift = 8 * fg;
         v8i fr[2];
         uint32_t sbw[2];
-        fr[0] = ld_frag(lb + moff0, lb + moff1);
+        fr[0] = ld_frag(lb + off0, lb + off1);
         sbw[0] = MX ? lsb[0] : 0u;
         v8i am[kMSub];
         int sae[kMSub];
 #pragma unroll
-        for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + moff0, la + s * 2048 + moff1);
+        for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) sae[s] = MX ? (int)((lsa[16 * s] >> shift) & 0xFFu) : 0;
         __builtin_amdgcn_sched_barrier(0);
@@ -628,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             const v8i bf = fr[T & 1];
             const int sbe = MX ? (int)((sbw[T & 1] >> shift) & 0xFFu) : 0;
             if constexpr (T + 1 < NSUB) {
-                fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + moff0, lb + (T + 1) * 2048 + moff1);
+                fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + off0, lb + (T + 1) * 2048 + off1);
                 if constexpr (MX) sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
             }
             if constexpr (T < 4) issue_part(jnext, std::integral_constant<int, ST ^ 1>{}, T);
