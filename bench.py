@@ -61,15 +61,23 @@ KERNEL_NAMES = {
 }
 
 
-def kernel_source_digest() -> str:
-    """Digest of the HIP sources; stored counter figures are valid only for
-    the kernels they were taken on."""
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (what the kernels are made of)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
+def kernel_source_digest(csrc: str | None = None) -> str:
+    """Digest of the HIP sources, comments and blank lines left out; stored
+    counter figures are valid only for the kernels they were taken on."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "fine_grained_fp8_quantize_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "fine_grained_fp8_quantize_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -21,8 +21,13 @@
 // m x 2 along n), 64 x BN/2 per wave. BN = 224 makes N = 7168 (Dgrad, Wgrad)
 // an exact multiple, so those grids are whole waves of the 256 CUs. Each
 // 128-byte K slab of the A and B tiles is copied global -> LDS by the direct
-// LDS-DMA load (global_load_lds_dwordx4), double buffered, with 16-byte
-// chunks XOR-swizzled by row so that fragment reads are bank-conflict free.
+// LDS-DMA load (global_load_lds_dwordx4) -- two stages, or for grouped-over-M
+// tiles two A and three B stages -- with 16-byte chunks XOR-swizzled by row.
+//
+// Modes: one GEMM; grouped over M (MoE Fprop/Dgrad); grouped over K (MoE
+// Wgrad). Two more dense variants accumulate in place across slabs instead
+// of promoting: microscaling operands (E8M0 block scales applied by the
+// scaled MFMA) and one scale per tensor (applied in the epilogue).
 // The MFMA computes the transposed tile: its row operand is B (n), its column
 // operand is A (m), so every lane holds four consecutive n of one m -- one A
 // scale per lane per m-subtile, and the B block scale is wave-uniform per
@@ -56,7 +61,8 @@ constexpr int kTileBytes = kBM * kSlab;
 // bytes). A fragment read has each 16-lane quarter of the wave fetch one
 // chunk from 16 consecutive rows; XOR with (row >> 1) & 7 sends those 16
 // reads to 16 different 16-byte bank groups (rows 2r and 2r+1 already sit
-// in opposite halves of the 64 banks), so the read is conflict-free. Tiles
+// in opposite halves of the 64 banks). With the fragment order below
+// (chunks g and g + 4) the counters show no bank conflicts at all. Tiles
 // and subtiles start at multiples of 16 rows, so tile-relative and
 // subtile-relative rows give the same chunk.
 __device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ ((row >> 1) & 7); }
