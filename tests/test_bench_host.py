@@ -92,3 +92,15 @@ def test_pmc_summary_ignores_kernels_outside_the_step(tmp_path):
         launches = [bench.Launch("gemm", None, 100.0, 1.0)]
     res = bench.pmc_summary(fetch, write, "x", 1, str(tmp_path / "t.json"), OnlyGemm())
     assert set(res["kernels"]) == {"gemm"}
+
+
+def test_kernel_source_digest_ignores_comments_only(tmp_path):
+    """Counter figures stay valid across comment edits, not across code edits."""
+    a, b, c = tmp_path / "a", tmp_path / "b", tmp_path / "c"
+    for d in (a, b, c):
+        d.mkdir()
+    (a / "k.hip").write_text("// header\nint f(int x) {\n    return x + 1;  // one\n}\n")
+    (b / "k.hip").write_text("/* a longer\n   header */\n\nint f(int x) {\n    return x + 1;\n}\n")
+    (c / "k.hip").write_text("// header\nint f(int x) {\n    return x + 2;  // one\n}\n")
+    assert bench.kernel_source_digest(str(a)) == bench.kernel_source_digest(str(b))
+    assert bench.kernel_source_digest(str(a)) != bench.kernel_source_digest(str(c))
