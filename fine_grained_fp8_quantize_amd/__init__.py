@@ -19,7 +19,20 @@ Layouts (row-major, K contiguous for GEMM operands):
   ``scale[n/128][k/128]`` (128x128 blocks), optionally also the transpose.
 * ``fp8_gemm(a, a_scale, b, b_scale)`` -- ``C[m][n] = dequant(A) dequant(B)^T``.
 * ``fp8_grouped_gemm(offsets, rows, a, a_scale, b, b_scale)`` -- per-expert
-  Fprop over an expert-sorted, 128-padded row layout.
+  Fprop (or Dgrad, with transposed weights) over an expert-sorted, 128-padded
+  row layout.
+* ``fp8_quantize_weight_grouped(w)`` -- ``w[E][n][k]`` quantized in one
+  launch, optionally with per-expert transposed copies.
+* ``fp8_quantize_act_scatter(x, dst_rows, m_total)`` -- quantize each token
+  once and scatter its codes and scales to its expert-sorted rows.
+* ``fp8_grouped_gemm_wgrad(offsets, a, a_scale, b, b_scale)`` -- per-expert
+  Wgrad over each expert's token segment.
+* ``fp8_retile_act_128x1(q, scale)`` -- a cached 1x128 activation re-tiled
+  into 128x1 token tiles.
+* ``fp8_quantize_mx`` / ``fp8_gemm_mx`` -- the microscaling variant (1x32
+  blocks, E8M0 scales, scaled MFMA).
+* ``fp8_gemm_tensor`` -- one scale per operand, the whole K sum in the MFMA
+  accumulators.
 
 E4M3 tensors are returned as ``torch.float8_e4m3fn`` (OCP E4M3FN bytes);
 ``uint8`` tensors are accepted wherever codes are inputs.

@@ -5,9 +5,12 @@
 // 128x1 token tiles for the Wgrad operands. Every group gets one FP32 scale
 // s = amax / 448 and its elements become E4M3 codes of x / s (page "Deepseek
 // Ai News Expert Interview", passages on E4M3 for all tensors and on sharing
-// exponent bits within small groups). All three kernels are HBM-bound:
-// 2 bytes read, 1 byte written and 4/128 (or 4/16384) bytes of scale per
-// element.
+// exponent bits within small groups). The kernels are HBM-bound: 2 bytes
+// read, 1 byte written and 4/128 (or 4/16384) bytes of scale per element
+// (the re-tile of a cached FP8 activation reads 1 byte instead of 2). Also
+// here: the scatter form of the 1x128 kernel (quantize before dispatch), the
+// microscaling quantizer, and the weight quantizer over several experts in
+// one launch.
 #include "fp8q_device.h"
 #include "launch.h"
 
