@@ -55,6 +55,7 @@ KERNEL_NAMES = {
     "quant_act_scatter": "quant_act_1x128_kernel<true>",
     "quant_act_128x1": "quant_act_128x1_kernel",
     "quant_weight": "quant_weight_kernel",
+    "quant_act_weight": "quant_act_weight_kernel",
     "quant_mx": "quant_mx_1x32_kernel",
     "retile_128x1": "retile_128x1_kernel",
     "gemm": "gemm_kernel",
@@ -165,10 +166,10 @@ class Workload:
             y = empty((m, n), bf16)
             self.flops = 2.0 * m * n * k
             self.launches = [
-                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(X[r], "1x128", q=xq, scale=xs),
-                       act_bytes(m, k)),
-                Launch("quant_weight", lambda r: fq.fp8_quantize_weight(W[r], q=wq, scale=ws),
-                       3 * n * k + 4 * (n // 128) * (k // 128)),
+                # x in 1x128 tiles and w in 128x128 blocks, one launch
+                Launch("quant_act_weight", lambda r: fq.fp8_quantize_act_weight(
+                    X[r], W[r], q=xq, scale=xs, wq=wq, wscale=ws),
+                       act_bytes(m, k) + 3 * n * k + 4 * (n // 128) * (k // 128)),
                 Launch("gemm", lambda r: fq.fp8_gemm(xq, xs, wq, ws, "block", bf16, out=y),
                        gemm_bytes(m, n, k, (n // 128) * (k // 128), 2, m), self.flops),
             ]
@@ -208,11 +209,11 @@ class Workload:
             self.flops = 2.0 * m * k_in * n_out
             nb = (n_out // 128) * (k_in // 128)
             self.launches = [
-                Launch("quant_act_1x128", lambda r: fq.fp8_quantize_act(DY[r], "1x128", q=dq, scale=ds),
-                       act_bytes(m, n_out)),
-                Launch("quant_weight", lambda r: fq.fp8_quantize_weight(
-                    W[r], transposed=True, q=wq, scale=ws, q_t=wqt, scale_t=wst),
-                       4 * n_out * k_in + 8 * nb),
+                # dy in 1x128 tiles and w in 128x128 blocks with the
+                # transposed copy the GEMM reads, one launch
+                Launch("quant_act_weight", lambda r: fq.fp8_quantize_act_weight(
+                    DY[r], W[r], transposed=True, q=dq, scale=ds, wq=wq, wscale=ws, wq_t=wqt, wscale_t=wst),
+                       act_bytes(m, n_out) + 4 * n_out * k_in + 8 * nb),
                 Launch("gemm", lambda r: fq.fp8_gemm(dq, ds, wqt, wst, "block", bf16, out=y),
                        gemm_bytes(m, k_in, n_out, nb, 2, m), self.flops),
             ]
@@ -406,7 +407,10 @@ class Workload:
         # the GEMM waits for both. The side stream's work of a step starts
         # after everything the main stream enqueued before it (the previous
         # step's GEMM included), so no buffer is overwritten while in use.
-        assert [ln.label for ln in self.launches][-1] == "gemm" and len(self.launches) == 3
+        assert self.launches[-1].label == "gemm"
+        if streams == 2 and len(self.launches) != 3:
+            raise SystemExit("--streams 2 overlaps two quantization launches; %s quantizes in %d"
+                             % (name, len(self.launches) - 1))
         self.side = torch.cuda.Stream() if streams == 2 else None
         self.mark = torch.cuda.Event()
         self.done = torch.cuda.Event()

@@ -23,6 +23,8 @@ Layouts (row-major, K contiguous for GEMM operands):
   row layout.
 * ``fp8_quantize_weight_grouped(w)`` -- ``w[E][n][k]`` quantized in one
   launch, optionally with per-expert transposed copies.
+* ``fp8_quantize_act_weight(x, w)`` -- a Linear layer's activation (1x128)
+  and weight (128x128, optionally transposed too) in one launch.
 * ``fp8_quantize_act_scatter(x, dst_rows, m_total)`` -- quantize each token
   once and scatter its codes and scales to its expert-sorted rows.
 * ``fp8_grouped_gemm_wgrad(offsets, a, a_scale, b, b_scale)`` -- per-expert
@@ -49,6 +51,7 @@ __all__ = [
     "fp8_quantize_act_scatter",
     "fp8_quantize_weight",
     "fp8_quantize_weight_grouped",
+    "fp8_quantize_act_weight",
     "fp8_gemm",
     "fp8_grouped_gemm",
     "fp8_grouped_gemm_wgrad",
@@ -96,6 +99,8 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_act.argtypes = [p, i64, i64, i64, cint, p, i64, p, i64, p]
     L.fp8_quantize_act_scatter.argtypes = [p, i64, i64, i64, i32, p, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
+    L.fp8_quantize_act_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, i64, i64, p, i64, p, i64,
+                                          p, i64, p, i64, p]
     L.fp8_quantize_weight_grouped.argtypes = [i32, p, i64, i64, i64, i64, p, i64, i64, p, i64, i64,
                                               p, i64, i64, p, i64, i64, p]
     L.fp8_quantize_mx.argtypes = [p, i64, i64, i64, p, i64, p, i64, p]
@@ -108,7 +113,7 @@ def _load() -> ctypes.CDLL:
     L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
-                 "fp8_quantize_weight_grouped", "fp8_gemm",
+                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_gemm",
                  "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
                  "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
@@ -269,6 +274,49 @@ def fp8_quantize_weight(w: torch.Tensor, transposed: bool = False, q: torch.Tens
         _stream(stream))
     _check(st, "fp8_quantize_weight")
     return (q, scale, q_t, scale_t) if transposed else (q, scale)
+
+
+def fp8_quantize_act_weight(x: torch.Tensor, w: torch.Tensor, transposed: bool = False,
+                            q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                            wq: torch.Tensor | None = None, wscale: torch.Tensor | None = None,
+                            wq_t: torch.Tensor | None = None, wscale_t: torch.Tensor | None = None, stream=None):
+    """A Linear layer's operands in one launch: ``x`` in 1x128 tiles (as
+    :func:`fp8_quantize_act`) and ``w`` in 128x128 blocks (as
+    :func:`fp8_quantize_weight`, with the transposed copy when ``transposed``).
+
+    Returns ``(q, scale, wq, wscale)`` or, transposed, ``(q, scale, wq,
+    wscale, wq_t, wscale_t)``."""
+    _need_gpu(x, w)
+    _rowmajor(x, "x")
+    _rowmajor(w, "w")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise Fp8qError("x and w must be bfloat16")
+    rows, cols = x.shape
+    n, k = w.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
+    if scale is None:
+        scale = torch.empty((cols // 128, rows), dtype=torch.float32, device=dev)
+    if wq is None:
+        wq = torch.empty((n, k), dtype=torch.float8_e4m3fn, device=dev)
+    if wscale is None:
+        wscale = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
+    if transposed:
+        if wq_t is None:
+            wq_t = torch.empty((k, n), dtype=torch.float8_e4m3fn, device=dev)
+        if wscale_t is None:
+            wscale_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device=dev)
+    _need_gpu(q, scale, wq, wscale, wq_t, wscale_t)
+    _codes(q, "q")
+    _codes(wq, "wq")
+    st = _load().fp8_quantize_act_weight(
+        _ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0), _ptr(scale), scale.stride(0),
+        _ptr(w), n, k, w.stride(0), _ptr(wq), wq.stride(0), _ptr(wscale), wscale.stride(0),
+        _ptr(wq_t if transposed else None), wq_t.stride(0) if transposed else 0,
+        _ptr(wscale_t if transposed else None), wscale_t.stride(0) if transposed else 0, _stream(stream))
+    _check(st, "fp8_quantize_act_weight")
+    return (q, scale, wq, wscale, wq_t, wscale_t) if transposed else (q, scale, wq, wscale)
 
 
 def fp8_quantize_weight_grouped(w: torch.Tensor, transposed: bool = False, q: torch.Tensor | None = None,

@@ -103,6 +103,37 @@ int fp8_quantize_weight_grouped(int32_t groups, const uint16_t* w, int64_t n, in
                                                 stride_st, stream));
 }
 
+int fp8_quantize_act_weight(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                            int64_t ld_q, float* scale, int64_t ld_s, const uint16_t* w, int64_t n, int64_t k,
+                            int64_t ld_w, uint8_t* wq, int64_t ld_wq, float* wscale, int64_t ld_ws,
+                            uint8_t* wq_t, int64_t ld_wqt, float* wscale_t, int64_t ld_wst, hipStream_t stream) {
+    // the checks of fp8_quantize_act (1x128) and fp8_quantize_weight, both
+    if (rows < 0 || cols < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+    const bool act = rows > 0 && cols > 0, wgt = n > 0 && k > 0;
+    if (act) {
+        if (!x || !q || !scale) return FP8Q_ERR_NULL;
+        if (ld_x < cols || cols % 128 != 0 || ld_q < cols || ld_s < rows) return FP8Q_ERR_SHAPE;
+        if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || ld_x % 8 != 0 || ld_q % 16 != 0)
+            return FP8Q_ERR_ALIGN;
+    }
+    if (wgt) {
+        if (!w || !wq || !wscale) return FP8Q_ERR_NULL;
+        if (wq_t && !wscale_t) return FP8Q_ERR_NULL;
+        if (n % 128 != 0 || k % 128 != 0 || ld_w < k || ld_wq < k || ld_ws < k / 128) return FP8Q_ERR_SHAPE;
+        if (wq_t && (ld_wqt < n || ld_wst < n / 128)) return FP8Q_ERR_SHAPE;
+        if (!aligned(w, 16) || !aligned(wq, 16) || !aligned(wscale, 4) || ld_w % 8 != 0 || ld_wq % 16 != 0)
+            return FP8Q_ERR_ALIGN;
+        if (wq_t && (!aligned(wq_t, 16) || !aligned(wscale_t, 4) || ld_wqt % 16 != 0)) return FP8Q_ERR_ALIGN;
+    }
+    if (!act && !wgt) return FP8Q_OK;
+    const int64_t act_blocks = act ? (rows + 15) / 16 * (cols / 128) / 4 + 1 : 0;
+    if (!grid_ok(act_blocks + (wgt ? n / 128 * (k / 128) : 0))) return FP8Q_ERR_SHAPE;
+    // an empty operand is skipped: its block range is empty
+    return hip_status(fp8q::launch_quant_act_weight(
+        x, act ? rows : 0, act ? cols : 0, ld_x, q, ld_q, scale, ld_s, w, wgt ? n : 0, wgt ? k : 0, ld_w, wq,
+        ld_wq, wscale, ld_ws, wq_t, ld_wqt, wscale_t, ld_wst, stream));
+}
+
 int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
                         uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                         uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,

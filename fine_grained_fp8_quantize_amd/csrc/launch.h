@@ -26,6 +26,14 @@ hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, i
                                const float* scale, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
                                float* scale_t, int64_t ld_st, hipStream_t stream);
 
+// 1x128 activation quantization and 128x128 weight quantization (optional
+// transposed copy) in one launch.
+hipError_t launch_quant_act_weight(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                   int64_t ld_q, float* scale, int64_t ld_s, const uint16_t* w, int64_t n,
+                                   int64_t k, int64_t ld_w, uint8_t* wq, int64_t ld_wq, float* ws, int64_t ld_ws,
+                                   uint8_t* wq_t, int64_t ld_wqt, float* ws_t, int64_t ld_wst,
+                                   hipStream_t stream);
+
 // groups weight matrices, group e at each base pointer + e * its stride
 // (elements); groups == 1 with zero strides is one matrix.
 hipError_t launch_quant_weight(int64_t groups, const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,

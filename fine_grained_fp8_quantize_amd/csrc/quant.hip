@@ -9,8 +9,8 @@
 // read, 1 byte written and 4/128 (or 4/16384) bytes of scale per element
 // (the re-tile of a cached FP8 activation reads 1 byte instead of 2). Also
 // here: the scatter form of the 1x128 kernel (quantize before dispatch), the
-// microscaling quantizer, and the weight quantizer over several experts in
-// one launch.
+// microscaling quantizer, the weight quantizer over several experts in one
+// launch, and one launch that quantizes a layer's activation and weight.
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -31,13 +31,15 @@ constexpr int kActRowsPerWave = 16;
 constexpr int kActWavesPerBlock = 4;
 constexpr int kMaxTopk = 8;  // destinations per source row (scatter)
 
+// The body of one 256-thread block (block index `block`); kernels below
+// call it, alone or next to the weight body.
 template <bool SCATTER>
-__global__ __launch_bounds__(256) void quant_act_1x128_kernel(
+__device__ __forceinline__ void act_1x128_body(
     const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
-    int64_t units, const int32_t* __restrict__ dst, int topk, int64_t m_total) {
+    int64_t units, const int32_t* __restrict__ dst, int topk, int64_t m_total, int64_t block) {
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * kActWavesPerBlock + (threadIdx.x >> 6);
+    const int64_t unit = block * kActWavesPerBlock + (threadIdx.x >> 6);
     if (unit >= units) return;  // whole wave
     const int64_t rg = unit / slabs;
     const int64_t j = unit - rg * slabs;
@@ -95,6 +97,15 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
             }
         }
     }
+}
+
+template <bool SCATTER>
+__global__ __launch_bounds__(256) void quant_act_1x128_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    int64_t units, const int32_t* __restrict__ dst, int topk, int64_t m_total) {
+    act_1x128_body<SCATTER>(x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units, dst, topk, m_total,
+                            (int64_t)blockIdx.x);
 }
 
 // ------------------------------------------------------------ MX (1x32)
@@ -403,16 +414,16 @@ struct WeightGroups {
 // rg = t/16, chunk g = t%16) holds rows 8rg..8rg+7 x columns 8g..8g+7. The
 // optional transposed copy is produced from the thread's 8x8 byte tile with
 // byte permutes, so block (bn, bk) of W^T gets exactly the same codes.
-__global__ __launch_bounds__(256) void quant_weight_kernel(
+__device__ __forceinline__ void weight_body(
     const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
     uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
-    WeightGroups grp) {
+    WeightGroups grp, int64_t block) {
     __shared__ uint32_t red[4];
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int g = t & 15, rg = t >> 4;
     // group (expert) of this block, then its block (bn, bk)
-    const int64_t e = blockIdx.x / grp.blocks, local = blockIdx.x - e * grp.blocks;
+    const int64_t e = block / grp.blocks, local = block - e * grp.blocks;
     w += e * grp.w;
     q += e * grp.q;
     scale += e * grp.s;
@@ -470,6 +481,59 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(
     }
 }
 
+__global__ __launch_bounds__(256) void quant_weight_kernel(
+    const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
+    WeightGroups grp) {
+    weight_body(w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp, (int64_t)blockIdx.x);
+}
+
+// ----------------------------------------------- activation + weight, one launch
+
+// A Linear layer's two operands in one launch: blocks [0, act_blocks) run
+// the 1x128 activation body, the rest the 128x128 weight body (block-uniform
+// branch). The arithmetic is that of the two kernels above, bit for bit; one
+// launch saves a launch gap and overlaps the two ramps and tails.
+struct ActArgs {
+    const uint16_t* x;
+    int64_t rows, slabs, ld_x;
+    uint8_t* q;
+    int64_t ld_q;
+    float* scale;
+    int64_t ld_s, units;
+};
+
+struct WeightArgs {
+    const uint16_t* w;
+    int64_t kblocks, ld_w;
+    uint8_t* q;
+    int64_t ld_q;
+    float* scale;
+    int64_t ld_s;
+    uint8_t* q_t;
+    int64_t ld_qt;
+    float* scale_t;
+    int64_t ld_st;
+};
+
+__global__ __launch_bounds__(256) void quant_act_weight_kernel(ActArgs a, int64_t act_blocks, WeightArgs wa,
+                                                               WeightGroups grp) {
+    const int64_t b = (int64_t)blockIdx.x;
+    // weight blocks first (they are the larger work items) unless they also
+    // write the transposed copy: measured, that case finishes sooner with the
+    // activation tiles first
+    const bool weight_first = wa.q_t == nullptr;
+    const bool is_weight = weight_first ? b < grp.blocks : b >= act_blocks;
+    const int64_t i = b - (is_weight ? (weight_first ? 0 : act_blocks) : (weight_first ? grp.blocks : 0));
+    if (is_weight)
+        weight_body(wa.w, wa.kblocks, wa.ld_w, wa.q, wa.ld_q, wa.scale, wa.ld_s, wa.q_t, wa.ld_qt, wa.scale_t,
+                    wa.ld_st, grp, i);
+    else
+        act_1x128_body<false>(a.x, a.rows, a.slabs, a.ld_x, a.q, a.ld_q, a.scale, a.ld_s, a.units, nullptr, 0,
+                              (int64_t)0, i);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------ launch
@@ -523,6 +587,42 @@ hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, i
     const int64_t blocks = tokens / 128 * cblocks;
     hipLaunchKernelGGL(retile_128x1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        q, ld_q, scale, ld_s, qt, ld_qt, scale_t, ld_st, cblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_weight(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                                   int64_t ld_q, float* scale, int64_t ld_s, const uint16_t* w, int64_t n,
+                                   int64_t k, int64_t ld_w, uint8_t* wq, int64_t ld_wq, float* ws, int64_t ld_ws,
+                                   uint8_t* wq_t, int64_t ld_wqt, float* ws_t, int64_t ld_wst,
+                                   hipStream_t stream) {
+    ActArgs a;
+    a.x = x;
+    a.rows = rows;
+    a.slabs = cols / 128;
+    a.ld_x = ld_x;
+    a.q = q;
+    a.ld_q = ld_q;
+    a.scale = scale;
+    a.ld_s = ld_s;
+    a.units = (rows + kActRowsPerWave - 1) / kActRowsPerWave * a.slabs;
+    const int64_t act_blocks = (a.units + kActWavesPerBlock - 1) / kActWavesPerBlock;
+    WeightArgs wa;
+    wa.w = w;
+    wa.kblocks = k / 128;
+    wa.ld_w = ld_w;
+    wa.q = wq;
+    wa.ld_q = ld_wq;
+    wa.scale = ws;
+    wa.ld_s = ld_ws;
+    wa.q_t = wq_t;
+    wa.ld_qt = ld_wqt;
+    wa.scale_t = ws_t;
+    wa.ld_st = ld_wst;
+    WeightGroups grp;
+    grp.blocks = n / 128 * wa.kblocks;
+    grp.w = grp.q = grp.s = grp.qt = grp.st = 0;
+    hipLaunchKernelGGL(quant_act_weight_kernel, dim3((unsigned)(act_blocks + grp.blocks)), dim3(256), 0, stream,
+                       a, act_blocks, wa, grp);
     return hipGetLastError();
 }
 

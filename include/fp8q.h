@@ -148,6 +148,25 @@ int fp8_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
                         hipStream_t stream);
 
 /*
+ * fp8_quantize_act_weight -- a Linear layer's two GEMM operands in one launch:
+ * fp8_quantize_act with FP8Q_TILE_1x128 on x, and fp8_quantize_weight on w
+ * (with the transposed copy when wq_t is given). Same groups, passages,
+ * layouts, alignment rules and results, bit for bit. One launch instead of
+ * two saves a launch gap and overlaps the two kernels' ramps and tails.
+ * Either operand may be empty (rows or cols == 0; n or k == 0): it is then
+ * skipped and its pointers are not read. x and w may overlap (both are only
+ * read); no output may overlap another, since the two halves of the launch
+ * run concurrently.
+ * Errors: those of the two calls (FP8Q_ERR_NULL, FP8Q_ERR_SHAPE,
+ *         FP8Q_ERR_ALIGN, FP8Q_ERR_HIP).
+ */
+int fp8_quantize_act_weight(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *q,
+                            int64_t ld_q, float *scale, int64_t ld_s, const uint16_t *w, int64_t n,
+                            int64_t k, int64_t ld_w, uint8_t *wq, int64_t ld_wq, float *wscale,
+                            int64_t ld_ws, uint8_t *wq_t, int64_t ld_wqt, float *wscale_t, int64_t ld_wst,
+                            hipStream_t stream);
+
+/*
  * fp8_quantize_weight_grouped -- fp8_quantize_weight over several weight
  * matrices of one shape (say the experts of an MoE layer) in one launch.
  *

@@ -291,6 +291,28 @@ def test_gemm_tensor_validation(lib):
     assert _tg(lib, c=A16c + 4) == ERR_ALIGN
 
 
+def _aw(lib, x=A16, rows=256, cols=512, ld_x=512, q=A16b, ld_q=512, s=A4, ld_s=256, w=A16c, n=256, k=384,
+        ld_w=384, wq=A16 + 0x100000, ld_wq=384, ws=A4 + 0x1000, ld_ws=3, wqt=0, ld_wqt=0, wst=0, ld_wst=0):
+    return lib.fp8_quantize_act_weight(x, rows, cols, ld_x, q, ld_q, s, ld_s, w, n, k, ld_w, wq, ld_wq, ws, ld_ws,
+                                       wqt, ld_wqt, wst, ld_wst, None)
+
+
+def test_quantize_act_weight_validation(lib):
+    assert _aw(lib, rows=0, n=0) == OK                           # both empty: nothing launched
+    assert _aw(lib, rows=-1) == ERR_SHAPE
+    assert _aw(lib, x=0) == ERR_NULL
+    assert _aw(lib, wq=0) == ERR_NULL
+    assert _aw(lib, wqt=A16c + 0x200000, ld_wqt=256) == ERR_NULL  # q_t without scale_t
+    assert _aw(lib, cols=500, ld_x=512, ld_q=512) == ERR_SHAPE
+    assert _aw(lib, n=200) == ERR_SHAPE
+    assert _aw(lib, ld_s=255) == ERR_SHAPE
+    assert _aw(lib, ld_ws=2) == ERR_SHAPE
+    assert _aw(lib, q=A16b + 8) == ERR_ALIGN
+    assert _aw(lib, ld_wq=392) == ERR_ALIGN
+    # an empty side is not checked (its pointers are not read)
+    assert _aw(lib, rows=0, n=0, x=0, w=0) == OK
+
+
 def _wg(lib, groups=3, w=A16, n=256, k=384, ld_w=384, sw=256 * 384, q=A16b, ld_q=384, sq=256 * 384,
         s=A4, ld_s=3, ss=6, qt=A16c, ld_qt=256, sqt=384 * 256, st=A4 + 0x1000, ld_st=2, sst=6):
     return lib.fp8_quantize_weight_grouped(groups, w, n, k, ld_w, sw, q, ld_q, sq, s, ld_s, ss,
@@ -316,7 +338,8 @@ def test_quantize_weight_grouped_validation(lib):
 
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
-                 "fp8_quantize_weight_grouped", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
+                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_gemm", "fp8_grouped_gemm",
+                 "fp8_grouped_gemm_wgrad",
                  "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))
 

@@ -277,3 +277,96 @@ def test_weight_grouped_moe_experts_sampled():
     """The 32 MoE expert weights [32][4096][7168] in one launch, with their
     transposed copies (the grouped Dgrad operand); experts 0, 17, 31 checked."""
     _check_grouped_weights(wl.grouped_fprop()["w"], "MoE", experts=(0, 17, 31))
+
+
+# ------------------------------------ activation and weight in one launch
+
+def _check_act_weight(x_bits, w_bits, what, transposed=True):
+    """fp8_quantize_act_weight equals the oracle's 1x128 and 128x128
+    quantizations (and the transposed copy) bit for bit."""
+    out = fq.fp8_quantize_act_weight(dev_bf16(x_bits), dev_bf16(w_bits), transposed=transposed)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act_1x128(x_bits)
+    assert_bits_equal(host_f32(out[1]), s_ref, what + " act scales")
+    assert_bits_equal(host_codes(out[0]), q_ref, what + " act codes")
+    wq_ref, ws_ref = oracle.quant_weight_128x128(w_bits)
+    assert_bits_equal(host_f32(out[3]), ws_ref, what + " weight scales")
+    assert_bits_equal(host_codes(out[2]), wq_ref, what + " weight codes")
+    if transposed:
+        assert_bits_equal(host_f32(out[5]), np.ascontiguousarray(ws_ref.T), what + " transposed scales")
+        assert_bits_equal(host_codes(out[4]), np.ascontiguousarray(wq_ref.T), what + " transposed codes")
+
+
+@pytest.mark.parametrize("rows", [1, 17, 129, 1000])
+def test_act_weight_ragged_rows(rows):
+    x = wl.activation(1, "tiny_fprop", 60, rows, 384, 100.0)
+    w = wl.weight(1, "tiny_fprop", 61, 256, 384)
+    _check_act_weight(x, w, "rows=%d" % rows, transposed=rows != 17)
+
+
+def test_act_weight_edge_tiles_and_blocks():
+    rng = np.random.default_rng(62)
+    e = _edge_rows(rng)
+    x = np.concatenate([e, wl.activation(1, "tiny_fprop", 63, e.shape[0], 128, None)], axis=1)
+    w = wl.weight(1, "tiny_fprop", 64, 384, 256)
+    w[0:128, 0:128] = 0
+    w[128:256, 128:256] = rng.integers(1, 0x80, (128, 128)).astype(np.uint16)
+    w[256, 7] = 0x7F7F
+    _check_act_weight(x, w, "edge")
+
+
+@pytest.mark.parametrize("name,transposed", [("tiny_fprop", True), ("dense_fprop", False), ("dense_fprop", True),
+                                              ("dgrad", True)])
+def test_act_weight_equals_separate_launches_full_size(name, transposed):
+    """At the Linear layer's full size the one launch writes exactly what the
+    two separate launches write (each of which the tests above pin to the
+    oracle at full size). Both block orders: weight blocks first without
+    the transposed copy, activation tiles first with it."""
+    g = {"tiny_fprop": wl.tiny_fprop, "dense_fprop": wl.dense_fprop, "dgrad": wl.dgrad}[name]()
+    x, w = dev_bf16(g["dy" if name == "dgrad" else "x"]), dev_bf16(g["w"])
+    got = fq.fp8_quantize_act_weight(x, w, transposed=transposed)
+    q, s = fq.fp8_quantize_act(x)
+    ref = fq.fp8_quantize_weight(w, transposed=transposed)
+    torch.cuda.synchronize()
+    for a, b, tag in zip(got, (q, s) + tuple(ref), ("q", "scale", "wq", "wscale", "wq_t", "wscale_t")):
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float8_e4m3fn else a.view(torch.int32),
+                           b.view(torch.uint8) if b.dtype == torch.float8_e4m3fn else b.view(torch.int32)), tag
+
+
+def test_act_weight_one_side_empty():
+    x = wl.activation(1, "tiny_fprop", 65, 40, 256, 100.0)
+    w = wl.weight(1, "tiny_fprop", 66, 128, 256)
+    empty_x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    empty_w = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    _, _, wq, ws = fq.fp8_quantize_act_weight(empty_x, dev_bf16(w))
+    q, s, _, _ = fq.fp8_quantize_act_weight(dev_bf16(x), empty_w)
+    torch.cuda.synchronize()
+    wq_ref, ws_ref = oracle.quant_weight_128x128(w)
+    assert_bits_equal(host_codes(wq), wq_ref, "weight alone codes")
+    assert_bits_equal(host_f32(ws), ws_ref, "weight alone scales")
+    q_ref, s_ref = oracle.quant_act_1x128(x)
+    assert_bits_equal(host_codes(q), q_ref, "act alone codes")
+    assert_bits_equal(host_f32(s), s_ref, "act alone scales")
+
+
+def test_act_weight_padded_leading_dimensions():
+    x = wl.activation(1, "tiny_fprop", 67, 70, 384, 100.0)
+    w = wl.weight(1, "tiny_fprop", 68, 256, 384)
+    xd = torch.zeros((70, 512), dtype=torch.bfloat16, device="cuda")
+    xd[:, :384] = dev_bf16(x)
+    wd = torch.zeros((256, 400), dtype=torch.bfloat16, device="cuda")
+    wd[:, :384] = dev_bf16(w)
+    q = torch.full((70, 400), 0x5A, dtype=torch.uint8, device="cuda")[:, :384]
+    s = torch.full((3, 80), 7.0, device="cuda")[:, :70]
+    wq = torch.full((256, 416), 0x5A, dtype=torch.uint8, device="cuda")[:, :384]
+    ws = torch.full((2, 5), 7.0, device="cuda")[:, :3]
+    fq.fp8_quantize_act_weight(xd[:, :384], wd[:, :384], q=q, scale=s, wq=wq, wscale=ws)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act_1x128(x)
+    wq_ref, ws_ref = oracle.quant_weight_128x128(w)
+    assert_bits_equal(host_codes(q.contiguous()), q_ref, "padded act codes")
+    assert_bits_equal(host_f32(s.contiguous()), s_ref, "padded act scales")
+    assert_bits_equal(host_codes(wq.contiguous()), wq_ref, "padded weight codes")
+    assert_bits_equal(host_f32(ws.contiguous()), ws_ref, "padded weight scales")
+    assert torch.all(q.as_strided((70, 16), (400, 1), q.storage_offset() + 384) == 0x5A)
+    assert torch.all(wq.as_strided((256, 32), (416, 1), wq.storage_offset() + 384) == 0x5A)
