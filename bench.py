@@ -443,6 +443,42 @@ class Workload:
                 self.done.record(s)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (reported with the oracle timing)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def tiny_one_thread(min_seconds: float = 1.0) -> dict:
+    """The oracle's whole Tiny Fprop step (128x256x512) on one thread: every
+    OpenMP and BLAS pool limited to 1 for the duration."""
+    import oracle
+    import workloads as wl
+    from threadpoolctl import threadpool_limits
+    d = wl.tiny_fprop()
+    m, k = d["x"].shape
+    n = d["w"].shape[0]
+    with threadpool_limits(limits=1):
+        steps, t0 = 0, time.perf_counter()
+        while True:
+            a_q, a_s = oracle.quant_act_1x128(d["x"])
+            b_q, b_s = oracle.quant_weight_128x128(d["w"])
+            oracle.gemm(a_q, a_s, b_q, b_s, "block")
+            steps += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_seconds:
+                break
+    return {"threads": 1, "steps": steps, "ms_per_step": round(1e3 * dt / steps, 4),
+            "gflops": round(2.0 * m * n * k * steps / dt / 1e9, 4)}
+
+
 def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 200) -> dict:
     """The oracle, as it stands, on the same Dense Fprop inputs (the whole step)."""
     import oracle
@@ -477,6 +513,8 @@ def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 2
         "sample": "%d full steps of the workload (X %dx%d 1x128 quantize, W %dx%d 128x128 "
                   "quantize, float64 dequantize + GEMM): scalar C quantizers with OpenMP and "
                   "numpy float64 matmul" % (steps, m, k, n, k),
+        "cpu_model": cpu_model(),
+        "tiny_fprop_one_thread": tiny_one_thread(),
     }
 
 

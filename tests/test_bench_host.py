@@ -104,3 +104,15 @@ def test_kernel_source_digest_ignores_comments_only(tmp_path):
     (c / "k.hip").write_text("// header\nint f(int x) {\n    return x + 2;  // one\n}\n")
     assert bench.kernel_source_digest(str(a)) == bench.kernel_source_digest(str(b))
     assert bench.kernel_source_digest(str(a)) != bench.kernel_source_digest(str(c))
+
+
+def test_cpu_baseline_extras_report_model_and_one_thread_tiny():
+    """The oracle timing names the host CPU and times the Tiny step on one
+    thread, leaving the thread pools as they were afterwards."""
+    from threadpoolctl import threadpool_info
+    bench.tiny_one_thread(min_seconds=0.0)  # loads the oracle's pools before they are recorded
+    before = sorted((p["user_api"], p["num_threads"]) for p in threadpool_info())
+    assert bench.cpu_model()
+    r = bench.tiny_one_thread(min_seconds=0.05)
+    assert r["threads"] == 1 and r["steps"] >= 1 and r["ms_per_step"] > 0 and r["gflops"] > 0
+    assert sorted((p["user_api"], p["num_threads"]) for p in threadpool_info()) == before
