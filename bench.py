@@ -101,6 +101,9 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one device copy of this size first (counter calibration)")
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON)
+    ap.add_argument("--counter-table", metavar="CSV",
+                    help="print a markdown table of a rocprofv3 counter CSV of this script, "
+                         "per kernel of the step")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter CSVs of this script into --traffic-json")
     return ap.parse_args()
@@ -577,6 +580,55 @@ def pmc_summary(fetch_csv: str, write_csv: str, config: str, probe_mib: int, out
     return res
 
 
+MI355X_SIMDS = 256 * 4   # 256 CUs x 4 SIMDs
+PEAK_CLOCK_HZ = 2.4e9
+
+
+def counter_table(path: str, wl_obj: Workload) -> str:
+    """Markdown table of one rocprofv3 counter CSV of this script: for each
+    kernel of the step, its dispatch count, mean duration and the mean of every
+    counter over its dispatches. Derived columns where their counters are
+    present:
+    * MFMA busy at peak clock: SQ_VALU_MFMA_BUSY_CYCLES (MFMA pipe cycles,
+      summed over the SIMDs) / (SIMDs x duration x 2.4 GHz);
+    * waiting: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share of wave cycles
+      spent in s_waitcnt (SQ_WAIT_INST_LDS likewise, waits on LDS)."""
+    disp = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(int(r["Dispatch_Id"]), {
+                "name": r["Kernel_Name"], "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), "c": {}})
+            d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    counters = sorted({c for d in disp.values() for c in d["c"]})
+    step_labels = [ln.label for ln in wl_obj.launches]
+    head = ["kernel", "dispatches", "mean us"] + counters
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in counters:
+        derived.append("MFMA busy at 2.4 GHz")
+    if "SQ_WAIT_INST_ANY" in counters and "SQ_WAVE_CYCLES" in counters:
+        derived.append("waiting (s_waitcnt)")
+    if "SQ_WAIT_INST_LDS" in counters and "SQ_WAVE_CYCLES" in counters:
+        derived.append("waiting on LDS")
+    out = ["| " + " | ".join(head + derived) + " |", "|" + "---|" * (len(head) + len(derived))]
+    for label, frag in KERNEL_NAMES.items():
+        if label not in step_labels:
+            continue
+        ds = [d for d in disp.values() if frag in d["name"]]
+        if not ds:
+            continue
+        ns = sum(d["ns"] for d in ds) / len(ds)
+        mean = {c: sum(d["c"].get(c, 0.0) for d in ds) / len(ds) for c in counters}
+        row = [label, str(len(ds)), "%.2f" % (ns / 1e3)] + ["%.0f" % mean[c] for c in counters]
+        if "MFMA busy at 2.4 GHz" in derived:
+            row.append("%.3f" % (mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (MI355X_SIMDS * ns * 1e-9 * PEAK_CLOCK_HZ)))
+        if "waiting (s_waitcnt)" in derived:
+            row.append("%.3f" % (mean["SQ_WAIT_INST_ANY"] / max(mean["SQ_WAVE_CYCLES"], 1.0)))
+        if "waiting on LDS" in derived:
+            row.append("%.3f" % (mean["SQ_WAIT_INST_LDS"] / max(mean["SQ_WAVE_CYCLES"], 1.0)))
+        out.append("| " + " | ".join(row) + " |")
+    return "\n".join(out)
+
+
 def stored_traffic(path: str, config: str):
     """Counter figures for this config, or None when absent or taken on other kernels."""
     try:
@@ -625,6 +677,13 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.counter_table:
+        wl_obj = Workload(args.config, 1) if torch.cuda.is_available() else None
+        if wl_obj is None:
+            raise SystemExit("--counter-table needs the workload shapes, which are built on the GPU")
+        print(counter_table(args.counter_table, wl_obj))
+        return
 
     if args.pmc_summary:
         wl_obj = Workload(args.config, 1) if torch.cuda.is_available() else None

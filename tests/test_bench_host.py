@@ -116,3 +116,26 @@ def test_cpu_baseline_extras_report_model_and_one_thread_tiny():
     r = bench.tiny_one_thread(min_seconds=0.05)
     assert r["threads"] == 1 and r["steps"] >= 1 and r["ms_per_step"] > 0 and r["gflops"] > 0
     assert sorted((p["user_api"], p["num_threads"]) for p in threadpool_info()) == before
+
+
+def test_counter_table_means_and_derived_columns(tmp_path):
+    """Per step kernel: means over its dispatches, MFMA busy at the peak clock
+    and the s_waitcnt share; kernels outside the step are left out."""
+    p = tmp_path / "c.csv"
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for did, name, t in ((1, "copyBuffer", 1000), (2, "void fp8q::gemm_kernel<256>(...)", 100000),
+                         (3, "void fp8q::gemm_kernel<256>(...)", 100000)):
+        for c, v in (("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 2.4e9 * 100e-6 / 2), ("SQ_WAIT_INST_ANY", 30.0),
+                     ("SQ_WAVE_CYCLES", 120.0)):
+            rows.append([did, name, c, v, 0, t])
+    with open(p, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        w.writerows(rows)
+
+    class W:
+        launches = [bench.Launch("gemm", None, 1.0)]
+    table = bench.counter_table(str(p), W()).splitlines()
+    assert len(table) == 3 and table[2].startswith("| gemm | 2 | 100.00 |")
+    assert table[2].rstrip(" |").endswith("0.500 | 0.250")
