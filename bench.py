@@ -71,12 +71,14 @@ def _code_only(text: str) -> str:
 
 
 def kernel_source_digest(csrc: str | None = None) -> str:
-    """Digest of the HIP sources, comments and blank lines left out; stored
-    counter figures are valid only for the kernels they were taken on."""
+    """Digest of the kernel sources (the .hip files, with their launchers, and
+    the headers they include), comments and blank lines left out; stored
+    counter figures are valid only for the kernels they were taken on. The
+    C ABI's host-side argument checks (.cpp) are not part of it."""
     h = hashlib.sha256()
     csrc = csrc or os.path.join(ROOT, "fine_grained_fp8_quantize_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h")):
             with open(os.path.join(csrc, name), encoding="utf-8") as f:
                 h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]

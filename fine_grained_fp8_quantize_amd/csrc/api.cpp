@@ -25,6 +25,17 @@ int hip_status(hipError_t e) {
 // A grid of more than 2^31 - 1 blocks is not launchable.
 bool grid_ok(int64_t blocks) { return blocks >= 0 && blocks <= 0x7FFFFFFFLL; }
 
+// Bytes [lo, hi) a row-major rows x cols matrix of elem-byte elements with
+// leading dimension ld occupies (rows, cols > 0).
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
 }  // namespace
 
 extern "C" {
@@ -126,6 +137,17 @@ int fp8_quantize_act_weight(const uint16_t* x, int64_t rows, int64_t cols, int64
         if (wq_t && (!aligned(wq_t, 16) || !aligned(wscale_t, 4) || ld_wqt % 16 != 0)) return FP8Q_ERR_ALIGN;
     }
     if (!act && !wgt) return FP8Q_OK;
+    if (act && wgt) {
+        // the two halves of the launch run concurrently: no output of one may
+        // share a byte with an output of the other
+        const Span a_out[2] = {span(q, rows, cols, ld_q, 1), span(scale, cols / 128, rows, ld_s, 4)};
+        const Span w_out[4] = {span(wq, n, k, ld_wq, 1), span(wscale, n / 128, k / 128, ld_ws, 4),
+                               wq_t ? span(wq_t, k, n, ld_wqt, 1) : Span{0, 0},
+                               wq_t ? span(wscale_t, k / 128, n / 128, ld_wst, 4) : Span{0, 0}};
+        for (const Span& x : a_out)
+            for (const Span& y : w_out)
+                if (overlap(x, y)) return FP8Q_ERR_SHAPE;
+    }
     const int64_t act_blocks = act ? (rows + 15) / 16 * (cols / 128) / 4 + 1 : 0;
     if (!grid_ok(act_blocks + (wgt ? n / 128 * (k / 128) : 0))) return FP8Q_ERR_SHAPE;
     // an empty operand is skipped: its block range is empty

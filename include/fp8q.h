@@ -155,10 +155,12 @@ int fp8_quantize_weight(const uint16_t *w, int64_t n, int64_t k, int64_t ld_w,
  * two saves a launch gap and overlaps the two kernels' ramps and tails.
  * Either operand may be empty (rows or cols == 0; n or k == 0): it is then
  * skipped and its pointers are not read. x and w may overlap (both are only
- * read); no output may overlap another, since the two halves of the launch
- * run concurrently.
+ * read). The two halves of the launch run concurrently, so no output of the
+ * activation (q, scale) may share a byte with an output of the weight (wq,
+ * wscale, wq_t, wscale_t).
  * Errors: those of the two calls (FP8Q_ERR_NULL, FP8Q_ERR_SHAPE,
- *         FP8Q_ERR_ALIGN, FP8Q_ERR_HIP).
+ *         FP8Q_ERR_ALIGN, FP8Q_ERR_HIP); FP8Q_ERR_SHAPE also when an
+ *         activation output overlaps a weight output.
  */
 int fp8_quantize_act_weight(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t *q,
                             int64_t ld_q, float *scale, int64_t ld_s, const uint16_t *w, int64_t n,

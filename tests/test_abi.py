@@ -311,6 +311,12 @@ def test_quantize_act_weight_validation(lib):
     assert _aw(lib, ld_wq=392) == ERR_ALIGN
     # an empty side is not checked (its pointers are not read)
     assert _aw(lib, rows=0, n=0, x=0, w=0) == OK
+    # outputs of the two halves must not overlap (checked before any launch)
+    assert _aw(lib, wq=A16b + 0x100) == ERR_SHAPE                   # codes over codes
+    assert _aw(lib, ws=A4 + 8) == ERR_SHAPE                         # scales over scales
+    assert _aw(lib, ws=A16b + 0x1000) == ERR_SHAPE                  # weight scales over act codes
+    assert _aw(lib, wqt=A4 + 0x800, ld_wqt=256, wst=A4 + 0x2000, ld_wst=2) == ERR_SHAPE  # Wt codes over act scales
+    assert _aw(lib, wqt=A16c + 0x200000, ld_wqt=256, wst=A16b, ld_wst=2) == ERR_SHAPE    # Wt scales over act codes
 
 
 def _wg(lib, groups=3, w=A16, n=256, k=384, ld_w=384, sw=256 * 384, q=A16b, ld_q=384, sq=256 * 384,

@@ -104,6 +104,9 @@ def test_kernel_source_digest_ignores_comments_only(tmp_path):
     (c / "k.hip").write_text("// header\nint f(int x) {\n    return x + 2;  // one\n}\n")
     assert bench.kernel_source_digest(str(a)) == bench.kernel_source_digest(str(b))
     assert bench.kernel_source_digest(str(a)) != bench.kernel_source_digest(str(c))
+    # host-side argument checks are not kernel code
+    (a / "api.cpp").write_text("int check(int n) { return n > 0; }\n")
+    assert bench.kernel_source_digest(str(a)) == bench.kernel_source_digest(str(b))
 
 
 def test_cpu_baseline_extras_report_model_and_one_thread_tiny():
