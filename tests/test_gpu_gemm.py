@@ -114,6 +114,36 @@ def test_row_scaled_ragged(m, n, tokens, out):
     _check_full(a_q, a_s, b_q, b_s, "row", out, "row m=%d n=%d k=%d %s" % (m, n, tokens, out))
 
 
+@pytest.mark.parametrize("kind", ["block", "row"])
+def test_padded_leading_dims_and_scale_strides(kind):
+    """Operands, scales and output as padded views (lda, ldb > k; ld_as > m;
+    ld_bs past the scale row; ldc > n): the result matches the oracle and
+    nothing outside the output window is written."""
+    m, n, k = 200, 256, 384
+    if kind == "block":
+        a_q, a_s = oracle.quant_act_1x128(wl.activation(4, "tiny_fprop", 96, m, k, 50.0))
+        b_q, b_s = oracle.quant_weight_128x128(wl.weight(4, "tiny_fprop", 97, n, k))
+    else:
+        a_q, a_s = oracle.quant_act_128x1(wl.activation(4, "wgrad", 96, k, m + 56, None))
+        b_q, b_s = oracle.quant_act_128x1(wl.activation(4, "wgrad", 97, k, n, 50.0))
+        a_q, a_s = a_q[:m], a_s[:, :m]   # rows 0..m-1 of the transposed operand
+    ap = torch.zeros((m, k + 32), dtype=torch.uint8, device="cuda")
+    bp = torch.zeros((n, k + 64), dtype=torch.uint8, device="cuda")
+    ap[:, :k] = dev_codes(np.ascontiguousarray(a_q)).view(torch.uint8)
+    bp[:, :k] = dev_codes(b_q).view(torch.uint8)
+    asp = torch.full((a_s.shape[0], m + 24), 7.0, device="cuda")
+    asp[:, :m] = dev_f32(np.ascontiguousarray(a_s))
+    bsp = torch.full((b_s.shape[0], b_s.shape[1] + 5), 7.0, device="cuda")
+    bsp[:, :b_s.shape[1]] = dev_f32(b_s)
+    c = torch.full((m, n + 8), float("nan"), dtype=torch.bfloat16, device="cuda")
+    fq.fp8_gemm(ap[:, :k], asp[:, :m], bp[:, :k], bsp[:, :b_s.shape[1]], kind, torch.bfloat16, out=c[:, :n])
+    torch.cuda.synchronize()
+    got = host_out(c)
+    assert np.all(np.isnan(got[:, n:])), "columns past n written"
+    assert_gemm_close(got[:, :n], oracle.gemm(np.ascontiguousarray(a_q), np.ascontiguousarray(a_s), b_q, b_s, kind),
+                      "padded %s" % kind)
+
+
 def test_k_zero_writes_zeros():
     """K = 0: the product is the zero matrix; every element of the window is
     written and nothing is read from the (unused) operands."""
