@@ -362,3 +362,41 @@ def test_grouped_dgrad_moe_config_one_weight_launch_sampled():
 def test_grouped_dgrad_moe_config_sampled():
     """MoE up-projection Dgrad: 32 experts, dY [rows][4096] -> dX [rows][7168]."""
     _grouped_dgrad_case(wl.moe_rows(0), n_out=4096, k_in=7168, sample=4)
+
+
+def test_grouped_padded_views_and_strides():
+    """Grouped Fprop with every operand a padded view: lda > k, ldb > k with
+    expert stride > n * ldb, block scales with ld_bs > k/128 and a padded
+    expert stride, ldc > n. Matches the oracle; nothing outside the output
+    window is written."""
+    rows = np.array([130, 0, 77, 256], dtype=np.int64)
+    n, k = 256, 384
+    g = wl.grouped_fprop(5, n=n, k=k, experts=len(rows), rows=rows)
+    offsets = g["offsets"]
+    a_q, a_s = oracle.quant_act_1x128(g["x"])
+    E, m_total = len(rows), a_q.shape[0]
+    b_q = np.empty((E, n, k), np.uint8)
+    b_s = np.empty((E, n // 128, k // 128), np.float32)
+    for e in range(E):
+        b_q[e], b_s[e] = oracle.quant_weight_128x128(g["w"][e])
+    ap = torch.zeros((m_total, k + 48), dtype=torch.uint8, device="cuda")
+    ap[:, :k] = dev_codes(a_q)
+    asp = torch.full((k // 128, m_total + 40), 7.0, device="cuda")
+    asp[:, :m_total] = dev_f32(a_s)
+    bp = torch.zeros((E, n + 16, k + 64), dtype=torch.uint8, device="cuda")
+    bp[:, :n, :k] = dev_codes(b_q)
+    bsp = torch.full((E, n // 128 + 1, k // 128 + 3), 7.0, device="cuda")
+    bsp[:, :n // 128, :k // 128] = dev_f32(b_s)
+    c = torch.full((m_total, n + 24), float("nan"), dtype=torch.bfloat16, device="cuda")
+    off_d = torch.from_numpy(offsets.astype(np.int32)).cuda()
+    rows_d = torch.from_numpy(rows.astype(np.int32)).cuda()
+    fq.fp8_grouped_gemm(off_d, rows_d, ap[:, :k], asp[:, :m_total], bp[:, :n, :k], bsp[:, :n // 128, :k // 128],
+                        torch.bfloat16, out=c[:, :n])
+    torch.cuda.synchronize()
+    got = host_out(c)
+    assert np.all(np.isnan(got[:, n:])), "columns past n written"
+    ref = oracle.grouped_gemm(offsets, rows, a_q, a_s, b_q, b_s)
+    real = np.concatenate([np.arange(offsets[e], offsets[e] + rows[e]) for e in range(E)]).astype(np.int64)
+    assert_gemm_close(got[real, :n], ref[real], "grouped padded views")
+    pad = np.setdiff1d(np.arange(m_total), real)
+    assert np.all(got[pad, :n] == 0), "padding rows not zero"

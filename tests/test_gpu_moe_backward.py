@@ -129,3 +129,41 @@ def test_grouped_wgrad_from_dispatch_cache_moe_sampled():
     dW [32][4096][7168]; experts 0, 9 and 31, 24 rows each."""
     _wgrad_from_dispatch_cache(wl.moe_rows(0), m=4096, k=7168, tokens=8192, top_k=8,
                                sample_experts=(0, 9, 31), sample_rows=24)
+
+
+def test_grouped_wgrad_padded_output_and_operand_views():
+    """Operands as padded views (lda, ldb past the token count; scale rows past
+    m and n) and dW as a padded [E][m][n] view (ldc > n, expert stride >
+    m * ldc): every expert matches the oracle and nothing outside the
+    windows is written."""
+    rows = [5, 0, 300]
+    m, n = 256, 136
+    dy, off = _packed(rows, m, 102, grad=True)
+    x, _ = _packed(rows, n, 103, grad=False)
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    b_q, b_s = oracle.quant_act_128x1(x)
+    kt = a_q.shape[1]
+    ap = torch.zeros((m, kt + 32), dtype=torch.uint8, device="cuda")
+    ap[:, :kt] = torch.from_numpy(a_q).cuda()
+    bp = torch.zeros((n, kt + 64), dtype=torch.uint8, device="cuda")
+    bp[:, :kt] = torch.from_numpy(b_q).cuda()
+    asp = torch.full((kt // 128, m + 8), 7.0, device="cuda")
+    asp[:, :m] = torch.from_numpy(a_s).cuda()
+    bsp = torch.full((kt // 128, n + 12), 7.0, device="cuda")
+    bsp[:, :n] = torch.from_numpy(b_s).cuda()
+    E = len(rows)
+    c = torch.full((E, m + 3, n + 8), float("nan"), dtype=torch.float32, device="cuda")
+    off_d = torch.from_numpy(off.astype(np.int32)).cuda()
+    fq.fp8_grouped_gemm_wgrad(off_d, ap[:, :kt], asp[:, :m], bp[:, :kt], bsp[:, :n], torch.float32,
+                              out=c[:, :m, :n])
+    torch.cuda.synchronize()
+    got = c.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(got[:, m:, :])) and np.all(np.isnan(got[:, :, n:])), "written outside the windows"
+    for e in range(E):
+        t0, t1 = int(off[e]), int(off[e + 1])
+        if t1 == t0:
+            assert np.all(got[e, :m, :n] == 0), "expert %d: empty segment must give zeros" % e
+            continue
+        ref = oracle.gemm(np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
+                          np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]), "row")
+        assert_gemm_close(got[e, :m, :n], ref, "padded wgrad expert %d" % e)
