@@ -1,0 +1,90 @@
+"""The library on the caller's streams: calls hold no state, so work enqueued
+on two streams at once gives the same bytes as the same work done one call
+after another, and a quantize + GEMM step captured into a HIP graph replays
+to the eager result (the kernels use no memset and no atomics).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import fine_grained_fp8_quantize_amd as fq
+import workloads as wl
+from gpu_util import dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _step(x, w, bufs):
+    """One Fprop step into preallocated buffers: X and W in one launch, then the GEMM."""
+    q, s, wq, ws, y = bufs
+    fq.fp8_quantize_act_weight(x, w, q=q, scale=s, wq=wq, wscale=ws)
+    fq.fp8_gemm(q, s, wq, ws, "block", torch.bfloat16, out=y)
+
+
+def _bufs(m, n, k):
+    return (torch.empty((m, k), dtype=torch.uint8, device="cuda"),
+            torch.empty((k // 128, m), dtype=torch.float32, device="cuda"),
+            torch.empty((n, k), dtype=torch.uint8, device="cuda"),
+            torch.empty((n // 128, k // 128), dtype=torch.float32, device="cuda"),
+            torch.empty((m, n), dtype=torch.bfloat16, device="cuda"))
+
+
+def _same(a, b):
+    """Bit-equal (any dtype, compared as bytes)."""
+    return torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_two_streams_at_once_match_serial():
+    m, n, k = 1024, 512, 2048
+    xs = [dev_bf16(wl.activation(6, "tiny_fprop", 110 + i, m, k, 50.0)) for i in range(2)]
+    ws = [dev_bf16(wl.weight(6, "tiny_fprop", 120 + i, n, k)) for i in range(2)]
+    serial = [_bufs(m, n, k) for _ in range(2)]
+    for i in range(2):
+        _step(xs[i], ws[i], serial[i])
+    torch.cuda.synchronize()
+    conc = [_bufs(m, n, k) for _ in range(2)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    start = torch.cuda.Event()
+    start.record()
+    for rep in range(3):          # several rounds, interleaved across the streams
+        for i in range(2):
+            streams[i].wait_event(start)
+            with torch.cuda.stream(streams[i]):
+                _step(xs[i], ws[i], conc[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        for a, b, what in zip(conc[i], serial[i], ("q", "scale", "wq", "wscale", "y")):
+            assert _same(a, b), "stream %d: %s differs from the serial run" % (i, what)
+
+
+def test_graph_replay_matches_eager():
+    m, n, k = 512, 256, 1024
+    inputs = [dev_bf16(wl.activation(7, "tiny_fprop", 130 + i, m, k, 50.0)) for i in range(3)]
+    w = dev_bf16(wl.weight(7, "tiny_fprop", 140, n, k))
+    x = torch.empty_like(inputs[0])
+    x.copy_(inputs[0])
+    bufs = _bufs(m, n, k)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        _step(x, w, bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _step(x, w, bufs)
+    torch.cuda.synchronize()
+    ref = _bufs(m, n, k)
+    for rep in range(6):
+        src = inputs[rep % 3]
+        x.copy_(src)                 # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _step(src, w, ref)           # the eager result for the same input
+        torch.cuda.synchronize()
+        for a, b, what in zip(bufs, ref, ("q", "scale", "wq", "wscale", "y")):
+            assert _same(a, b), "replay %d: %s differs from eager" % (rep, what)
+    assert not np.isnan(bufs[4].float().cpu().numpy()).any()
