@@ -56,6 +56,7 @@ KERNEL_NAMES = {
     "quant_act_128x1": "quant_act_128x1_kernel",
     "quant_weight": "quant_weight_kernel",
     "quant_act_weight": "quant_act_weight_kernel",
+    "quant_act_128x1_pair": "quant_act_128x1_pair_kernel",
     "quant_mx": "quant_mx_1x32_kernel",
     "retile_128x1": "retile_128x1_kernel",
     "gemm": "gemm_kernel",
@@ -235,10 +236,10 @@ class Workload:
             y = empty((n_out, k_in), f32)
             self.flops = 2.0 * n_out * k_in * t
             self.launches = [
-                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
-                       act_bytes(t, n_out)),
-                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(X[r], "128x1", q=bq, scale=bs),
-                       act_bytes(t, k_in)),
+                # dY and X in 128x1 token tiles, one launch
+                Launch("quant_act_128x1_pair", lambda r: fq.fp8_quantize_act_128x1_pair(
+                    DY[r], X[r], q0=aq, scale0=as_, q1=bq, scale1=bs),
+                       act_bytes(t, n_out) + act_bytes(t, k_in)),
                 Launch("gemm", lambda r: fq.fp8_gemm(aq, as_, bq, bs, "row", f32, out=y),
                        gemm_bytes(n_out, k_in, t, k_in * (t // 128), 4, n_out), self.flops),
             ]

@@ -25,6 +25,8 @@ Layouts (row-major, K contiguous for GEMM operands):
   launch, optionally with per-expert transposed copies.
 * ``fp8_quantize_act_weight(x, w)`` -- a Linear layer's activation (1x128)
   and weight (128x128, optionally transposed too) in one launch.
+* ``fp8_quantize_act_128x1_pair(dy, x)`` -- the two Wgrad operands in 128x1
+  token tiles in one launch.
 * ``fp8_quantize_act_scatter(x, dst_rows, m_total)`` -- quantize each token
   once and scatter its codes and scales to its expert-sorted rows.
 * ``fp8_grouped_gemm_wgrad(offsets, a, a_scale, b, b_scale)`` -- per-expert
@@ -52,6 +54,7 @@ __all__ = [
     "fp8_quantize_weight",
     "fp8_quantize_weight_grouped",
     "fp8_quantize_act_weight",
+    "fp8_quantize_act_128x1_pair",
     "fp8_gemm",
     "fp8_grouped_gemm",
     "fp8_grouped_gemm_wgrad",
@@ -101,6 +104,7 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64, p]
     L.fp8_quantize_act_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, i64, i64, p, i64, p, i64,
                                           p, i64, p, i64, p]
+    L.fp8_quantize_act_128x1_pair.argtypes = [i64, p, i64, i64, p, i64, p, i64, p, i64, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight_grouped.argtypes = [i32, p, i64, i64, i64, i64, p, i64, i64, p, i64, i64,
                                               p, i64, i64, p, i64, i64, p]
     L.fp8_quantize_mx.argtypes = [p, i64, i64, i64, p, i64, p, i64, p]
@@ -113,7 +117,7 @@ def _load() -> ctypes.CDLL:
     L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
-                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_gemm",
+                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair", "fp8_gemm",
                  "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
                  "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
@@ -317,6 +321,40 @@ def fp8_quantize_act_weight(x: torch.Tensor, w: torch.Tensor, transposed: bool =
         _ptr(wscale_t if transposed else None), wscale_t.stride(0) if transposed else 0, _stream(stream))
     _check(st, "fp8_quantize_act_weight")
     return (q, scale, wq, wscale, wq_t, wscale_t) if transposed else (q, scale, wq, wscale)
+
+
+def fp8_quantize_act_128x1_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Tensor | None = None,
+                                scale0: torch.Tensor | None = None, q1: torch.Tensor | None = None,
+                                scale1: torch.Tensor | None = None, stream=None):
+    """The two Wgrad operands (``x0 = dY``, ``x1 = X``, one token count) in
+    128x1 token tiles in one launch, as :func:`fp8_quantize_act` with
+    ``tiling="128x1"`` on each. Returns ``(q0, scale0, q1, scale1)``."""
+    _need_gpu(x0, x1)
+    _rowmajor(x0, "x0")
+    _rowmajor(x1, "x1")
+    if x0.dtype != torch.bfloat16 or x1.dtype != torch.bfloat16:
+        raise Fp8qError("x0 and x1 must be bfloat16")
+    tokens, c0 = x0.shape
+    if x1.shape[0] != tokens:
+        raise Fp8qError("x0 and x1 must have the same token count")
+    c1 = x1.shape[1]
+    dev = x0.device
+    if q0 is None:
+        q0 = torch.empty((c0, tokens), dtype=torch.float8_e4m3fn, device=dev)
+    if scale0 is None:
+        scale0 = torch.empty((tokens // 128, c0), dtype=torch.float32, device=dev)
+    if q1 is None:
+        q1 = torch.empty((c1, tokens), dtype=torch.float8_e4m3fn, device=dev)
+    if scale1 is None:
+        scale1 = torch.empty((tokens // 128, c1), dtype=torch.float32, device=dev)
+    _need_gpu(q0, scale0, q1, scale1)
+    _codes(q0, "q0")
+    _codes(q1, "q1")
+    st = _load().fp8_quantize_act_128x1_pair(
+        tokens, _ptr(x0), c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
+        _ptr(x1), c1, x1.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1), scale1.stride(0), _stream(stream))
+    _check(st, "fp8_quantize_act_128x1_pair")
+    return q0, scale0, q1, scale1
 
 
 def fp8_quantize_weight_grouped(w: torch.Tensor, transposed: bool = False, q: torch.Tensor | None = None,

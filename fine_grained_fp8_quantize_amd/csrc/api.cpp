@@ -156,6 +156,45 @@ int fp8_quantize_act_weight(const uint16_t* x, int64_t rows, int64_t cols, int64
         ld_wq, wscale, ld_ws, wq_t, ld_wqt, wscale_t, ld_wst, stream));
 }
 
+int fp8_quantize_act_128x1_pair(int64_t tokens, const uint16_t* x0, int64_t cols0, int64_t ld_x0, uint8_t* q0,
+                                int64_t ld_q0, float* scale0, int64_t ld_s0, const uint16_t* x1, int64_t cols1,
+                                int64_t ld_x1, uint8_t* q1, int64_t ld_q1, float* scale1, int64_t ld_s1,
+                                hipStream_t stream) {
+    // the checks of fp8_quantize_act (128x1) on each operand
+    if (tokens < 0 || cols0 < 0 || cols1 < 0) return FP8Q_ERR_SHAPE;
+    const bool op0 = tokens > 0 && cols0 > 0, op1 = tokens > 0 && cols1 > 0;
+    const uint16_t* xs[2] = {x0, x1};
+    uint8_t* qs[2] = {q0, q1};
+    float* ss[2] = {scale0, scale1};
+    const int64_t cols[2] = {cols0, cols1}, ld_x[2] = {ld_x0, ld_x1}, ld_q[2] = {ld_q0, ld_q1},
+                  ld_s[2] = {ld_s0, ld_s1};
+    const bool on[2] = {op0, op1};
+    for (int i = 0; i < 2; ++i) {
+        if (!on[i]) continue;
+        if (!xs[i] || !qs[i] || !ss[i]) return FP8Q_ERR_NULL;
+        if (ld_x[i] < cols[i] || tokens % 128 != 0 || cols[i] % 8 != 0 || ld_q[i] < tokens || ld_s[i] < cols[i])
+            return FP8Q_ERR_SHAPE;
+        if (!aligned(xs[i], 16) || !aligned(qs[i], 16) || !aligned(ss[i], 4) || ld_x[i] % 8 != 0 ||
+            ld_q[i] % 16 != 0)
+            return FP8Q_ERR_ALIGN;
+    }
+    if (!op0 && !op1) return FP8Q_OK;
+    if (op0 && op1) {
+        // the two halves of the launch run concurrently: their outputs must be disjoint
+        const Span o0[2] = {span(q0, cols0, tokens, ld_q0, 1), span(scale0, tokens / 128, cols0, ld_s0, 4)};
+        const Span o1[2] = {span(q1, cols1, tokens, ld_q1, 1), span(scale1, tokens / 128, cols1, ld_s1, 4)};
+        for (const Span& a : o0)
+            for (const Span& b : o1)
+                if (overlap(a, b)) return FP8Q_ERR_SHAPE;
+    }
+    const int64_t blocks = tokens / 128 * ((op0 ? (cols0 + 127) / 128 : 0) + (op1 ? (cols1 + 127) / 128 : 0));
+    if (!grid_ok(blocks)) return FP8Q_ERR_SHAPE;
+    // an empty operand is skipped: its block range is empty
+    return hip_status(fp8q::launch_quant_act_128x1_pair(tokens, x0, op0 ? cols0 : 0, ld_x0, q0, ld_q0, scale0,
+                                                        ld_s0, x1, op1 ? cols1 : 0, ld_x1, q1, ld_q1, scale1,
+                                                        ld_s1, stream));
+}
+
 int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
                         uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                         uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,

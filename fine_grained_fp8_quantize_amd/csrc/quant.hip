@@ -10,7 +10,8 @@
 // (the re-tile of a cached FP8 activation reads 1 byte instead of 2). Also
 // here: the scatter form of the 1x128 kernel (quantize before dispatch), the
 // microscaling quantizer, the weight quantizer over several experts in one
-// launch, and one launch that quantizes a layer's activation and weight.
+// launch, one launch that quantizes a layer's activation and weight, and one
+// that quantizes both Wgrad operands in 128x1 tiles.
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -176,10 +177,12 @@ __global__ __launch_bounds__(256) void quant_mx_1x32_kernel(
 // with full 16-byte stores.
 constexpr int kTrStride = 144;  // bytes per transposed row (128 + 16 pad)
 
-__global__ __launch_bounds__(256) void quant_act_128x1_kernel(
+// The body of one 256-thread block (panel index `block`); the kernels below
+// call it, alone or for two operands in one grid.
+__device__ __forceinline__ void act_128x1_body(
     const uint16_t* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ qt, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
-    int64_t cblocks) {
+    int64_t cblocks, int64_t block) {
     __shared__ uint32_t red[4][16][4];
     __shared__ float s_sh[128];
     __shared__ float y_sh[128];
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(256) void quant_act_128x1_kernel(
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int g = t & 15, r = t >> 4;
-    const int64_t tb = blockIdx.x / cblocks, cb = blockIdx.x - tb * cblocks;
+    const int64_t tb = block / cblocks, cb = block - tb * cblocks;
     const int64_t t0 = tb * 128, c0 = cb * 128;
     const int64_t ch = c0 + 8 * g;
     const bool valid = ch < cols;  // cols % 8 == 0: a chunk is all in or all out
@@ -273,6 +276,33 @@ __global__ __launch_bounds__(256) void quant_act_128x1_kernel(
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(src + 16 * i);
     }
+}
+
+__global__ __launch_bounds__(256) void quant_act_128x1_kernel(
+    const uint16_t* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld_x,
+    uint8_t* __restrict__ qt, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    int64_t cblocks) {
+    act_128x1_body(x, tokens, cols, ld_x, qt, ld_q, scale, ld_s, cblocks, (int64_t)blockIdx.x);
+}
+
+// Both Wgrad operands (dY and X, one token count) in one grid: blocks below
+// a_blocks take panels of the first, the rest panels of the second.
+struct Act128Args {
+    const uint16_t* x;
+    int64_t cols, ld_x;
+    uint8_t* qt;
+    int64_t ld_q;
+    float* scale;
+    int64_t ld_s, cblocks;
+};
+
+__global__ __launch_bounds__(256) void quant_act_128x1_pair_kernel(int64_t tokens, Act128Args a,
+                                                                   int64_t a_blocks, Act128Args b) {
+    const int64_t blk = (int64_t)blockIdx.x;
+    const bool first = blk < a_blocks;  // block-uniform: the barriers inside stay whole
+    const Act128Args& o = first ? a : b;
+    act_128x1_body(o.x, tokens, o.cols, o.ld_x, o.qt, o.ld_q, o.scale, o.ld_s, o.cblocks,
+                   first ? blk : blk - a_blocks);
 }
 
 // ------------------------------------------------- cached activation re-tile
@@ -577,6 +607,19 @@ hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t col
     const int64_t blocks = tokens / 128 * cblocks;
     hipLaunchKernelGGL(quant_act_128x1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        x, tokens, cols, ld_x, qt, ld_q, scale, ld_s, cblocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_128x1_pair(int64_t tokens, const uint16_t* x0, int64_t cols0, int64_t ld_x0,
+                                       uint8_t* q0, int64_t ld_q0, float* s0, int64_t ld_s0,
+                                       const uint16_t* x1, int64_t cols1, int64_t ld_x1, uint8_t* q1,
+                                       int64_t ld_q1, float* s1, int64_t ld_s1, hipStream_t stream) {
+    Act128Args a{x0, cols0, ld_x0, q0, ld_q0, s0, ld_s0, (cols0 + 127) / 128};
+    Act128Args b{x1, cols1, ld_x1, q1, ld_q1, s1, ld_s1, (cols1 + 127) / 128};
+    const int64_t a_blocks = tokens / 128 * a.cblocks;
+    const int64_t blocks = a_blocks + tokens / 128 * b.cblocks;
+    hipLaunchKernelGGL(quant_act_128x1_pair_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, tokens, a,
+                       a_blocks, b);
     return hipGetLastError();
 }
 

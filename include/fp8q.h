@@ -169,6 +169,26 @@ int fp8_quantize_act_weight(const uint16_t *x, int64_t rows, int64_t cols, int64
                             hipStream_t stream);
 
 /*
+ * fp8_quantize_act_128x1_pair -- the two Wgrad operands in one launch:
+ * fp8_quantize_act with FP8Q_TILE_128x1 on x0[tokens][cols0] and on
+ * x1[tokens][cols1] (dY and X of one token count), page dssusan.co.kr Q&A
+ * board, Figure 6 (Wgrad in FP8). Same tiles, layouts (q transposed
+ * [cols][ld_q], scale [tokens/128][ld_s]), alignment rules and results, bit
+ * for bit, as the two separate calls. One launch instead of two removes a
+ * launch gap and overlaps the two kernels' ramps and tails.
+ * An operand with cols == 0 (or tokens == 0) is skipped and its pointers
+ * are not read. The two halves of the launch run concurrently, so no output
+ * of one operand (q, scale) may share a byte with an output of the other.
+ * Errors: those of fp8_quantize_act (FP8Q_ERR_NULL, FP8Q_ERR_SHAPE,
+ *         FP8Q_ERR_ALIGN, FP8Q_ERR_HIP); FP8Q_ERR_SHAPE also when the outputs
+ *         of the two operands overlap.
+ */
+int fp8_quantize_act_128x1_pair(int64_t tokens, const uint16_t *x0, int64_t cols0, int64_t ld_x0, uint8_t *q0,
+                                int64_t ld_q0, float *scale0, int64_t ld_s0, const uint16_t *x1, int64_t cols1,
+                                int64_t ld_x1, uint8_t *q1, int64_t ld_q1, float *scale1, int64_t ld_s1,
+                                hipStream_t stream);
+
+/*
  * fp8_quantize_weight_grouped -- fp8_quantize_weight over several weight
  * matrices of one shape (say the experts of an MoE layer) in one launch.
  *

@@ -319,6 +319,31 @@ def test_quantize_act_weight_validation(lib):
     assert _aw(lib, wqt=A16c + 0x200000, ld_wqt=256, wst=A16b, ld_wst=2) == ERR_SHAPE    # Wt scales over act codes
 
 
+def _p128(lib, tokens=256, x0=A16, c0=256, ld_x0=256, q0=A16b, ld_q0=256, s0=A4, ld_s0=256, x1=A16c, c1=136,
+          ld_x1=136, q1=A16 + 0x100000, ld_q1=256, s1=A4 + 0x1000, ld_s1=136):
+    return lib.fp8_quantize_act_128x1_pair(tokens, x0, c0, ld_x0, q0, ld_q0, s0, ld_s0, x1, c1, ld_x1, q1, ld_q1,
+                                           s1, ld_s1, None)
+
+
+def test_quantize_act_128x1_pair_validation(lib):
+    assert _p128(lib, tokens=0) == OK                              # nothing to do
+    assert _p128(lib, c0=0, c1=0) == OK
+    assert _p128(lib, tokens=-128) == ERR_SHAPE
+    assert _p128(lib, tokens=200) == ERR_SHAPE                     # tokens % 128
+    assert _p128(lib, c1=132, ld_x1=136, ld_s1=136) == ERR_SHAPE   # cols % 8
+    assert _p128(lib, ld_q0=128) == ERR_SHAPE                      # ld_q < tokens
+    assert _p128(lib, ld_s1=128) == ERR_SHAPE                      # ld_s < cols
+    assert _p128(lib, x1=0) == ERR_NULL
+    assert _p128(lib, q0=A16b + 8) == ERR_ALIGN
+    assert _p128(lib, ld_x1=140) == ERR_ALIGN                      # ld_x % 8
+    # empty operands are not read (both empty: nothing is launched)
+    assert _p128(lib, c0=0, c1=0, x0=0, q0=0, s0=0, x1=0, q1=0, s1=0) == OK
+    # outputs of the two halves must not overlap
+    assert _p128(lib, q1=A16b + 0x400) == ERR_SHAPE
+    assert _p128(lib, s1=A4 + 0x100) == ERR_SHAPE
+    assert _p128(lib, s1=A16b + 0x100) == ERR_SHAPE
+
+
 def _wg(lib, groups=3, w=A16, n=256, k=384, ld_w=384, sw=256 * 384, q=A16b, ld_q=384, sq=256 * 384,
         s=A4, ld_s=3, ss=6, qt=A16c, ld_qt=256, sqt=384 * 256, st=A4 + 0x1000, ld_st=2, sst=6):
     return lib.fp8_quantize_weight_grouped(groups, w, n, k, ld_w, sw, q, ld_q, sq, s, ld_s, ss,
@@ -344,7 +369,8 @@ def test_quantize_weight_grouped_validation(lib):
 
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
-                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_gemm", "fp8_grouped_gemm",
+                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair", "fp8_gemm",
+                 "fp8_grouped_gemm",
                  "fp8_grouped_gemm_wgrad",
                  "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))

@@ -370,3 +370,50 @@ def test_act_weight_padded_leading_dimensions():
     assert_bits_equal(host_f32(ws.contiguous()), ws_ref, "padded weight scales")
     assert torch.all(q.as_strided((70, 16), (400, 1), q.storage_offset() + 384) == 0x5A)
     assert torch.all(wq.as_strided((256, 32), (416, 1), wq.storage_offset() + 384) == 0x5A)
+
+
+# ------------------------------------- both Wgrad operands (128x1) in one launch
+
+def test_act_128x1_pair_equals_separate_launches_full_size():
+    """The Wgrad operands dY [8192][2048] and X [8192][7168] in one launch:
+    byte-identical to the two separate 128x1 launches (each pinned to the
+    oracle at full size above)."""
+    g = wl.wgrad()
+    dy, x = dev_bf16(g["dy"]), dev_bf16(g["x"])
+    got = fq.fp8_quantize_act_128x1_pair(dy, x)
+    ref = fq.fp8_quantize_act(dy, "128x1") + fq.fp8_quantize_act(x, "128x1")
+    torch.cuda.synchronize()
+    for a, b, tag in zip(got, ref, ("q0", "scale0", "q1", "scale1")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), tag
+
+
+@pytest.mark.parametrize("cols0,cols1", [(8, 264), (200, 128), (128, 0), (0, 72)])
+def test_act_128x1_pair_ragged_and_empty_sides(cols0, cols1):
+    tokens = 256
+    x0 = wl.activation(1, "wgrad", 70, tokens, max(cols0, 8), None)[:, :cols0]
+    x1 = wl.activation(1, "wgrad", 71, tokens, max(cols1, 8), 50.0)[:, :cols1]
+    d0 = torch.empty((tokens, cols0), dtype=torch.bfloat16, device="cuda") if cols0 == 0 else dev_bf16(x0)
+    d1 = torch.empty((tokens, cols1), dtype=torch.bfloat16, device="cuda") if cols1 == 0 else dev_bf16(x1)
+    q0, s0, q1, s1 = fq.fp8_quantize_act_128x1_pair(d0, d1)
+    torch.cuda.synchronize()
+    for cols, x, q, s, tag in ((cols0, x0, q0, s0, "x0"), (cols1, x1, q1, s1, "x1")):
+        if cols == 0:
+            continue
+        q_ref, s_ref = oracle.quant_act_128x1(np.ascontiguousarray(x))
+        assert_bits_equal(host_f32(s), s_ref, tag + " scales")
+        assert_bits_equal(host_codes(q), q_ref, tag + " codes")
+
+
+def test_act_128x1_pair_edge_tiles():
+    rng = np.random.default_rng(72)
+    e = _edge_rows(rng)                                           # [10][128] special tiles
+    # the 10 special tiles as token columns, plus 6 plain ones: [128][16]
+    x0 = np.concatenate([e.T, wl.activation(1, "wgrad", 73, 128, 128, None)[:, :6]], axis=1)
+    x0 = np.concatenate([x0, x0[::-1]], axis=0)                   # [256][16]
+    x1 = wl.activation(1, "wgrad", 74, 256, 136, 50.0)
+    q0, s0, q1, s1 = fq.fp8_quantize_act_128x1_pair(dev_bf16(x0), dev_bf16(x1))
+    torch.cuda.synchronize()
+    for x, q, s, tag in ((x0, q0, s0, "edge"), (x1, q1, s1, "plain")):
+        q_ref, s_ref = oracle.quant_act_128x1(np.ascontiguousarray(x))
+        assert_bits_equal(host_f32(s), s_ref, tag + " scales")
+        assert_bits_equal(host_codes(q), q_ref, tag + " codes")
