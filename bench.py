@@ -57,6 +57,7 @@ KERNEL_NAMES = {
     "quant_weight": "quant_weight_kernel",
     "quant_act_weight": "quant_act_weight_kernel",
     "quant_act_128x1_pair": "quant_act_128x1_pair_kernel",
+    "quant_retile_128x1": "quant_retile_128x1_kernel",
     "quant_mx": "quant_mx_1x32_kernel",
     "retile_128x1": "retile_128x1_kernel",
     "gemm": "gemm_kernel",
@@ -265,11 +266,11 @@ class Workload:
             y = empty((n_out, k_in), f32)
             self.flops = 2.0 * n_out * k_in * t
             self.launches = [
-                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
-                       act_bytes(t, n_out)),
-                # codes + 1x128 scales in, codes + 128x1 scales out
-                Launch("retile_128x1", lambda r: fq.fp8_retile_act_128x1(XQ[r], XS[r], q_t=bq, scale_t=bs),
-                       2 * t * k_in + 8 * t * k_in // 128),
+                # dY quantized 128x1 and the cache re-tiled (codes + 1x128
+                # scales in, codes + 128x1 scales out), one launch
+                Launch("quant_retile_128x1", lambda r: fq.fp8_quantize_act_128x1_retile(
+                    DY[r], XQ[r], XS[r], q0=aq, scale0=as_, q1=bq, scale1=bs),
+                       act_bytes(t, n_out) + 2 * t * k_in + 8 * t * k_in // 128),
                 Launch("gemm", lambda r: fq.fp8_gemm(aq, as_, bq, bs, "row", f32, out=y),
                        gemm_bytes(n_out, k_in, t, k_in * (t // 128), 4, n_out), self.flops),
             ]
@@ -336,10 +337,10 @@ class Workload:
             self.flops = 2.0 * real * n_out * k_in   # real tokens only
             self.bound = "hbm"                        # 3.8 GB of fp32 gradients written
             self.launches = [
-                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
-                       act_bytes(m_total, n_out)),
-                Launch("retile_128x1", lambda r: fq.fp8_retile_act_128x1(XQ[r], XS[r], q_t=bq, scale_t=bs),
-                       2 * m_total * k_in + 8 * m_total * k_in // 128),
+                # dY quantized 128x1 and the dispatch cache re-tiled, one launch
+                Launch("quant_retile_128x1", lambda r: fq.fp8_quantize_act_128x1_retile(
+                    DY[r], XQ[r], XS[r], q0=aq, scale0=as_, q1=bq, scale1=bs),
+                       act_bytes(m_total, n_out) + 2 * m_total * k_in + 8 * m_total * k_in // 128),
                 Launch("gemm", lambda r: fq.fp8_grouped_gemm_wgrad(offd, aq, as_, bq, bs, f32, out=y),
                        (n_out + k_in) * m_total * (1 + 4 / 128) + 4 * E * n_out * k_in, self.flops),
             ]
@@ -363,10 +364,10 @@ class Workload:
             self.flops = 2.0 * real * n_out * k_in   # real tokens only
             self.bound = "hbm"                        # 3.8 GB of fp32 gradients written
             self.launches = [
-                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(DY[r], "128x1", q=aq, scale=as_),
-                       act_bytes(m_total, n_out)),
-                Launch("quant_act_128x1", lambda r: fq.fp8_quantize_act(X[r], "128x1", q=bq, scale=bs),
-                       act_bytes(m_total, k_in)),
+                # dY and X (expert-sorted) in 128x1 token tiles, one launch
+                Launch("quant_act_128x1_pair", lambda r: fq.fp8_quantize_act_128x1_pair(
+                    DY[r], X[r], q0=aq, scale0=as_, q1=bq, scale1=bs),
+                       act_bytes(m_total, n_out) + act_bytes(m_total, k_in)),
                 Launch("gemm", lambda r: fq.fp8_grouped_gemm_wgrad(offd, aq, as_, bq, bs, f32, out=y),
                        (n_out + k_in) * m_total * (1 + 4 / 128) + 4 * E * n_out * k_in, self.flops),
             ]

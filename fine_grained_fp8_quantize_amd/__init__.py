@@ -27,6 +27,8 @@ Layouts (row-major, K contiguous for GEMM operands):
   and weight (128x128, optionally transposed too) in one launch.
 * ``fp8_quantize_act_128x1_pair(dy, x)`` -- the two Wgrad operands in 128x1
   token tiles in one launch.
+* ``fp8_quantize_act_128x1_retile(dy, xq, xs)`` -- the same when X comes from
+  the FP8 activation cache (dY quantized, X re-tiled) in one launch.
 * ``fp8_quantize_act_scatter(x, dst_rows, m_total)`` -- quantize each token
   once and scatter its codes and scales to its expert-sorted rows.
 * ``fp8_grouped_gemm_wgrad(offsets, a, a_scale, b, b_scale)`` -- per-expert
@@ -55,6 +57,7 @@ __all__ = [
     "fp8_quantize_weight_grouped",
     "fp8_quantize_act_weight",
     "fp8_quantize_act_128x1_pair",
+    "fp8_quantize_act_128x1_retile",
     "fp8_gemm",
     "fp8_grouped_gemm",
     "fp8_grouped_gemm_wgrad",
@@ -105,6 +108,8 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_act_weight.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, i64, i64, p, i64, p, i64,
                                           p, i64, p, i64, p]
     L.fp8_quantize_act_128x1_pair.argtypes = [i64, p, i64, i64, p, i64, p, i64, p, i64, i64, p, i64, p, i64, p]
+    L.fp8_quantize_act_128x1_retile.argtypes = [i64, p, i64, i64, p, i64, p, i64, p, i64, i64, p, i64, p, i64, p,
+                                                i64, p]
     L.fp8_quantize_weight_grouped.argtypes = [i32, p, i64, i64, i64, i64, p, i64, i64, p, i64, i64,
                                               p, i64, i64, p, i64, i64, p]
     L.fp8_quantize_mx.argtypes = [p, i64, i64, i64, p, i64, p, i64, p]
@@ -117,9 +122,9 @@ def _load() -> ctypes.CDLL:
     L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
-                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair", "fp8_gemm",
-                 "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_gemm_mx",
-                 "fp8_retile_act_128x1", "fp8_gemm_tensor"):
+                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair",
+                 "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
+                 "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
     L.fp8q_status_string.argtypes = [cint]
     L.fp8q_status_string.restype = ctypes.c_char_p
@@ -354,6 +359,46 @@ def fp8_quantize_act_128x1_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Te
         tokens, _ptr(x0), c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
         _ptr(x1), c1, x1.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1), scale1.stride(0), _stream(stream))
     _check(st, "fp8_quantize_act_128x1_pair")
+    return q0, scale0, q1, scale1
+
+
+def fp8_quantize_act_128x1_retile(x0: torch.Tensor, xq: torch.Tensor, xs: torch.Tensor,
+                                  q0: torch.Tensor | None = None, scale0: torch.Tensor | None = None,
+                                  q1: torch.Tensor | None = None, scale1: torch.Tensor | None = None, stream=None):
+    """The two Wgrad operands in one launch when X comes from the FP8 cache:
+    ``x0`` (dY, bf16) in 128x1 token tiles as :func:`fp8_quantize_act`, and the
+    cached 1x128 codes ``xq[tokens][cols]`` with scales ``xs[cols/128][tokens]``
+    re-tiled as :func:`fp8_retile_act_128x1`. Returns ``(q0, scale0, q1, scale1)``."""
+    _need_gpu(x0, xq, xs)
+    _rowmajor(x0, "x0")
+    _rowmajor(xq, "xq")
+    _rowmajor(xs, "xs")
+    if x0.dtype != torch.bfloat16:
+        raise Fp8qError("x0 must be bfloat16")
+    _codes(xq, "xq")
+    if xs.dtype != torch.float32:
+        raise Fp8qError("xs must be float32")
+    tokens, c0 = x0.shape
+    if xq.shape[0] != tokens:
+        raise Fp8qError("x0 and xq must have the same token count")
+    c1 = xq.shape[1]
+    dev = x0.device
+    if q0 is None:
+        q0 = torch.empty((c0, tokens), dtype=torch.float8_e4m3fn, device=dev)
+    if scale0 is None:
+        scale0 = torch.empty((tokens // 128, c0), dtype=torch.float32, device=dev)
+    if q1 is None:
+        q1 = torch.empty((c1, tokens), dtype=torch.float8_e4m3fn, device=dev)
+    if scale1 is None:
+        scale1 = torch.empty((tokens // 128, c1), dtype=torch.float32, device=dev)
+    _need_gpu(q0, scale0, q1, scale1)
+    _codes(q0, "q0")
+    _codes(q1, "q1")
+    st = _load().fp8_quantize_act_128x1_retile(
+        tokens, _ptr(x0), c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
+        _ptr(xq), c1, xq.stride(0), _ptr(xs), xs.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1),
+        scale1.stride(0), _stream(stream))
+    _check(st, "fp8_quantize_act_128x1_retile")
     return q0, scale0, q1, scale1
 
 

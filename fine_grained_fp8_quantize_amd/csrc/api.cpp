@@ -195,6 +195,46 @@ int fp8_quantize_act_128x1_pair(int64_t tokens, const uint16_t* x0, int64_t cols
                                                         ld_s1, stream));
 }
 
+int fp8_quantize_act_128x1_retile(int64_t tokens, const uint16_t* x0, int64_t cols0, int64_t ld_x0, uint8_t* q0,
+                                  int64_t ld_q0, float* scale0, int64_t ld_s0, const uint8_t* xq, int64_t cols1,
+                                  int64_t ld_xq, const float* xs, int64_t ld_xs, uint8_t* q1, int64_t ld_q1,
+                                  float* scale1, int64_t ld_s1, hipStream_t stream) {
+    // the checks of fp8_quantize_act (128x1) on x0 and of fp8_retile_act_128x1 on the cache
+    if (tokens < 0 || cols0 < 0 || cols1 < 0) return FP8Q_ERR_SHAPE;
+    const bool op0 = tokens > 0 && cols0 > 0, op1 = tokens > 0 && cols1 > 0;
+    if (op0) {
+        if (!x0 || !q0 || !scale0) return FP8Q_ERR_NULL;
+        if (ld_x0 < cols0 || tokens % 128 != 0 || cols0 % 8 != 0 || ld_q0 < tokens || ld_s0 < cols0)
+            return FP8Q_ERR_SHAPE;
+        if (!aligned(x0, 16) || !aligned(q0, 16) || !aligned(scale0, 4) || ld_x0 % 8 != 0 || ld_q0 % 16 != 0)
+            return FP8Q_ERR_ALIGN;
+    }
+    if (op1) {
+        if (!xq || !xs || !q1 || !scale1) return FP8Q_ERR_NULL;
+        if (tokens % 128 != 0 || cols1 % 128 != 0 || ld_xq < cols1 || ld_xs < tokens || ld_q1 < tokens ||
+            ld_s1 < cols1)
+            return FP8Q_ERR_SHAPE;
+        if (!aligned(xq, 16) || !aligned(xs, 16) || !aligned(q1, 16) || !aligned(scale1, 4) || ld_xq % 16 != 0 ||
+            ld_xs % 4 != 0 || ld_q1 % 16 != 0)
+            return FP8Q_ERR_ALIGN;
+    }
+    if (!op0 && !op1) return FP8Q_OK;
+    if (op0 && op1) {
+        // the two halves of the launch run concurrently: their outputs must be disjoint
+        const Span o0[2] = {span(q0, cols0, tokens, ld_q0, 1), span(scale0, tokens / 128, cols0, ld_s0, 4)};
+        const Span o1[2] = {span(q1, cols1, tokens, ld_q1, 1), span(scale1, tokens / 128, cols1, ld_s1, 4)};
+        for (const Span& a : o0)
+            for (const Span& b : o1)
+                if (overlap(a, b)) return FP8Q_ERR_SHAPE;
+    }
+    const int64_t blocks = tokens / 128 * ((op0 ? (cols0 + 127) / 128 : 0) + (op1 ? cols1 / 128 : 0));
+    if (!grid_ok(blocks)) return FP8Q_ERR_SHAPE;
+    // an empty operand is skipped: its block range is empty
+    return hip_status(fp8q::launch_quant_retile_128x1(tokens, x0, op0 ? cols0 : 0, ld_x0, q0, ld_q0, scale0, ld_s0,
+                                                      xq, op1 ? cols1 : 0, ld_xq, xs, ld_xs, q1, ld_q1, scale1,
+                                                      ld_s1, stream));
+}
+
 int fp8_quantize_weight(const uint16_t* w, int64_t n, int64_t k, int64_t ld_w,
                         uint8_t* q, int64_t ld_q, float* scale, int64_t ld_s,
                         uint8_t* q_t, int64_t ld_qt, float* scale_t, int64_t ld_st,

@@ -26,6 +26,10 @@ hipError_t launch_quant_act_128x1_pair(int64_t tokens, const uint16_t* x0, int64
                                        const uint16_t* x1, int64_t cols1, int64_t ld_x1, uint8_t* q1,
                                        int64_t ld_q1, float* s1, int64_t ld_s1, hipStream_t stream);
 
+hipError_t launch_quant_retile_128x1(int64_t tokens, const uint16_t* x0, int64_t cols0, int64_t ld_x0,
+                                     uint8_t* q0, int64_t ld_q0, float* s0, int64_t ld_s0, const uint8_t* xq,
+                                     int64_t cols1, int64_t ld_xq, const float* xs, int64_t ld_xs, uint8_t* q1,
+                                     int64_t ld_q1, float* s1, int64_t ld_s1, hipStream_t stream);
 hipError_t launch_retile_128x1(const uint8_t* q, int64_t tokens, int64_t cols, int64_t ld_q,
                                const float* scale, int64_t ld_s, uint8_t* qt, int64_t ld_qt,
                                float* scale_t, int64_t ld_st, hipStream_t stream);

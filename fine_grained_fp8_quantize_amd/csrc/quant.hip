@@ -10,8 +10,9 @@
 // (the re-tile of a cached FP8 activation reads 1 byte instead of 2). Also
 // here: the scatter form of the 1x128 kernel (quantize before dispatch), the
 // microscaling quantizer, the weight quantizer over several experts in one
-// launch, one launch that quantizes a layer's activation and weight, and one
-// that quantizes both Wgrad operands in 128x1 tiles.
+// launch, one launch that quantizes a layer's activation and weight, and
+// launches that make both Wgrad operands in 128x1 tiles (from bf16, or dY
+// from bf16 and X from the FP8 cache).
 #include "fp8q_device.h"
 #include "launch.h"
 
@@ -177,16 +178,26 @@ __global__ __launch_bounds__(256) void quant_mx_1x32_kernel(
 // with full 16-byte stores.
 constexpr int kTrStride = 144;  // bytes per transposed row (128 + 16 pad)
 
+// LDS of one 128x128 panel block: the amax partials of the 4 waves, the
+// 128 scales and their reciprocals, and the transposed codes.
+template <int R>
+struct PanelLds {
+    uint32_t (*red)[16][R];
+    float* s_sh;
+    float* y_sh;
+    uint8_t* tr;
+};
+
 // The body of one 256-thread block (panel index `block`); the kernels below
-// call it, alone or for two operands in one grid.
+// call it, alone or beside another operand in one grid.
 __device__ __forceinline__ void act_128x1_body(
     const uint16_t* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ qt, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
-    int64_t cblocks, int64_t block) {
-    __shared__ uint32_t red[4][16][4];
-    __shared__ float s_sh[128];
-    __shared__ float y_sh[128];
-    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+    int64_t cblocks, int64_t block, PanelLds<4> lds) {
+    uint32_t (*const red)[16][4] = lds.red;
+    float* const s_sh = lds.s_sh;
+    float* const y_sh = lds.y_sh;
+    uint8_t* const tr = lds.tr;
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int g = t & 15, r = t >> 4;
@@ -282,7 +293,12 @@ __global__ __launch_bounds__(256) void quant_act_128x1_kernel(
     const uint16_t* __restrict__ x, int64_t tokens, int64_t cols, int64_t ld_x,
     uint8_t* __restrict__ qt, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
     int64_t cblocks) {
-    act_128x1_body(x, tokens, cols, ld_x, qt, ld_q, scale, ld_s, cblocks, (int64_t)blockIdx.x);
+    __shared__ uint32_t red[4][16][4];
+    __shared__ float s_sh[128];
+    __shared__ float y_sh[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+    act_128x1_body(x, tokens, cols, ld_x, qt, ld_q, scale, ld_s, cblocks, (int64_t)blockIdx.x,
+                   PanelLds<4>{red, s_sh, y_sh, tr});
 }
 
 // Both Wgrad operands (dY and X, one token count) in one grid: blocks below
@@ -298,11 +314,15 @@ struct Act128Args {
 
 __global__ __launch_bounds__(256) void quant_act_128x1_pair_kernel(int64_t tokens, Act128Args a,
                                                                    int64_t a_blocks, Act128Args b) {
+    __shared__ uint32_t red[4][16][4];
+    __shared__ float s_sh[128];
+    __shared__ float y_sh[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
     const int64_t blk = (int64_t)blockIdx.x;
     const bool first = blk < a_blocks;  // block-uniform: the barriers inside stay whole
     const Act128Args& o = first ? a : b;
     act_128x1_body(o.x, tokens, o.cols, o.ld_x, o.qt, o.ld_q, o.scale, o.ld_s, o.cblocks,
-                   first ? blk : blk - a_blocks);
+                   first ? blk : blk - a_blocks, PanelLds<4>{red, s_sh, y_sh, tr});
 }
 
 // ------------------------------------------------- cached activation re-tile
@@ -316,18 +336,18 @@ __global__ __launch_bounds__(256) void quant_act_128x1_pair_kernel(int64_t token
 // group r = t/16, channel chunk g = t%16) loads 8 tokens x 8 channels of
 // codes (one 8-byte load per token) and the 8 tokens' scales. The code of an
 // output element keeps the sign bit of the input code (s_token >= 0).
-__global__ __launch_bounds__(256) void retile_128x1_kernel(
+__device__ __forceinline__ void retile_128x1_body(
     const uint8_t* __restrict__ q, int64_t ld_q, const float* __restrict__ scale, int64_t ld_s,
     uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
-    int64_t cblocks) {
-    __shared__ uint32_t red[4][16][8];
-    __shared__ float s_sh[128];
-    __shared__ float y_sh[128];
-    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+    int64_t cblocks, int64_t block, PanelLds<8> lds) {
+    uint32_t (*const red)[16][8] = lds.red;
+    float* const s_sh = lds.s_sh;
+    float* const y_sh = lds.y_sh;
+    uint8_t* const tr = lds.tr;
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int g = t & 15, r = t >> 4;
-    const int64_t tb = blockIdx.x / cblocks, cb = blockIdx.x - tb * cblocks;
+    const int64_t tb = block / cblocks, cb = block - tb * cblocks;
     const int64_t t0 = tb * 128, c0 = cb * 128;
 
     uint2 code[8];
@@ -429,6 +449,48 @@ __global__ __launch_bounds__(256) void retile_128x1_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(src + 16 * i);
+}
+
+__global__ __launch_bounds__(256) void retile_128x1_kernel(
+    const uint8_t* __restrict__ q, int64_t ld_q, const float* __restrict__ scale, int64_t ld_s,
+    uint8_t* __restrict__ qt, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
+    int64_t cblocks) {
+    __shared__ uint32_t red[4][16][8];
+    __shared__ float s_sh[128];
+    __shared__ float y_sh[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+    retile_128x1_body(q, ld_q, scale, ld_s, qt, ld_qt, scale_t, ld_st, cblocks, (int64_t)blockIdx.x,
+                      PanelLds<8>{red, s_sh, y_sh, tr});
+}
+
+// The Wgrad operands when X comes from the FP8 activation cache, in one
+// grid: blocks below a_blocks quantize panels of dY in 128x1 tiles, the rest
+// re-tile panels of the cached X. Both bodies share one set of LDS arrays,
+// sized for the larger.
+struct RetileArgs {
+    const uint8_t* q;
+    int64_t ld_q;
+    const float* scale;
+    int64_t ld_s;
+    uint8_t* qt;
+    int64_t ld_qt;
+    float* scale_t;
+    int64_t ld_st, cblocks;
+};
+
+__global__ __launch_bounds__(256) void quant_retile_128x1_kernel(int64_t tokens, Act128Args a, int64_t a_blocks,
+                                                                 RetileArgs b) {
+    __shared__ uint32_t red[4][16][8];
+    __shared__ float s_sh[128];
+    __shared__ float y_sh[128];
+    __shared__ __attribute__((aligned(16))) uint8_t tr[128 * kTrStride];
+    const int64_t blk = (int64_t)blockIdx.x;
+    if (blk < a_blocks)  // block-uniform: the barriers inside stay whole
+        act_128x1_body(a.x, tokens, a.cols, a.ld_x, a.qt, a.ld_q, a.scale, a.ld_s, a.cblocks, blk,
+                       PanelLds<4>{reinterpret_cast<uint32_t(*)[16][4]>(red), s_sh, y_sh, tr});
+    else
+        retile_128x1_body(b.q, b.ld_q, b.scale, b.ld_s, b.qt, b.ld_qt, b.scale_t, b.ld_st, b.cblocks,
+                          blk - a_blocks, PanelLds<8>{red, s_sh, y_sh, tr});
 }
 
 // ---------------------------------------------------------------- 128x128
@@ -619,6 +681,19 @@ hipError_t launch_quant_act_128x1_pair(int64_t tokens, const uint16_t* x0, int64
     const int64_t a_blocks = tokens / 128 * a.cblocks;
     const int64_t blocks = a_blocks + tokens / 128 * b.cblocks;
     hipLaunchKernelGGL(quant_act_128x1_pair_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, tokens, a,
+                       a_blocks, b);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_retile_128x1(int64_t tokens, const uint16_t* x0, int64_t cols0, int64_t ld_x0,
+                                     uint8_t* q0, int64_t ld_q0, float* s0, int64_t ld_s0, const uint8_t* xq,
+                                     int64_t cols1, int64_t ld_xq, const float* xs, int64_t ld_xs, uint8_t* q1,
+                                     int64_t ld_q1, float* s1, int64_t ld_s1, hipStream_t stream) {
+    Act128Args a{x0, cols0, ld_x0, q0, ld_q0, s0, ld_s0, (cols0 + 127) / 128};
+    RetileArgs b{xq, ld_xq, xs, ld_xs, q1, ld_q1, s1, ld_s1, cols1 / 128};
+    const int64_t a_blocks = tokens / 128 * a.cblocks;
+    const int64_t blocks = a_blocks + tokens / 128 * b.cblocks;
+    hipLaunchKernelGGL(quant_retile_128x1_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, tokens, a,
                        a_blocks, b);
     return hipGetLastError();
 }

@@ -189,6 +189,27 @@ int fp8_quantize_act_128x1_pair(int64_t tokens, const uint16_t *x0, int64_t cols
                                 hipStream_t stream);
 
 /*
+ * fp8_quantize_act_128x1_retile -- the two Wgrad operands in one launch when
+ * X comes from the FP8 activation cache: fp8_quantize_act with
+ * FP8Q_TILE_128x1 on x0[tokens][cols0] (dY), and fp8_retile_act_128x1 on the
+ * cached 1x128 codes xq[tokens][ld_xq] and scales xs[cols1/128][ld_xs] of X
+ * (page "Is aI Hitting a Wall?", passage on keeping activations in FP8 for
+ * the backward pass; page dssusan.co.kr Q&A board, Figure 6). Same tiles,
+ * layouts, alignment rules and results, bit for bit, as the two calls; one
+ * launch instead of two.
+ * An operand with no columns (or tokens == 0) is skipped and its pointers
+ * are not read. The two halves of the launch run concurrently, so no output
+ * of one operand (q, scale) may share a byte with an output of the other.
+ * Errors: those of the two calls (FP8Q_ERR_NULL, FP8Q_ERR_SHAPE,
+ *         FP8Q_ERR_ALIGN, FP8Q_ERR_HIP); FP8Q_ERR_SHAPE also when the outputs
+ *         of the two operands overlap.
+ */
+int fp8_quantize_act_128x1_retile(int64_t tokens, const uint16_t *x0, int64_t cols0, int64_t ld_x0, uint8_t *q0,
+                                  int64_t ld_q0, float *scale0, int64_t ld_s0, const uint8_t *xq, int64_t cols1,
+                                  int64_t ld_xq, const float *xs, int64_t ld_xs, uint8_t *q1, int64_t ld_q1,
+                                  float *scale1, int64_t ld_s1, hipStream_t stream);
+
+/*
  * fp8_quantize_weight_grouped -- fp8_quantize_weight over several weight
  * matrices of one shape (say the experts of an MoE layer) in one launch.
  *

@@ -344,6 +344,26 @@ def test_quantize_act_128x1_pair_validation(lib):
     assert _p128(lib, s1=A16b + 0x100) == ERR_SHAPE
 
 
+def _qr(lib, tokens=256, x0=A16, c0=256, ld_x0=256, q0=A16b, ld_q0=256, s0=A4, ld_s0=256, xq=A16c, c1=256,
+        ld_xq=256, xs=A4 + 0x2000, ld_xs=256, q1=A16 + 0x100000, ld_q1=256, s1=A4 + 0x1000, ld_s1=256):
+    return lib.fp8_quantize_act_128x1_retile(tokens, x0, c0, ld_x0, q0, ld_q0, s0, ld_s0, xq, c1, ld_xq, xs, ld_xs,
+                                             q1, ld_q1, s1, ld_s1, None)
+
+
+def test_quantize_act_128x1_retile_validation(lib):
+    assert _qr(lib, tokens=0) == OK
+    assert _qr(lib, c0=0, c1=0, x0=0, q0=0, s0=0, xq=0, xs=0, q1=0, s1=0) == OK   # nothing read or launched
+    assert _qr(lib, tokens=-128) == ERR_SHAPE
+    assert _qr(lib, tokens=200) == ERR_SHAPE
+    assert _qr(lib, c1=136, ld_xq=256, ld_s1=256) == ERR_SHAPE     # the cache is re-tiled in whole 128 columns
+    assert _qr(lib, ld_xs=128) == ERR_SHAPE                        # ld_xs < tokens
+    assert _qr(lib, xq=0) == ERR_NULL
+    assert _qr(lib, xs=A4 + 0x2004) == ERR_ALIGN                   # cache scales 16-byte aligned
+    assert _qr(lib, ld_xs=258) == ERR_ALIGN
+    assert _qr(lib, q1=A16b + 0x400) == ERR_SHAPE                  # outputs of the two halves overlap
+    assert _qr(lib, s1=A4 + 0x100) == ERR_SHAPE
+
+
 def _wg(lib, groups=3, w=A16, n=256, k=384, ld_w=384, sw=256 * 384, q=A16b, ld_q=384, sq=256 * 384,
         s=A4, ld_s=3, ss=6, qt=A16c, ld_qt=256, sqt=384 * 256, st=A4 + 0x1000, ld_st=2, sst=6):
     return lib.fp8_quantize_weight_grouped(groups, w, n, k, ld_w, sw, q, ld_q, sq, s, ld_s, ss,
@@ -369,9 +389,8 @@ def test_quantize_weight_grouped_validation(lib):
 
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
-                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair", "fp8_gemm",
-                 "fp8_grouped_gemm",
-                 "fp8_grouped_gemm_wgrad",
+                 "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair",
+                 "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
                  "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))
 

@@ -113,3 +113,42 @@ def test_retile_empty_is_noop():
     s = torch.empty((2, 0), dtype=torch.float32, device="cuda")
     qt, st = fq.fp8_retile_act_128x1(q, s)
     assert qt.shape == (256, 0) and st.shape == (0, 256)
+
+
+# ---------------------------- dY quantized and the X cache re-tiled, one launch
+
+def test_quant_retile_one_launch_equals_separate_full_size():
+    """The Wgrad config from the cache: dY [8192][2048] quantized 128x1 and
+    the cached X [8192][7168] re-tiled, in one launch, byte-identical to the
+    two separate launches (each pinned to the oracle above)."""
+    g = wl.wgrad()
+    dy = dev_bf16(g["dy"])
+    xq_h, xs_h = oracle.quant_act_1x128(g["x"])
+    xq, xs = dev_codes(xq_h), dev_f32(xs_h)
+    got = fq.fp8_quantize_act_128x1_retile(dy, xq, xs)
+    ref = fq.fp8_quantize_act(dy, "128x1") + fq.fp8_retile_act_128x1(xq, xs)
+    torch.cuda.synchronize()
+    for a, b, tag in zip(got, ref, ("q0", "scale0", "q1", "scale1")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), tag
+
+
+@pytest.mark.parametrize("cols0,cols1", [(136, 256), (8, 128), (0, 384), (264, 0)])
+def test_quant_retile_one_launch_against_the_oracle(cols0, cols1):
+    tokens = 384
+    dy = wl.activation(3, "wgrad", 90, tokens, max(cols0, 8), None)[:, :cols0]
+    x = wl.activation(3, "wgrad", 91, tokens, max(cols1, 128), 50.0)[:, :cols1]
+    xq_h, xs_h = oracle.quant_act_1x128(np.ascontiguousarray(x)) if cols1 else (
+        np.zeros((tokens, 0), np.uint8), np.zeros((0, tokens), np.float32))
+    d0 = dev_bf16(dy) if cols0 else torch.empty((tokens, 0), dtype=torch.bfloat16, device="cuda")
+    xq = dev_codes(xq_h) if cols1 else torch.empty((tokens, 0), dtype=torch.uint8, device="cuda")
+    xs = dev_f32(xs_h) if cols1 else torch.empty((0, tokens), dtype=torch.float32, device="cuda")
+    q0, s0, q1, s1 = fq.fp8_quantize_act_128x1_retile(d0, xq, xs)
+    torch.cuda.synchronize()
+    if cols0:
+        q_ref, s_ref = oracle.quant_act_128x1(np.ascontiguousarray(dy))
+        assert_bits_equal(host_f32(s0), s_ref, "dY scales")
+        assert_bits_equal(host_codes(q0), q_ref, "dY codes")
+    if cols1:
+        qt_ref, st_ref = oracle.retile_128x1(xq_h, xs_h)
+        assert_bits_equal(host_f32(s1), st_ref, "X re-tile scales")
+        assert_bits_equal(host_codes(q1), qt_ref, "X re-tile codes")
