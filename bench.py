@@ -59,6 +59,7 @@ KERNEL_NAMES = {
     "quant_act_128x1_pair": "quant_act_128x1_pair_kernel",
     "quant_retile_128x1": "quant_retile_128x1_kernel",
     "quant_mx": "quant_mx_1x32_kernel",
+    "quant_mx_pair": "quant_mx_1x32_pair_kernel",
     "retile_128x1": "retile_128x1_kernel",
     "gemm": "gemm_kernel",
 }
@@ -197,8 +198,9 @@ class Workload:
             def mx_bytes(r, c):   # bf16 in, codes + one byte per 32 values out
                 return 2 * r * c + r * c + r * c // 32
             self.launches = [
-                Launch("quant_mx", lambda r: fq.fp8_quantize_mx(X[r], q=xq, scale=xs), mx_bytes(m, k)),
-                Launch("quant_mx", lambda r: fq.fp8_quantize_mx(W[r], q=wq, scale=ws), mx_bytes(n, k)),
+                # X and W in 1x32 blocks, one launch
+                Launch("quant_mx_pair", lambda r: fq.fp8_quantize_mx_pair(
+                    X[r], W[r], q0=xq, scale0=xs, q1=wq, scale1=ws), mx_bytes(m, k) + mx_bytes(n, k)),
                 Launch("gemm", lambda r: fq.fp8_gemm_mx(xq, xs, wq, ws, bf16, out=y),
                        m * k + n * k + (m + n) * k // 32 + 2 * m * n, self.flops),
             ]

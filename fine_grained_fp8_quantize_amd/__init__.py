@@ -35,8 +35,9 @@ Layouts (row-major, K contiguous for GEMM operands):
   Wgrad over each expert's token segment.
 * ``fp8_retile_act_128x1(q, scale)`` -- a cached 1x128 activation re-tiled
   into 128x1 token tiles.
-* ``fp8_quantize_mx`` / ``fp8_gemm_mx`` -- the microscaling variant (1x32
-  blocks, E8M0 scales, scaled MFMA).
+* ``fp8_quantize_mx`` / ``fp8_quantize_mx_pair`` / ``fp8_gemm_mx`` -- the
+  microscaling variant (1x32 blocks, E8M0 scales, scaled MFMA); the pair
+  quantizes both GEMM operands in one launch.
 * ``fp8_gemm_tensor`` -- one scale per operand, the whole K sum in the MFMA
   accumulators.
 
@@ -58,6 +59,7 @@ __all__ = [
     "fp8_quantize_act_weight",
     "fp8_quantize_act_128x1_pair",
     "fp8_quantize_act_128x1_retile",
+    "fp8_quantize_mx_pair",
     "fp8_gemm",
     "fp8_grouped_gemm",
     "fp8_grouped_gemm_wgrad",
@@ -110,6 +112,7 @@ def _load() -> ctypes.CDLL:
     L.fp8_quantize_act_128x1_pair.argtypes = [i64, p, i64, i64, p, i64, p, i64, p, i64, i64, p, i64, p, i64, p]
     L.fp8_quantize_act_128x1_retile.argtypes = [i64, p, i64, i64, p, i64, p, i64, p, i64, i64, p, i64, p, i64, p,
                                                 i64, p]
+    L.fp8_quantize_mx_pair.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, i64, i64, p, i64, p, i64, p]
     L.fp8_quantize_weight_grouped.argtypes = [i32, p, i64, i64, i64, i64, p, i64, i64, p, i64, i64,
                                               p, i64, i64, p, i64, i64, p]
     L.fp8_quantize_mx.argtypes = [p, i64, i64, i64, p, i64, p, i64, p]
@@ -124,7 +127,8 @@ def _load() -> ctypes.CDLL:
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
                  "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair",
                  "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
-                 "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
+                 "fp8_quantize_mx", "fp8_quantize_mx_pair", "fp8_gemm_mx", "fp8_retile_act_128x1",
+                 "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
     L.fp8q_status_string.argtypes = [cint]
     L.fp8q_status_string.restype = ctypes.c_char_p
@@ -582,6 +586,36 @@ def fp8_quantize_mx(x: torch.Tensor, q: torch.Tensor | None = None, scale: torch
                                  scale.stride(0), _stream(stream))
     _check(st, "fp8_quantize_mx")
     return q, scale
+
+
+def fp8_quantize_mx_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Tensor | None = None,
+                         scale0: torch.Tensor | None = None, q1: torch.Tensor | None = None,
+                         scale1: torch.Tensor | None = None, stream=None):
+    """Both operands of the microscaling GEMM in one launch, as
+    :func:`fp8_quantize_mx` on each. Returns ``(q0, scale0, q1, scale1)``."""
+    _need_gpu(x0, x1)
+    _rowmajor(x0, "x0")
+    _rowmajor(x1, "x1")
+    if x0.dtype != torch.bfloat16 or x1.dtype != torch.bfloat16:
+        raise Fp8qError("x0 and x1 must be bfloat16")
+    (r0, c0), (r1, c1) = x0.shape, x1.shape
+    dev = x0.device
+    if q0 is None:
+        q0 = torch.empty((r0, c0), dtype=torch.float8_e4m3fn, device=dev)
+    if scale0 is None:
+        scale0 = torch.empty((c0 // 128, r0), dtype=torch.int32, device=dev)
+    if q1 is None:
+        q1 = torch.empty((r1, c1), dtype=torch.float8_e4m3fn, device=dev)
+    if scale1 is None:
+        scale1 = torch.empty((c1 // 128, r1), dtype=torch.int32, device=dev)
+    _need_gpu(q0, scale0, q1, scale1)
+    _codes(q0, "q0")
+    _codes(q1, "q1")
+    st = _load().fp8_quantize_mx_pair(
+        _ptr(x0), r0, c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
+        _ptr(x1), r1, c1, x1.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1), scale1.stride(0), _stream(stream))
+    _check(st, "fp8_quantize_mx_pair")
+    return q0, scale0, q1, scale1
 
 
 def fp8_gemm_mx(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,

@@ -344,6 +344,46 @@ int fp8_quantize_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
     return hip_status(fp8q::launch_quant_mx(x, rows, cols, ld_x, q, ld_q, scale, ld_s, stream));
 }
 
+int fp8_quantize_mx_pair(const uint16_t* x0, int64_t rows0, int64_t cols0, int64_t ld_x0, uint8_t* q0,
+                         int64_t ld_q0, uint32_t* scale0, int64_t ld_s0, const uint16_t* x1, int64_t rows1,
+                         int64_t cols1, int64_t ld_x1, uint8_t* q1, int64_t ld_q1, uint32_t* scale1,
+                         int64_t ld_s1, hipStream_t stream) {
+    // the checks of fp8_quantize_mx on each matrix
+    if (rows0 < 0 || cols0 < 0 || rows1 < 0 || cols1 < 0) return FP8Q_ERR_SHAPE;
+    const uint16_t* xs[2] = {x0, x1};
+    uint8_t* qs[2] = {q0, q1};
+    uint32_t* ss[2] = {scale0, scale1};
+    const int64_t rows[2] = {rows0, rows1}, cols[2] = {cols0, cols1}, ld_x[2] = {ld_x0, ld_x1},
+                  ld_q[2] = {ld_q0, ld_q1}, ld_s[2] = {ld_s0, ld_s1};
+    const bool on[2] = {rows0 > 0 && cols0 > 0, rows1 > 0 && cols1 > 0};
+    for (int i = 0; i < 2; ++i) {
+        if (!on[i]) continue;
+        if (!xs[i] || !qs[i] || !ss[i]) return FP8Q_ERR_NULL;
+        if (cols[i] % 128 != 0 || ld_x[i] < cols[i] || ld_q[i] < cols[i] || ld_s[i] < rows[i])
+            return FP8Q_ERR_SHAPE;
+        if (!aligned(xs[i], 16) || !aligned(qs[i], 16) || !aligned(ss[i], 4) || ld_x[i] % 8 != 0 ||
+            ld_q[i] % 16 != 0)
+            return FP8Q_ERR_ALIGN;
+    }
+    if (!on[0] && !on[1]) return FP8Q_OK;
+    if (on[0] && on[1]) {
+        // the two halves of the launch run concurrently: their outputs must be disjoint
+        const Span o0[2] = {span(q0, rows0, cols0, ld_q0, 1), span(scale0, cols0 / 128, rows0, ld_s0, 4)};
+        const Span o1[2] = {span(q1, rows1, cols1, ld_q1, 1), span(scale1, cols1 / 128, rows1, ld_s1, 4)};
+        for (const Span& a : o0)
+            for (const Span& b : o1)
+                if (overlap(a, b)) return FP8Q_ERR_SHAPE;
+    }
+    int64_t blocks = 0;
+    for (int i = 0; i < 2; ++i)
+        if (on[i]) blocks += (rows[i] + 15) / 16 * (cols[i] / 128) / 4 + 1;
+    if (!grid_ok(blocks)) return FP8Q_ERR_SHAPE;
+    // an empty matrix is skipped: its block range is empty
+    return hip_status(fp8q::launch_quant_mx_pair(x0, on[0] ? rows0 : 0, on[0] ? cols0 : 0, ld_x0, q0, ld_q0, scale0,
+                                                 ld_s0, x1, on[1] ? rows1 : 0, on[1] ? cols1 : 0, ld_x1, q1, ld_q1,
+                                                 scale1, ld_s1, stream));
+}
+
 int fp8_gemm_mx(int64_t m, int64_t n, int64_t k,
                 const uint8_t* a, int64_t lda, const uint32_t* a_scale, int64_t ld_as,
                 const uint8_t* b, int64_t ldb, const uint32_t* b_scale, int64_t ld_bs,

@@ -18,6 +18,10 @@ hipError_t launch_quant_act_scatter(const uint16_t* x, int64_t tokens, int64_t c
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
                            int64_t ld_q, uint32_t* scale, int64_t ld_s, hipStream_t stream);
 
+hipError_t launch_quant_mx_pair(const uint16_t* x0, int64_t rows0, int64_t cols0, int64_t ld_x0, uint8_t* q0,
+                                int64_t ld_q0, uint32_t* s0, int64_t ld_s0, const uint16_t* x1, int64_t rows1,
+                                int64_t cols1, int64_t ld_x1, uint8_t* q1, int64_t ld_q1, uint32_t* s1,
+                                int64_t ld_s1, hipStream_t stream);
 hipError_t launch_quant_act_128x1(const uint16_t* x, int64_t tokens, int64_t cols, int64_t ld_x,
                                   uint8_t* qt, int64_t ld_q, float* scale, int64_t ld_s,
                                   hipStream_t stream);

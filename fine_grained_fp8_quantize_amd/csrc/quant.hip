@@ -119,12 +119,14 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
 // to [-127, 127], -127 for an all-zero block; codes are E4M3_RNE_sat(x / 2^e).
 // Same wave layout as the 1x128 kernel; a 32-element block is one quad of
 // lanes. The scale of row r, slab j is one uint32: byte b = block 4j + b.
-__global__ __launch_bounds__(256) void quant_mx_1x32_kernel(
+// The body of one 256-thread block (block index `block`); the kernels below
+// call it for one matrix, or for both GEMM operands in one grid.
+__device__ __forceinline__ void mx_1x32_body(
     const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
     uint8_t* __restrict__ q, int64_t ld_q, uint32_t* __restrict__ scale, int64_t ld_s,
-    int64_t units) {
+    int64_t units, int64_t block) {
     const int lane = threadIdx.x & 63;
-    const int64_t unit = (int64_t)blockIdx.x * kActWavesPerBlock + (threadIdx.x >> 6);
+    const int64_t unit = block * kActWavesPerBlock + (threadIdx.x >> 6);
     if (unit >= units) return;  // whole wave
     const int64_t rg = unit / slabs;
     const int64_t j = unit - rg * slabs;
@@ -166,6 +168,31 @@ __global__ __launch_bounds__(256) void quant_mx_1x32_kernel(
                 reinterpret_cast<uint8_t*>(scale + j * ld_s + row[u])[c >> 2] = (uint8_t)(e + 127);
         }
     }
+}
+
+__global__ __launch_bounds__(256) void quant_mx_1x32_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t slabs, int64_t ld_x,
+    uint8_t* __restrict__ q, int64_t ld_q, uint32_t* __restrict__ scale, int64_t ld_s,
+    int64_t units) {
+    mx_1x32_body(x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units, (int64_t)blockIdx.x);
+}
+
+// Both operands of the microscaling GEMM in one grid: blocks below a_blocks
+// take units of the first matrix, the rest units of the second.
+struct MxArgs {
+    const uint16_t* x;
+    int64_t rows, slabs, ld_x;
+    uint8_t* q;
+    int64_t ld_q;
+    uint32_t* scale;
+    int64_t ld_s, units;
+};
+
+__global__ __launch_bounds__(256) void quant_mx_1x32_pair_kernel(MxArgs a, int64_t a_blocks, MxArgs b) {
+    const int64_t blk = (int64_t)blockIdx.x;
+    const bool first = blk < a_blocks;
+    const MxArgs& o = first ? a : b;
+    mx_1x32_body(o.x, o.rows, o.slabs, o.ld_x, o.q, o.ld_q, o.scale, o.ld_s, o.units, first ? blk : blk - a_blocks);
 }
 
 // ------------------------------------------------------------------ 128x1
@@ -659,6 +686,20 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_
     const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
     hipLaunchKernelGGL(quant_mx_1x32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_mx_pair(const uint16_t* x0, int64_t rows0, int64_t cols0, int64_t ld_x0, uint8_t* q0,
+                                int64_t ld_q0, uint32_t* s0, int64_t ld_s0, const uint16_t* x1, int64_t rows1,
+                                int64_t cols1, int64_t ld_x1, uint8_t* q1, int64_t ld_q1, uint32_t* s1,
+                                int64_t ld_s1, hipStream_t stream) {
+    MxArgs a{x0, rows0, cols0 / 128, ld_x0, q0, ld_q0, s0, ld_s0, 0};
+    MxArgs b{x1, rows1, cols1 / 128, ld_x1, q1, ld_q1, s1, ld_s1, 0};
+    a.units = (rows0 + kActRowsPerWave - 1) / kActRowsPerWave * a.slabs;
+    b.units = (rows1 + kActRowsPerWave - 1) / kActRowsPerWave * b.slabs;
+    const int64_t a_blocks = (a.units + kActWavesPerBlock - 1) / kActWavesPerBlock;
+    const int64_t blocks = a_blocks + (b.units + kActWavesPerBlock - 1) / kActWavesPerBlock;
+    hipLaunchKernelGGL(quant_mx_1x32_pair_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, a_blocks, b);
     return hipGetLastError();
 }
 

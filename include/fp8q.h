@@ -379,6 +379,23 @@ int fp8_quantize_mx(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld_x,
                     int64_t ld_q, uint32_t *scale, int64_t ld_s, hipStream_t stream);
 
 /*
+ * fp8_quantize_mx_pair -- fp8_quantize_mx on the two operands of the
+ * microscaling GEMM (x0[rows0][cols0] and x1[rows1][cols1]) in one launch,
+ * page "Deepseek Ai News Expert Interview", same passage. Same layouts,
+ * alignment rules and results, bit for bit, as the two calls; one launch
+ * instead of two. A matrix with no rows or columns is skipped and its
+ * pointers are not read. The two halves of the launch run concurrently, so
+ * no output of one matrix (q, scale) may share a byte with an output of the
+ * other.
+ * Errors: those of fp8_quantize_mx; FP8Q_ERR_SHAPE also when the outputs of
+ *         the two matrices overlap.
+ */
+int fp8_quantize_mx_pair(const uint16_t *x0, int64_t rows0, int64_t cols0, int64_t ld_x0, uint8_t *q0,
+                         int64_t ld_q0, uint32_t *scale0, int64_t ld_s0, const uint16_t *x1, int64_t rows1,
+                         int64_t cols1, int64_t ld_x1, uint8_t *q1, int64_t ld_q1, uint32_t *scale1,
+                         int64_t ld_s1, hipStream_t stream);
+
+/*
  * fp8_gemm_mx -- C = dequant_mx(A) * dequant_mx(B)^T.
  *
  * Both operands are K-contiguous MX codes with their scale words (as written

@@ -364,6 +364,25 @@ def test_quantize_act_128x1_retile_validation(lib):
     assert _qr(lib, s1=A4 + 0x100) == ERR_SHAPE
 
 
+def _mxp(lib, x0=A16, r0=64, c0=256, ld_x0=256, q0=A16b, ld_q0=256, s0=A4, ld_s0=64, x1=A16c, r1=40, c1=128,
+         ld_x1=128, q1=A16 + 0x100000, ld_q1=128, s1=A4 + 0x1000, ld_s1=40):
+    return lib.fp8_quantize_mx_pair(x0, r0, c0, ld_x0, q0, ld_q0, s0, ld_s0, x1, r1, c1, ld_x1, q1, ld_q1, s1, ld_s1,
+                                    None)
+
+
+def test_quantize_mx_pair_validation(lib):
+    assert _mxp(lib, r0=0, r1=0) == OK
+    assert _mxp(lib, c0=0, c1=0, x0=0, q0=0, s0=0, x1=0, q1=0, s1=0) == OK   # nothing read or launched
+    assert _mxp(lib, r1=-1) == ERR_SHAPE
+    assert _mxp(lib, c0=200, ld_x0=256, ld_q0=256) == ERR_SHAPE
+    assert _mxp(lib, ld_s1=39) == ERR_SHAPE
+    assert _mxp(lib, q1=0) == ERR_NULL
+    assert _mxp(lib, x0=A16 + 8) == ERR_ALIGN
+    assert _mxp(lib, ld_q1=136) == ERR_ALIGN
+    assert _mxp(lib, q1=A16b + 0x100) == ERR_SHAPE                  # outputs of the two halves overlap
+    assert _mxp(lib, s1=A4 + 0x10) == ERR_SHAPE
+
+
 def _wg(lib, groups=3, w=A16, n=256, k=384, ld_w=384, sw=256 * 384, q=A16b, ld_q=384, sq=256 * 384,
         s=A4, ld_s=3, ss=6, qt=A16c, ld_qt=256, sqt=384 * 256, st=A4 + 0x1000, ld_st=2, sst=6):
     return lib.fp8_quantize_weight_grouped(groups, w, n, k, ld_w, sw, q, ld_q, sq, s, ld_s, ss,
@@ -391,7 +410,8 @@ def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
                  "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair",
                  "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
-                 "fp8_quantize_mx", "fp8_gemm_mx", "fp8_retile_act_128x1", "fp8_gemm_tensor"):
+                 "fp8_quantize_mx", "fp8_quantize_mx_pair", "fp8_gemm_mx", "fp8_retile_act_128x1",
+                 "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))
 
 

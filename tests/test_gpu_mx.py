@@ -126,3 +126,33 @@ def test_mx_gemm_padded_leading_dims():
     a_q, a_e = oracle.quant_mx_1x32(a)
     b_q, b_e = oracle.quant_mx_1x32(b)
     assert_gemm_close(got[:, :n], oracle.gemm_mx(a_q, a_e, b_q, b_e), "mx gemm padded")
+
+
+# ----------------------------------------- both GEMM operands in one launch
+
+def test_mx_pair_equals_separate_launches_full_size():
+    """X and W of the Dense Fprop shapes in one launch: byte-identical to two
+    fp8_quantize_mx launches (each pinned to the oracle at full size above)."""
+    d = wl.dense_fprop()
+    x, w = dev_bf16(d["x"]), dev_bf16(d["w"])
+    got = fq.fp8_quantize_mx_pair(x, w)
+    ref = fq.fp8_quantize_mx(x) + fq.fp8_quantize_mx(w)
+    torch.cuda.synchronize()
+    for a, b, tag in zip(got, ref, ("q0", "scale0", "q1", "scale1")):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), tag
+
+
+@pytest.mark.parametrize("r0,c0,r1,c1", [(17, 384, 130, 256), (1, 128, 0, 128), (0, 256, 33, 512)])
+def test_mx_pair_against_the_oracle(r0, c0, r1, c1):
+    x0 = wl.activation(2, "tiny_fprop", 96, max(r0, 1), c0, 50.0)[:r0]
+    x1 = wl.weight(2, "tiny_fprop", 97, max(r1, 1), c1)[:r1]
+    d0 = dev_bf16(x0) if r0 else torch.empty((0, c0), dtype=torch.bfloat16, device="cuda")
+    d1 = dev_bf16(x1) if r1 else torch.empty((0, c1), dtype=torch.bfloat16, device="cuda")
+    q0, s0, q1, s1 = fq.fp8_quantize_mx_pair(d0, d1)
+    torch.cuda.synchronize()
+    for rows, x, q, s, tag in ((r0, x0, q0, s0, "x0"), (r1, x1, q1, s1, "x1")):
+        if rows == 0:
+            continue
+        q_ref, e_ref = oracle.quant_mx_1x32(np.ascontiguousarray(x))
+        assert_bits_equal(_words_to_bytes(s, rows), e_ref, tag + " E8M0 bytes")
+        assert_bits_equal(host_codes(q), q_ref, tag + " codes")
