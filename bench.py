@@ -5,15 +5,20 @@ already resident in HBM: quantize the operands (activations in 1x128 tiles,
 weights in 128x128 blocks, or both Wgrad operands in 128x1 tiles) and run the
 block-scaled FP8 GEMM, in that order on one stream (``--streams 2`` puts the
 two independent quantizations on two streams; that measures slower). The
-default workload is the dense Fprop layer
-X[4096][7168] x W[4096][7168]^T with bf16 output.
+default workload is the largest single-GPU configuration, the grouped MoE
+Fprop: 8192 tokens [8192][7168] quantized before dispatch into 32 local
+experts (Zipf(1.1) routing, 8192 routed rows, 10112 after 128-padding), the
+32 expert weights [32][4096][7168] quantized in 128x128 blocks, and the
+grouped GEMM with bf16 output.
 
 Prints ONE JSON line: the whole-step throughput in TFLOP/s (2*M*N*K per step),
 the GEMM kernel's roofline (its launches timed with HIP events on the launch
 stream inside the timed region, where only the GEMM is bracketed: each event
 pair costs the step GPU time), every kernel's own time and rate (from a second
 pass with every launch bracketed), and the CPU oracle timed on the host as a
-reported baseline.
+reported baseline. The roofline carries the GEMM's fraction of both peaks,
+dense FP8 MFMA and HBM; ``bound`` names the one its arithmetic intensity
+puts it under.
 
     python bench.py [--steps K] [--warmup W] [--streams 1|2]
                     [--config dense_fprop|dgrad|wgrad|grouped_fprop|grouped_dgrad|
@@ -94,7 +99,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prewarm-s", type=float, default=0.5,
                     help="seconds of untimed steps before the warmup steps (clock ramp)")
-    ap.add_argument("--config", default="dense_fprop", choices=CONFIGS)
+    ap.add_argument("--config", default="grouped_fprop", choices=CONFIGS)
     ap.add_argument("--rotate", type=int, default=3,
                     help="bf16 input sets cycled over the steps, so that the inputs of one "
                          "step are not left in the 256 MiB MALL by the step before")
@@ -382,7 +387,10 @@ class Workload:
             X = sets(d["x"])
             E, n, k = len(rows), 4096, X[0].shape[1]
             # the expert weights of the grouped MoE config (1.9 GB: far beyond the MALL)
-            w = dev(wl.weight(0, "grouped_fprop", 1, E, n, k).reshape(E * n, k))
+            w_bits = wl.weight(0, "grouped_fprop", 1, E, n, k)
+            w = dev(w_bits.reshape(E * n, k))
+            self.host = {"dispatch": d, "w": w_bits}
+            self.bound = "hbm"   # 452 flop/B: below the MFMA/HBM ridge (~629 flop/B)
             tokens = X[0].shape[0]
             m_total = int(d["offsets"][-1])
             real = int(rows.sum())
@@ -488,15 +496,22 @@ def tiny_one_thread(min_seconds: float = 1.0) -> dict:
             "gflops": round(2.0 * m * n * k * steps / dt / 1e9, 4)}
 
 
-def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 200) -> dict:
-    """The oracle, as it stands, on the same Dense Fprop inputs (the whole step)."""
-    import oracle
+def _oracle_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover - informational only
         blas_threads = 1
     omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return max(omp, blas_threads)
+
+
+def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 200) -> dict:
+    """The oracle, as it stands, on the same inputs as the GPU step: whole
+    steps repeated until at least min_seconds of CPU work (at least one)."""
+    import oracle
+    if wl_obj.name == "grouped_fprop":
+        return cpu_baseline_grouped(wl_obj, min_seconds)
     d = wl_obj.host
     m, k = d["x"].shape
     n = d["w"].shape[0]
@@ -515,13 +530,56 @@ def cpu_baseline(wl_obj: Workload, min_seconds: float = 10.0, max_steps: int = 2
     return {
         "value": round(2.0 * m * n * k * steps / dt / 1e12, 4),
         "unit": "TFLOP/s",
-        "cores": max(omp, blas_threads),
+        "cores": _oracle_threads(),
         "kind": "oracle",
         "seconds": round(dt, 3),
         "steps": steps,
         "sample": "%d full steps of the workload (X %dx%d 1x128 quantize, W %dx%d 128x128 "
                   "quantize, float64 dequantize + GEMM): scalar C quantizers with OpenMP and "
                   "numpy float64 matmul" % (steps, m, k, n, k),
+        "cpu_model": cpu_model(),
+        "tiny_fprop_one_thread": tiny_one_thread(),
+    }
+
+
+def cpu_baseline_grouped(wl_obj: Workload, min_seconds: float = 10.0) -> dict:
+    """The oracle's whole grouped MoE Fprop step on the same routed inputs:
+    quantize the 8192 tokens before dispatch and scatter them to their
+    expert-sorted rows, quantize the 32 expert weights in 128x128 blocks,
+    then the float64 per-expert GEMM over the real rows. Whole steps until
+    at least min_seconds (one step is several seconds on the host)."""
+    import numpy as np
+
+    import oracle
+    d, w = wl_obj.host["dispatch"], wl_obj.host["w"]
+    rows, off = d["rows"], d["offsets"]
+    m_total = int(off[-1])
+    E, n, k = w.shape
+    flops = 2.0 * float(rows.sum()) * n * k
+    b_q = np.empty((E, n, k), np.uint8)
+    b_s = np.empty((E, n // 128, k // 128), np.float32)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        a_q, a_s, _ = oracle.quant_act_scatter(d["x"], d["dst_rows"], m_total)
+        for e in range(E):
+            b_q[e], b_s[e] = oracle.quant_weight_128x128(w[e])
+        c = oracle.grouped_gemm(off, rows, a_q, a_s, b_q, b_s)
+        del c
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {
+        "value": round(flops * steps / dt / 1e12, 4),
+        "unit": "TFLOP/s",
+        "cores": _oracle_threads(),
+        "kind": "oracle",
+        "seconds": round(dt, 3),
+        "steps": steps,
+        "sample": "%d full steps of the grouped workload (8192 tokens x %d quantized 1x128 and "
+                  "scattered to %d expert-sorted rows, %d expert weights %dx%d quantized 128x128, "
+                  "float64 per-expert GEMM over %d real rows): scalar C quantizers with OpenMP and "
+                  "numpy float64 matmul" % (steps, k, m_total, E, n, k, int(rows.sum())),
         "cpu_model": cpu_model(),
         "tiny_fprop_one_thread": tiny_one_thread(),
     }
@@ -811,7 +869,12 @@ def main():
                                         "grouped_wgrad_cached": " (grouped over K)",
                                         "mx_fprop": " (microscaling)"}.get(args.config, "")),
             "algorithmic_bytes": int(gemm[0].bytes),
-            "tflops": round(gemm_tflops, 2),
+            "algorithmic_flops": int(gemm[0].flops),
+            # both roofs, whichever binds: dense FP8 MFMA and HBM
+            "mfma": {"achieved": round(gemm_tflops, 2), "peak": FP8_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / FP8_DENSE_PEAK_TFLOPS, 4)},
+            "hbm": {"achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gemm_gbs / HBM_PEAK_GBS, 4)},
             "ms": round(gemm_ms, 4),
             "ms_median": round(gemm_timed[len(gemm_timed) // 2], 4),
             "timing": "event pair around every GEMM launch of the timed steps",

@@ -74,7 +74,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+# FP8Q_LIBRARY names another build of the same C ABI (the sanitizer build of
+# the host-side layer, for the CPU test suites); by default the in-tree one.
+_LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(_HERE, "libfp8q.so")
 
 TILE_1x128 = 0
 TILE_128x1 = 1
@@ -184,6 +186,34 @@ def _codes(t: torch.Tensor, name: str) -> torch.Tensor:
     raise Fp8qError("%s must hold E4M3 codes (float8_e4m3fn or uint8), got %s" % (name, t.dtype))
 
 
+def _empty(shape, dtype, device, stream):
+    """A new output tensor. With an explicit ``stream`` the memory is taken on
+    that stream, the one the kernel writes it on, so that the caching
+    allocator does not hand the block to other work while the kernel runs."""
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _check_tensor(t: torch.Tensor, shape, dtypes, name: str) -> None:
+    """Exact shape, an accepted dtype and a unit stride in the last dimension:
+    the C ABI sees only a pointer and leading dimensions, so a tensor smaller
+    than the launch assumes would be written or read out of bounds."""
+    if t.dtype not in dtypes:
+        raise Fp8qError("%s has dtype %s, expected %s" % (name, t.dtype, " or ".join(str(d) for d in dtypes)))
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise Fp8qError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(int(v) for v in shape)))
+    if t.numel() > 0 and t.stride(-1) != 1:
+        raise Fp8qError("%s must have a unit stride in its last dimension" % name)
+    if t.numel() > 0 and any(t.stride(i) < 0 for i in range(t.dim())):
+        raise Fp8qError("%s has a negative stride" % name)
+
+
+_CODES = (torch.float8_e4m3fn, torch.uint8)
+_F32 = (torch.float32,)
+
+
 # ------------------------------------------------------------- quantization
 
 def fp8_quantize_act(x: torch.Tensor, tiling: str = "1x128", q: torch.Tensor | None = None,
@@ -194,7 +224,7 @@ def fp8_quantize_act(x: torch.Tensor, tiling: str = "1x128", q: torch.Tensor | N
     ``tiling="128x1"``: returns ``q[cols][rows]`` (transposed, token-contiguous)
     and ``scale[rows/128][cols]``.
     """
-    _need_gpu(x)
+    _need_gpu(x, q, scale)
     _rowmajor(x, "x")
     if x.dtype != torch.bfloat16:
         raise Fp8qError("x must be bfloat16")
@@ -203,18 +233,14 @@ def fp8_quantize_act(x: torch.Tensor, tiling: str = "1x128", q: torch.Tensor | N
     if t is None:
         raise Fp8qError("tiling must be '1x128' or '128x1'")
     dev = x.device
-    if t == TILE_1x128:
-        if q is None:
-            q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
-        if scale is None:
-            scale = torch.empty((cols // 128, rows), dtype=torch.float32, device=dev)
-    else:
-        if q is None:
-            q = torch.empty((cols, rows), dtype=torch.float8_e4m3fn, device=dev)
-        if scale is None:
-            scale = torch.empty((rows // 128, cols), dtype=torch.float32, device=dev)
-    _need_gpu(q, scale)
-    _codes(q, "q")
+    q_shape = (rows, cols) if t == TILE_1x128 else (cols, rows)
+    s_shape = (cols // 128, rows) if t == TILE_1x128 else (rows // 128, cols)
+    if q is None:
+        q = _empty(q_shape, torch.float8_e4m3fn, dev, stream)
+    if scale is None:
+        scale = _empty(s_shape, torch.float32, dev, stream)
+    _check_tensor(q, q_shape, _CODES, "q")
+    _check_tensor(scale, s_shape, _F32, "scale")
     st = _load().fp8_quantize_act(_ptr(x), rows, cols, x.stride(0), t, _ptr(q), q.stride(0),
                                   _ptr(scale), scale.stride(0), _stream(stream))
     _check(st, "fp8_quantize_act")
@@ -232,7 +258,7 @@ def fp8_quantize_act_scatter(x: torch.Tensor, dst_rows: torch.Tensor, m_total: i
     ``q[m_total][cols]`` and ``scale[cols/128][m_total]``; rows no route names
     (segment padding) are left as they were.
     """
-    _need_gpu(x, dst_rows)
+    _need_gpu(x, dst_rows, q, scale)
     _rowmajor(x, "x")
     if not dst_rows.is_contiguous():
         raise Fp8qError("dst_rows must be contiguous [tokens][topk]")
@@ -244,11 +270,11 @@ def fp8_quantize_act_scatter(x: torch.Tensor, dst_rows: torch.Tensor, m_total: i
     topk = dst_rows.shape[1]
     dev = x.device
     if q is None:
-        q = torch.empty((m_total, cols), dtype=torch.float8_e4m3fn, device=dev)
+        q = _empty((m_total, cols), torch.float8_e4m3fn, dev, stream)
     if scale is None:
-        scale = torch.empty((cols // 128, m_total), dtype=torch.float32, device=dev)
-    _need_gpu(q, scale)
-    _codes(q, "q")
+        scale = _empty((cols // 128, m_total), torch.float32, dev, stream)
+    _check_tensor(q, (m_total, cols), _CODES, "q")
+    _check_tensor(scale, (cols // 128, m_total), _F32, "scale")
     st = _load().fp8_quantize_act_scatter(_ptr(x), tokens, cols, x.stride(0), topk, _ptr(dst_rows),
                                           m_total, _ptr(q), q.stride(0), _ptr(scale),
                                           scale.stride(0), _stream(stream))
@@ -264,22 +290,25 @@ def fp8_quantize_weight(w: torch.Tensor, transposed: bool = False, q: torch.Tens
     Returns ``(q, scale)``, or ``(q, scale, q_t, scale_t)`` when ``transposed``
     (``q_t[k][n]``, ``scale_t[k/128][n/128]``: the exact transpose, for Dgrad).
     """
-    _need_gpu(w)
+    _need_gpu(w, q, scale, q_t, scale_t)
     _rowmajor(w, "w")
     if w.dtype != torch.bfloat16:
         raise Fp8qError("w must be bfloat16")
     n, k = w.shape
     dev = w.device
     if q is None:
-        q = torch.empty((n, k), dtype=torch.float8_e4m3fn, device=dev)
+        q = _empty((n, k), torch.float8_e4m3fn, dev, stream)
     if scale is None:
-        scale = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
+        scale = _empty((n // 128, k // 128), torch.float32, dev, stream)
+    _check_tensor(q, (n, k), _CODES, "q")
+    _check_tensor(scale, (n // 128, k // 128), _F32, "scale")
     if transposed:
         if q_t is None:
-            q_t = torch.empty((k, n), dtype=torch.float8_e4m3fn, device=dev)
+            q_t = _empty((k, n), torch.float8_e4m3fn, dev, stream)
         if scale_t is None:
-            scale_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device=dev)
-    _need_gpu(q, scale, q_t, scale_t)
+            scale_t = _empty((k // 128, n // 128), torch.float32, dev, stream)
+        _check_tensor(q_t, (k, n), _CODES, "q_t")
+        _check_tensor(scale_t, (k // 128, n // 128), _F32, "scale_t")
     st = _load().fp8_quantize_weight(
         _ptr(w), n, k, w.stride(0), _ptr(q), q.stride(0), _ptr(scale), scale.stride(0),
         _ptr(q_t if transposed else None), q_t.stride(0) if transposed else 0,
@@ -299,7 +328,7 @@ def fp8_quantize_act_weight(x: torch.Tensor, w: torch.Tensor, transposed: bool =
 
     Returns ``(q, scale, wq, wscale)`` or, transposed, ``(q, scale, wq,
     wscale, wq_t, wscale_t)``."""
-    _need_gpu(x, w)
+    _need_gpu(x, w, q, scale, wq, wscale, wq_t, wscale_t)
     _rowmajor(x, "x")
     _rowmajor(w, "w")
     if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
@@ -308,21 +337,24 @@ def fp8_quantize_act_weight(x: torch.Tensor, w: torch.Tensor, transposed: bool =
     n, k = w.shape
     dev = x.device
     if q is None:
-        q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=dev)
+        q = _empty((rows, cols), torch.float8_e4m3fn, dev, stream)
     if scale is None:
-        scale = torch.empty((cols // 128, rows), dtype=torch.float32, device=dev)
+        scale = _empty((cols // 128, rows), torch.float32, dev, stream)
     if wq is None:
-        wq = torch.empty((n, k), dtype=torch.float8_e4m3fn, device=dev)
+        wq = _empty((n, k), torch.float8_e4m3fn, dev, stream)
     if wscale is None:
-        wscale = torch.empty((n // 128, k // 128), dtype=torch.float32, device=dev)
+        wscale = _empty((n // 128, k // 128), torch.float32, dev, stream)
+    _check_tensor(q, (rows, cols), _CODES, "q")
+    _check_tensor(scale, (cols // 128, rows), _F32, "scale")
+    _check_tensor(wq, (n, k), _CODES, "wq")
+    _check_tensor(wscale, (n // 128, k // 128), _F32, "wscale")
     if transposed:
         if wq_t is None:
-            wq_t = torch.empty((k, n), dtype=torch.float8_e4m3fn, device=dev)
+            wq_t = _empty((k, n), torch.float8_e4m3fn, dev, stream)
         if wscale_t is None:
-            wscale_t = torch.empty((k // 128, n // 128), dtype=torch.float32, device=dev)
-    _need_gpu(q, scale, wq, wscale, wq_t, wscale_t)
-    _codes(q, "q")
-    _codes(wq, "wq")
+            wscale_t = _empty((k // 128, n // 128), torch.float32, dev, stream)
+        _check_tensor(wq_t, (k, n), _CODES, "wq_t")
+        _check_tensor(wscale_t, (k // 128, n // 128), _F32, "wscale_t")
     st = _load().fp8_quantize_act_weight(
         _ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0), _ptr(scale), scale.stride(0),
         _ptr(w), n, k, w.stride(0), _ptr(wq), wq.stride(0), _ptr(wscale), wscale.stride(0),
@@ -332,13 +364,30 @@ def fp8_quantize_act_weight(x: torch.Tensor, w: torch.Tensor, transposed: bool =
     return (q, scale, wq, wscale, wq_t, wscale_t) if transposed else (q, scale, wq, wscale)
 
 
+def _outputs_128x1(tokens, c0, c1, dev, stream, q0, scale0, q1, scale1):
+    """Outputs of the two 128x1 operands: allocated when absent, checked otherwise."""
+    if q0 is None:
+        q0 = _empty((c0, tokens), torch.float8_e4m3fn, dev, stream)
+    if scale0 is None:
+        scale0 = _empty((tokens // 128, c0), torch.float32, dev, stream)
+    if q1 is None:
+        q1 = _empty((c1, tokens), torch.float8_e4m3fn, dev, stream)
+    if scale1 is None:
+        scale1 = _empty((tokens // 128, c1), torch.float32, dev, stream)
+    _check_tensor(q0, (c0, tokens), _CODES, "q0")
+    _check_tensor(scale0, (tokens // 128, c0), _F32, "scale0")
+    _check_tensor(q1, (c1, tokens), _CODES, "q1")
+    _check_tensor(scale1, (tokens // 128, c1), _F32, "scale1")
+    return q0, scale0, q1, scale1
+
+
 def fp8_quantize_act_128x1_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Tensor | None = None,
                                 scale0: torch.Tensor | None = None, q1: torch.Tensor | None = None,
                                 scale1: torch.Tensor | None = None, stream=None):
     """The two Wgrad operands (``x0 = dY``, ``x1 = X``, one token count) in
     128x1 token tiles in one launch, as :func:`fp8_quantize_act` with
     ``tiling="128x1"`` on each. Returns ``(q0, scale0, q1, scale1)``."""
-    _need_gpu(x0, x1)
+    _need_gpu(x0, x1, q0, scale0, q1, scale1)
     _rowmajor(x0, "x0")
     _rowmajor(x1, "x1")
     if x0.dtype != torch.bfloat16 or x1.dtype != torch.bfloat16:
@@ -347,18 +396,7 @@ def fp8_quantize_act_128x1_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Te
     if x1.shape[0] != tokens:
         raise Fp8qError("x0 and x1 must have the same token count")
     c1 = x1.shape[1]
-    dev = x0.device
-    if q0 is None:
-        q0 = torch.empty((c0, tokens), dtype=torch.float8_e4m3fn, device=dev)
-    if scale0 is None:
-        scale0 = torch.empty((tokens // 128, c0), dtype=torch.float32, device=dev)
-    if q1 is None:
-        q1 = torch.empty((c1, tokens), dtype=torch.float8_e4m3fn, device=dev)
-    if scale1 is None:
-        scale1 = torch.empty((tokens // 128, c1), dtype=torch.float32, device=dev)
-    _need_gpu(q0, scale0, q1, scale1)
-    _codes(q0, "q0")
-    _codes(q1, "q1")
+    q0, scale0, q1, scale1 = _outputs_128x1(tokens, c0, c1, x0.device, stream, q0, scale0, q1, scale1)
     st = _load().fp8_quantize_act_128x1_pair(
         tokens, _ptr(x0), c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
         _ptr(x1), c1, x1.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1), scale1.stride(0), _stream(stream))
@@ -373,31 +411,18 @@ def fp8_quantize_act_128x1_retile(x0: torch.Tensor, xq: torch.Tensor, xs: torch.
     ``x0`` (dY, bf16) in 128x1 token tiles as :func:`fp8_quantize_act`, and the
     cached 1x128 codes ``xq[tokens][cols]`` with scales ``xs[cols/128][tokens]``
     re-tiled as :func:`fp8_retile_act_128x1`. Returns ``(q0, scale0, q1, scale1)``."""
-    _need_gpu(x0, xq, xs)
+    _need_gpu(x0, xq, xs, q0, scale0, q1, scale1)
     _rowmajor(x0, "x0")
     _rowmajor(xq, "xq")
-    _rowmajor(xs, "xs")
     if x0.dtype != torch.bfloat16:
         raise Fp8qError("x0 must be bfloat16")
     _codes(xq, "xq")
-    if xs.dtype != torch.float32:
-        raise Fp8qError("xs must be float32")
     tokens, c0 = x0.shape
     if xq.shape[0] != tokens:
         raise Fp8qError("x0 and xq must have the same token count")
     c1 = xq.shape[1]
-    dev = x0.device
-    if q0 is None:
-        q0 = torch.empty((c0, tokens), dtype=torch.float8_e4m3fn, device=dev)
-    if scale0 is None:
-        scale0 = torch.empty((tokens // 128, c0), dtype=torch.float32, device=dev)
-    if q1 is None:
-        q1 = torch.empty((c1, tokens), dtype=torch.float8_e4m3fn, device=dev)
-    if scale1 is None:
-        scale1 = torch.empty((tokens // 128, c1), dtype=torch.float32, device=dev)
-    _need_gpu(q0, scale0, q1, scale1)
-    _codes(q0, "q0")
-    _codes(q1, "q1")
+    _check_tensor(xs, (c1 // 128, tokens), _F32, "xs")
+    q0, scale0, q1, scale1 = _outputs_128x1(tokens, c0, c1, x0.device, stream, q0, scale0, q1, scale1)
     st = _load().fp8_quantize_act_128x1_retile(
         tokens, _ptr(x0), c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
         _ptr(xq), c1, xq.stride(0), _ptr(xs), xs.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1),
@@ -416,7 +441,7 @@ def fp8_quantize_weight_grouped(w: torch.Tensor, transposed: bool = False, q: to
     also ``q_t[E][k][n]`` and ``scale_t[E][k/128][n/128]`` (each expert's exact
     transpose, contiguous per expert, for Dgrad).
     """
-    _need_gpu(w)
+    _need_gpu(w, q, scale, q_t, scale_t)
     if w.dtype != torch.bfloat16:
         raise Fp8qError("w must be bfloat16")
     if w.dim() != 3 or w.stride(2) != 1:
@@ -424,19 +449,18 @@ def fp8_quantize_weight_grouped(w: torch.Tensor, transposed: bool = False, q: to
     groups, n, k = w.shape
     dev = w.device
     if q is None:
-        q = torch.empty((groups, n, k), dtype=torch.float8_e4m3fn, device=dev)
+        q = _empty((groups, n, k), torch.float8_e4m3fn, dev, stream)
     if scale is None:
-        scale = torch.empty((groups, n // 128, k // 128), dtype=torch.float32, device=dev)
+        scale = _empty((groups, n // 128, k // 128), torch.float32, dev, stream)
+    _check_tensor(q, (groups, n, k), _CODES, "q")
+    _check_tensor(scale, (groups, n // 128, k // 128), _F32, "scale")
     if transposed:
         if q_t is None:
-            q_t = torch.empty((groups, k, n), dtype=torch.float8_e4m3fn, device=dev)
+            q_t = _empty((groups, k, n), torch.float8_e4m3fn, dev, stream)
         if scale_t is None:
-            scale_t = torch.empty((groups, k // 128, n // 128), dtype=torch.float32, device=dev)
-    _need_gpu(q, scale, q_t, scale_t)
-    for name, t in (("q", q), ("scale", scale)) + ((("q_t", q_t), ("scale_t", scale_t)) if transposed else ()):
-        if t.dim() != 3 or t.stride(2) != 1:
-            raise Fp8qError("%s must be a 3-d tensor with a contiguous last dimension" % name)
-    _codes(q, "q")
+            scale_t = _empty((groups, k // 128, n // 128), torch.float32, dev, stream)
+        _check_tensor(q_t, (groups, k, n), _CODES, "q_t")
+        _check_tensor(scale_t, (groups, k // 128, n // 128), _F32, "scale_t")
     st = _load().fp8_quantize_weight_grouped(
         groups, _ptr(w), n, k, w.stride(1), w.stride(0),
         _ptr(q), q.stride(1), q.stride(0), _ptr(scale), scale.stride(1), scale.stride(0),
@@ -458,13 +482,23 @@ def _out_code(out_dtype) -> int:
     raise Fp8qError("out_dtype must be torch.bfloat16 or torch.float32")
 
 
+def _gemm_out(out, shape, out_dtype, dev, stream):
+    """The GEMM output: allocated when absent; otherwise its dtype must be
+    ``out_dtype`` (the kernels write elements of that size) and its shape
+    exactly ``shape``, with unit column stride."""
+    if out is None:
+        out = _empty(shape, out_dtype, dev, stream)
+    _check_tensor(out, shape, (out_dtype,), "out")
+    return out
+
+
 def fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
              b_scale_kind: str = "block", out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
              stream=None) -> torch.Tensor:
     """``C[m][n] = sum_k deq(A)[m][k] deq(B)[n][k]`` with per-128-slab promotion.
 
     ``a[m][k]`` codes with ``a_scale[k/128][m]``; ``b[n][k]`` codes with
-    ``b_scale[n/128][k/128]`` (``"block"``) or ``b_scale[k/128][n]`` (``"row"``).
+    ``b_scale[ceil(n/128)][k/128]`` (``"block"``) or ``b_scale[k/128][n]`` (``"row"``).
     """
     _need_gpu(a, a_scale, b, b_scale, out)
     _rowmajor(a, "a")
@@ -479,12 +513,10 @@ def fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: t
     if kind is None:
         raise Fp8qError("b_scale_kind must be 'block' or 'row'")
     oc = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    elif out.dtype != out_dtype:
-        raise Fp8qError("out has dtype %s, expected %s" % (out.dtype, out_dtype))
-    if a_scale.dtype != torch.float32 or b_scale.dtype != torch.float32:
-        raise Fp8qError("scales must be float32")
+    _check_tensor(a_scale, (k // 128, m), _F32, "a_scale")
+    _check_tensor(b_scale, ((n + 127) // 128, k // 128) if kind == BSCALE_BLOCK128 else (k // 128, n),
+                  _F32, "b_scale")
+    out = _gemm_out(out, (m, n), out_dtype, a.device, stream)
     st = _load().fp8_gemm(m, n, k, _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
                           _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0), kind,
                           _ptr(out), out.stride(0), oc, _stream(stream))
@@ -508,16 +540,21 @@ def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | Non
     _codes(b, "b")
     if group_offsets.dtype != torch.int32 or (group_rows is not None and group_rows.dtype != torch.int32):
         raise Fp8qError("group_offsets / group_rows must be int32")
-    if b.dim() != 3 or b.stride(2) != 1 or b_scale.dim() != 3:
-        raise Fp8qError("b must be [E][n][k] and b_scale [E][n/128][k/128]")
+    if b.dim() != 3 or b.stride(2) != 1:
+        raise Fp8qError("b must be [E][n][k] with k contiguous")
     groups = b.shape[0]
-    if group_offsets.numel() != groups + 1:
-        raise Fp8qError("group_offsets needs E+1 entries")
+    if group_offsets.dim() != 1 or group_offsets.numel() != groups + 1 or not group_offsets.is_contiguous():
+        raise Fp8qError("group_offsets needs E+1 contiguous entries")
+    if group_rows is not None and (group_rows.numel() != groups or not group_rows.is_contiguous()):
+        raise Fp8qError("group_rows needs E contiguous entries")
     m_total, k = a.shape
     n = b.shape[1]
+    if b.shape[2] != k:
+        raise Fp8qError("a and b disagree on K (%d vs %d)" % (k, b.shape[2]))
     oc = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((m_total, n), dtype=out_dtype, device=a.device)
+    _check_tensor(a_scale, (k // 128, m_total), _F32, "a_scale")
+    _check_tensor(b_scale, (groups, n // 128, k // 128), _F32, "b_scale")
+    out = _gemm_out(out, (m_total, n), out_dtype, a.device, stream)
     st = _load().fp8_grouped_gemm(
         groups, _ptr(group_offsets), _ptr(group_rows), m_total, n, k,
         _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
@@ -543,18 +580,17 @@ def fp8_grouped_gemm_wgrad(group_offsets: torch.Tensor, a: torch.Tensor, a_scale
     _rowmajor(b, "b")
     _codes(a, "a")
     _codes(b, "b")
-    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1:
-        raise Fp8qError("group_offsets must be a 1-D int32 tensor")
+    if group_offsets.dtype != torch.int32 or group_offsets.dim() != 1 or not group_offsets.is_contiguous():
+        raise Fp8qError("group_offsets must be a contiguous 1-D int32 tensor")
     groups = group_offsets.numel() - 1
     m, k_total = a.shape
     n = b.shape[0]
     if b.shape[1] != k_total:
         raise Fp8qError("a and b must cover the same tokens")
     oc = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((groups, m, n), dtype=out_dtype, device=a.device)
-    if out.dim() != 3 or out.stride(2) != 1:
-        raise Fp8qError("out must be [E][m][n] with unit column stride")
+    _check_tensor(a_scale, (k_total // 128, m), _F32, "a_scale")
+    _check_tensor(b_scale, (k_total // 128, n), _F32, "b_scale")
+    out = _gemm_out(out, (groups, m, n), out_dtype, a.device, stream)
     st = _load().fp8_grouped_gemm_wgrad(
         groups, _ptr(group_offsets), k_total, m, n,
         _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
@@ -566,22 +602,25 @@ def fp8_grouped_gemm_wgrad(group_offsets: torch.Tensor, a: torch.Tensor, a_scale
 
 # ------------------------------------------------------------- microscaling
 
+_WORDS = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
 def fp8_quantize_mx(x: torch.Tensor, q: torch.Tensor | None = None, scale: torch.Tensor | None = None,
                     stream=None):
     """Microscaling quantization (32-element blocks along each row, E8M0
     power-of-two scales, E4M3 codes). Returns ``q[rows][cols]`` and the scale
     words ``scale[cols/128][rows]`` (int32 tensor of 4 E8M0 bytes each)."""
-    _need_gpu(x)
+    _need_gpu(x, q, scale)
     _rowmajor(x, "x")
     if x.dtype != torch.bfloat16:
         raise Fp8qError("x must be bfloat16")
     rows, cols = x.shape
     if q is None:
-        q = torch.empty((rows, cols), dtype=torch.float8_e4m3fn, device=x.device)
+        q = _empty((rows, cols), torch.float8_e4m3fn, x.device, stream)
     if scale is None:
-        scale = torch.empty((cols // 128, rows), dtype=torch.int32, device=x.device)
-    _need_gpu(q, scale)
-    _codes(q, "q")
+        scale = _empty((cols // 128, rows), torch.int32, x.device, stream)
+    _check_tensor(q, (rows, cols), _CODES, "q")
+    _check_tensor(scale, (cols // 128, rows), _WORDS, "scale")
     st = _load().fp8_quantize_mx(_ptr(x), rows, cols, x.stride(0), _ptr(q), q.stride(0), _ptr(scale),
                                  scale.stride(0), _stream(stream))
     _check(st, "fp8_quantize_mx")
@@ -593,7 +632,7 @@ def fp8_quantize_mx_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Tensor | 
                          scale1: torch.Tensor | None = None, stream=None):
     """Both operands of the microscaling GEMM in one launch, as
     :func:`fp8_quantize_mx` on each. Returns ``(q0, scale0, q1, scale1)``."""
-    _need_gpu(x0, x1)
+    _need_gpu(x0, x1, q0, scale0, q1, scale1)
     _rowmajor(x0, "x0")
     _rowmajor(x1, "x1")
     if x0.dtype != torch.bfloat16 or x1.dtype != torch.bfloat16:
@@ -601,16 +640,17 @@ def fp8_quantize_mx_pair(x0: torch.Tensor, x1: torch.Tensor, q0: torch.Tensor | 
     (r0, c0), (r1, c1) = x0.shape, x1.shape
     dev = x0.device
     if q0 is None:
-        q0 = torch.empty((r0, c0), dtype=torch.float8_e4m3fn, device=dev)
+        q0 = _empty((r0, c0), torch.float8_e4m3fn, dev, stream)
     if scale0 is None:
-        scale0 = torch.empty((c0 // 128, r0), dtype=torch.int32, device=dev)
+        scale0 = _empty((c0 // 128, r0), torch.int32, dev, stream)
     if q1 is None:
-        q1 = torch.empty((r1, c1), dtype=torch.float8_e4m3fn, device=dev)
+        q1 = _empty((r1, c1), torch.float8_e4m3fn, dev, stream)
     if scale1 is None:
-        scale1 = torch.empty((c1 // 128, r1), dtype=torch.int32, device=dev)
-    _need_gpu(q0, scale0, q1, scale1)
-    _codes(q0, "q0")
-    _codes(q1, "q1")
+        scale1 = _empty((c1 // 128, r1), torch.int32, dev, stream)
+    _check_tensor(q0, (r0, c0), _CODES, "q0")
+    _check_tensor(scale0, (c0 // 128, r0), _WORDS, "scale0")
+    _check_tensor(q1, (r1, c1), _CODES, "q1")
+    _check_tensor(scale1, (c1 // 128, r1), _WORDS, "scale1")
     st = _load().fp8_quantize_mx_pair(
         _ptr(x0), r0, c0, x0.stride(0), _ptr(q0), q0.stride(0), _ptr(scale0), scale0.stride(0),
         _ptr(x1), r1, c1, x1.stride(0), _ptr(q1), q1.stride(0), _ptr(scale1), scale1.stride(0), _stream(stream))
@@ -628,10 +668,13 @@ def fp8_gemm_mx(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale
     _codes(a, "a")
     _codes(b, "b")
     m, k = a.shape
-    n = b.shape[0]
+    n, kb = b.shape
+    if kb != k:
+        raise Fp8qError("a and b disagree on K (%d vs %d)" % (k, kb))
     oc = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
+    _check_tensor(a_scale, (k // 128, m), _WORDS, "a_scale")
+    _check_tensor(b_scale, (k // 128, n), _WORDS, "b_scale")
+    out = _gemm_out(out, (m, n), out_dtype, a.device, stream)
     st = _load().fp8_gemm_mx(m, n, k, _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
                              _ptr(b), b.stride(0), _ptr(b_scale), b_scale.stride(0),
                              _ptr(out), out.stride(0), oc, _stream(stream))
@@ -646,16 +689,15 @@ def fp8_retile_act_128x1(q: torch.Tensor, scale: torch.Tensor, q_t: torch.Tensor
     ``q_t[cols][tokens]`` and scales ``scale_t[tokens/128][cols]``."""
     _need_gpu(q, scale, q_t, scale_t)
     _rowmajor(q, "q")
-    _rowmajor(scale, "scale")
     _codes(q, "q")
-    if scale.dtype != torch.float32:
-        raise Fp8qError("scale must be float32")
     tokens, cols = q.shape
+    _check_tensor(scale, (cols // 128, tokens), _F32, "scale")
     if q_t is None:
-        q_t = torch.empty((cols, tokens), dtype=torch.float8_e4m3fn, device=q.device)
+        q_t = _empty((cols, tokens), torch.float8_e4m3fn, q.device, stream)
     if scale_t is None:
-        scale_t = torch.empty((tokens // 128, cols), dtype=torch.float32, device=q.device)
-    _codes(q_t, "q_t")
+        scale_t = _empty((tokens // 128, cols), torch.float32, q.device, stream)
+    _check_tensor(q_t, (cols, tokens), _CODES, "q_t")
+    _check_tensor(scale_t, (tokens // 128, cols), _F32, "scale_t")
     st = _load().fp8_retile_act_128x1(_ptr(q), tokens, cols, q.stride(0), _ptr(scale), scale.stride(0),
                                       _ptr(q_t), q_t.stride(0), _ptr(scale_t), scale_t.stride(0),
                                       _stream(stream))
@@ -682,10 +724,7 @@ def fp8_gemm_tensor(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_s
     if a_scale.numel() != 1 or b_scale.numel() != 1:
         raise Fp8qError("per-tensor scales hold one element each")
     oc = _out_code(out_dtype)
-    if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=a.device)
-    elif out.dtype != out_dtype:
-        raise Fp8qError("out has dtype %s, expected %s" % (out.dtype, out_dtype))
+    out = _gemm_out(out, (m, n), out_dtype, a.device, stream)
     st = _load().fp8_gemm_tensor(m, n, k, _ptr(a), a.stride(0), _ptr(a_scale), _ptr(b), b.stride(0),
                                  _ptr(b_scale), _ptr(out), out.stride(0), oc, _stream(stream))
     _check(st, "fp8_gemm_tensor")

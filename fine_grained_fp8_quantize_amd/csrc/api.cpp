@@ -6,7 +6,11 @@
 // synchronizes.
 #include "fp8q.h"
 
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <vector>
 
 #include "launch.h"
 
@@ -35,6 +39,37 @@ Span span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t elem) {
     return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * elem)};
 }
 bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// FP8Q_DEBUG=1 in the environment (read on every grouped call): the grouped
+// entry points copy the device arrays that describe the expert segments to
+// the host and check the contract their kernels trust. This synchronizes
+// the caller's stream, so it is off by default.
+bool debug_checks() {
+    const char* v = getenv("FP8Q_DEBUG");
+    return v && v[0] == '1' && v[1] == '\0';
+}
+
+// group_offsets[0] == 0, non-decreasing multiples of 128 ending at total;
+// 0 <= group_rows[e] <= segment e (when given).
+int check_segments_on_host(int32_t groups, const int32_t* group_offsets, const int32_t* group_rows, int64_t total,
+                           hipStream_t stream) {
+    std::vector<int32_t> off(groups + 1), rows(group_rows ? groups : 0);
+    hipError_t e = hipMemcpyAsync(off.data(), group_offsets, off.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                                  stream);
+    if (e == hipSuccess && group_rows)
+        e = hipMemcpyAsync(rows.data(), group_rows, rows.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+    if (off[0] != 0 || off[groups] != total) return FP8Q_ERR_SHAPE;
+    for (int32_t g = 0; g < groups; ++g) {
+        if (off[g + 1] < off[g] || off[g + 1] % 128 != 0) return FP8Q_ERR_SHAPE;
+        if (group_rows && (rows[g] < 0 || rows[g] > off[g + 1] - off[g])) return FP8Q_ERR_SHAPE;
+    }
+    return FP8Q_OK;
+}
+
+// blocks * ld_bs < FP8Q_MAX_BSCALE_SPAN without overflowing int64 (blocks >= 1)
+bool bscale_span_ok(int64_t blocks, int64_t ld_bs) { return ld_bs < FP8Q_MAX_BSCALE_SPAN / blocks; }
 
 }  // namespace
 
@@ -250,6 +285,8 @@ static int check_gemm_common(int64_t m, int64_t n, int64_t k, const uint8_t* a, 
     // k == 0: C is all zeros; A, B and their scales are not read (may be NULL)
     if (!c || (k > 0 && (!a || !b || !a_scale || !b_scale))) return FP8Q_ERR_NULL;
     if (k % 128 != 0 || ldc < n || (k > 0 && (lda < k || ldb < k || ld_as < m))) return FP8Q_ERR_SHAPE;
+    // tile rows are addressed by 32-bit offsets from the tile origin
+    if (k > 0 && (lda > FP8Q_MAX_GEMM_LD || ldb > FP8Q_MAX_GEMM_LD)) return FP8Q_ERR_SHAPE;
     if (!aligned(c, 16) || ldc % 8 != 0) return FP8Q_ERR_ALIGN;
     if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
                   lda % 16 != 0 || ldb % 16 != 0))
@@ -266,7 +303,9 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
     if (m == 0 || n == 0) return FP8Q_OK;
     int st = check_gemm_common(m, n, k, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
     if (st != FP8Q_OK) return st;
-    if (k > 0 && b_scale_kind == FP8Q_BSCALE_BLOCK128 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
+    if (k > 0 && b_scale_kind == FP8Q_BSCALE_BLOCK128 &&
+        (ld_bs < k / 128 || !bscale_span_ok((n + 127) / 128, ld_bs)))
+        return FP8Q_ERR_SHAPE;
     if (k > 0 && b_scale_kind == FP8Q_BSCALE_ROW128 && ld_bs < n) return FP8Q_ERR_SHAPE;
     if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) + 8)) return FP8Q_ERR_SHAPE;
     fp8q::GemmProblem g = {};
@@ -291,11 +330,15 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     int st = check_gemm_common(m_total, n, k, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
     if (st != FP8Q_OK) return st;
     if (m_total % 128 != 0 || n % 128 != 0 || m_total > 0x7FFFFFFFLL) return FP8Q_ERR_SHAPE;
-    if (k > 0 && ld_bs < k / 128) return FP8Q_ERR_SHAPE;
+    if (k > 0 && (ld_bs < k / 128 || !bscale_span_ok(n / 128, ld_bs))) return FP8Q_ERR_SHAPE;
     // the experts' weights are only read: their rows may interleave
     if (stride_b < 0 || stride_bs < 0) return FP8Q_ERR_SHAPE;
     if (stride_b % 16 != 0) return FP8Q_ERR_ALIGN;
     if (!grid_ok((m_total / 128) * ((n + 255) / 256) + 256)) return FP8Q_ERR_SHAPE;
+    if (debug_checks()) {
+        st = check_segments_on_host(groups, group_offsets, group_rows, m_total, stream);
+        if (st != FP8Q_OK) return st;
+    }
     fp8q::GemmProblem g = {};
     g.m = m_total; g.n = n; g.k = k;
     g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;
@@ -321,6 +364,10 @@ int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t* group_offsets, int64_t
     if (k_total > 0x7FFFFFFFLL || (k_total > 0 && ld_bs < n) || stride_c < m * ldc) return FP8Q_ERR_SHAPE;
     if (stride_c % 8 != 0) return FP8Q_ERR_ALIGN;
     if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) * groups + 256)) return FP8Q_ERR_SHAPE;
+    if (debug_checks()) {
+        st = check_segments_on_host(groups, group_offsets, nullptr, k_total, stream);
+        if (st != FP8Q_OK) return st;
+    }
     fp8q::GemmProblem g = {};
     g.m = m; g.n = n; g.k = k_total;
     g.a = a; g.lda = lda; g.a_scale = a_scale; g.ld_as = ld_as;

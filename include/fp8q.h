@@ -41,7 +41,11 @@
  *     the call returns once the launch is enqueued;
  *   - arguments are validated on the host before anything is launched; on any
  *     error nothing is launched and nothing is written;
- *   - calls are thread-safe and keep no state besides the last HIP error code.
+ *   - calls are thread-safe and keep no state besides the last HIP error code;
+ *   - FP8Q_DEBUG=1 in the environment adds host-side checks of the device
+ *     arrays the grouped GEMMs trust (fp8_grouped_gemm, fp8_grouped_gemm_wgrad):
+ *     they are copied to the host on `stream`, which is then synchronized, and a
+ *     contract violation returns FP8Q_ERR_SHAPE before anything is launched.
  */
 #ifndef FP8Q_H
 #define FP8Q_H
@@ -69,6 +73,18 @@ extern "C" {
 #define FP8Q_BSCALE_ROW128    1 /* B scales per (128-slab, row): [k/128][ld]      */
 #define FP8Q_OUT_BF16         0 /* output rounded to bf16, nearest-even           */
 #define FP8Q_OUT_F32          1 /* output as fp32                                 */
+
+/*
+ * Limits of the GEMM entry points (fp8_gemm, fp8_grouped_gemm,
+ * fp8_grouped_gemm_wgrad, fp8_gemm_mx, fp8_gemm_tensor). A block addresses
+ * the rows of its operand tiles, and the 128x128 block scales of its B tile,
+ * by 32-bit byte offsets from the tile origin, so:
+ *   lda, ldb <= FP8Q_MAX_GEMM_LD (elements = bytes of FP8 codes);
+ *   with 128x128 B block scales, ceil(n/128) * ld_bs < FP8Q_MAX_BSCALE_SPAN.
+ * Larger values return FP8Q_ERR_SHAPE before anything is launched.
+ */
+#define FP8Q_MAX_GEMM_LD      16777216LL   /* 2^24 */
+#define FP8Q_MAX_BSCALE_SPAN  1073741824LL /* 2^30 floats */
 
 /*
  * fp8_quantize_act -- fine-grained activation quantization.
@@ -257,7 +273,8 @@ int fp8_quantize_weight_grouped(int32_t groups, const uint16_t *w, int64_t n, in
  *          to nearest even) or FP8Q_OUT_F32. Every element of the m x n
  *          window is written; k == 0 writes zeros (A, B and their scales
  *          are then not read and may be NULL).
- * Shapes:  m, n >= 0 (any value; ragged tiles are handled), k % 128 == 0.
+ * Shapes:  m, n >= 0 (any value; ragged tiles are handled), k % 128 == 0;
+ *          lda, ldb and the block-scale span within the limits above.
  * Alignment: a, b, c 16-byte aligned; lda, ldb % 16 == 0; ldc % 8 == 0;
  *          scales 4-byte aligned.
  * m == 0 or n == 0: returns FP8Q_OK without launching.
@@ -300,10 +317,12 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
  *               then b + e*N with ldb = E*N (stride_b = N), and its block
  *               scales b_scale + e*N/128 with ld_bs = E*N/128.
  * c             [m_total][ldc]; out_dtype as in fp8_gemm.
- * Shapes:       n % 128 == 0, k % 128 == 0.
+ * Shapes:       n % 128 == 0, k % 128 == 0; lda, ldb and
+ *               (n/128) * ld_bs within the GEMM limits above.
  * Alignment:    as fp8_gemm; stride_b % 16 == 0.
  * The device arrays are trusted: offsets that break the contract give
- * unspecified output (the kernels still stay within the m_total rows).
+ * unspecified output (the kernels still stay within the m_total rows);
+ * with FP8Q_DEBUG=1 they are checked on the host first (see above).
  * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
  *         FP8Q_ERR_HIP.
  */
@@ -342,9 +361,11 @@ int fp8_grouped_gemm(int32_t groups, const int32_t *group_offsets, const int32_t
  *               ldc >= n, stride_c >= m * ldc, stride_c % 8 == 0. An expert
  *               with an empty segment gets dW_e = 0 (k_total == 0: all are
  *               zero, and A, B and their scales may be NULL).
+ * Shapes:       lda, ldb within the GEMM limits above.
  * Alignment:    as fp8_gemm.
  * The device array is trusted: segments outside [0, k_total] are skipped
- * (their dW_e is not written).
+ * (their dW_e is not written); with FP8Q_DEBUG=1 it is checked on the host
+ * first (see above).
  * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
  *         FP8Q_ERR_HIP.
  */
@@ -405,7 +426,8 @@ int fp8_quantize_mx_pair(const uint16_t *x0, int64_t rows0, int64_t cols0, int64
  * a, a_scale  [m][lda], lda >= k; words [k/128][ld_as], ld_as >= m.
  * b, b_scale  [n][ldb], ldb >= k; words [k/128][ld_bs], ld_bs >= n.
  * c           [m][ldc], ldc >= n; out_dtype FP8Q_OUT_BF16 or FP8Q_OUT_F32.
- * Shapes:     m, n >= 0, k % 128 == 0 (k == 0 writes zeros).
+ * Shapes:     m, n >= 0, k % 128 == 0 (k == 0 writes zeros); lda, ldb
+ *             within the GEMM limits above.
  * Alignment:  as fp8_gemm.
  * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
  *         FP8Q_ERR_HIP.
@@ -456,7 +478,8 @@ int fp8_retile_act_128x1(const uint8_t *q, int64_t tokens, int64_t cols, int64_t
  * b        codes [n][ldb], ldb >= k.    b_scale  one fp32 (device).
  * c        [m][ldc], ldc >= n; out_dtype FP8Q_OUT_BF16 or FP8Q_OUT_F32.
  * Shapes:  m, n >= 0, k % 128 == 0 (k == 0 writes zeros; a, b and the
- *          scales are then not read and may be NULL).
+ *          scales are then not read and may be NULL); lda, ldb within the
+ *          GEMM limits above.
  * Alignment: as fp8_gemm.
  * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
  *         FP8Q_ERR_HIP.

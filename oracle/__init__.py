@@ -30,10 +30,11 @@ _LIB = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load (building if needed) the C oracle."""
+    """Load (building if needed) the C oracle; FP8Q_ORACLE_LIBRARY names
+    another build of it (the sanitizer build of the CPU suites)."""
     global _LIB
     if _LIB is None:
-        path = _build.build(force=False)
+        path = os.environ.get("FP8Q_ORACLE_LIBRARY") or _build.build(force=False)
         L = ctypes.CDLL(path)
         u8p = ctypes.POINTER(ctypes.c_uint8)
         u16p = ctypes.POINTER(ctypes.c_uint16)

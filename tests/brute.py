@@ -109,10 +109,11 @@ def e4m3_value(code: int) -> Fraction:
     raise ValueError("NaN code")
 
 
-def gemm_exact(a_codes, a_scales, b_codes, b_scales) -> list[list[Fraction]]:
+def gemm_exact(a_codes, a_scales, b_codes, b_scales, absolute=False) -> list[list[Fraction]]:
     """C[m][n] = sum_k (dec(a[m][k]) * a_scales[m][k]) * (dec(b[n][k]) * b_scales[n][k]), exactly.
 
     Scales are given per element (already expanded from their tiles/blocks).
+    absolute: the sum of the terms' magnitudes instead (for error bounds).
     """
     M, K = len(a_codes), len(a_codes[0])
     N = len(b_codes)
@@ -122,8 +123,9 @@ def gemm_exact(a_codes, a_scales, b_codes, b_scales) -> list[list[Fraction]]:
         for n in range(N):
             acc = Fraction(0)
             for k in range(K):
-                acc += (e4m3_value(a_codes[m][k]) * Fraction(a_scales[m][k])) * \
+                term = (e4m3_value(a_codes[m][k]) * Fraction(a_scales[m][k])) * \
                        (e4m3_value(b_codes[n][k]) * Fraction(b_scales[n][k]))
+                acc += abs(term) if absolute else term
             row.append(acc)
         out.append(row)
     return out

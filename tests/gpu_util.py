@@ -75,3 +75,34 @@ def assert_gemm_close(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
     assert e["normwise"] <= NORM_TOL, "%s: normwise %.3e > %.1e" % (what, e["normwise"], NORM_TOL)
     assert e["worst_elem_ratio"] <= 1.0, "%s: element error %.3f x bound" % (what, e["worst_elem_ratio"])
     return e
+
+
+def nan_out(shape, dtype) -> torch.Tensor:
+    """A GEMM output buffer filled with NaN: an element the kernel leaves
+    unwritten stays NaN and fails the finiteness check."""
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
+
+
+def assert_grouped_close(got: np.ndarray, ref: np.ndarray, offsets, rows, what: str) -> dict:
+    """Grouped output [m_total][n]: every real row of every expert against the
+    oracle, with rms(ref) taken over all real rows together (the compared
+    output); every padding row exactly zero; nothing non-finite anywhere."""
+    assert np.all(np.isfinite(got)), what + ": non-finite output (an unwritten tile?)"
+    real = np.concatenate([np.arange(int(offsets[e]), int(offsets[e]) + int(rows[e]))
+                           for e in range(len(rows))] + [np.zeros(0, np.int64)]).astype(np.int64)
+    pad = np.setdiff1d(np.arange(got.shape[0]), real)
+    assert np.all(got[pad] == 0), what + ": padding rows not zero"
+    if real.size == 0:
+        return {}
+    return assert_gemm_close(got[real], ref[real], what)
+
+
+_CACHE: dict = {}
+
+
+def cached(key, fn):
+    """Memoize an expensive oracle result (say the 32 expert weights'
+    quantization) across the tests of one process."""
+    if key not in _CACHE:
+        _CACHE[key] = fn()
+    return _CACHE[key]

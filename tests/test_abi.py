@@ -179,6 +179,27 @@ def test_gemm_validation(lib):
     assert _g(lib, ldc=204) == ERR_ALIGN
 
 
+def test_gemm_operand_pitch_limits(lib):
+    """Tile rows are addressed by 32-bit offsets from the tile origin, so row
+    pitches above 2^24 bytes (and 128x128 block-scale spans of 2^30 floats or
+    more) are refused on the host; at the limit the call is valid."""
+    big = 1 << 24
+    assert _g(lib, lda=big + 16) == ERR_SHAPE
+    assert _g(lib, ldb=big + 16) == ERR_SHAPE
+    assert _g(lib, ld_bs=(1 << 30) // 2) == ERR_SHAPE          # ceil(200/128) = 2 block rows
+    assert _g(lib, ld_bs=(1 << 62)) == ERR_SHAPE               # no overflow in the span check
+    assert _g(lib, kind=1, lda=big + 16, ld_bs=200) == ERR_SHAPE
+    assert _gg(lib, lda=big + 16) == ERR_SHAPE
+    assert _gg(lib, ldb=big + 16) == ERR_SHAPE
+    assert _gg(lib, ld_bs=(1 << 30) // 2) == ERR_SHAPE         # 2 block rows per expert
+    assert _gw(lib, lda=big + 16) == ERR_SHAPE
+    assert _mxg(lib, ldb=big + 16) == ERR_SHAPE
+    assert _tg(lib, lda=big + 16) == ERR_SHAPE
+    if not torch.cuda.is_available():   # valid at the limit: fails only at the launch
+        assert _g(lib, lda=big) == ERR_HIP
+        assert _g(lib, ldb=big) == ERR_HIP
+
+
 def _gg(lib, groups=4, off=A16, rows=0, m=512, n=256, k=256, a=A16b, lda=256, a_s=A4, ld_as=512,
         b=A16c, ldb=256, sb=256 * 256, b_s=A4, ld_bs=2, sbs=4, c=A16, ldc=256, out=0):
     return lib.fp8_grouped_gemm(groups, off, rows, m, n, k, a, lda, a_s, ld_as, b, ldb, sb,
@@ -422,3 +443,35 @@ def test_binding_refuses_cpu_tensors():
     w = torch.zeros((128, 128), dtype=torch.bfloat16)
     with pytest.raises(fq.Fp8qError):
         fq.fp8_quantize_weight(w)
+
+
+def test_binding_checks_shapes_dtypes_and_strides():
+    """The binding's own checks (the C ABI sees only pointers and leading
+    dimensions, so a tensor smaller than the launch assumes must be refused
+    in Python): dtype, exact shape, unit stride in the last dimension."""
+    t = torch.zeros((4, 6), dtype=torch.float32)
+    fq._check_tensor(t, (4, 6), fq._F32, "t")
+    with pytest.raises(fq.Fp8qError, match="dtype"):
+        fq._check_tensor(t.to(torch.bfloat16), (4, 6), fq._F32, "t")
+    with pytest.raises(fq.Fp8qError, match="shape"):
+        fq._check_tensor(t, (4, 7), fq._F32, "t")
+    with pytest.raises(fq.Fp8qError, match="shape"):
+        fq._check_tensor(t, (3, 6), fq._F32, "t")
+    with pytest.raises(fq.Fp8qError, match="unit stride"):
+        fq._check_tensor(t.t(), (6, 4), fq._F32, "t")
+    # a view with a padded leading dimension is fine
+    fq._check_tensor(torch.zeros((4, 8))[:, :6], (4, 6), fq._F32, "t")
+    # GEMM outputs: wrong dtype (a bf16 buffer for fp32 output would be
+    # written past its end), wrong shape, transposed view
+    out = torch.zeros((5, 7), dtype=torch.bfloat16)
+    assert fq._gemm_out(out, (5, 7), torch.bfloat16, "cpu", None) is out
+    with pytest.raises(fq.Fp8qError, match="dtype"):
+        fq._gemm_out(out, (5, 7), torch.float32, "cpu", None)
+    with pytest.raises(fq.Fp8qError, match="shape"):
+        fq._gemm_out(out, (5, 8), torch.bfloat16, "cpu", None)
+    with pytest.raises(fq.Fp8qError, match="unit stride"):
+        fq._gemm_out(torch.zeros((7, 5), dtype=torch.bfloat16).t(), (5, 7), torch.bfloat16, "cpu", None)
+    # codes accept E4M3 or uint8 only
+    fq._check_tensor(torch.zeros((2, 16), dtype=torch.uint8), (2, 16), fq._CODES, "q")
+    with pytest.raises(fq.Fp8qError, match="dtype"):
+        fq._check_tensor(torch.zeros((2, 16), dtype=torch.int8), (2, 16), fq._CODES, "q")

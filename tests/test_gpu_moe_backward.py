@@ -14,7 +14,7 @@ import torch
 import fine_grained_fp8_quantize_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import assert_bits_equal, assert_gemm_close, dev_bf16, host_codes, host_f32, host_out
+from gpu_util import assert_bits_equal, assert_gemm_close, dev_bf16, host_codes, host_f32, host_out, nan_out
 
 pytestmark = pytest.mark.gpu
 
@@ -32,32 +32,35 @@ def _packed(rows, cols, tensor_id, grad):
     return out, off
 
 
-def _wgrad_case(rows, m, n, out_dtype=torch.float32, sample_experts=None, sample_rows=None):
+def _wgrad_case(rows, m, n, out_dtype=torch.float32):
     dy, off = _packed(rows, m, 100, grad=True)
     x, _ = _packed(rows, n, 101, grad=False)
     aq, as_ = fq.fp8_quantize_act(dev_bf16(dy), "128x1")
     bq, bs = fq.fp8_quantize_act(dev_bf16(x), "128x1")
     off_d = torch.from_numpy(off.astype(np.int32)).cuda()
-    out = fq.fp8_grouped_gemm_wgrad(off_d, aq, as_, bq, bs, out_dtype)
+    out = fq.fp8_grouped_gemm_wgrad(off_d, aq, as_, bq, bs, out_dtype,
+                                    out=nan_out((len(rows), m, n), out_dtype))
     torch.cuda.synchronize()
     a_q, a_s = oracle.quant_act_128x1(dy)
     b_q, b_s = oracle.quant_act_128x1(x)
     assert_bits_equal(host_codes(aq), a_q, "dY^T codes")
     assert_bits_equal(host_f32(as_), a_s, "dY^T scales")
-    experts = range(len(rows)) if sample_experts is None else sample_experts
-    for e in experts:
+    _compare_experts(out, off, rows, a_q, a_s, b_q, b_s, "wgrad")
+
+
+def _compare_experts(out, off, rows, a_q, a_s, b_q, b_s, what):
+    """Every dW_e in full against the oracle's row-scale GEMM over expert e's
+    token segment (rms over that dW_e); an empty segment must give zeros."""
+    for e in range(len(rows)):
         t0, t1 = int(off[e]), int(off[e + 1])
-        got_e = out[e]
-        idx = np.arange(m) if sample_rows is None else np.unique(np.concatenate(
-            [[0, m - 1], np.random.default_rng(e).choice(m, sample_rows, replace=False)]))
-        got = host_out(got_e[torch.from_numpy(idx).cuda()])
+        got = host_out(out[e])
         if t1 == t0:
-            assert np.all(got == 0), "expert %d: empty segment must give zeros" % e
+            assert np.all(got == 0), "%s expert %d: empty segment must give zeros" % (what, e)
             continue
-        ref = oracle.gemm_rows(idx, np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
-                               np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]),
-                               "row")
-        assert_gemm_close(got, ref, "wgrad expert %d (%d tokens)" % (e, rows[e]))
+        ref = oracle.gemm(np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
+                          np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]),
+                          "row")
+        assert_gemm_close(got, ref, "%s expert %d (%d tokens)" % (what, e, rows[e]))
 
 
 def test_grouped_wgrad_edge_segments():
@@ -73,16 +76,13 @@ def test_grouped_wgrad_all_empty():
     _wgrad_case([0, 0, 0], m=256, n=256)
 
 
-def test_grouped_wgrad_moe_config_sampled():
+def test_grouped_wgrad_moe_config_full():
     """MoE up-projection Wgrad: 32 experts, dW_e [4096][7168] over each expert's
-    tokens (8192 routed rows, 10112 padded); 4 experts and rows sampled."""
-    rows = wl.moe_rows(0)
-    big = int(np.argmax(rows))
-    small = int(np.argmin(rows))
-    _wgrad_case(rows, m=4096, n=7168, sample_experts=[0, big, small, 31], sample_rows=12)
+    tokens (8192 routed rows, 10112 padded); every dW_e compared in full."""
+    _wgrad_case(wl.moe_rows(0), m=4096, n=7168)
 
 
-def _wgrad_from_dispatch_cache(rows, m, k, tokens, top_k, sample_experts=None, sample_rows=None):
+def _wgrad_from_dispatch_cache(rows, m, k, tokens, top_k):
     """MoE Wgrad with X taken from the FP8 cache the dispatch quantizer wrote:
     the expert-sorted 1x128 codes and scales (padding rows zeroed before the
     scatter) re-tiled to 128x1 token tiles, then the grouped-over-K GEMM.
@@ -98,37 +98,25 @@ def _wgrad_from_dispatch_cache(rows, m, k, tokens, top_k, sample_experts=None, s
     dy, _ = _packed(rows, m, 102, grad=True)
     aq, as_ = fq.fp8_quantize_act(dev_bf16(dy), "128x1")
     off_d = torch.from_numpy(off.astype(np.int32)).cuda()
-    out = fq.fp8_grouped_gemm_wgrad(off_d, aq, as_, bq, bs, torch.float32)
+    out = fq.fp8_grouped_gemm_wgrad(off_d, aq, as_, bq, bs, torch.float32,
+                                    out=nan_out((len(rows), m, k), torch.float32))
     torch.cuda.synchronize()
     xq_ref, xs_ref, _ = oracle.quant_act_scatter(d["x"], d["dst_rows"], m_total)
     b_q, b_s = oracle.retile_128x1(xq_ref, xs_ref)
     assert_bits_equal(host_codes(bq), b_q, "re-tiled cache codes")
     assert_bits_equal(host_f32(bs), b_s, "re-tiled cache scales")
     a_q, a_s = oracle.quant_act_128x1(dy)
-    experts = range(len(rows)) if sample_experts is None else sample_experts
-    for e in experts:
-        t0, t1 = int(off[e]), int(off[e + 1])
-        idx = np.arange(m) if sample_rows is None else np.unique(np.concatenate(
-            [[0, m - 1], np.random.default_rng(e).choice(m, sample_rows, replace=False)]))
-        got = host_out(out[e][torch.from_numpy(idx).cuda()])
-        if t1 == t0:
-            assert np.all(got == 0), "expert %d: empty segment must give zeros" % e
-            continue
-        ref = oracle.gemm_rows(idx, np.ascontiguousarray(a_q[:, t0:t1]), np.ascontiguousarray(a_s[t0 // 128:t1 // 128]),
-                               np.ascontiguousarray(b_q[:, t0:t1]), np.ascontiguousarray(b_s[t0 // 128:t1 // 128]),
-                               "row")
-        assert_gemm_close(got, ref, "cached-X wgrad expert %d (%d tokens)" % (e, rows[e]))
+    _compare_experts(out, off, rows, a_q, a_s, b_q, b_s, "cached-X wgrad")
 
 
 def test_grouped_wgrad_from_dispatch_cache_small():
     _wgrad_from_dispatch_cache([5, 0, 130, 64, 1], m=256, k=384, tokens=200, top_k=2)
 
 
-def test_grouped_wgrad_from_dispatch_cache_moe_sampled():
+def test_grouped_wgrad_from_dispatch_cache_moe_full():
     """The MoE config: 8192 tokens x 7168, top-8 routes into 32 local experts,
-    dW [32][4096][7168]; experts 0, 9 and 31, 24 rows each."""
-    _wgrad_from_dispatch_cache(wl.moe_rows(0), m=4096, k=7168, tokens=8192, top_k=8,
-                               sample_experts=(0, 9, 31), sample_rows=24)
+    dW [32][4096][7168]; every dW_e compared in full."""
+    _wgrad_from_dispatch_cache(wl.moe_rows(0), m=4096, k=7168, tokens=8192, top_k=8)
 
 
 def test_grouped_wgrad_padded_output_and_operand_views():

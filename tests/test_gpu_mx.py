@@ -13,7 +13,7 @@ import torch
 import fine_grained_fp8_quantize_amd as fq
 import oracle
 import workloads as wl
-from gpu_util import assert_bits_equal, assert_gemm_close, dev_bf16, host_codes, host_out
+from gpu_util import assert_bits_equal, assert_gemm_close, dev_bf16, host_codes, host_out, nan_out
 
 pytestmark = pytest.mark.gpu
 
@@ -63,20 +63,17 @@ def test_mx_quant_special_blocks():
     _check_quant(np.stack(rows), "special blocks")
 
 
-def _gemm_case(m, n, k, out_dtype=torch.bfloat16, sample=None, seed=0):
+def _gemm_case(m, n, k, out_dtype=torch.bfloat16, seed=0):
     a = wl.activation(seed, "tiny_fprop", 96, m, k, 50.0)
     b = wl.weight(seed, "tiny_fprop", 97, n, k)
     aq, asc = fq.fp8_quantize_mx(dev_bf16(a))
     bq, bsc = fq.fp8_quantize_mx(dev_bf16(b))
-    c = fq.fp8_gemm_mx(aq, asc, bq, bsc, out_dtype)
+    c = fq.fp8_gemm_mx(aq, asc, bq, bsc, out_dtype, out=nan_out((m, n), out_dtype))
     torch.cuda.synchronize()
     got = host_out(c)
     a_q, a_e = oracle.quant_mx_1x32(a)
     b_q, b_e = oracle.quant_mx_1x32(b)
-    rows = np.arange(m) if sample is None else np.unique(np.concatenate(
-        [[0, 1, m - 1], np.random.default_rng(seed).choice(m, sample, replace=False)]))
-    ref = oracle.gemm_mx(a_q[rows], a_e[rows], b_q, b_e)
-    assert_gemm_close(got[rows], ref, "mx gemm %dx%dx%d" % (m, n, k))
+    assert_gemm_close(got, oracle.gemm_mx(a_q, a_e, b_q, b_e), "mx gemm %dx%dx%d" % (m, n, k))
 
 
 def test_mx_gemm_tiny_all_elements():
@@ -87,8 +84,8 @@ def test_mx_gemm_ragged_and_f32():
     _gemm_case(300, 200, 384, out_dtype=torch.float32)
 
 
-def test_mx_gemm_dense_fprop_sampled():
-    _gemm_case(4096, 4096, 7168, sample=40)
+def test_mx_gemm_dense_fprop_full():
+    _gemm_case(4096, 4096, 7168)
 
 
 def test_mx_gemm_k0_writes_zeros():
@@ -104,7 +101,7 @@ def test_mx_gemm_k0_writes_zeros():
 
 def test_mx_gemm_224_wide_tiles():
     """N = 7168 makes the launcher pick 224-wide n tiles (32 x 224)."""
-    _gemm_case(512, 7168, 256, sample=24, seed=3)
+    _gemm_case(512, 7168, 256, seed=3)
 
 
 def test_mx_gemm_padded_leading_dims():

@@ -373,6 +373,94 @@ def test_grouped_is_per_expert_gemm_with_zero_padding():
         assert np.all(c[r0 + r:off[e + 1]] == 0)
 
 
+def test_grouped_brute_force_tiny():
+    """oracle.grouped_gemm against exact rationals on a tiny grouped problem.
+    The segment of each expert is found here from the real row counts alone
+    (each expert's rows rounded up to a multiple of 128, in expert order), and
+    every real output row is the exact sum over K of the dequantized codes of
+    its own A row and its own expert's weight; padding rows are zero."""
+    rows = [0, 1, 2, 1]
+    n, k = 256, 256
+    rng = np.random.default_rng(77)
+    seg = [128 * ((r + 127) // 128) for r in rows]
+    m_total = sum(seg)
+    offsets = np.concatenate([[0], np.cumsum(seg)]).astype(np.int64)
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    qa = rng.choice(finite, size=(m_total, k)).astype(np.uint8)
+    sa = rng.uniform(0.01, 3.0, (k // 128, m_total)).astype(np.float32)
+    E = len(rows)
+    qb = rng.choice(finite, size=(E, n, k)).astype(np.uint8)
+    sb = rng.uniform(0.01, 3.0, (E, n // 128, k // 128)).astype(np.float32)
+    c = oracle.grouped_gemm(offsets, np.array(rows), qa, sa, qb, sb)
+    start = 0
+    for e, r in enumerate(rows):
+        real = list(range(start, start + r))
+        if real:
+            a_codes = [[int(v) for v in qa[i]] for i in real]
+            a_sc = [[float(sa[kk // 128][i]) for kk in range(k)] for i in real]
+            b_codes = [[int(v) for v in qb[e][j]] for j in range(n)]
+            b_sc = [[float(sb[e][j // 128][kk // 128]) for kk in range(k)] for j in range(n)]
+            exact = brute.gemm_exact(a_codes, a_sc, b_codes, b_sc)
+            # float64 dot products of K terms are within K * 2^-53 * sum |terms|
+            # of the exact value (the dequantized operands themselves are exact)
+            abs_sum = brute.gemm_exact(a_codes, a_sc, b_codes, b_sc, absolute=True)
+            got = c[start:start + r]
+            for ii in range(r):
+                for j in range(n):
+                    ref = exact[ii][j]
+                    bound = k * 2.0 ** -53 * float(abs_sum[ii][j])
+                    assert abs(Fraction(float(got[ii, j])) - ref) <= bound, (e, ii, j, got[ii, j], float(ref))
+        pad_end = start + 128 * ((r + 127) // 128)
+        assert np.all(c[start + r:pad_end] == 0), "expert %d padding rows" % e
+        start = pad_end
+    assert start == m_total
+
+
+def test_grouped_experts_take_their_own_weight():
+    """Invariant: if expert e's weight is 2^e times expert 0's (exact in bf16,
+    and quantizing 2^e W gives W's codes with scales times 2^e), every real
+    row of expert e equals 2^e times the dense GEMM of that row with W; with
+    equal weights, the grouped output on the real rows is the dense GEMM of
+    the gathered rows. A segment read from the wrong offset, or an expert
+    paired with the wrong weight, breaks one of the two."""
+    rows = np.array([3, 0, 130, 1, 64])
+    n, k = 128, 384
+    g = wl.grouped_fprop(2, n=n, k=k, experts=len(rows), rows=rows)
+    qa, sa = oracle.quant_act_1x128(g["x"])
+    w0 = g["w"][0]
+    E = len(rows)
+    qb = np.empty((E, n, k), np.uint8)
+    sb = np.empty((E, n // 128, k // 128), np.float32)
+    for e in range(E):
+        we = wl.f32_to_bf16_bits(wl.bf16_bits_to_f32(w0) * np.float32(2.0 ** e))
+        qb[e], sb[e] = oracle.quant_weight_128x128(we)
+    q0, s0 = oracle.quant_weight_128x128(w0)
+    for e in range(E):
+        assert np.array_equal(qb[e], q0)
+        assert np.array_equal(sb[e], s0 * np.float32(2.0 ** e))
+    off = g["offsets"]
+    c = oracle.grouped_gemm(off, rows, qa, sa, qb, sb)
+    real = np.concatenate([np.arange(off[e], off[e] + rows[e]) for e in range(E)]).astype(np.int64)
+    expert_of = np.concatenate([np.full(rows[e], e) for e in range(E)])
+    ga, gs = np.ascontiguousarray(qa[real]), np.ascontiguousarray(sa[:, real])
+    dense = oracle.gemm(ga, gs, q0, s0)
+    # the float64 sums may round differently in a different row batch: allow
+    # K * 2^-53 of the sum of the terms' magnitudes
+    tol = k * 2.0 ** -53 * (np.abs(oracle.dequant_rows_1x128(ga, gs)) @
+                            np.abs(oracle.dequant_block_128x128(q0, s0)).T)
+    scale = (2.0 ** expert_of)[:, None]
+    assert np.all(np.abs(c[real] - dense * scale) <= tol * scale)
+    same = oracle.grouped_gemm(off, rows, qa, sa, np.repeat(q0[None], E, 0), np.repeat(s0[None], E, 0))
+    assert np.all(np.abs(same[real] - dense) <= tol)
+    # and the pairing is visible: expert e's rows are not those of any other scaling
+    for e in range(E):
+        sel = expert_of == e
+        if sel.any() and e > 0:
+            assert np.max(np.abs(c[real][sel] - dense[sel])) > 1e-3
+    pad = np.setdiff1d(np.arange(qa.shape[0]), real)
+    assert np.all(c[pad] == 0) and np.all(same[pad] == 0)
+
+
 def test_bf16_round_diagnostic():
     """The bf16 rounding helper (diagnostic only) matches torch's float32 -> bf16 cast."""
     v = np.random.default_rng(6).standard_normal(10000) * 10
