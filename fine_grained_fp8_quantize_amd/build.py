@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8q.so")
 
 SOURCES = ["api.cpp", "quant.hip", "gemm.hip"]
-HEADERS = ["fp8q_device.h", "launch.h"]
+HEADERS = ["fp8q_device.h", "gemm_common.h", "launch.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -68,8 +68,9 @@ int check_segments_on_host(int32_t groups, const int32_t* group_offsets, const i
     return FP8Q_OK;
 }
 
-// blocks * ld_bs < FP8Q_MAX_BSCALE_SPAN without overflowing int64 (blocks >= 1)
-bool bscale_span_ok(int64_t blocks, int64_t ld_bs) { return ld_bs < FP8Q_MAX_BSCALE_SPAN / blocks; }
+// rows * ld < FP8Q_MAX_SCALE_SPAN without overflowing int64 (a scale array of
+// `rows` rows with leading dimension ld, in floats)
+bool scale_span_ok(int64_t rows, int64_t ld) { return rows <= 0 || ld < FP8Q_MAX_SCALE_SPAN / rows; }
 
 }  // namespace
 
@@ -285,8 +286,9 @@ static int check_gemm_common(int64_t m, int64_t n, int64_t k, const uint8_t* a, 
     // k == 0: C is all zeros; A, B and their scales are not read (may be NULL)
     if (!c || (k > 0 && (!a || !b || !a_scale || !b_scale))) return FP8Q_ERR_NULL;
     if (k % 128 != 0 || ldc < n || (k > 0 && (lda < k || ldb < k || ld_as < m))) return FP8Q_ERR_SHAPE;
-    // tile rows are addressed by 32-bit offsets from the tile origin
-    if (k > 0 && (lda > FP8Q_MAX_GEMM_LD || ldb > FP8Q_MAX_GEMM_LD)) return FP8Q_ERR_SHAPE;
+    // tiles and scales are addressed through 31-bit buffer ranges
+    if (k > 0 && (lda > FP8Q_MAX_GEMM_LD || ldb > FP8Q_MAX_GEMM_LD || !scale_span_ok(k / 128, ld_as)))
+        return FP8Q_ERR_SHAPE;
     if (!aligned(c, 16) || ldc % 8 != 0) return FP8Q_ERR_ALIGN;
     if (k > 0 && (!aligned(a, 16) || !aligned(b, 16) || !aligned(a_scale, 4) || !aligned(b_scale, 4) ||
                   lda % 16 != 0 || ldb % 16 != 0))
@@ -304,9 +306,10 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
     int st = check_gemm_common(m, n, k, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
     if (st != FP8Q_OK) return st;
     if (k > 0 && b_scale_kind == FP8Q_BSCALE_BLOCK128 &&
-        (ld_bs < k / 128 || !bscale_span_ok((n + 127) / 128, ld_bs)))
+        (ld_bs < k / 128 || !scale_span_ok((n + 127) / 128, ld_bs)))
         return FP8Q_ERR_SHAPE;
-    if (k > 0 && b_scale_kind == FP8Q_BSCALE_ROW128 && ld_bs < n) return FP8Q_ERR_SHAPE;
+    if (k > 0 && b_scale_kind == FP8Q_BSCALE_ROW128 && (ld_bs < n || !scale_span_ok(k / 128, ld_bs)))
+        return FP8Q_ERR_SHAPE;
     if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) + 8)) return FP8Q_ERR_SHAPE;
     fp8q::GemmProblem g = {};
     g.m = m; g.n = n; g.k = k;
@@ -330,7 +333,7 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     int st = check_gemm_common(m_total, n, k, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
     if (st != FP8Q_OK) return st;
     if (m_total % 128 != 0 || n % 128 != 0 || m_total > 0x7FFFFFFFLL) return FP8Q_ERR_SHAPE;
-    if (k > 0 && (ld_bs < k / 128 || !bscale_span_ok(n / 128, ld_bs))) return FP8Q_ERR_SHAPE;
+    if (k > 0 && (ld_bs < k / 128 || !scale_span_ok(n / 128, ld_bs))) return FP8Q_ERR_SHAPE;
     // the experts' weights are only read: their rows may interleave
     if (stride_b < 0 || stride_bs < 0) return FP8Q_ERR_SHAPE;
     if (stride_b % 16 != 0) return FP8Q_ERR_ALIGN;
@@ -361,7 +364,9 @@ int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t* group_offsets, int64_t
     if (!group_offsets) return FP8Q_ERR_NULL;
     int st = check_gemm_common(m, n, k_total, a, lda, a_scale, ld_as, b, ldb, b_scale, c, ldc, out_dtype);
     if (st != FP8Q_OK) return st;
-    if (k_total > 0x7FFFFFFFLL || (k_total > 0 && ld_bs < n) || stride_c < m * ldc) return FP8Q_ERR_SHAPE;
+    if (k_total > 0x7FFFFFFFLL || (k_total > 0 && (ld_bs < n || !scale_span_ok(k_total / 128, ld_bs))) ||
+        stride_c < m * ldc)
+        return FP8Q_ERR_SHAPE;
     if (stride_c % 8 != 0) return FP8Q_ERR_ALIGN;
     if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) * groups + 256)) return FP8Q_ERR_SHAPE;
     if (debug_checks()) {
@@ -442,7 +447,7 @@ int fp8_gemm_mx(int64_t m, int64_t n, int64_t k,
     const float* bs = reinterpret_cast<const float*>(b_scale);
     int st = check_gemm_common(m, n, k, a, lda, as, ld_as, b, ldb, bs, c, ldc, out_dtype);
     if (st != FP8Q_OK) return st;
-    if (k > 0 && ld_bs < n) return FP8Q_ERR_SHAPE;
+    if (k > 0 && (ld_bs < n || !scale_span_ok(k / 128, ld_bs))) return FP8Q_ERR_SHAPE;
     if (!grid_ok(((m + 255) / 256) * ((n + 223) / 224) + 8)) return FP8Q_ERR_SHAPE;
     fp8q::GemmProblem g = {};
     g.m = m; g.n = n; g.k = k;

@@ -33,204 +33,19 @@
 // scale per lane per m-subtile, and the B block scale is wave-uniform per
 // 16-column subtile. Waves whose rows are all past the real rows (grouped
 // padding, ragged M) skip their MFMAs.
-#include "fp8q_device.h"
-#include "launch.h"
+#include "gemm_common.h"
 
-#include <type_traits>
-#include <utility>
+// Cache policy of the LDS-DMA copies: the expert weights of a grouped-over-M
+// GEMM are streamed from HBM once per m-tile, so they are loaded
+// non-temporal (NT, bit 1 of the cache-policy operand on gfx950); everything
+// else keeps the default policy. Paired on one MI355X, NT weights took the
+// MoE grouped GEMM from 372 to 359 us; NT on the B operand of dense GEMMs,
+// which is re-read from L2 by the tiles of a band, made Dgrad 14% slower.
+constexpr int kPolicyDefault = 0;
+constexpr int kPolicyNonTemporal = 2;
 
 namespace fp8q {
 namespace {
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-constexpr int kSlab = 128;  // K elements per promotion interval
-constexpr int kBM = 256;
-constexpr int kBNMax = 256;  // LDS is laid out for the widest n tile
-constexpr int kThreads = 512;
-constexpr int kWaveM = 64;
-constexpr int kMSub = kWaveM / 16;
-
-// LDS per stage: one 256x128-byte tile of A, one of B, 256 A scales and up
-// to 256 B scales (two stages: 135168 bytes).
-constexpr int kTileBytes = kBM * kSlab;
-
-// Physical 16-byte chunk of logical chunk c in LDS row `row` (rows are 128
-// bytes). A fragment read has each 16-lane quarter of the wave fetch one
-// chunk from 16 consecutive rows; XOR with (row >> 1) & 7 sends those 16
-// reads to 16 different 16-byte bank groups (rows 2r and 2r+1 already sit
-// in opposite halves of the 64 banks). With the fragment order below
-// (chunks g and g + 4) the counters show no bank conflicts at all. Tiles
-// and subtiles start at multiples of 16 rows, so tile-relative and
-// subtile-relative rows give the same chunk.
-__device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ ((row >> 1) & 7); }
-
-struct Params {
-    int64_t m, n, k;
-    const uint8_t* a;
-    int64_t lda;
-    const float* a_scale;
-    int64_t ld_as;
-    const uint8_t* b;
-    int64_t ldb;
-    const float* b_scale;
-    int64_t ld_bs;
-    void* c;
-    int64_t ldc;
-    int32_t groups;
-    const int32_t* group_offsets;
-    const int32_t* group_rows;
-    int64_t stride_b;
-    int64_t stride_bs;
-    int64_t stride_c_bytes;  // grouped over K: distance between expert outputs
-};
-
-// Which rows of the output a block tile owns.
-struct TileRows {
-    int64_t m0;        // first row of the tile
-    int64_t row_hi;    // rows >= row_hi belong to someone else: not stored
-    int64_t real_end;  // rows in [real_end, row_hi) are padding: stored as 0
-    int64_t n0;
-    const uint8_t* b;
-    const float* b_scale;
-    int slab0;         // first K slab of the tile's contraction
-    int slabs;         // number of K slabs
-    void* c;           // output matrix the tile belongs to
-};
-
-// Kernel modes: one GEMM; grouped over M (MoE Fprop/Dgrad: experts own row
-// segments, one weight each); grouped over K (MoE Wgrad: experts own token
-// segments of the contraction, one output each).
-constexpr int kDense = 0;
-constexpr int kGroupedM = 1;
-constexpr int kGroupedK = 2;
-
-// Dense tile order: block -> XCD x = block % 8 gets the contiguous slot
-// range [x*per, (x+1)*per); slots walk 4-row bands of tiles so the blocks
-// resident on one XCD share A and B panels in its L2.
-template <int BN>
-__device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
-    const int tiles_m = (int)((p.m + kBM - 1) / kBM);
-    const int tiles_n = (int)((p.n + BN - 1) / BN);
-    const int total = tiles_m * tiles_n;
-    const int per = (total + 7) / 8;
-    const int slot = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (slot >= total) return false;
-    constexpr int G = 4;
-    const int group = slot / (G * tiles_n);
-    const int first_m = group * G;
-    const int gm = min(tiles_m - first_m, G);
-    const int within = slot - group * G * tiles_n;
-    const int tm = first_m + within % gm;
-    const int tn = within / gm;
-    t.m0 = (int64_t)tm * kBM;
-    t.row_hi = p.m;
-    t.real_end = p.m;
-    t.n0 = (int64_t)tn * BN;
-    t.b = p.b;
-    t.b_scale = p.b_scale;
-    t.slab0 = 0;
-    t.slabs = (int)(p.k / kSlab);
-    t.c = p.c;
-    return true;
-}
-
-// Grouped tiles. Expert e's segment [off[e], off[e+1]) is cut into 256-row
-// m-tiles: whole tiles of real rows, then a tail tile whose first 1-4 64-row
-// quarters hold real rows, then tiles of padding only (written as zeros).
-// Slots run expert by expert, inside an expert by n-tile and then m-tile, so
-// the m-tiles that share a 256 x K panel of W_e -- the tail included -- are
-// consecutive and run together on one XCD, where the panel is fetched into
-// L2 once. (Every tile streams the same K x 256 weight panel, so tiles with
-// few real rows take about as long as full ones: ordering by tile size buys
-// no balance, and measured ~5% slower than this order.)
-struct ExpertSplit {
-    int beg;    // first row of the segment
-    int tiles;  // m-tiles of the segment
-};
-
-__device__ __forceinline__ ExpertSplit expert_split(const Params& p, int e) {
-    ExpertSplit x;
-    x.beg = p.group_offsets[e];
-    const int seg = max(p.group_offsets[e + 1] - x.beg, 0);
-    x.tiles = (seg + kBM - 1) / kBM;
-    return x;
-}
-
-// Block b runs on XCD b % 8; round r of that XCD's 32 CUs takes the 32
-// consecutive slots 256 r + 32 (b % 8) + [0, 32). Every round is then spread
-// evenly over the XCDs and panel reuse stays inside one L2. The grid is a
-// multiple of 256 blocks, so this is a bijection onto its slots.
-template <int BN>
-__device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
-    const int tiles_n = (int)((p.n + BN - 1) / BN);
-    const int q = (int)(blockIdx.x >> 3);
-    int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
-    for (int e = 0; e < p.groups; ++e) {
-        const ExpertSplit x = expert_split(p, e);
-        const int k = x.tiles;
-        if (slot < k * tiles_n) {
-            const int tn = slot / k, mt = slot % k;
-            const int end = x.beg + max(p.group_offsets[e + 1] - x.beg, 0);
-            t.m0 = x.beg + (int64_t)mt * kBM;
-            // offsets that break the contract must not move stores outside C
-            if (t.m0 < 0 || t.m0 >= p.m) return false;
-            t.row_hi = min(min((int64_t)end, t.m0 + kBM), p.m);
-            const int seg = end - x.beg;
-            const int real = p.group_rows ? min(max(p.group_rows[e], 0), seg) : seg;
-            t.real_end = x.beg + (int64_t)real;
-            t.n0 = (int64_t)tn * BN;
-            t.b = p.b + e * p.stride_b;
-            t.b_scale = p.b_scale + e * p.stride_bs;
-            t.slab0 = 0;
-            t.slabs = (int)(p.k / kSlab);
-            t.c = p.c;
-            return true;
-        }
-        slot -= k * tiles_n;
-    }
-    return false;
-}
-
-// Grouped-over-K tiles (MoE Wgrad): expert e contracts over its token segment
-// [off[e], off[e+1]) (a multiple of 128: whole slabs) and owns the output
-// matrix c + e * stride_c. Every expert has the same tiles_m x tiles_n tiles;
-// slots run expert by expert, inside an expert in the dense order (bands of
-// 4 m-tiles). Blocks take slots in XCD rounds as grouped_tile does, so the
-// 32 tiles an XCD runs together share the expert's A and B panels in L2.
-// An expert without rows still writes its (zero) output.
-template <int BN>
-__device__ __forceinline__ bool grouped_k_tile(const Params& p, TileRows& t) {
-    const int tiles_m = (int)((p.m + kBM - 1) / kBM);
-    const int tiles_n = (int)((p.n + BN - 1) / BN);
-    const int per = tiles_m * tiles_n;
-    const int q = (int)(blockIdx.x >> 3);
-    const int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
-    if (slot >= per * p.groups) return false;
-    const int e = slot / per;
-    const int within_e = slot - e * per;
-    constexpr int G = 4;
-    const int group = within_e / (G * tiles_n);
-    const int first_m = group * G;
-    const int gm = min(tiles_m - first_m, G);
-    const int within = within_e - group * G * tiles_n;
-    const int beg = p.group_offsets[e];
-    const int seg = max(p.group_offsets[e + 1] - beg, 0);
-    // offsets that break the contract must not move reads outside A and B
-    if (beg < 0 || (int64_t)beg + seg > p.k) return false;
-    t.m0 = (int64_t)(first_m + within % gm) * kBM;
-    t.row_hi = p.m;
-    t.real_end = p.m;
-    t.n0 = (int64_t)(within / gm) * BN;
-    t.b = p.b;
-    t.b_scale = p.b_scale;
-    t.slab0 = beg / kSlab;
-    t.slabs = seg / kSlab;
-    t.c = static_cast<char*>(p.c) + (int64_t)e * p.stride_c_bytes;
-    return true;
-}
 
 // ---------------------------------------------------------------- LDS
 // Every stage of every operand is its own __shared__ array. The copy of slab
@@ -270,26 +85,6 @@ __device__ __forceinline__ float* stage_sa() {
 template <int S>
 __device__ __forceinline__ float* stage_sb() {
     if constexpr (S == 0) return lds_sb0; else return lds_sb1;
-}
-
-// s_waitcnt with vmcnt = N and the other counters left at their maxima.
-constexpr int waitcnt_vm(int n) { return 0x0F70 | n; }
-
-template <int N>
-__device__ __forceinline__ void wait_dma_and_barrier() {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
-    __builtin_amdgcn_s_barrier();
-}
-
-__device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
-    const v4i lo = *reinterpret_cast<const v4i*>(p0);
-    const v4i hi = *reinterpret_cast<const v4i*>(p1);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-template <int... Is, class F>
-__device__ __forceinline__ void unroll(std::integer_sequence<int, Is...>, F&& f) {
-    (f(std::integral_constant<int, Is>{}), ...);
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -403,13 +198,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         // (offset computed outside the builtin's argument list: a lambda
         // call there keeps the host pass from emitting the kernel's stub)
         const uint32_t off = a_off(i);
-        __builtin_amdgcn_global_load_lds(ga + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(ga + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, kPolicyDefault);
     };
     auto copy_b = [&](int j, auto st, int i) {
         uint8_t* base = stage_b<decltype(st)::value>() + 32 * wave * kSlab;
         const uint8_t* gb = tileB + (int64_t)j * kSlab;
         const uint32_t off = b_off(i);
-        __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(base + i * 8 * kSlab), 16, 0,
+                                         GROUPED ? kPolicyNonTemporal : kPolicyDefault);
     };
     auto issue_part = [&](int j, auto st, int i) {
         copy_a(j, st, i);
@@ -804,30 +600,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             }
         }
     }
-}
-
-Params to_params(const GemmProblem& g) {
-    Params p;
-    p.m = g.m;
-    p.n = g.n;
-    p.k = g.k;
-    p.a = g.a;
-    p.lda = g.lda;
-    p.a_scale = g.a_scale;
-    p.ld_as = g.ld_as;
-    p.b = g.b;
-    p.ldb = g.ldb;
-    p.b_scale = g.b_scale;
-    p.ld_bs = g.ld_bs;
-    p.c = g.c;
-    p.ldc = g.ldc;
-    p.groups = g.groups;
-    p.group_offsets = g.group_offsets;
-    p.group_rows = g.group_rows;
-    p.stride_b = g.stride_b;
-    p.stride_bs = g.stride_bs;
-    p.stride_c_bytes = g.stride_c * (g.out_f32 ? 4 : 2);
-    return p;
 }
 
 // blocks: the dense slots rounded up to a multiple of 8.

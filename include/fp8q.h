@@ -77,14 +77,16 @@ extern "C" {
 /*
  * Limits of the GEMM entry points (fp8_gemm, fp8_grouped_gemm,
  * fp8_grouped_gemm_wgrad, fp8_gemm_mx, fp8_gemm_tensor). A block addresses
- * the rows of its operand tiles, and the 128x128 block scales of its B tile,
- * by 32-bit byte offsets from the tile origin, so:
+ * its operand tiles and their scales through buffer ranges of at most
+ * 2^31 - 1 bytes from the tile origin, so:
  *   lda, ldb <= FP8Q_MAX_GEMM_LD (elements = bytes of FP8 codes);
- *   with 128x128 B block scales, ceil(n/128) * ld_bs < FP8Q_MAX_BSCALE_SPAN.
+ *   every scale array spans fewer than FP8Q_MAX_SCALE_SPAN floats:
+ *   (k/128) * ld_as, and (k/128) * ld_bs (per-row B scales) or
+ *   ceil(n/128) * ld_bs (128x128 B block scales).
  * Larger values return FP8Q_ERR_SHAPE before anything is launched.
  */
-#define FP8Q_MAX_GEMM_LD      16777216LL   /* 2^24 */
-#define FP8Q_MAX_BSCALE_SPAN  1073741824LL /* 2^30 floats */
+#define FP8Q_MAX_GEMM_LD      8388480LL    /* 2^23 - 128 */
+#define FP8Q_MAX_SCALE_SPAN   536870912LL  /* 2^29 floats (2 GiB) */
 
 /*
  * fp8_quantize_act -- fine-grained activation quantization.
@@ -274,7 +276,7 @@ int fp8_quantize_weight_grouped(int32_t groups, const uint16_t *w, int64_t n, in
  *          window is written; k == 0 writes zeros (A, B and their scales
  *          are then not read and may be NULL).
  * Shapes:  m, n >= 0 (any value; ragged tiles are handled), k % 128 == 0;
- *          lda, ldb and the block-scale span within the limits above.
+ *          lda, ldb and the scale spans within the limits above.
  * Alignment: a, b, c 16-byte aligned; lda, ldb % 16 == 0; ldc % 8 == 0;
  *          scales 4-byte aligned.
  * m == 0 or n == 0: returns FP8Q_OK without launching.
@@ -317,8 +319,8 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
  *               then b + e*N with ldb = E*N (stride_b = N), and its block
  *               scales b_scale + e*N/128 with ld_bs = E*N/128.
  * c             [m_total][ldc]; out_dtype as in fp8_gemm.
- * Shapes:       n % 128 == 0, k % 128 == 0; lda, ldb and
- *               (n/128) * ld_bs within the GEMM limits above.
+ * Shapes:       n % 128 == 0, k % 128 == 0; lda, ldb and the scale
+ *               spans within the GEMM limits above.
  * Alignment:    as fp8_gemm; stride_b % 16 == 0.
  * The device arrays are trusted: offsets that break the contract give
  * unspecified output (the kernels still stay within the m_total rows);
@@ -361,7 +363,7 @@ int fp8_grouped_gemm(int32_t groups, const int32_t *group_offsets, const int32_t
  *               ldc >= n, stride_c >= m * ldc, stride_c % 8 == 0. An expert
  *               with an empty segment gets dW_e = 0 (k_total == 0: all are
  *               zero, and A, B and their scales may be NULL).
- * Shapes:       lda, ldb within the GEMM limits above.
+ * Shapes:       lda, ldb and the scale spans within the GEMM limits above.
  * Alignment:    as fp8_gemm.
  * The device array is trusted: segments outside [0, k_total] are skipped
  * (their dW_e is not written); with FP8Q_DEBUG=1 it is checked on the host

@@ -180,24 +180,31 @@ def test_gemm_validation(lib):
 
 
 def test_gemm_operand_pitch_limits(lib):
-    """Tile rows are addressed by 32-bit offsets from the tile origin, so row
-    pitches above 2^24 bytes (and 128x128 block-scale spans of 2^30 floats or
-    more) are refused on the host; at the limit the call is valid."""
-    big = 1 << 24
+    """Tiles and scales are addressed through 31-bit buffer ranges from the
+    tile origin, so row pitches above 2^23 - 128 bytes and scale arrays of
+    2^29 floats or more are refused on the host; at the limit the call is
+    valid."""
+    big = (1 << 23) - 128
+    span = 1 << 29
     assert _g(lib, lda=big + 16) == ERR_SHAPE
     assert _g(lib, ldb=big + 16) == ERR_SHAPE
-    assert _g(lib, ld_bs=(1 << 30) // 2) == ERR_SHAPE          # ceil(200/128) = 2 block rows
+    assert _g(lib, ld_bs=span // 2) == ERR_SHAPE               # ceil(200/128) = 2 block rows
     assert _g(lib, ld_bs=(1 << 62)) == ERR_SHAPE               # no overflow in the span check
+    assert _g(lib, ld_as=span // 2) == ERR_SHAPE               # 2 slabs of A scales
+    assert _g(lib, kind=1, ld_bs=span // 2) == ERR_SHAPE       # 2 slabs of row scales
     assert _g(lib, kind=1, lda=big + 16, ld_bs=200) == ERR_SHAPE
     assert _gg(lib, lda=big + 16) == ERR_SHAPE
     assert _gg(lib, ldb=big + 16) == ERR_SHAPE
-    assert _gg(lib, ld_bs=(1 << 30) // 2) == ERR_SHAPE         # 2 block rows per expert
+    assert _gg(lib, ld_bs=span // 2) == ERR_SHAPE              # 2 block rows per expert
     assert _gw(lib, lda=big + 16) == ERR_SHAPE
+    assert _gw(lib, ld_bs=span // 4) == ERR_SHAPE              # 4 token slabs of row scales
     assert _mxg(lib, ldb=big + 16) == ERR_SHAPE
+    assert _mxg(lib, ld_bs=span // 2) == ERR_SHAPE
     assert _tg(lib, lda=big + 16) == ERR_SHAPE
     if not torch.cuda.is_available():   # valid at the limit: fails only at the launch
         assert _g(lib, lda=big) == ERR_HIP
         assert _g(lib, ldb=big) == ERR_HIP
+        assert _g(lib, ld_as=span // 2 - 1) == ERR_HIP
 
 
 def _gg(lib, groups=4, off=A16, rows=0, m=512, n=256, k=256, a=A16b, lda=256, a_s=A4, ld_as=512,
