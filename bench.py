@@ -644,7 +644,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, config: str, probe_mib: int, out
     return res
 
 
-MI355X_SIMDS = 256 * 4   # 256 CUs x 4 SIMDs
+MI355X_CUS = 256
+MI355X_SIMDS = MI355X_CUS * 4   # 4 SIMDs per CU
 PEAK_CLOCK_HZ = 2.4e9
 
 
@@ -656,7 +657,12 @@ def counter_table(path: str, wl_obj: Workload) -> str:
     * MFMA busy at peak clock: SQ_VALU_MFMA_BUSY_CYCLES (MFMA pipe cycles,
       summed over the SIMDs) / (SIMDs x duration x 2.4 GHz);
     * waiting: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES, the share of wave cycles
-      spent in s_waitcnt (SQ_WAIT_INST_LDS likewise, waits on LDS)."""
+      spent in s_waitcnt (SQ_WAIT_INST_LDS likewise, waits on LDS);
+    * the memory path: the mean L1 -> L2 read latency in cycles
+      (TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ), the L2 hit rate
+      (TCC_HIT / (TCC_HIT + TCC_MISS)) and the share of L1 cycles stalled on
+      data pending from L2 (TCP_PENDING_STALL_CYCLES over 256 L1s x duration x
+      2.4 GHz, a lower bound when the clock runs below its peak)."""
     disp = {}
     with open(path, newline="") as f:
         for r in csv.DictReader(f):
@@ -673,6 +679,12 @@ def counter_table(path: str, wl_obj: Workload) -> str:
         derived.append("waiting (s_waitcnt)")
     if "SQ_WAIT_INST_LDS" in counters and "SQ_WAVE_CYCLES" in counters:
         derived.append("waiting on LDS")
+    if "TCP_TCC_READ_REQ_LATENCY_sum" in counters and "TCP_TCC_READ_REQ_sum" in counters:
+        derived.append("L1->L2 read latency (cycles)")
+    if "TCC_HIT_sum" in counters and "TCC_MISS_sum" in counters:
+        derived.append("L2 hit rate")
+    if "TCP_PENDING_STALL_CYCLES_sum" in counters:
+        derived.append("L1 stalled on L2 data")
     out = ["| " + " | ".join(head + derived) + " |", "|" + "---|" * (len(head) + len(derived))]
     for label, frag in KERNEL_NAMES.items():
         if label not in step_labels:
@@ -689,6 +701,12 @@ def counter_table(path: str, wl_obj: Workload) -> str:
             row.append("%.3f" % (mean["SQ_WAIT_INST_ANY"] / max(mean["SQ_WAVE_CYCLES"], 1.0)))
         if "waiting on LDS" in derived:
             row.append("%.3f" % (mean["SQ_WAIT_INST_LDS"] / max(mean["SQ_WAVE_CYCLES"], 1.0)))
+        if "L1->L2 read latency (cycles)" in derived:
+            row.append("%.0f" % (mean["TCP_TCC_READ_REQ_LATENCY_sum"] / max(mean["TCP_TCC_READ_REQ_sum"], 1.0)))
+        if "L2 hit rate" in derived:
+            row.append("%.3f" % (mean["TCC_HIT_sum"] / max(mean["TCC_HIT_sum"] + mean["TCC_MISS_sum"], 1.0)))
+        if "L1 stalled on L2 data" in derived:
+            row.append("%.3f" % (mean["TCP_PENDING_STALL_CYCLES_sum"] / (MI355X_CUS * ns * 1e-9 * PEAK_CLOCK_HZ)))
         out.append("| " + " | ".join(row) + " |")
     return "\n".join(out)
 
