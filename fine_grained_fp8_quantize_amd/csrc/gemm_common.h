@@ -114,9 +114,10 @@ __device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
 // Slots run expert by expert, inside an expert by n-tile and then m-tile, so
 // the m-tiles that share a 256 x K panel of W_e -- the tail included -- are
 // consecutive and run together on one XCD, where the panel is fetched into
-// L2 once. (Every tile streams the same K x 256 weight panel, so tiles with
-// few real rows take about as long as full ones: ordering by tile size buys
-// no balance, and measured ~5% slower than this order.)
+// L2 once. (Every tile streams the same K x 256 weight panel, and its padding
+// rows cost one repeated line, so a tile with 128 real rows still takes about
+// 3/4 of a full tile's time: ordering by tile size buys no balance, and
+// measured ~5% slower than this order.)
 struct ExpertSplit {
     int beg;    // first row of the segment
     int tiles;  // m-tiles of the segment
