@@ -25,7 +25,10 @@
 // tiles two A and three B stages -- with 16-byte chunks XOR-swizzled by row.
 //
 // Modes: one GEMM; grouped over M (MoE Fprop/Dgrad); grouped over K (MoE
-// Wgrad). Two more dense variants accumulate in place across slabs instead
+// Wgrad); one GEMM of several rounds of whole tiles, run by one looping block
+// per CU that copies each next tile's first slab during the last slab of the
+// tile before (Dgrad-like shapes: short K, several rounds).
+// Two more dense variants accumulate in place across slabs instead
 // of promoting: microscaling operands (E8M0 block scales applied by the
 // scaled MFMA) and one scale per tensor (applied in the epilogue).
 // The MFMA computes the transposed tile: its row operand is B (n), its column
@@ -98,6 +101,7 @@ __device__ __forceinline__ float* stage_sb() {
 template <int BN, bool ROWSCALE, bool OUT_F32, int MODE, bool MX = false, bool TENSOR = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     constexpr bool GROUPED = MODE == kGroupedM;
+    constexpr bool ROUNDS = MODE == kDenseRounds;
     static_assert(!MX || (ROWSCALE && MODE == kDense), "microscaling: dense, per-row staging");
     static_assert(!TENSOR || (ROWSCALE && MODE == kDense && !MX), "per-tensor: dense, no staged scales");
     constexpr bool INPLACE = MX || TENSOR;  // MFMA accumulates across slabs
@@ -107,6 +111,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // With 224-wide tiles a wave's 112 columns can straddle two 128-wide
     // weight blocks; each 16-column subtile still lies inside one block.
     constexpr bool STRADDLE = !ROWSCALE && (WN % 128 != 0);
+    static_assert(!ROUNDS || (!MX && !TENSOR), "rounds: promoted block or row scales");
 
     // Grouped tiles stream each expert's weights from HBM once: they keep two
     // B slabs in flight (three B stages) and take their scales through
@@ -120,8 +125,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     } else if constexpr (MODE == kGroupedK) {
         if (!grouped_k_tile<BN>(p, tr)) return;
     } else {
-        if (!dense_tile<BN>(p, tr)) return;
+        if (!dense_tile<BN>(p, 0, tr)) return;
     }
+
+    // Several rounds: this block's tiles one after another. The last step of
+    // a tile copies the next tile's first slab (and its scales) instead of a
+    // slab of its own, so the next tile starts computing at once while the
+    // stores of the tile before are still in flight.
+    bool prefetched = false;
+    for (int it = 0;; ++it) {
+    TileRows nx;
+    bool has_next = false;
+    if constexpr (ROUNDS) has_next = dense_tile<BN>(p, it + 1, nx);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -156,23 +171,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // area. Waves 4-7 copy B scales into the sB area: with per-row scaling the
     // slab's B scales (64 each); with 128x128 blocks, lane l copies the scale
     // of n-block (n0/128 + l%4), the at most three blocks a tile touches.
+    const int64_t ld_s = wave < 4 ? p.ld_as : (ROWSCALE ? p.ld_bs : 1);
+    // the wave's scale source of tile t's first slab: a base and a lane offset
+    auto scale_src = [&](const TileRows& t, const float*& base, uint32_t& off) {
+        if (wave < 4) {
+            base = p.a_scale + t.m0;
+            off = (uint32_t)(min(t.m0 + 64 * wave + lane, m_last) - t.m0) * 4u;
+        } else if (ROWSCALE) {
+            base = t.b_scale + t.n0;
+            off = (uint32_t)(min(t.n0 + min(64 * (wave - 4) + lane, BN - 1), n_last) - t.n0) * 4u;
+        } else {
+            base = t.b_scale;
+            off = (uint32_t)(min(t.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
+        }
+        base += (int64_t)t.slab0 * ld_s;
+    };
     const float* scale_base;
-    int64_t ld_s;
     uint32_t offS;
-    if (wave < 4) {
-        scale_base = p.a_scale + tr.m0;
-        ld_s = p.ld_as;
-        offS = (uint32_t)(min(tr.m0 + 64 * wave + lane, m_last) - tr.m0) * 4u;
-    } else if (ROWSCALE) {
-        scale_base = tr.b_scale + tr.n0;
-        ld_s = p.ld_bs;
-        offS = (uint32_t)(min(tr.n0 + min(64 * (wave - 4) + lane, BN - 1), n_last) - tr.n0) * 4u;
-    } else {
-        scale_base = tr.b_scale;
-        ld_s = 1;
-        offS = (uint32_t)(min(tr.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
+    scale_src(tr, scale_base, offS);
+
+    // What one step copies: A and B slab bases and the wave's scale source.
+    struct CopySrc {
+        const uint8_t* a;
+        const uint8_t* b;
+        const uint8_t* s;
+        uint32_t offs;
+    };
+    auto src_of = [&](int j) {
+        return CopySrc{tileA + (int64_t)j * kSlab, tileB + (int64_t)j * kSlab,
+                       reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s), offS};
+    };
+    // the next tile's first slab (rounds; every tile whole, so the lane
+    // offsets of the A and B copies are those of this tile)
+    CopySrc next0 = src_of(0);
+    if constexpr (ROUNDS) {
+        if (has_next) {
+            const float* nb;
+            uint32_t no;
+            scale_src(nx, nb, no);
+            next0 = CopySrc{p.a + nx.m0 * p.lda, nx.b + nx.n0 * p.ldb, reinterpret_cast<const uint8_t*>(nb), no};
+        }
     }
-    scale_base += (int64_t)tr.slab0 * ld_s;  // the tile's first slab
 
     // Part i (0..3) of this wave's copy of slab j into stage st: 8 rows of
     // A and 8 rows of B; part 3 also carries the scales. Computing waves
@@ -192,38 +231,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         const int row = 32 * wave + 8 * i + (lane >> 3);
         return (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + swz_chunk(lane & 7, row) * 16;
     };
-    auto copy_a = [&](int j, auto st, int i) {
+    auto copy_a_from = [&](const uint8_t* ga, auto st, int i) {
         uint8_t* base = stage_a<decltype(st)::value>() + 32 * wave * kSlab;
-        const uint8_t* ga = tileA + (int64_t)j * kSlab;
         // (offset computed outside the builtin's argument list: a lambda
         // call there keeps the host pass from emitting the kernel's stub)
         const uint32_t off = a_off(i);
         __builtin_amdgcn_global_load_lds(ga + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, kPolicyDefault);
     };
-    auto copy_b = [&](int j, auto st, int i) {
+    auto copy_b_from = [&](const uint8_t* gb, auto st, int i) {
         uint8_t* base = stage_b<decltype(st)::value>() + 32 * wave * kSlab;
-        const uint8_t* gb = tileB + (int64_t)j * kSlab;
         const uint32_t off = b_off(i);
         __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(base + i * 8 * kSlab), 16, 0,
                                          GROUPED ? kPolicyNonTemporal : kPolicyDefault);
     };
-    auto issue_part = [&](int j, auto st, int i) {
-        copy_a(j, st, i);
-        copy_b(j, st, i);
+    auto copy_a = [&](int j, auto st, int i) { copy_a_from(tileA + (int64_t)j * kSlab, st, i); };
+    auto copy_b = [&](int j, auto st, int i) { copy_b_from(tileB + (int64_t)j * kSlab, st, i); };
+    auto issue_part = [&](const CopySrc& src, auto st, int i) {
+        copy_a_from(src.a, st, i);
+        copy_b_from(src.b, st, i);
         if constexpr (!DEEP && !TENSOR) {
             if (i == 3) {
                 constexpr int S = decltype(st)::value;
-                const uint8_t* gs = reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s);
                 float* dst = wave < 4 ? stage_sa<S>() + 64 * wave : stage_sb<S>() + 64 * (wave - 4);
-                __builtin_amdgcn_global_load_lds(gs + offS, (lds_void*)dst, 4, 0, 0);
+                __builtin_amdgcn_global_load_lds(src.s + src.offs, (lds_void*)dst, 4, 0, 0);
             }
         }
     };
-    auto issue = [&](int j, auto st) {
+    auto issue = [&](const CopySrc& src, auto st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) issue_part(j, st, i);
+        for (int i = 0; i < 4; ++i) issue_part(src, st, i);
     };
-    int jnext = 0;  // slab the current step prefetches
+    CopySrc nsrc = src_of(0);  // what the current step prefetches
 
     // ---- fragment addresses: lane (i = l%16, g = l/16) reads 32 bytes of
     // row i, the 16-byte chunks g and g + 4 of every 16-row subtile. In the
@@ -346,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             if constexpr (T + 1 < NSUB)
                 read_b(std::integral_constant<int, T + 1>{}, fr[(T + 1) & 1], fsb[(T + 1) & 1]);
             if constexpr (!GROUPED && T < 4)
-                issue_part(jnext, std::integral_constant<int, ST ^ 1>{}, T);
+                issue_part(nsrc, std::integral_constant<int, ST ^ 1>{}, T);
 #pragma unroll
             for (int s = 0; s < ACT; ++s)
                 pc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], zero, 0, 0, 0, 0, 0, 0);
@@ -432,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
                 fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + off0, lb + (T + 1) * 2048 + off1);
                 if constexpr (MX) sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
             }
-            if constexpr (T < 4) issue_part(jnext, std::integral_constant<int, ST ^ 1>{}, T);
+            if constexpr (T < 4) issue_part(nsrc, std::integral_constant<int, ST ^ 1>{}, T);
 #pragma unroll
             for (int s = 0; s < ACT; ++s) {
                 // (zero scale operands select the unscaled instruction)
@@ -456,23 +494,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     auto mainloop = [&](auto act_tag) {
         constexpr int ACT = decltype(act_tag)::value;
         const float no_sab[kMSub] = {0.f, 0.f, 0.f, 0.f};
+        // A step waits for its slab at its start; with several rounds at its
+        // end instead (the same wait, for the copy it issued), so that the
+        // last step of a tile leaves the next tile's first slab ready and the
+        // tile's stores are never waited for.
         auto step = [&](auto stage_tag, int j) {
             constexpr int ST = decltype(stage_tag)::value;
-            wait_dma_and_barrier<0>();
+            if constexpr (!ROUNDS) wait_dma_and_barrier<0>();
             // Prefetch the next slab into the other stage: spread over the
             // first n-subtiles, or all at once for a wave without MFMA work.
-            // The last step re-loads its own slab there instead (never read),
-            // keeping the body branch-free.
-            jnext = min(j + 1, slabs - 1);
-            if constexpr (ACT == 0) issue(jnext, std::integral_constant<int, ST ^ 1>{});
+            // The last step copies the next tile's first slab there (rounds)
+            // or re-loads its own slab (never read), keeping the body
+            // branch-free.
+            nsrc = src_of(min(j + 1, slabs - 1));
+            if constexpr (ROUNDS) {
+                // (values, not lvalues: a select between two objects' fields
+                // would keep every local of the kernel in scratch memory)
+                const bool cross = j + 1 >= slabs && has_next;
+                nsrc = CopySrc{pick(cross, next0.a, nsrc.a), pick(cross, next0.b, nsrc.b),
+                               pick(cross, next0.s, nsrc.s), pick(cross, next0.offs, nsrc.offs)};
+            }
+            if constexpr (ACT == 0) issue(nsrc, std::integral_constant<int, ST ^ 1>{});
             if constexpr (ACT > 0) {
                 if constexpr (INPLACE)
                     compute_inplace(stage_tag, act_tag);
                 else
                     compute(stage_tag, stage_tag, act_tag, no_sab);
             }
+            if constexpr (ROUNDS) wait_dma_and_barrier<0>();
         };
-        if (slabs > 0) issue(0, std::integral_constant<int, 0>{});
+        if (slabs > 0 && !prefetched) {
+            issue(src_of(0), std::integral_constant<int, 0>{});
+            if constexpr (ROUNDS) wait_dma_and_barrier<0>();
+        }
         int j = 0;
         for (; j + 2 <= slabs; j += 2) {
             step(std::integral_constant<int, 0>{}, j);
@@ -554,17 +608,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             case 1: mainloop_deep(std::integral_constant<int, 1>{}); break;
             default: mainloop_deep(std::integral_constant<int, 0>{}); break;
         }
-    } else if (act > 0) {
+    } else if (ROUNDS || act > 0) {
         mainloop(std::integral_constant<int, 4>{});  // ragged-M rows are computed and dropped
     } else {
         mainloop(std::integral_constant<int, 0>{});
     }
-    // Drain the last (unused) prefetches before the block's LDS can be reused.
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // Drain the last (unused) prefetches before the block's LDS can be reused
+    // (with several rounds every step has waited for its copy already).
+    if constexpr (!ROUNDS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
     // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
     // (k == 0: the scales may be NULL and are not read; C is zero)
     const float alpha = (TENSOR && p.k > 0) ? p.a_scale[0] * p.b_scale[0] : 1.0f;
+    if constexpr (ROUNDS) {
+        // whole tiles: no edge guards (their branches would keep these loops
+        // rolled inside the tile loop)
+#pragma unroll
+        for (int s = 0; s < kMSub; ++s) {
+            const int64_t m = wrow + s * 16 + fi;
+#pragma unroll
+            for (int t = 0; t < NSUB; ++t) {
+                const int64_t n = wcol + t * 16 + 4 * fg;
+                const v4f v = acc[t][s];
+                if constexpr (OUT_F32) {
+                    *reinterpret_cast<v4f*>(reinterpret_cast<float*>(tr.c) + m * p.ldc + n) = v;
+                } else {
+                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tr.c) + m * p.ldc + n) =
+                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                }
+            }
+        }
+    } else {
 #pragma unroll
     for (int s = 0; s < kMSub; ++s) {
         const int64_t m = wrow + s * 16 + fi;
@@ -600,6 +674,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
             }
         }
     }
+    }
+    if (!has_next) break;
+    tr = nx;
+    prefetched = true;
+    }
 }
 
 // blocks: the dense slots rounded up to a multiple of 8.
@@ -617,6 +696,26 @@ hipError_t dispatch_dense(const GemmProblem& g, int64_t blocks, hipStream_t stre
             hipLaunchKernelGGL((gemm_kernel<BN, false, true, kDense>), grid, block, 0, stream, p);
         else
             hipLaunchKernelGGL((gemm_kernel<BN, false, false, kDense>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+// A dense GEMM of several rounds of whole tiles: 256 blocks, one per CU,
+// each looping over its tiles (see dense_tile).
+template <int BN>
+hipError_t dispatch_rounds(const GemmProblem& g, hipStream_t stream) {
+    const Params p = to_params(g);
+    const dim3 grid(256), block(kThreads);
+    if (g.b_rowscale) {
+        if (g.out_f32)
+            hipLaunchKernelGGL((gemm_kernel<BN, true, true, kDenseRounds>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<BN, true, false, kDenseRounds>), grid, block, 0, stream, p);
+    } else {
+        if (g.out_f32)
+            hipLaunchKernelGGL((gemm_kernel<BN, false, true, kDenseRounds>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_kernel<BN, false, false, kDenseRounds>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -679,10 +778,22 @@ int64_t grid_cost(int64_t m, int64_t n, int64_t bn) {
 
 }  // namespace
 
+// Several rounds of whole 224-wide tiles, with an even number of slabs: one
+// looping block per CU. (Paired on one MI355X, bit-identical output: Dgrad
+// 4096 x 7168 x 2048 took 64.2 against 65.4 us, and 8192 x 7168 x 2048 118.9
+// against 123.7 us; a 256-wide looping tile, which needs a few more registers
+// than the kernel has, gained nothing on 8192 x 4096 x 7168.)
+bool use_rounds(const GemmProblem& g) {
+    const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
+    const int64_t slabs = g.k / kSlab;
+    return tiles > 256 && g.m % kBM == 0 && g.n % 224 == 0 && slabs >= 2 && slabs % 2 == 0;
+}
+
 hipError_t launch_gemm(const GemmProblem& g, hipStream_t stream) {
     // 224-wide n tiles when the grid then takes less time on the 256 CUs,
     // e.g. N = 7168 = 32 x 224 (Dgrad, Wgrad); otherwise 256-wide.
     if (grid_cost(g.m, g.n, 224) < grid_cost(g.m, g.n, 256)) {
+        if (use_rounds(g)) return dispatch_rounds<224>(g, stream);
         const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 223) / 224);
         return dispatch_dense<224>(g, (tiles + 7) / 8 * 8, stream);
     }

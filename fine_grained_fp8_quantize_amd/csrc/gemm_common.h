@@ -73,22 +73,31 @@ struct TileRows {
 
 // Kernel modes: one GEMM; grouped over M (MoE Fprop/Dgrad: experts own row
 // segments, one weight each); grouped over K (MoE Wgrad: experts own token
-// segments of the contraction, one output each).
+// segments of the contraction, one output each); one GEMM whose tiles take
+// several rounds of the CUs, run by one block per CU that loops over its
+// tiles (every tile whole: M and N multiples of the tile, an even number of
+// slabs) and fetches each next tile's first slab under the stores of the
+// tile before.
 constexpr int kDense = 0;
 constexpr int kGroupedM = 1;
 constexpr int kGroupedK = 2;
+constexpr int kDenseRounds = 3;
 
-// Dense tile order: block -> XCD x = block % 8 gets the contiguous slot
-// range [x*per, (x+1)*per); slots walk 4-row bands of tiles so the blocks
-// resident on one XCD share A and B panels in its L2.
+// Dense tile order: slot s belongs to XCD s / per, where per = ceil(tiles/8);
+// block b runs on XCD b % 8, and its i-th tile (one-tile-per-block launches:
+// its only tile, i = 0) is slot (b % 8) * per + b / 8 + 32 i. Within an XCD,
+// slots walk 4-row bands of tiles, so the blocks resident on one XCD share A
+// and B panels in its L2. Rounds of a looping grid of 256 blocks take the
+// same slots at the same time as a grid of one block per tile would.
 template <int BN>
-__device__ __forceinline__ bool dense_tile(const Params& p, TileRows& t) {
+__device__ __forceinline__ bool dense_tile(const Params& p, int i, TileRows& t) {
     const int tiles_m = (int)((p.m + kBM - 1) / kBM);
     const int tiles_n = (int)((p.n + BN - 1) / BN);
     const int total = tiles_m * tiles_n;
     const int per = (total + 7) / 8;
-    const int slot = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    if (slot >= total) return false;
+    const int q = (int)(blockIdx.x / 8) + 32 * i;
+    const int slot = (int)(blockIdx.x % 8) * per + q;
+    if (q >= per || slot >= total) return false;
     constexpr int G = 4;
     const int group = slot / (G * tiles_n);
     const int first_m = group * G;
@@ -218,6 +227,12 @@ __device__ __forceinline__ v8i ld_frag(const uint8_t* p0, const uint8_t* p1) {
     const v4i lo = *reinterpret_cast<const v4i*>(p0);
     const v4i hi = *reinterpret_cast<const v4i*>(p1);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// c ? a : b on values
+template <class T>
+__device__ __forceinline__ T pick(bool c, T a, T b) {
+    return c ? a : b;
 }
 
 template <int... Is, class F>

@@ -389,3 +389,34 @@ def test_grouped_padded_views_and_strides():
     assert_gemm_close(got[real, :n], ref[real], "grouped padded views")
     pad = np.setdiff1d(np.arange(m_total), real)
     assert np.all(got[pad, :n] == 0), "padding rows not zero"
+
+
+# ------------------------------------------------------------ looping grid
+
+@pytest.mark.parametrize("m,n,k,out", [
+    (4096, 7168, 256, "bf16"),    # 2 rounds of 224-wide tiles, the minimum 2 slabs
+    (4096, 7168, 256, "f32"),
+    (5120, 7168, 512, "bf16"),    # 640 tiles: some blocks run 3 tiles, others 2
+    (6144, 7168, 256, "f32"),     # 3 rounds
+    (8192, 3584, 256, "bf16"),    # N = 16 x 224
+    (4096, 7168, 384, "bf16"),    # odd slab count: one tile per block instead
+])
+def test_block_scaled_several_rounds(m, n, k, out):
+    """Shapes whose whole 224-wide tiles take several rounds of the CUs run
+    one looping block per CU, which copies each next tile's first slab under
+    the tile before; every element of every tile against the oracle."""
+    x = wl.activation(5, "dgrad", 40, m, k, 50.0)
+    w = wl.weight(5, "dgrad", 41, n, k)
+    a_q, a_s = oracle.quant_act_1x128(x)
+    b_q, b_s = oracle.quant_weight_128x128(w)
+    _check_full(a_q, a_s, b_q, b_s, "block", out, "rounds block m=%d n=%d k=%d %s" % (m, n, k, out))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_row_scaled_several_rounds(out):
+    m, n, tokens = 4096, 7168, 256
+    dy = wl.activation(5, "wgrad", 42, tokens, m, None)
+    x = wl.activation(5, "wgrad", 43, tokens, n, 50.0)
+    a_q, a_s = oracle.quant_act_128x1(dy)
+    b_q, b_s = oracle.quant_act_128x1(x)
+    _check_full(a_q, a_s, b_q, b_s, "row", out, "rounds row %s" % out)
