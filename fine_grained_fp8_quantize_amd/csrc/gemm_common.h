@@ -127,6 +127,11 @@ __device__ __forceinline__ bool dense_tile(const Params& p, int i, TileRows& t) 
 // rows cost one repeated line, so a tile with 128 real rows still takes about
 // 3/4 of a full tile's time: ordering by tile size buys no balance, and
 // measured ~5% slower than this order.)
+// Experts run last to first: the grouped weight quantizer writes them first
+// to last, so right after it the last experts' codes are the ones still held
+// by the memory-side cache. Measured on one MI355X in the quantize-then-GEMM
+// step: 388.6 against 400.0 us for the MoE Fprop GEMM (bit-identical output),
+// and no difference when GEMMs run back to back.
 struct ExpertSplit {
     int beg;    // first row of the segment
     int tiles;  // m-tiles of the segment
@@ -149,7 +154,8 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
     const int tiles_n = (int)((p.n + BN - 1) / BN);
     const int q = (int)(blockIdx.x >> 3);
     int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
-    for (int e = 0; e < p.groups; ++e) {
+    for (int ee = 0; ee < p.groups; ++ee) {
+        const int e = p.groups - 1 - ee;
         const ExpertSplit x = expert_split(p, e);
         const int k = x.tiles;
         if (slot < k * tiles_n) {
