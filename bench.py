@@ -71,11 +71,12 @@ KERNEL_NAMES = {
 
 
 def _code_only(text: str) -> str:
-    """Source text without comments and blank lines (what the kernels are made of)."""
+    """Source text without comments, blank lines and indentation (what the
+    kernels are made of)."""
     import re
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
-    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+    return "\n".join(line.strip() for line in text.splitlines() if line.strip())
 
 
 def kernel_source_digest(csrc: str | None = None) -> str:

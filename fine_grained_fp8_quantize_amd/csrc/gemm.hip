@@ -134,550 +134,550 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
     // stores of the tile before are still in flight.
     bool prefetched = false;
     for (int it = 0;; ++it) {
-    TileRows nx;
-    bool has_next = false;
-    if constexpr (ROUNDS) has_next = dense_tile<BN>(p, it + 1, nx);
+        TileRows nx;
+        bool has_next = false;
+        if constexpr (ROUNDS) has_next = dense_tile<BN>(p, it + 1, nx);
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int slabs = tr.slabs;
-    const int64_t m_last = p.m - 1;
-    const int64_t n_last = p.n - 1;
+        const int tid = threadIdx.x;
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave >> 1, wn = wave & 1;
+        const int slabs = tr.slabs;
+        const int64_t m_last = p.m - 1;
+        const int64_t n_last = p.n - 1;
 
-    // ---- LDS-DMA sources: wave w copies rows [32w, 32w+32) of both tiles,
-    // 8 rows (1 KB) per instruction; lane l -> row 8i + l/8, chunk l%8.
-    // Rows past the tile or the matrix are clamped to valid rows (loaded,
-    // never used). Addresses are a wave-uniform base (tile origin + slab) plus
-    // a 32-bit per-lane offset, which maps onto the saddr + voffset form.
-    const uint8_t* const tileA = p.a + tr.m0 * p.lda + (int64_t)tr.slab0 * kSlab;
-    const uint8_t* const tileB = tr.b + tr.n0 * p.ldb + (int64_t)tr.slab0 * kSlab;
-    // In a grouped tile, A rows past the tile's real rows only feed outputs
-    // that are written as zeros or not at all (an output row depends on its
-    // own A row only): every lane of such an 8-row chunk reads the same
-    // 128-byte line, so the copy costs one L2 line instead of 1 KB.
-    const int a_rows = (int)min((int64_t)kBM, min(tr.real_end, tr.row_hi) - tr.m0);
-    uint32_t offA[4], offB[4];
+        // ---- LDS-DMA sources: wave w copies rows [32w, 32w+32) of both tiles,
+        // 8 rows (1 KB) per instruction; lane l -> row 8i + l/8, chunk l%8.
+        // Rows past the tile or the matrix are clamped to valid rows (loaded,
+        // never used). Addresses are a wave-uniform base (tile origin + slab) plus
+        // a 32-bit per-lane offset, which maps onto the saddr + voffset form.
+        const uint8_t* const tileA = p.a + tr.m0 * p.lda + (int64_t)tr.slab0 * kSlab;
+        const uint8_t* const tileB = tr.b + tr.n0 * p.ldb + (int64_t)tr.slab0 * kSlab;
+        // In a grouped tile, A rows past the tile's real rows only feed outputs
+        // that are written as zeros or not at all (an output row depends on its
+        // own A row only): every lane of such an 8-row chunk reads the same
+        // 128-byte line, so the copy costs one L2 line instead of 1 KB.
+        const int a_rows = (int)min((int64_t)kBM, min(tr.real_end, tr.row_hi) - tr.m0);
+        uint32_t offA[4], offB[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 32 * wave + 8 * i + (lane >> 3);
-        const int chunk = swz_chunk(lane & 7, row);
-        const int src = (GROUPED && 32 * wave + 8 * i >= a_rows) ? max(a_rows - 1, 0) : row;
-        offA[i] = (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + chunk * 16;
-        offB[i] = (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + chunk * 16;
-    }
-    // Scales: waves 0-3 copy the slab's 256 A scales (64 each) into the sA
-    // area. Waves 4-7 copy B scales into the sB area: with per-row scaling the
-    // slab's B scales (64 each); with 128x128 blocks, lane l copies the scale
-    // of n-block (n0/128 + l%4), the at most three blocks a tile touches.
-    const int64_t ld_s = wave < 4 ? p.ld_as : (ROWSCALE ? p.ld_bs : 1);
-    // the wave's scale source of tile t's first slab: a base and a lane offset
-    auto scale_src = [&](const TileRows& t, const float*& base, uint32_t& off) {
-        if (wave < 4) {
-            base = p.a_scale + t.m0;
-            off = (uint32_t)(min(t.m0 + 64 * wave + lane, m_last) - t.m0) * 4u;
-        } else if (ROWSCALE) {
-            base = t.b_scale + t.n0;
-            off = (uint32_t)(min(t.n0 + min(64 * (wave - 4) + lane, BN - 1), n_last) - t.n0) * 4u;
-        } else {
-            base = t.b_scale;
-            off = (uint32_t)(min(t.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 32 * wave + 8 * i + (lane >> 3);
+            const int chunk = swz_chunk(lane & 7, row);
+            const int src = (GROUPED && 32 * wave + 8 * i >= a_rows) ? max(a_rows - 1, 0) : row;
+            offA[i] = (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + chunk * 16;
+            offB[i] = (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + chunk * 16;
         }
-        base += (int64_t)t.slab0 * ld_s;
-    };
-    const float* scale_base;
-    uint32_t offS;
-    scale_src(tr, scale_base, offS);
-
-    // What one step copies: A and B slab bases and the wave's scale source.
-    struct CopySrc {
-        const uint8_t* a;
-        const uint8_t* b;
-        const uint8_t* s;
-        uint32_t offs;
-    };
-    auto src_of = [&](int j) {
-        return CopySrc{tileA + (int64_t)j * kSlab, tileB + (int64_t)j * kSlab,
-                       reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s), offS};
-    };
-    // the next tile's first slab (rounds; every tile whole, so the lane
-    // offsets of the A and B copies are those of this tile)
-    CopySrc next0 = src_of(0);
-    if constexpr (ROUNDS) {
-        if (has_next) {
-            const float* nb;
-            uint32_t no;
-            scale_src(nx, nb, no);
-            next0 = CopySrc{p.a + nx.m0 * p.lda, nx.b + nx.n0 * p.ldb, reinterpret_cast<const uint8_t*>(nb), no};
-        }
-    }
-
-    // Part i (0..3) of this wave's copy of slab j into stage st: 8 rows of
-    // A and 8 rows of B; part 3 also carries the scales. Computing waves
-    // spread the parts over their first n-subtiles, which keeps the LDS-DMA
-    // writes from bunching up behind the barrier.
-    // Three-stage kernels recompute the offsets of each copy (a few VALU
-    // operations at the step boundary) instead of holding eight registers
-    // through the MFMA loop.
-    auto a_off = [&](int i) -> uint32_t {
-        if constexpr (!DEEP) return offA[i];
-        const int row = 32 * wave + 8 * i + (lane >> 3);
-        const int src = 32 * wave + 8 * i >= a_rows ? max(a_rows - 1, 0) : row;
-        return (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + swz_chunk(lane & 7, row) * 16;
-    };
-    auto b_off = [&](int i) -> uint32_t {
-        if constexpr (!DEEP) return offB[i];
-        const int row = 32 * wave + 8 * i + (lane >> 3);
-        return (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + swz_chunk(lane & 7, row) * 16;
-    };
-    auto copy_a_from = [&](const uint8_t* ga, auto st, int i) {
-        uint8_t* base = stage_a<decltype(st)::value>() + 32 * wave * kSlab;
-        // (offset computed outside the builtin's argument list: a lambda
-        // call there keeps the host pass from emitting the kernel's stub)
-        const uint32_t off = a_off(i);
-        __builtin_amdgcn_global_load_lds(ga + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, kPolicyDefault);
-    };
-    auto copy_b_from = [&](const uint8_t* gb, auto st, int i) {
-        uint8_t* base = stage_b<decltype(st)::value>() + 32 * wave * kSlab;
-        const uint32_t off = b_off(i);
-        __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(base + i * 8 * kSlab), 16, 0,
-                                         GROUPED ? kPolicyNonTemporal : kPolicyDefault);
-    };
-    auto copy_a = [&](int j, auto st, int i) { copy_a_from(tileA + (int64_t)j * kSlab, st, i); };
-    auto copy_b = [&](int j, auto st, int i) { copy_b_from(tileB + (int64_t)j * kSlab, st, i); };
-    auto issue_part = [&](const CopySrc& src, auto st, int i) {
-        copy_a_from(src.a, st, i);
-        copy_b_from(src.b, st, i);
-        if constexpr (!DEEP && !TENSOR) {
-            if (i == 3) {
-                constexpr int S = decltype(st)::value;
-                float* dst = wave < 4 ? stage_sa<S>() + 64 * wave : stage_sb<S>() + 64 * (wave - 4);
-                __builtin_amdgcn_global_load_lds(src.s + src.offs, (lds_void*)dst, 4, 0, 0);
-            }
-        }
-    };
-    auto issue = [&](const CopySrc& src, auto st) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) issue_part(src, st, i);
-    };
-    CopySrc nsrc = src_of(0);  // what the current step prefetches
-
-    // ---- fragment addresses: lane (i = l%16, g = l/16) reads 32 bytes of
-    // row i, the 16-byte chunks g and g + 4 of every 16-row subtile. In the
-    // 16x16x128 FP8 MFMA the 32 bytes of lane group g are K[16g, 16g+16) and
-    // K[64+16g, 64+16g+16) of the slab, and the scale of K block b (32
-    // elements) comes from lane group b (measured on gfx950); with chunks g
-    // and g + 4, block b is chunks 2b and 2b+1 -- the microscaling
-    // quantizer's block b. The unscaled MFMA is blind to the order (A and B
-    // share it), and this order reads LDS without bank conflicts (counted:
-    // chunks 2g and 2g+1 cost ~11M conflict cycles per Dense Fprop GEMM).
-    const int fi = lane & 15, fg = lane >> 4;
-    const uint32_t off0 = fi * kSlab + swz_chunk(fg, fi) * 16;
-    const uint32_t off1 = fi * kSlab + swz_chunk(fg + 4, fi) * 16;
-    const uint32_t fragA = wm * kWaveM * kSlab;
-    const uint32_t fragB = wn * WN * kSlab;
-    // Block scales: the wave's first column lies in n-block nb0; sB holds the
-    // tile's blocks from n0/128 on. Subtiles T < split are in nb0, the rest in
-    // nb0 + 1 (only possible when STRADDLE).
-    const int64_t wcol = tr.n0 + wn * WN;
-    const int nb_rel = (int)(wcol / 128 - tr.n0 / 128);
-    const int split = (int)((128 - (wcol & 127)) / 16);
-
-    // Real rows of the wave (grouped padding, ragged M): m-subtiles past them
-    // skip their MFMAs. act is wave-uniform.
-    const int64_t wrow = tr.m0 + wm * kWaveM;
-    const int64_t live = min(tr.real_end, tr.row_hi) - wrow;
-    const int act = (int)max((int64_t)0, min((int64_t)kMSub, (live + 15) / 16));
-
-    v4f acc[NSUB][kMSub];
-#pragma unroll
-    for (int t = 0; t < NSUB; ++t)
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) acc[t][s] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
-
-    // Three-stage kernel: the lane's four A scales and the wave's B block
-    // scale of slab j, loaded into registers one step ahead.
-    const int row_a0 = (int)(wrow - tr.m0) + fi;       // the lane's row in m-subtile 0
-    const int row_a_last = (int)(m_last - tr.m0);
-    const float* const bscale_row = tr.b_scale + min(wcol, n_last) / 128 * p.ld_bs;
-    auto load_scales = [&](int j, float (&sa)[kMSub], float& sb) {
-        const float* as = p.a_scale + tr.m0 + (int64_t)j * p.ld_as;
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) sa[s] = as[min(row_a0 + 16 * s, row_a_last)];
-        sb = bscale_row[j];
-    };
-
-    // Block-scale dense kernels defer the promotion of each slab's last
-    // subtile into the next slab (carry_p * carry_f; zero before the first).
-    constexpr bool DEFER = !ROWSCALE && !DEEP;
-    v4f carry_p[kMSub];
-    float carry_f[kMSub];
-#pragma unroll
-    for (int s = 0; s < kMSub; ++s) {
-        carry_p[s] = zero;
-        carry_f[s] = 0.f;
-    }
-
-    // One slab of MFMAs + promotion for the first ACT m-subtiles of the wave,
-    // on A stage AS and B stage BS (two-stage kernels: AS = BS, scales from
-    // LDS; three-stage kernels: the products sA * sB come in sab_in).
-    auto compute = [&](auto a_tag, auto b_tag, auto act_tag, const float (&sab_in)[kMSub]) {
-        constexpr int ST = decltype(a_tag)::value;
-        constexpr int BS = decltype(b_tag)::value;
-        constexpr int ACT = decltype(act_tag)::value;
-        const uint8_t* const la = stage_a<ST>() + fragA;
-        const uint8_t* const lb = stage_b<BS>() + fragB;
-        const float* const lsa = stage_sa<ST % 2>() + wm * kWaveM + fi;
-        const float* const lsb = stage_sb<ST % 2>();
-        // B fragment of n-subtile T (and, with per-row B scales, the lane's
-        // four scales)
-        auto read_b = [&](auto t_tag, v8i& bf, v4f& sbv) {
-            constexpr int T = decltype(t_tag)::value;
-            bf = ld_frag(lb + T * 2048 + off0, lb + T * 2048 + off1);
-            if constexpr (ROWSCALE)
-                sbv = *reinterpret_cast<const v4f*>(lsb + wn * WN + 4 * fg + 16 * T);
-        };
-        v8i fr[2];
-        v4f fsb[2];
-        v4f pc[kMSub], pp[kMSub];
-        v4f sbp;
-        // Reads in the order the first MFMAs use them -- B fragment 0, A
-        // fragments 0..3, then the scales (first needed by the promotion in
-        // subtile 1) -- so the first MFMA waits for four reads, not all.
-        read_b(std::integral_constant<int, 0>{}, fr[0], fsb[0]);
-        v8i am[kMSub];
-        float sa[kMSub];
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) sa[s] = DEEP ? 0.f : lsa[16 * s];
-        const float sb0 = (ROWSCALE || DEEP) ? 0.f : lsb[nb_rel];
-        const float sb1 = (ROWSCALE || !STRADDLE) ? 0.f : lsb[nb_rel + 1];
-        float sab0[kMSub], sab1[kMSub];
-        // Software pipeline over the n-subtiles: while the MFMAs of subtile T
-        // run, the fragment of T+1 is in flight and the partials of T-1 are
-        // promoted (acc += P * sA * sB), one FMA group after each MFMA.
-        auto promote = [&](auto t_tag, const v4f& sbn) {
-            constexpr int T = decltype(t_tag)::value;
-#pragma unroll
-            for (int s = 0; s < ACT; ++s) {
-                if constexpr (ROWSCALE) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        acc[T][s][r] = __builtin_fmaf(pp[s][r], sa[s] * sbn[r], acc[T][s][r]);
-                } else {
-                    float f = sab0[s];
-                    if constexpr (STRADDLE) f = T < split ? sab0[s] : sab1[s];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[T][s][r] = __builtin_fmaf(pp[s][r], f, acc[T][s][r]);
-                }
-            }
-        };
-        __builtin_amdgcn_sched_barrier(0);
-        unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
-            constexpr int T = decltype(t_tag)::value;
-            constexpr int NEXT_READS = ROWSCALE ? 3 : 2;
-            const v8i bf = fr[T & 1];
-            if constexpr (T + 1 < NSUB)
-                read_b(std::integral_constant<int, T + 1>{}, fr[(T + 1) & 1], fsb[(T + 1) & 1]);
-            if constexpr (!GROUPED && T < 4)
-                issue_part(nsrc, std::integral_constant<int, ST ^ 1>{}, T);
-#pragma unroll
-            for (int s = 0; s < ACT; ++s)
-                pc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], zero, 0, 0, 0, 0, 0, 0);
-            if constexpr (T == 0) {
-                // the previous slab's last subtile (deferred), then this
-                // slab's scale products
-                if constexpr (DEFER) {
-#pragma unroll
-                    for (int s = 0; s < ACT; ++s)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            acc[NSUB - 1][s][r] = __builtin_fmaf(carry_p[s][r], carry_f[s], acc[NSUB - 1][s][r]);
-                }
-#pragma unroll
-                for (int s = 0; s < kMSub; ++s) {
-                    sab0[s] = DEEP ? sab_in[s] : sa[s] * sb0;
-                    if constexpr (STRADDLE) sab1[s] = sa[s] * sb1;
-                }
+        // Scales: waves 0-3 copy the slab's 256 A scales (64 each) into the sA
+        // area. Waves 4-7 copy B scales into the sB area: with per-row scaling the
+        // slab's B scales (64 each); with 128x128 blocks, lane l copies the scale
+        // of n-block (n0/128 + l%4), the at most three blocks a tile touches.
+        const int64_t ld_s = wave < 4 ? p.ld_as : (ROWSCALE ? p.ld_bs : 1);
+        // the wave's scale source of tile t's first slab: a base and a lane offset
+        auto scale_src = [&](const TileRows& t, const float*& base, uint32_t& off) {
+            if (wave < 4) {
+                base = p.a_scale + t.m0;
+                off = (uint32_t)(min(t.m0 + 64 * wave + lane, m_last) - t.m0) * 4u;
+            } else if (ROWSCALE) {
+                base = t.b_scale + t.n0;
+                off = (uint32_t)(min(t.n0 + min(64 * (wave - 4) + lane, BN - 1), n_last) - t.n0) * 4u;
             } else {
-                promote(std::integral_constant<int, T - 1>{}, sbp);
+                base = t.b_scale;
+                off = (uint32_t)(min(t.n0 / 128 + (lane & 3), n_last / 128) * p.ld_bs) * 4u;
             }
-            // Order: the first MFMA (its wait covers only the fragment read
-            // one subtile earlier), the next fragment's reads, this subtile's
-            // copy part, then the FMA group of one m-subtile after each MFMA.
-            constexpr int FMAS = ROWSCALE ? 8 : (STRADDLE ? 5 : 4);
-            constexpr bool HAS_FMAS = T > 0 || DEFER;
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NEXT_READS, 0);
-            if constexpr (!GROUPED && T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
-            if constexpr (HAS_FMAS) __builtin_amdgcn_sched_group_barrier(0x002, T > 0 ? FMAS : 4, 0);
-#pragma unroll
-            for (int s = 1; s < ACT; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if constexpr (HAS_FMAS) __builtin_amdgcn_sched_group_barrier(0x002, T > 0 ? FMAS : 4, 0);
-            }
-#pragma unroll
-            for (int s = 0; s < ACT; ++s) pp[s] = pc[s];
-            sbp = fsb[T & 1];
-            __builtin_amdgcn_sched_barrier(0);
-        });
-        if constexpr (DEFER) {
-            // the last subtile is promoted at the start of the next slab,
-            // where the VALU otherwise waits for the fragment reads
-#pragma unroll
-            for (int s = 0; s < kMSub; ++s) {
-                carry_p[s] = pp[s];
-                carry_f[s] = (!STRADDLE || NSUB - 1 < split) ? sab0[s] : sab1[s];
-            }
-        } else {
-            promote(std::integral_constant<int, NSUB - 1>{}, sbp);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
-
-    // One slab of the in-place GEMMs. Microscaling: the scaled MFMA takes
-    // each lane's E8M0 byte (lane group g supplies block g's byte, see the
-    // fragment addresses) and accumulates into acc directly. Per-tensor: the
-    // plain MFMA accumulates into acc directly.
-    auto compute_inplace = [&](auto a_tag, auto act_tag) {
-        constexpr int ST = decltype(a_tag)::value;
-        constexpr int ACT = decltype(act_tag)::value;
-        const uint8_t* const la = stage_a<ST>() + fragA;
-        const uint8_t* const lb = stage_b<ST>() + fragB;
-        const uint32_t* const lsa = reinterpret_cast<const uint32_t*>(stage_sa<ST>()) + wm * kWaveM + fi;
-        const uint32_t* const lsb = reinterpret_cast<const uint32_t*>(stage_sb<ST>()) + wn * WN + fi;
-        const int shift = 8 * fg;
-        v8i fr[2];
-        uint32_t sbw[2];
-        fr[0] = ld_frag(lb + off0, lb + off1);
-        sbw[0] = MX ? lsb[0] : 0u;
-        v8i am[kMSub];
-        int sae[kMSub];
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
-#pragma unroll
-        for (int s = 0; s < kMSub; ++s) sae[s] = MX ? (int)((lsa[16 * s] >> shift) & 0xFFu) : 0;
-        __builtin_amdgcn_sched_barrier(0);
-        unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
-            constexpr int T = decltype(t_tag)::value;
-            const v8i bf = fr[T & 1];
-            const int sbe = MX ? (int)((sbw[T & 1] >> shift) & 0xFFu) : 0;
-            if constexpr (T + 1 < NSUB) {
-                fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + off0, lb + (T + 1) * 2048 + off1);
-                if constexpr (MX) sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
-            }
-            if constexpr (T < 4) issue_part(nsrc, std::integral_constant<int, ST ^ 1>{}, T);
-#pragma unroll
-            for (int s = 0; s < ACT; ++s) {
-                // (zero scale operands select the unscaled instruction)
-                if constexpr (MX)
-                    acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
-                                                                                0, sbe, 0, sae[s]);
-                else
-                    acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
-                                                                                0, 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, MX ? 3 : 2, 0);
-            if constexpr (T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, ACT - 1, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
-    // The K loop for a wave with ACT live m-subtiles (ACT = 0: the wave only
-    // does its share of the copies and the barriers).
-    auto mainloop = [&](auto act_tag) {
-        constexpr int ACT = decltype(act_tag)::value;
-        const float no_sab[kMSub] = {0.f, 0.f, 0.f, 0.f};
-        // A step waits for its slab at its start; with several rounds at its
-        // end instead (the same wait, for the copy it issued), so that the
-        // last step of a tile leaves the next tile's first slab ready and the
-        // tile's stores are never waited for.
-        auto step = [&](auto stage_tag, int j) {
-            constexpr int ST = decltype(stage_tag)::value;
-            if constexpr (!ROUNDS) wait_dma_and_barrier<0>();
-            // Prefetch the next slab into the other stage: spread over the
-            // first n-subtiles, or all at once for a wave without MFMA work.
-            // The last step copies the next tile's first slab there (rounds)
-            // or re-loads its own slab (never read), keeping the body
-            // branch-free.
-            nsrc = src_of(min(j + 1, slabs - 1));
-            if constexpr (ROUNDS) {
-                // (values, not lvalues: a select between two objects' fields
-                // would keep every local of the kernel in scratch memory)
-                const bool cross = j + 1 >= slabs && has_next;
-                nsrc = CopySrc{pick(cross, next0.a, nsrc.a), pick(cross, next0.b, nsrc.b),
-                               pick(cross, next0.s, nsrc.s), pick(cross, next0.offs, nsrc.offs)};
-            }
-            if constexpr (ACT == 0) issue(nsrc, std::integral_constant<int, ST ^ 1>{});
-            if constexpr (ACT > 0) {
-                if constexpr (INPLACE)
-                    compute_inplace(stage_tag, act_tag);
-                else
-                    compute(stage_tag, stage_tag, act_tag, no_sab);
-            }
-            if constexpr (ROUNDS) wait_dma_and_barrier<0>();
+            base += (int64_t)t.slab0 * ld_s;
         };
-        if (slabs > 0 && !prefetched) {
-            issue(src_of(0), std::integral_constant<int, 0>{});
-            if constexpr (ROUNDS) wait_dma_and_barrier<0>();
-        }
-        int j = 0;
-        for (; j + 2 <= slabs; j += 2) {
-            step(std::integral_constant<int, 0>{}, j);
-            step(std::integral_constant<int, 1>{}, j + 1);
-        }
-        if (j < slabs) step(std::integral_constant<int, 0>{}, j);
-        if constexpr (DEFER && ACT > 0) {
-#pragma unroll
-            for (int s = 0; s < ACT; ++s)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[NSUB - 1][s][r] = __builtin_fmaf(carry_p[s][r], carry_f[s], acc[NSUB - 1][s][r]);
-        }
-    };
+        const float* scale_base;
+        uint32_t offS;
+        scale_src(tr, scale_base, offS);
 
-    // Three-stage K loop: slab j lives in A stage j % 2 and B stage j % 3.
-    // Step j waits until only this wave's youngest copy (the 4 B parts of
-    // slab j + 1) may still be in flight, then prefetches the scales and A of
-    // slab j + 1 and the B of slab j + 2, in that order (the wait count
-    // relies on it). Clamped slab indices keep the tail branch-free.
-    auto mainloop_deep = [&](auto act_tag) {
-        constexpr int ACT = decltype(act_tag)::value;
-        float sa_nx[kMSub], sb_nx;
-        auto copy_all_a = [&](int jj, auto st) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) copy_a(jj, st, i);
+        // What one step copies: A and B slab bases and the wave's scale source.
+        struct CopySrc {
+            const uint8_t* a;
+            const uint8_t* b;
+            const uint8_t* s;
+            uint32_t offs;
         };
-        auto copy_all_b = [&](int jj, auto st) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) copy_b(jj, st, i);
+        auto src_of = [&](int j) {
+            return CopySrc{tileA + (int64_t)j * kSlab, tileB + (int64_t)j * kSlab,
+                           reinterpret_cast<const uint8_t*>(scale_base + (int64_t)j * ld_s), offS};
         };
-        auto step = [&](auto a_tag, auto b_tag, int j) {
-            constexpr int AS = decltype(a_tag)::value;
-            constexpr int BS = decltype(b_tag)::value;
-            wait_dma_and_barrier<4>();
-            float sab[kMSub];
-#pragma unroll
-            for (int s = 0; s < kMSub; ++s) sab[s] = sa_nx[s] * sb_nx;
-            load_scales(min(j + 1, slabs - 1), sa_nx, sb_nx);
-            copy_all_a(min(j + 1, slabs - 1), std::integral_constant<int, AS ^ 1>{});
-            __builtin_amdgcn_sched_barrier(0);
-            copy_all_b(min(j + 2, slabs - 1), std::integral_constant<int, (BS + 2) % 3>{});
-            __builtin_amdgcn_sched_barrier(0);
-            if constexpr (ACT > 0) compute(a_tag, b_tag, act_tag, sab);
-        };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        if (slabs == 0) return;
-        load_scales(0, sa_nx, sb_nx);
-        copy_all_a(0, I0{});
-        __builtin_amdgcn_sched_barrier(0);
-        copy_all_b(0, I0{});
-        __builtin_amdgcn_sched_barrier(0);
-        copy_all_b(min(1, slabs - 1), I1{});
-        __builtin_amdgcn_sched_barrier(0);
-        int j = 0;
-        for (; j + 6 <= slabs; j += 6) {
-            step(I0{}, I0{}, j);
-            step(I1{}, I1{}, j + 1);
-            step(I0{}, I2{}, j + 2);
-            step(I1{}, I0{}, j + 3);
-            step(I0{}, I1{}, j + 4);
-            step(I1{}, I2{}, j + 5);
+        // the next tile's first slab (rounds; every tile whole, so the lane
+        // offsets of the A and B copies are those of this tile)
+        CopySrc next0 = src_of(0);
+        if constexpr (ROUNDS) {
+            if (has_next) {
+                const float* nb;
+                uint32_t no;
+                scale_src(nx, nb, no);
+                next0 = CopySrc{p.a + nx.m0 * p.lda, nx.b + nx.n0 * p.ldb, reinterpret_cast<const uint8_t*>(nb), no};
+            }
         }
-        const int rem = slabs - j;
-        if (rem > 0) step(I0{}, I0{}, j);
-        if (rem > 1) step(I1{}, I1{}, j + 1);
-        if (rem > 2) step(I0{}, I2{}, j + 2);
-        if (rem > 3) step(I1{}, I0{}, j + 3);
-        if (rem > 4) step(I0{}, I1{}, j + 4);
-    };
-    if constexpr (GROUPED) {
-        // expert tails: only the live m-subtiles do MFMA work
-        switch (act) {
-            case 4: mainloop_deep(std::integral_constant<int, 4>{}); break;
-            case 3: mainloop_deep(std::integral_constant<int, 3>{}); break;
-            case 2: mainloop_deep(std::integral_constant<int, 2>{}); break;
-            case 1: mainloop_deep(std::integral_constant<int, 1>{}); break;
-            default: mainloop_deep(std::integral_constant<int, 0>{}); break;
-        }
-    } else if (ROUNDS || act > 0) {
-        mainloop(std::integral_constant<int, 4>{});  // ragged-M rows are computed and dropped
-    } else {
-        mainloop(std::integral_constant<int, 0>{});
-    }
-    // Drain the last (unused) prefetches before the block's LDS can be reused
-    // (with several rounds every step has waited for its copy already).
-    if constexpr (!ROUNDS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
-    // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
-    // (k == 0: the scales may be NULL and are not read; C is zero)
-    const float alpha = (TENSOR && p.k > 0) ? p.a_scale[0] * p.b_scale[0] : 1.0f;
-    if constexpr (ROUNDS) {
-        // whole tiles: no edge guards (their branches would keep these loops
-        // rolled inside the tile loop)
+        // Part i (0..3) of this wave's copy of slab j into stage st: 8 rows of
+        // A and 8 rows of B; part 3 also carries the scales. Computing waves
+        // spread the parts over their first n-subtiles, which keeps the LDS-DMA
+        // writes from bunching up behind the barrier.
+        // Three-stage kernels recompute the offsets of each copy (a few VALU
+        // operations at the step boundary) instead of holding eight registers
+        // through the MFMA loop.
+        auto a_off = [&](int i) -> uint32_t {
+            if constexpr (!DEEP) return offA[i];
+            const int row = 32 * wave + 8 * i + (lane >> 3);
+            const int src = 32 * wave + 8 * i >= a_rows ? max(a_rows - 1, 0) : row;
+            return (uint32_t)((min(tr.m0 + src, m_last) - tr.m0) * p.lda) + swz_chunk(lane & 7, row) * 16;
+        };
+        auto b_off = [&](int i) -> uint32_t {
+            if constexpr (!DEEP) return offB[i];
+            const int row = 32 * wave + 8 * i + (lane >> 3);
+            return (uint32_t)((min(tr.n0 + min(row, BN - 1), n_last) - tr.n0) * p.ldb) + swz_chunk(lane & 7, row) * 16;
+        };
+        auto copy_a_from = [&](const uint8_t* ga, auto st, int i) {
+            uint8_t* base = stage_a<decltype(st)::value>() + 32 * wave * kSlab;
+            // (offset computed outside the builtin's argument list: a lambda
+            // call there keeps the host pass from emitting the kernel's stub)
+            const uint32_t off = a_off(i);
+            __builtin_amdgcn_global_load_lds(ga + off, (lds_void*)(base + i * 8 * kSlab), 16, 0, kPolicyDefault);
+        };
+        auto copy_b_from = [&](const uint8_t* gb, auto st, int i) {
+            uint8_t* base = stage_b<decltype(st)::value>() + 32 * wave * kSlab;
+            const uint32_t off = b_off(i);
+            __builtin_amdgcn_global_load_lds(gb + off, (lds_void*)(base + i * 8 * kSlab), 16, 0,
+                                             GROUPED ? kPolicyNonTemporal : kPolicyDefault);
+        };
+        auto copy_a = [&](int j, auto st, int i) { copy_a_from(tileA + (int64_t)j * kSlab, st, i); };
+        auto copy_b = [&](int j, auto st, int i) { copy_b_from(tileB + (int64_t)j * kSlab, st, i); };
+        auto issue_part = [&](const CopySrc& src, auto st, int i) {
+            copy_a_from(src.a, st, i);
+            copy_b_from(src.b, st, i);
+            if constexpr (!DEEP && !TENSOR) {
+                if (i == 3) {
+                    constexpr int S = decltype(st)::value;
+                    float* dst = wave < 4 ? stage_sa<S>() + 64 * wave : stage_sb<S>() + 64 * (wave - 4);
+                    __builtin_amdgcn_global_load_lds(src.s + src.offs, (lds_void*)dst, 4, 0, 0);
+                }
+            }
+        };
+        auto issue = [&](const CopySrc& src, auto st) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) issue_part(src, st, i);
+        };
+        CopySrc nsrc = src_of(0);  // what the current step prefetches
+
+        // ---- fragment addresses: lane (i = l%16, g = l/16) reads 32 bytes of
+        // row i, the 16-byte chunks g and g + 4 of every 16-row subtile. In the
+        // 16x16x128 FP8 MFMA the 32 bytes of lane group g are K[16g, 16g+16) and
+        // K[64+16g, 64+16g+16) of the slab, and the scale of K block b (32
+        // elements) comes from lane group b (measured on gfx950); with chunks g
+        // and g + 4, block b is chunks 2b and 2b+1 -- the microscaling
+        // quantizer's block b. The unscaled MFMA is blind to the order (A and B
+        // share it), and this order reads LDS without bank conflicts (counted:
+        // chunks 2g and 2g+1 cost ~11M conflict cycles per Dense Fprop GEMM).
+        const int fi = lane & 15, fg = lane >> 4;
+        const uint32_t off0 = fi * kSlab + swz_chunk(fg, fi) * 16;
+        const uint32_t off1 = fi * kSlab + swz_chunk(fg + 4, fi) * 16;
+        const uint32_t fragA = wm * kWaveM * kSlab;
+        const uint32_t fragB = wn * WN * kSlab;
+        // Block scales: the wave's first column lies in n-block nb0; sB holds the
+        // tile's blocks from n0/128 on. Subtiles T < split are in nb0, the rest in
+        // nb0 + 1 (only possible when STRADDLE).
+        const int64_t wcol = tr.n0 + wn * WN;
+        const int nb_rel = (int)(wcol / 128 - tr.n0 / 128);
+        const int split = (int)((128 - (wcol & 127)) / 16);
+
+        // Real rows of the wave (grouped padding, ragged M): m-subtiles past them
+        // skip their MFMAs. act is wave-uniform.
+        const int64_t wrow = tr.m0 + wm * kWaveM;
+        const int64_t live = min(tr.real_end, tr.row_hi) - wrow;
+        const int act = (int)max((int64_t)0, min((int64_t)kMSub, (live + 15) / 16));
+
+        v4f acc[NSUB][kMSub];
+#pragma unroll
+        for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) acc[t][s] = v4f{0.f, 0.f, 0.f, 0.f};
+
+        const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+        // Three-stage kernel: the lane's four A scales and the wave's B block
+        // scale of slab j, loaded into registers one step ahead.
+        const int row_a0 = (int)(wrow - tr.m0) + fi;       // the lane's row in m-subtile 0
+        const int row_a_last = (int)(m_last - tr.m0);
+        const float* const bscale_row = tr.b_scale + min(wcol, n_last) / 128 * p.ld_bs;
+        auto load_scales = [&](int j, float (&sa)[kMSub], float& sb) {
+            const float* as = p.a_scale + tr.m0 + (int64_t)j * p.ld_as;
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) sa[s] = as[min(row_a0 + 16 * s, row_a_last)];
+            sb = bscale_row[j];
+        };
+
+        // Block-scale dense kernels defer the promotion of each slab's last
+        // subtile into the next slab (carry_p * carry_f; zero before the first).
+        constexpr bool DEFER = !ROWSCALE && !DEEP;
+        v4f carry_p[kMSub];
+        float carry_f[kMSub];
 #pragma unroll
         for (int s = 0; s < kMSub; ++s) {
-            const int64_t m = wrow + s * 16 + fi;
-#pragma unroll
-            for (int t = 0; t < NSUB; ++t) {
-                const int64_t n = wcol + t * 16 + 4 * fg;
-                const v4f v = acc[t][s];
-                if constexpr (OUT_F32) {
-                    *reinterpret_cast<v4f*>(reinterpret_cast<float*>(tr.c) + m * p.ldc + n) = v;
-                } else {
-                    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tr.c) + m * p.ldc + n) =
-                        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-                }
-            }
+            carry_p[s] = zero;
+            carry_f[s] = 0.f;
         }
-    } else {
+
+        // One slab of MFMAs + promotion for the first ACT m-subtiles of the wave,
+        // on A stage AS and B stage BS (two-stage kernels: AS = BS, scales from
+        // LDS; three-stage kernels: the products sA * sB come in sab_in).
+        auto compute = [&](auto a_tag, auto b_tag, auto act_tag, const float (&sab_in)[kMSub]) {
+            constexpr int ST = decltype(a_tag)::value;
+            constexpr int BS = decltype(b_tag)::value;
+            constexpr int ACT = decltype(act_tag)::value;
+            const uint8_t* const la = stage_a<ST>() + fragA;
+            const uint8_t* const lb = stage_b<BS>() + fragB;
+            const float* const lsa = stage_sa<ST % 2>() + wm * kWaveM + fi;
+            const float* const lsb = stage_sb<ST % 2>();
+            // B fragment of n-subtile T (and, with per-row B scales, the lane's
+            // four scales)
+            auto read_b = [&](auto t_tag, v8i& bf, v4f& sbv) {
+                constexpr int T = decltype(t_tag)::value;
+                bf = ld_frag(lb + T * 2048 + off0, lb + T * 2048 + off1);
+                if constexpr (ROWSCALE)
+                    sbv = *reinterpret_cast<const v4f*>(lsb + wn * WN + 4 * fg + 16 * T);
+            };
+            v8i fr[2];
+            v4f fsb[2];
+            v4f pc[kMSub], pp[kMSub];
+            v4f sbp;
+            // Reads in the order the first MFMAs use them -- B fragment 0, A
+            // fragments 0..3, then the scales (first needed by the promotion in
+            // subtile 1) -- so the first MFMA waits for four reads, not all.
+            read_b(std::integral_constant<int, 0>{}, fr[0], fsb[0]);
+            v8i am[kMSub];
+            float sa[kMSub];
 #pragma unroll
-    for (int s = 0; s < kMSub; ++s) {
-        const int64_t m = wrow + s * 16 + fi;
-        if (m >= tr.row_hi) continue;
-        const bool pad = m >= tr.real_end;
+            for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
 #pragma unroll
-        for (int t = 0; t < NSUB; ++t) {
-            const int64_t n = wcol + t * 16 + 4 * fg;
-            if (n >= tr.n0 + BN) continue;
-            v4f v = pad ? zero : acc[t][s];
-            if constexpr (TENSOR) v = v * alpha;
-            if constexpr (OUT_F32) {
-                float* dst = reinterpret_cast<float*>(tr.c) + m * p.ldc + n;
-                if (n + 3 < p.n) {
-                    *reinterpret_cast<v4f*>(dst) = v;
+            for (int s = 0; s < kMSub; ++s) sa[s] = DEEP ? 0.f : lsa[16 * s];
+            const float sb0 = (ROWSCALE || DEEP) ? 0.f : lsb[nb_rel];
+            const float sb1 = (ROWSCALE || !STRADDLE) ? 0.f : lsb[nb_rel + 1];
+            float sab0[kMSub], sab1[kMSub];
+            // Software pipeline over the n-subtiles: while the MFMAs of subtile T
+            // run, the fragment of T+1 is in flight and the partials of T-1 are
+            // promoted (acc += P * sA * sB), one FMA group after each MFMA.
+            auto promote = [&](auto t_tag, const v4f& sbn) {
+                constexpr int T = decltype(t_tag)::value;
+#pragma unroll
+                for (int s = 0; s < ACT; ++s) {
+                    if constexpr (ROWSCALE) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            acc[T][s][r] = __builtin_fmaf(pp[s][r], sa[s] * sbn[r], acc[T][s][r]);
+                    } else {
+                        float f = sab0[s];
+                        if constexpr (STRADDLE) f = T < split ? sab0[s] : sab1[s];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[T][s][r] = __builtin_fmaf(pp[s][r], f, acc[T][s][r]);
+                    }
+                }
+            };
+            __builtin_amdgcn_sched_barrier(0);
+            unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
+                constexpr int T = decltype(t_tag)::value;
+                constexpr int NEXT_READS = ROWSCALE ? 3 : 2;
+                const v8i bf = fr[T & 1];
+                if constexpr (T + 1 < NSUB)
+                    read_b(std::integral_constant<int, T + 1>{}, fr[(T + 1) & 1], fsb[(T + 1) & 1]);
+                if constexpr (!GROUPED && T < 4)
+                    issue_part(nsrc, std::integral_constant<int, ST ^ 1>{}, T);
+#pragma unroll
+                for (int s = 0; s < ACT; ++s)
+                    pc[s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], zero, 0, 0, 0, 0, 0, 0);
+                if constexpr (T == 0) {
+                    // the previous slab's last subtile (deferred), then this
+                    // slab's scale products
+                    if constexpr (DEFER) {
+#pragma unroll
+                        for (int s = 0; s < ACT; ++s)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[NSUB - 1][s][r] = __builtin_fmaf(carry_p[s][r], carry_f[s], acc[NSUB - 1][s][r]);
+                    }
+#pragma unroll
+                    for (int s = 0; s < kMSub; ++s) {
+                        sab0[s] = DEEP ? sab_in[s] : sa[s] * sb0;
+                        if constexpr (STRADDLE) sab1[s] = sa[s] * sb1;
+                    }
                 } else {
+                    promote(std::integral_constant<int, T - 1>{}, sbp);
+                }
+                // Order: the first MFMA (its wait covers only the fragment read
+                // one subtile earlier), the next fragment's reads, this subtile's
+                // copy part, then the FMA group of one m-subtile after each MFMA.
+                constexpr int FMAS = ROWSCALE ? 8 : (STRADDLE ? 5 : 4);
+                constexpr bool HAS_FMAS = T > 0 || DEFER;
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, NEXT_READS, 0);
+                if constexpr (!GROUPED && T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
+                if constexpr (HAS_FMAS) __builtin_amdgcn_sched_group_barrier(0x002, T > 0 ? FMAS : 4, 0);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (n + r < p.n) dst[r] = v[r];
+                for (int s = 1; s < ACT; ++s) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (HAS_FMAS) __builtin_amdgcn_sched_group_barrier(0x002, T > 0 ? FMAS : 4, 0);
+                }
+#pragma unroll
+                for (int s = 0; s < ACT; ++s) pp[s] = pc[s];
+                sbp = fsb[T & 1];
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (DEFER) {
+                // the last subtile is promoted at the start of the next slab,
+                // where the VALU otherwise waits for the fragment reads
+#pragma unroll
+                for (int s = 0; s < kMSub; ++s) {
+                    carry_p[s] = pp[s];
+                    carry_f[s] = (!STRADDLE || NSUB - 1 < split) ? sab0[s] : sab1[s];
                 }
             } else {
-                uint16_t* dst = reinterpret_cast<uint16_t*>(tr.c) + m * p.ldc + n;
-                const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-                if (n + 3 < p.n) {
-                    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-                } else {
-                    const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
-                                           (uint16_t)(hi >> 16)};
+                promote(std::integral_constant<int, NSUB - 1>{}, sbp);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        // One slab of the in-place GEMMs. Microscaling: the scaled MFMA takes
+        // each lane's E8M0 byte (lane group g supplies block g's byte, see the
+        // fragment addresses) and accumulates into acc directly. Per-tensor: the
+        // plain MFMA accumulates into acc directly.
+        auto compute_inplace = [&](auto a_tag, auto act_tag) {
+            constexpr int ST = decltype(a_tag)::value;
+            constexpr int ACT = decltype(act_tag)::value;
+            const uint8_t* const la = stage_a<ST>() + fragA;
+            const uint8_t* const lb = stage_b<ST>() + fragB;
+            const uint32_t* const lsa = reinterpret_cast<const uint32_t*>(stage_sa<ST>()) + wm * kWaveM + fi;
+            const uint32_t* const lsb = reinterpret_cast<const uint32_t*>(stage_sb<ST>()) + wn * WN + fi;
+            const int shift = 8 * fg;
+            v8i fr[2];
+            uint32_t sbw[2];
+            fr[0] = ld_frag(lb + off0, lb + off1);
+            sbw[0] = MX ? lsb[0] : 0u;
+            v8i am[kMSub];
+            int sae[kMSub];
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) am[s] = ld_frag(la + s * 2048 + off0, la + s * 2048 + off1);
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) sae[s] = MX ? (int)((lsa[16 * s] >> shift) & 0xFFu) : 0;
+            __builtin_amdgcn_sched_barrier(0);
+            unroll(std::make_integer_sequence<int, NSUB>{}, [&](auto t_tag) {
+                constexpr int T = decltype(t_tag)::value;
+                const v8i bf = fr[T & 1];
+                const int sbe = MX ? (int)((sbw[T & 1] >> shift) & 0xFFu) : 0;
+                if constexpr (T + 1 < NSUB) {
+                    fr[(T + 1) & 1] = ld_frag(lb + (T + 1) * 2048 + off0, lb + (T + 1) * 2048 + off1);
+                    if constexpr (MX) sbw[(T + 1) & 1] = lsb[16 * (T + 1)];
+                }
+                if constexpr (T < 4) issue_part(nsrc, std::integral_constant<int, ST ^ 1>{}, T);
+#pragma unroll
+                for (int s = 0; s < ACT; ++s) {
+                    // (zero scale operands select the unscaled instruction)
+                    if constexpr (MX)
+                        acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
+                                                                                    0, sbe, 0, sae[s]);
+                    else
+                        acc[T][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, am[s], acc[T][s], 0, 0,
+                                                                                    0, 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (T + 1 < NSUB) __builtin_amdgcn_sched_group_barrier(0x100, MX ? 3 : 2, 0);
+                if constexpr (T < 4) __builtin_amdgcn_sched_group_barrier(0x020, T == 3 ? 3 : 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, ACT - 1, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+
+        // The K loop for a wave with ACT live m-subtiles (ACT = 0: the wave only
+        // does its share of the copies and the barriers).
+        auto mainloop = [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+            const float no_sab[kMSub] = {0.f, 0.f, 0.f, 0.f};
+            // A step waits for its slab at its start; with several rounds at its
+            // end instead (the same wait, for the copy it issued), so that the
+            // last step of a tile leaves the next tile's first slab ready and the
+            // tile's stores are never waited for.
+            auto step = [&](auto stage_tag, int j) {
+                constexpr int ST = decltype(stage_tag)::value;
+                if constexpr (!ROUNDS) wait_dma_and_barrier<0>();
+                // Prefetch the next slab into the other stage: spread over the
+                // first n-subtiles, or all at once for a wave without MFMA work.
+                // The last step copies the next tile's first slab there (rounds)
+                // or re-loads its own slab (never read), keeping the body
+                // branch-free.
+                nsrc = src_of(min(j + 1, slabs - 1));
+                if constexpr (ROUNDS) {
+                    // (values, not lvalues: a select between two objects' fields
+                    // would keep every local of the kernel in scratch memory)
+                    const bool cross = j + 1 >= slabs && has_next;
+                    nsrc = CopySrc{pick(cross, next0.a, nsrc.a), pick(cross, next0.b, nsrc.b),
+                                   pick(cross, next0.s, nsrc.s), pick(cross, next0.offs, nsrc.offs)};
+                }
+                if constexpr (ACT == 0) issue(nsrc, std::integral_constant<int, ST ^ 1>{});
+                if constexpr (ACT > 0) {
+                    if constexpr (INPLACE)
+                        compute_inplace(stage_tag, act_tag);
+                    else
+                        compute(stage_tag, stage_tag, act_tag, no_sab);
+                }
+                if constexpr (ROUNDS) wait_dma_and_barrier<0>();
+            };
+            if (slabs > 0 && !prefetched) {
+                issue(src_of(0), std::integral_constant<int, 0>{});
+                if constexpr (ROUNDS) wait_dma_and_barrier<0>();
+            }
+            int j = 0;
+            for (; j + 2 <= slabs; j += 2) {
+                step(std::integral_constant<int, 0>{}, j);
+                step(std::integral_constant<int, 1>{}, j + 1);
+            }
+            if (j < slabs) step(std::integral_constant<int, 0>{}, j);
+            if constexpr (DEFER && ACT > 0) {
+#pragma unroll
+                for (int s = 0; s < ACT; ++s)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < p.n) dst[r] = h[r];
+                        acc[NSUB - 1][s][r] = __builtin_fmaf(carry_p[s][r], carry_f[s], acc[NSUB - 1][s][r]);
+            }
+        };
+
+        // Three-stage K loop: slab j lives in A stage j % 2 and B stage j % 3.
+        // Step j waits until only this wave's youngest copy (the 4 B parts of
+        // slab j + 1) may still be in flight, then prefetches the scales and A of
+        // slab j + 1 and the B of slab j + 2, in that order (the wait count
+        // relies on it). Clamped slab indices keep the tail branch-free.
+        auto mainloop_deep = [&](auto act_tag) {
+            constexpr int ACT = decltype(act_tag)::value;
+            float sa_nx[kMSub], sb_nx;
+            auto copy_all_a = [&](int jj, auto st) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) copy_a(jj, st, i);
+            };
+            auto copy_all_b = [&](int jj, auto st) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) copy_b(jj, st, i);
+            };
+            auto step = [&](auto a_tag, auto b_tag, int j) {
+                constexpr int AS = decltype(a_tag)::value;
+                constexpr int BS = decltype(b_tag)::value;
+                wait_dma_and_barrier<4>();
+                float sab[kMSub];
+#pragma unroll
+                for (int s = 0; s < kMSub; ++s) sab[s] = sa_nx[s] * sb_nx;
+                load_scales(min(j + 1, slabs - 1), sa_nx, sb_nx);
+                copy_all_a(min(j + 1, slabs - 1), std::integral_constant<int, AS ^ 1>{});
+                __builtin_amdgcn_sched_barrier(0);
+                copy_all_b(min(j + 2, slabs - 1), std::integral_constant<int, (BS + 2) % 3>{});
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (ACT > 0) compute(a_tag, b_tag, act_tag, sab);
+            };
+            using I0 = std::integral_constant<int, 0>;
+            using I1 = std::integral_constant<int, 1>;
+            using I2 = std::integral_constant<int, 2>;
+            if (slabs == 0) return;
+            load_scales(0, sa_nx, sb_nx);
+            copy_all_a(0, I0{});
+            __builtin_amdgcn_sched_barrier(0);
+            copy_all_b(0, I0{});
+            __builtin_amdgcn_sched_barrier(0);
+            copy_all_b(min(1, slabs - 1), I1{});
+            __builtin_amdgcn_sched_barrier(0);
+            int j = 0;
+            for (; j + 6 <= slabs; j += 6) {
+                step(I0{}, I0{}, j);
+                step(I1{}, I1{}, j + 1);
+                step(I0{}, I2{}, j + 2);
+                step(I1{}, I0{}, j + 3);
+                step(I0{}, I1{}, j + 4);
+                step(I1{}, I2{}, j + 5);
+            }
+            const int rem = slabs - j;
+            if (rem > 0) step(I0{}, I0{}, j);
+            if (rem > 1) step(I1{}, I1{}, j + 1);
+            if (rem > 2) step(I0{}, I2{}, j + 2);
+            if (rem > 3) step(I1{}, I0{}, j + 3);
+            if (rem > 4) step(I0{}, I1{}, j + 4);
+        };
+        if constexpr (GROUPED) {
+            // expert tails: only the live m-subtiles do MFMA work
+            switch (act) {
+                case 4: mainloop_deep(std::integral_constant<int, 4>{}); break;
+                case 3: mainloop_deep(std::integral_constant<int, 3>{}); break;
+                case 2: mainloop_deep(std::integral_constant<int, 2>{}); break;
+                case 1: mainloop_deep(std::integral_constant<int, 1>{}); break;
+                default: mainloop_deep(std::integral_constant<int, 0>{}); break;
+            }
+        } else if (ROUNDS || act > 0) {
+            mainloop(std::integral_constant<int, 4>{});  // ragged-M rows are computed and dropped
+        } else {
+            mainloop(std::integral_constant<int, 0>{});
+        }
+        // Drain the last (unused) prefetches before the block's LDS can be reused
+        // (with several rounds every step has waited for its copy already).
+        if constexpr (!ROUNDS) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+        // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
+        // (k == 0: the scales may be NULL and are not read; C is zero)
+        const float alpha = (TENSOR && p.k > 0) ? p.a_scale[0] * p.b_scale[0] : 1.0f;
+        if constexpr (ROUNDS) {
+            // whole tiles: no edge guards (their branches would keep these loops
+            // rolled inside the tile loop)
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) {
+                const int64_t m = wrow + s * 16 + fi;
+#pragma unroll
+                for (int t = 0; t < NSUB; ++t) {
+                    const int64_t n = wcol + t * 16 + 4 * fg;
+                    const v4f v = acc[t][s];
+                    if constexpr (OUT_F32) {
+                        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(tr.c) + m * p.ldc + n) = v;
+                    } else {
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(tr.c) + m * p.ldc + n) =
+                            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < kMSub; ++s) {
+                const int64_t m = wrow + s * 16 + fi;
+                if (m >= tr.row_hi) continue;
+                const bool pad = m >= tr.real_end;
+#pragma unroll
+                for (int t = 0; t < NSUB; ++t) {
+                    const int64_t n = wcol + t * 16 + 4 * fg;
+                    if (n >= tr.n0 + BN) continue;
+                    v4f v = pad ? zero : acc[t][s];
+                    if constexpr (TENSOR) v = v * alpha;
+                    if constexpr (OUT_F32) {
+                        float* dst = reinterpret_cast<float*>(tr.c) + m * p.ldc + n;
+                        if (n + 3 < p.n) {
+                            *reinterpret_cast<v4f*>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (n + r < p.n) dst[r] = v[r];
+                        }
+                    } else {
+                        uint16_t* dst = reinterpret_cast<uint16_t*>(tr.c) + m * p.ldc + n;
+                        const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+                        if (n + 3 < p.n) {
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+                        } else {
+                            const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
+                                                   (uint16_t)(hi >> 16)};
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (n + r < p.n) dst[r] = h[r];
+                        }
+                    }
                 }
             }
         }
-    }
-    }
-    if (!has_next) break;
-    tr = nx;
-    prefetched = true;
+        if (!has_next) break;
+        tr = nx;
+        prefetched = true;
     }
 }
 
