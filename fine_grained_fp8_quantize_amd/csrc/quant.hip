@@ -523,24 +523,34 @@ __global__ __launch_bounds__(256) void quant_retile_128x1_kernel(int64_t tokens,
 // ---------------------------------------------------------------- 128x128
 
 // Several weight matrices (experts) in one launch: group e starts at the
-// base pointers plus e times these strides (elements); blocks per group.
+// base pointers plus e times these strides (elements); work units (pairs of
+// 128x128 blocks) per group.
 struct WeightGroups {
-    int64_t blocks;
+    int64_t units;
     int64_t w, q, s, qt, st;
-    bool stage_t;  // write the transposed copy through LDS (whole-row stores)
 };
 
 // Grids of at least this many weight blocks (8 per CU) write the transposed
-// copy through LDS: measured, 32 MoE experts quantize in 724 instead of
-// 754 us that way, while a single 2048x7168 weight (896 blocks, too few to
-// hide the extra barrier) takes 15.0 instead of 14.0 us.
+// copy through LDS (STAGE_T kernels): measured, 32 MoE experts quantize in
+// 724 instead of 754 us that way, while a single 2048x7168 weight (896
+// blocks, too few to hide the extra barrier) takes 15.0 instead of 14.0 us.
+// Kernels without the staging hold no LDS for it.
+constexpr int64_t kPairBlocks = 4096;
 constexpr int64_t kStageTBlocks = 2048;
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void store_nt8(uint8_t* p, uint32_t lo, uint32_t hi) {
+    __builtin_nontemporal_store(u32x2_t{lo, hi}, reinterpret_cast<u32x2_t*>(p));
+}
 
 // One 256-thread block quantizes one 128x128 weight block: thread (row group
 // rg = t/16, chunk g = t%16) holds rows 8rg..8rg+7 x columns 8g..8g+7. The
 // optional transposed copy is produced from the thread's 8x8 byte tile with
-// byte permutes, so block (bn, bk) of W^T gets exactly the same codes.
-__device__ __forceinline__ void weight_body(
+// byte permutes, so block (bn, bk) of W^T gets exactly the same codes. (The
+// unit of grids too small for pairs of blocks to balance over the CUs.)
+template <bool STAGE_T>
+__device__ __forceinline__ void weight_block_body(
     const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
     uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
@@ -549,7 +559,7 @@ __device__ __forceinline__ void weight_body(
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int g = t & 15, rg = t >> 4;
     // group (expert) of this block, then its block (bn, bk)
-    const int64_t e = block / grp.blocks, local = block - e * grp.blocks;
+    const int64_t e = block / grp.units, local = block - e * grp.units;
     w += e * grp.w;
     q += e * grp.q;
     scale += e * grp.s;
@@ -590,10 +600,10 @@ __device__ __forceinline__ void weight_body(
         }
         code[i][0] = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[i].x, v[i].y));
         code[i][1] = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[i].z, v[i].w));
-        *reinterpret_cast<uint2*>(q + (n0 + i) * ld_q + k0) = make_uint2(code[i][0], code[i][1]);
+        store_nt8(q + (n0 + i) * ld_q + k0, code[i][0], code[i][1]);
     }
     if (t == 0) scale[bn * ld_s + bk] = gs.s;
-    if (q_t != nullptr && !grp.stage_t) {
+    if (q_t != nullptr && !STAGE_T) {
         if (t == 0) scale_t[bk * ld_st + bn] = gs.s;
         // Column kk of the 8x8 tile = byte (kk % 4) of word (kk / 4) of rows 0..7.
 #pragma unroll
@@ -605,37 +615,181 @@ __device__ __forceinline__ void weight_body(
             *reinterpret_cast<uint2*>(q_t + (k0 + kk) * ld_qt + bn * 128 + 8 * rg) = make_uint2(lo, hi);
         }
     }
-    if (q_t != nullptr && grp.stage_t) {  // block-uniform: the barrier below is reached by all or none
-        // The transposed block goes through LDS so that every store writes
-        // whole 128-byte rows of q_t. Column kk of the thread's 8x8 tile =
-        // byte (kk % 4) of word (kk / 4) of rows 0..7.
-        __shared__ __attribute__((aligned(16))) uint8_t trw[128 * kTrStride];
-        if (t == 0) scale_t[bk * ld_st + bn] = gs.s;
+    if constexpr (STAGE_T) {
+        if (q_t != nullptr) {  // block-uniform: the barrier below is reached by all or none
+            // The transposed block goes through LDS so that every store writes
+            // whole 128-byte rows of q_t. Column kk of the thread's 8x8 tile =
+            // byte (kk % 4) of word (kk / 4) of rows 0..7.
+            __shared__ __attribute__((aligned(16))) uint8_t trw[128 * kTrStride];
+            if (t == 0) scale_t[bk * ld_st + bn] = gs.s;
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) {
-            const int d = kk >> 2;
-            const uint32_t byte = (uint32_t)(kk & 3);
-            const uint32_t lo = gather_byte4(code[0][d], code[1][d], code[2][d], code[3][d], byte);
-            const uint32_t hi = gather_byte4(code[4][d], code[5][d], code[6][d], code[7][d], byte);
-            *reinterpret_cast<uint2*>(&trw[(8 * g + kk) * kTrStride + 8 * rg]) = make_uint2(lo, hi);
+            for (int kk = 0; kk < 8; ++kk) {
+                const int d = kk >> 2;
+                const uint32_t byte = (uint32_t)(kk & 3);
+                const uint32_t lo = gather_byte4(code[0][d], code[1][d], code[2][d], code[3][d], byte);
+                const uint32_t hi = gather_byte4(code[4][d], code[5][d], code[6][d], code[7][d], byte);
+                *reinterpret_cast<uint2*>(&trw[(8 * g + kk) * kTrStride + 8 * rg]) = make_uint2(lo, hi);
+            }
+            __syncthreads();
+            // thread t writes half h of transposed row kr (64 bytes)
+            const int kr = t >> 1, h = t & 1;
+            uint8_t* dst = q_t + (bk * 128 + kr) * ld_qt + bn * 128 + 64 * h;
+            const uint8_t* src = &trw[kr * kTrStride + 64 * h];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(src + 16 * i);
         }
-        __syncthreads();
-        // thread t writes half h of transposed row kr (64 bytes)
-        const int kr = t >> 1, h = t & 1;
-        uint8_t* dst = q_t + (bk * 128 + kr) * ld_qt + bn * 128 + 64 * h;
-        const uint8_t* src = &trw[kr * kTrStride + 64 * h];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(dst + 16 * i) = *reinterpret_cast<const uint4*>(src + 16 * i);
     }
 }
 
+// One 256-thread block quantizes two horizontally adjacent 128x128 weight
+// blocks, (bn, 2p) and (bn, 2p + 1); the second exists only when the number
+// of K blocks is even or p is not the last pair. Lane l of wave wv works on
+// block sel = (l / 16) % 2, rows 16 rb .. 16 rb + 15 with rb = 2 wv + l / 32,
+// columns 8 g .. 8 g + 7 with g = l % 16. Every load instruction then reads
+// 512 contiguous bytes of each of two rows, and codes are stored
+// non-temporal. (A streaming probe of this traffic, 2 B read and 1 B written
+// per element over the 32 MoE experts, measured 457 us this way against
+// 512 us with one block per workgroup -- 4 rows x 256 bytes per load -- and
+// plain stores; each code store instruction covers whole 128-byte lines.)
+// The optional transposed copy is produced from the thread's
+// 16x8 byte tile with byte permutes, so block (bk, bn) of W^T gets exactly
+// the same codes.
+template <bool STAGE_T>
+__device__ __forceinline__ void weight_pair_body(
+    const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
+    WeightGroups grp, int64_t unit) {
+    __shared__ uint32_t red[4][2];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int sel = (lane >> 4) & 1, g = lane & 15, rb = 2 * wv + (lane >> 5);
+    // group (expert) of this unit, then its pair of blocks
+    const int64_t e = unit / grp.units, local = unit - e * grp.units;
+    w += e * grp.w;
+    q += e * grp.q;
+    scale += e * grp.s;
+    if (q_t != nullptr) {
+        q_t += e * grp.qt;
+        scale_t += e * grp.st;
+    }
+    const int64_t pairs = (kblocks + 1) / 2;
+    const int64_t bn = local / pairs, bk0 = 2 * (local - bn * pairs);
+    const int64_t bk = bk0 + sel;
+    const bool valid = bk < kblocks;  // lane-divergent only in the last pair of an odd row
+    const int64_t n0 = bn * 128 + 16 * rb, k0 = bk * 128 + 8 * g;
+
+    uint4 v[16];
+    if (valid) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = load_nt16(w + (n0 + i) * ld_w + k0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    const uint32_t mask = 0x7FFF7FFFu;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        m = pk_max_u16(m, pk_max_u16(pk_max_u16(v[i].x & mask, v[i].y & mask),
+                                     pk_max_u16(v[i].z & mask, v[i].w & mask)));
+    // a DPP row of 16 lanes is one (row band, block); lanes l and l ^ 32 hold
+    // the wave's two row bands of the same block
+    m = row16_max(umax32(m & 0xFFFFu, m >> 16));
+    m = umax32(m, (uint32_t)__shfl_xor((int)m, 32));
+    if ((lane & 47) == 0) red[wv][sel] = m;  // lanes 0 (block 0) and 16 (block 1)
+    __syncthreads();
+    m = umax32(umax32(red[0][sel], red[1][sel]), umax32(red[2][sel], red[3][sel]));
+    const GroupScale gs = group_scale(m);
+    const bool writes_scale = valid && wv == 0 && (lane & 47) == 0;
+
+    uint32_t code[16][2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float a[8] = {bf16_lo(v[i].x), bf16_hi(v[i].x), bf16_lo(v[i].y), bf16_hi(v[i].y),
+                      bf16_lo(v[i].z), bf16_hi(v[i].z), bf16_lo(v[i].w), bf16_hi(v[i].w)};
+        float qv[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) qv[c] = quot_fast(__builtin_fabsf(a[c]), gs);
+        if (gs.slow) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) qv[c] = quot_slow(__builtin_fabsf(a[c]), gs);
+        }
+        code[i][0] = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[i].x, v[i].y));
+        code[i][1] = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[i].z, v[i].w));
+        if (valid) store_nt8(q + (n0 + i) * ld_q + k0, code[i][0], code[i][1]);
+    }
+    if (writes_scale) scale[bn * ld_s + bk] = gs.s;
+    if (q_t == nullptr) return;
+
+    // Column kk of the thread's tile, rows 0..15: byte kk % 4 of word kk / 4
+    // of each row, four rows per word.
+    auto column = [&](int kk, uint32_t (&c4)[4]) {
+        const int d = kk >> 2;
+        const uint32_t byte = (uint32_t)(kk & 3);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            c4[j] = gather_byte4(code[4 * j][d], code[4 * j + 1][d], code[4 * j + 2][d], code[4 * j + 3][d], byte);
+    };
+    if (writes_scale) scale_t[bk * ld_st + bn] = gs.s;
+    // (The transposed copy keeps plain stores: a store instruction here
+    // covers parts of many 128-byte lines, and non-temporal partial-line
+    // stores measured 4x slower.)
+    if constexpr (!STAGE_T) {
+        if (valid) {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                uint32_t c4[4];
+                column(kk, c4);
+                *reinterpret_cast<uint4*>(q_t + (k0 + kk) * ld_qt + n0) = make_uint4(c4[0], c4[1], c4[2], c4[3]);
+            }
+        }
+    } else {
+        // Staged: both transposed blocks go through LDS; then each store
+        // instruction of the block writes 32 whole 128-byte rows (8 lanes per
+        // row). (q_t and the kernel variant are block-uniform, so the barrier
+        // is reached by all threads.)
+        __shared__ __attribute__((aligned(16))) uint8_t trw[2][128 * kTrStride];
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            uint32_t c4[4];
+            column(kk, c4);
+            *reinterpret_cast<uint4*>(&trw[sel][(8 * g + kk) * kTrStride + 16 * rb]) =
+                make_uint4(c4[0], c4[1], c4[2], c4[3]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int idx = 256 * i + t;  // (transposed block, row, 16-byte chunk)
+            const int ws = idx >> 10, kr = (idx >> 3) & 127, c = idx & 7;
+            if (bk0 + ws < kblocks)
+                *reinterpret_cast<uint4*>(q_t + ((bk0 + ws) * 128 + kr) * ld_qt + bn * 128 + 16 * c) =
+                    *reinterpret_cast<const uint4*>(&trw[ws][kr * kTrStride + 16 * c]);
+        }
+    }
+}
+
+// Work unit `unit` of a weight grid: a pair of blocks (PAIR) or one block.
+template <bool STAGE_T, bool PAIR>
+__device__ __forceinline__ void weight_unit(
+    const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
+    uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
+    uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
+    WeightGroups grp, int64_t unit) {
+    if constexpr (PAIR)
+        weight_pair_body<STAGE_T>(w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp, unit);
+    else
+        weight_block_body<STAGE_T>(w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp, unit);
+}
+
+template <bool STAGE_T, bool PAIR>
 __global__ __launch_bounds__(256) void quant_weight_kernel(
     const uint16_t* __restrict__ w, int64_t kblocks, int64_t ld_w,
     uint8_t* __restrict__ q, int64_t ld_q, float* __restrict__ scale, int64_t ld_s,
     uint8_t* __restrict__ q_t, int64_t ld_qt, float* __restrict__ scale_t, int64_t ld_st,
     WeightGroups grp) {
-    weight_body(w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp, (int64_t)blockIdx.x);
+    weight_unit<STAGE_T, PAIR>(w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp,
+                               (int64_t)blockIdx.x);
 }
 
 // ----------------------------------------------- activation + weight, one launch
@@ -666,6 +820,7 @@ struct WeightArgs {
     int64_t ld_st;
 };
 
+template <bool STAGE_T, bool PAIR>
 __global__ __launch_bounds__(256) void quant_act_weight_kernel(ActArgs a, int64_t act_blocks, WeightArgs wa,
                                                                WeightGroups grp) {
     const int64_t b = (int64_t)blockIdx.x;
@@ -673,11 +828,11 @@ __global__ __launch_bounds__(256) void quant_act_weight_kernel(ActArgs a, int64_
     // write the transposed copy: measured, that case finishes sooner with the
     // activation tiles first
     const bool weight_first = wa.q_t == nullptr;
-    const bool is_weight = weight_first ? b < grp.blocks : b >= act_blocks;
-    const int64_t i = b - (is_weight ? (weight_first ? 0 : act_blocks) : (weight_first ? grp.blocks : 0));
+    const bool is_weight = weight_first ? b < grp.units : b >= act_blocks;
+    const int64_t i = b - (is_weight ? (weight_first ? 0 : act_blocks) : (weight_first ? grp.units : 0));
     if (is_weight)
-        weight_body(wa.w, wa.kblocks, wa.ld_w, wa.q, wa.ld_q, wa.scale, wa.ld_s, wa.q_t, wa.ld_qt, wa.scale_t,
-                    wa.ld_st, grp, i);
+        weight_unit<STAGE_T, PAIR>(wa.w, wa.kblocks, wa.ld_w, wa.q, wa.ld_q, wa.scale, wa.ld_s, wa.q_t, wa.ld_qt,
+                                   wa.scale_t, wa.ld_st, grp, i);
     else
         act_1x128_body<false>(a.x, a.rows, a.slabs, a.ld_x, a.q, a.ld_q, a.scale, a.ld_s, a.units, nullptr, 0,
                               (int64_t)0, i);
@@ -807,12 +962,22 @@ hipError_t launch_quant_act_weight(const uint16_t* x, int64_t rows, int64_t cols
     wa.ld_qt = ld_wqt;
     wa.scale_t = ws_t;
     wa.ld_st = ld_wst;
+    // Pairs of blocks when the weight blocks run first (no transposed copy):
+    // the activation tiles then fill the tail. With the transposed copy the
+    // activation tiles go first, and the weights keep the finer single-block
+    // units for the tail.
+    const bool pair = wq_t == nullptr;
+    const bool stage = wq_t != nullptr && n / 128 * wa.kblocks >= kStageTBlocks;
     WeightGroups grp;
-    grp.blocks = n / 128 * wa.kblocks;
+    grp.units = n / 128 * (pair ? (wa.kblocks + 1) / 2 : wa.kblocks);
     grp.w = grp.q = grp.s = grp.qt = grp.st = 0;
-    grp.stage_t = grp.blocks >= kStageTBlocks;
-    hipLaunchKernelGGL(quant_act_weight_kernel, dim3((unsigned)(act_blocks + grp.blocks)), dim3(256), 0, stream,
-                       a, act_blocks, wa, grp);
+    const dim3 grid((unsigned)(act_blocks + grp.units)), block(256);
+    if (pair)
+        hipLaunchKernelGGL((quant_act_weight_kernel<false, true>), grid, block, 0, stream, a, act_blocks, wa, grp);
+    else if (stage)
+        hipLaunchKernelGGL((quant_act_weight_kernel<true, false>), grid, block, 0, stream, a, act_blocks, wa, grp);
+    else
+        hipLaunchKernelGGL((quant_act_weight_kernel<false, false>), grid, block, 0, stream, a, act_blocks, wa, grp);
     return hipGetLastError();
 }
 
@@ -821,16 +986,31 @@ hipError_t launch_quant_weight(int64_t groups, const uint16_t* w, int64_t n, int
                                int64_t ld_s, int64_t stride_s, uint8_t* q_t, int64_t ld_qt, int64_t stride_qt,
                                float* scale_t, int64_t ld_st, int64_t stride_st, hipStream_t stream) {
     const int64_t kblocks = k / 128;
+    const int64_t blocks = groups * (n / 128) * kblocks;
+    // Pairs of blocks for grids of at least 16 blocks per CU; smaller grids
+    // keep single-block units, which balance better over the CUs.
+    const bool pair = blocks >= kPairBlocks;
+    const bool stage = q_t != nullptr && blocks >= kStageTBlocks;
     WeightGroups grp;
-    grp.blocks = n / 128 * kblocks;
+    grp.units = n / 128 * (pair ? (kblocks + 1) / 2 : kblocks);
     grp.w = stride_w;
     grp.q = stride_q;
     grp.s = stride_s;
     grp.qt = stride_qt;
     grp.st = stride_st;
-    grp.stage_t = groups * grp.blocks >= kStageTBlocks;
-    hipLaunchKernelGGL(quant_weight_kernel, dim3((unsigned)(groups * grp.blocks)), dim3(256), 0, stream,
-                       w, kblocks, ld_w, q, ld_q, scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp);
+    const dim3 grid((unsigned)(groups * grp.units)), block(256);
+    if (pair && stage)
+        hipLaunchKernelGGL((quant_weight_kernel<true, true>), grid, block, 0, stream, w, kblocks, ld_w, q, ld_q,
+                           scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp);
+    else if (pair)
+        hipLaunchKernelGGL((quant_weight_kernel<false, true>), grid, block, 0, stream, w, kblocks, ld_w, q, ld_q,
+                           scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp);
+    else if (stage)
+        hipLaunchKernelGGL((quant_weight_kernel<true, false>), grid, block, 0, stream, w, kblocks, ld_w, q, ld_q,
+                           scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp);
+    else
+        hipLaunchKernelGGL((quant_weight_kernel<false, false>), grid, block, 0, stream, w, kblocks, ld_w, q, ld_q,
+                           scale, ld_s, q_t, ld_qt, scale_t, ld_st, grp);
     return hipGetLastError();
 }
 

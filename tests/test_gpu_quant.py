@@ -214,6 +214,41 @@ def test_weight_edge_blocks():
     assert_bits_equal(host_codes(qt), np.ascontiguousarray(q_ref.T), "edge transposed codes")
 
 
+@pytest.mark.parametrize("n,k", [(256, 128), (384, 640), (128, 1152)])
+def test_weight_odd_block_columns(n, k):
+    """An odd number of 128-column blocks (1, 5, 9): the last work unit of
+    each block row holds one block instead of two."""
+    w = wl.weight(3, "tiny_fprop", 60, n, k)
+    w[0:128, k - 128:k] = 0                               # all-zero last block
+    q, s, qt, st = fq.fp8_quantize_weight(dev_bf16(w), transposed=True)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_weight_128x128(w)
+    tag = "odd blocks %dx%d" % (n, k)
+    assert_bits_equal(host_f32(s), s_ref, tag + " scales")
+    assert_bits_equal(host_codes(q), q_ref, tag + " codes")
+    assert_bits_equal(host_f32(st), np.ascontiguousarray(s_ref.T), tag + " transposed scales")
+    assert_bits_equal(host_codes(qt), np.ascontiguousarray(q_ref.T), tag + " transposed codes")
+
+
+@pytest.mark.parametrize("experts", [8, 16])
+def test_weight_grouped_staged_transpose_odd_blocks(experts):
+    """Enough blocks for the LDS-staged transposed copy (experts x 8 x 33
+    blocks: 2112 in single-block units, 4224 in pairs of blocks), with an odd
+    number of block columns per expert."""
+    w = np.stack([wl.weight(3, "tiny_fprop", 70 + e, 1024, 4224) for e in range(experts)])
+    w[1, 128:256, 4096:4224] = 0                          # all-zero last (unpaired) block
+    _check_grouped_weights(w, "staged odd %d" % experts)
+
+
+@pytest.mark.parametrize("n,k", [(256, 384), (128, 128), (384, 1152)])
+def test_act_weight_pairs_odd_block_columns(n, k):
+    """X + W in one launch without the transposed copy (weights in pairs of
+    blocks) and an odd number of block columns."""
+    x = wl.activation(3, "tiny_fprop", 80, 17, k, 100.0)
+    w = wl.weight(3, "tiny_fprop", 81, n, k)
+    _check_act_weight(x, w, "pairs odd %dx%d" % (n, k), transposed=False)
+
+
 def test_empty_inputs_are_noops():
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
     q, s = fq.fp8_quantize_act(x)
