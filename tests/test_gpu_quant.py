@@ -92,6 +92,13 @@ def test_act_1x128_ragged_rows(rows):
     _check_act_1x128(bits, "rows=%d" % rows)
 
 
+@pytest.mark.parametrize("rows,cols", [(9, 128), (1000, 640), (8, 256)])
+def test_act_1x128_slab_pairs(rows, cols):
+    """A wave takes two slabs of 8 rows: one slab (its pair half empty), an odd
+    slab count, and exactly one unit."""
+    _check_act_1x128(wl.activation(1, "tiny_fprop", 23, rows, cols, 100.0), "rows=%d cols=%d" % (rows, cols))
+
+
 def test_act_1x128_edge_tiles():
     rng = np.random.default_rng(11)
     e = _edge_rows(rng)
