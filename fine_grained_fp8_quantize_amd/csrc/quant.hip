@@ -37,14 +37,12 @@ namespace {
 constexpr int kActWavesPerBlock = 4;
 constexpr int kMaxTopk = 8;  // destinations per source row (scatter)
 
-// Work units of the 1x128 quantizer: one wave takes 8 rows x 2 slabs (16
-// tiles), so that every load instruction reads 512 contiguous bytes of each
-// of two rows.
+// Work units of the 1x128 and microscaling quantizers: one wave takes 8
+// rows x 2 slabs (16 tiles), so that every load instruction reads 512
+// contiguous bytes of each of two rows.
 __host__ __device__ constexpr int64_t act_units(int64_t rows, int64_t slabs) {
     return (rows + 7) / 8 * ((slabs + 1) / 2);
 }
-// Units of the microscaling quantizer: 16 rows x one slab per wave.
-constexpr int kMxRowsPerWave = 16;
 
 // 8-byte non-temporal store (whole 128-byte lines per 16 lanes at the call
 // sites)
@@ -143,9 +141,9 @@ __global__ __launch_bounds__(256) void quant_act_1x128_kernel(
 // elements of a row share an E8M0 power-of-two scale 2^e with
 // e = floor(log2(amax)) - 8 (8: exponent of E4M3's largest normal), clamped
 // to [-127, 127], -127 for an all-zero block; codes are E4M3_RNE_sat(x / 2^e).
-// One wave takes 16 rows x one slab (lane l: rows 16 rg + 4 u + l / 16,
-// columns 8 (l % 16) .. +7); a 32-element block is one quad of
-// lanes. The scale of row r, slab j is one uint32: byte b = block 4j + b.
+// Same wave layout as the 1x128 kernel (8 rows x 2 slabs per wave, one slab
+// of one row per 16 lanes); a 32-element block is one quad of lanes. The
+// scale of row r, slab j is one uint32: byte b = block 4j + b.
 // The body of one 256-thread block (block index `block`); the kernels below
 // call it for one matrix, or for both GEMM operands in one grid.
 __device__ __forceinline__ void mx_1x32_body(
@@ -155,17 +153,21 @@ __device__ __forceinline__ void mx_1x32_body(
     const int lane = threadIdx.x & 63;
     const int64_t unit = block * kActWavesPerBlock + (threadIdx.x >> 6);
     if (unit >= units) return;  // whole wave
-    const int64_t rg = unit / slabs;
-    const int64_t j = unit - rg * slabs;
-    const int rr = lane >> 4, c = lane & 15;
+    const int64_t pairs = (slabs + 1) / 2;
+    const int64_t rg = unit / pairs;
+    const int64_t j = 2 * (unit - rg * pairs) + ((lane >> 4) & 1);
+    const bool jvalid = j < slabs;
+    const int rr = lane >> 5, c = lane & 15;
 
     uint4 v[4];
     int64_t row[4];
+    bool live[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        row[u] = rg * kMxRowsPerWave + u * 4 + rr;
+        row[u] = rg * 8 + u * 2 + rr;
+        live[u] = row[u] < rows && jvalid;
         v[u] = make_uint4(0, 0, 0, 0);
-        if (row[u] < rows)
+        if (live[u])
             v[u] = load_nt16(x + row[u] * ld_x + j * 128 + c * 8);
     }
 #pragma unroll
@@ -189,8 +191,8 @@ __device__ __forceinline__ void mx_1x32_body(
         for (int i = 0; i < 8; ++i) qv[i] = __builtin_fabsf(a[i]) * factor;  // exact
         const uint32_t w0 = pack_e4m3x4(qv[0], qv[1], qv[2], qv[3], bf16x4_sign_bytes(v[u].x, v[u].y));
         const uint32_t w1 = pack_e4m3x4(qv[4], qv[5], qv[6], qv[7], bf16x4_sign_bytes(v[u].z, v[u].w));
-        if (row[u] < rows) {
-            *reinterpret_cast<uint2*>(q + row[u] * ld_q + j * 128 + c * 8) = make_uint2(w0, w1);
+        if (live[u]) {
+            store_nt8(q + row[u] * ld_q + j * 128 + c * 8, w0, w1);
             if ((c & 3) == 0)
                 reinterpret_cast<uint8_t*>(scale + j * ld_s + row[u])[c >> 2] = (uint8_t)(e + 127);
         }
@@ -889,7 +891,7 @@ hipError_t launch_quant_act_scatter(const uint16_t* x, int64_t tokens, int64_t c
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
                            int64_t ld_q, uint32_t* scale, int64_t ld_s, hipStream_t stream) {
     const int64_t slabs = cols / 128;
-    const int64_t units = (rows + kMxRowsPerWave - 1) / kMxRowsPerWave * slabs;
+    const int64_t units = act_units(rows, slabs);
     const int64_t blocks = (units + kActWavesPerBlock - 1) / kActWavesPerBlock;
     hipLaunchKernelGGL(quant_mx_1x32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        x, rows, slabs, ld_x, q, ld_q, scale, ld_s, units);
@@ -902,8 +904,8 @@ hipError_t launch_quant_mx_pair(const uint16_t* x0, int64_t rows0, int64_t cols0
                                 int64_t ld_s1, hipStream_t stream) {
     MxArgs a{x0, rows0, cols0 / 128, ld_x0, q0, ld_q0, s0, ld_s0, 0};
     MxArgs b{x1, rows1, cols1 / 128, ld_x1, q1, ld_q1, s1, ld_s1, 0};
-    a.units = (rows0 + kMxRowsPerWave - 1) / kMxRowsPerWave * a.slabs;
-    b.units = (rows1 + kMxRowsPerWave - 1) / kMxRowsPerWave * b.slabs;
+    a.units = act_units(rows0, a.slabs);
+    b.units = act_units(rows1, b.slabs);
     const int64_t a_blocks = (a.units + kActWavesPerBlock - 1) / kActWavesPerBlock;
     const int64_t blocks = a_blocks + (b.units + kActWavesPerBlock - 1) / kActWavesPerBlock;
     hipLaunchKernelGGL(quant_mx_1x32_pair_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, a_blocks, b);
