@@ -552,8 +552,8 @@ __global__ __launch_bounds__(256) void quant_retile_128x1_kernel(int64_t tokens,
 // ---------------------------------------------------------------- 128x128
 
 // Several weight matrices (experts) in one launch: group e starts at the
-// base pointers plus e times these strides (elements); work units (pairs of
-// 128x128 blocks) per group.
+// base pointers plus e times these strides (elements); work units (single
+// 128x128 blocks or pairs of them) per group.
 struct WeightGroups {
     int64_t units;
     int64_t w, q, s, qt, st;
@@ -563,10 +563,11 @@ struct WeightGroups {
 // copy through LDS (STAGE_T kernels): measured, 32 MoE experts quantize in
 // 724 instead of 754 us that way, while a single 2048x7168 weight (896
 // blocks, too few to hide the extra barrier) takes 15.0 instead of 14.0 us.
-// Kernels without the staging hold no LDS for it.
+// Kernels without the staging hold no LDS for it. Grids of at least
+// kPairBlocks weight blocks (16 per CU) take pairs of blocks per workgroup;
+// smaller grids keep single-block units, which end the grid more evenly.
 constexpr int64_t kPairBlocks = 4096;
 constexpr int64_t kStageTBlocks = 2048;
-
 
 // One 256-thread block quantizes one 128x128 weight block: thread (row group
 // rg = t/16, chunk g = t%16) holds rows 8rg..8rg+7 x columns 8g..8g+7. The
