@@ -559,8 +559,8 @@ struct WeightGroups {
     int64_t w, q, s, qt, st;
 };
 
-// Grids of at least this many weight blocks (8 per CU) write the transposed
-// copy through LDS (STAGE_T kernels): measured, 32 MoE experts quantize in
+// Grids of at least kStageTBlocks weight blocks (8 per CU) write the
+// transposed copy through LDS (STAGE_T kernels): measured, 32 MoE experts quantize in
 // 724 instead of 754 us that way, while a single 2048x7168 weight (896
 // blocks, too few to hide the extra barrier) takes 15.0 instead of 14.0 us.
 // Kernels without the staging hold no LDS for it. Grids of at least
