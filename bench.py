@@ -66,7 +66,7 @@ KERNEL_NAMES = {
     "quant_mx": "quant_mx_1x32_kernel",
     "quant_mx_pair": "quant_mx_1x32_pair_kernel",
     "retile_128x1": "retile_128x1_kernel",
-    "gemm": "gemm_kernel",
+    "gemm": ("gemm_kernel", "grouped_fixup_kernel"),  # a grouped GEMM may add its fix-up kernel
 }
 
 
@@ -146,6 +146,9 @@ class Workload:
 
         def empty(shape, dt):
             return torch.empty(shape, dtype=dt, device="cuda")
+
+        # the grouped GEMM's workspace (the K-split of a partial last round)
+        gws = empty((fq.GROUPED_WORKSPACE_BYTES,), u8)
 
         def sets(bits):
             # `rotate` device copies of one bf16 input; step i reads copy i % rotate
@@ -310,7 +313,8 @@ class Workload:
                 Launch("quant_weight", lambda r: fq.fp8_quantize_weight_grouped(
                     w, transposed=True, q=wq, scale=ws, q_t=wqt, scale_t=wst),
                        4 * E * n_out * k_in + 8 * nb),
-                Launch("gemm", lambda r: fq.fp8_grouped_gemm(offd, rws, dq, ds, wqt, wst, bf16, out=y),
+                Launch("gemm", lambda r: fq.fp8_grouped_gemm(offd, rws, dq, ds, wqt, wst, bf16, out=y,
+                                                             workspace=gws),
                        gemm_bytes(real, E * k_in, n_out, nb, 2, 0) + 2 * m_total * k_in, self.flops),
             ]
             self.desc = {"workload": name, "experts": E, "rows_real": real, "rows_padded": m_total,
@@ -412,7 +416,8 @@ class Workload:
                        3 * E * n * k + 4 * nb),
                 # real rows of A read; every padded row of C written (padding rows are zeroed)
                 Launch("gemm", lambda r: fq.fp8_grouped_gemm(
-                    off, rws, xq, xs, wq.view(E, n, k), ws.view(E, n // 128, k // 128), bf16, out=y),
+                    off, rws, xq, xs, wq.view(E, n, k), ws.view(E, n // 128, k // 128), bf16, out=y,
+                    workspace=gws),
                        gemm_bytes(real, E * n, k, nb, 2, 0) + 2 * m_total * n, self.flops),
             ]
             self.desc = {"workload": name, "experts": E, "tokens": tokens, "top_k": 8,
@@ -617,16 +622,23 @@ def pmc_summary(fetch_csv: str, write_csv: str, config: str, probe_mib: int, out
         factor = probe / (copies[0][2] * 1024.0)
         res[key + "_factor"] = round(factor, 4)
         step_labels = {ln.label for ln in wl_obj.launches}
-        for label, frag in KERNEL_NAMES.items():
+        for label, frags in KERNEL_NAMES.items():
             if label not in step_labels:
                 continue  # e.g. set-up dispatches outside the step (the FP8 cache)
-            vals = [r[2] for r in rows if frag in r[1]]
-            if vals:
-                per = max(ln.dispatches for ln in wl_obj.launches if ln.label == label)
+            frags = (frags,) if isinstance(frags, str) else frags
+            # per launch: for each kernel the launch dispatches, the average
+            # over its dispatches times the dispatches one launch makes
+            per = max(ln.dispatches for ln in wl_obj.launches if ln.label == label)
+            total, seen = 0.0, 0
+            for frag in frags:
+                vals = [r[2] for r in rows if frag in r[1]]
+                if vals:
+                    total += sum(vals) / len(vals) * per
+                    seen += len(vals)
+            if seen:
                 ent = res.setdefault("kernels", {}).setdefault(label, {})
-                # per launch: the dispatch average times the dispatches one launch makes
-                ent[key + "_bytes"] = round(sum(vals) / len(vals) * per * 1024.0 * factor)
-                ent["dispatches"] = len(vals)
+                ent[key + "_bytes"] = round(total * 1024.0 * factor)
+                ent["dispatches"] = seen
     for label, ent in res.get("kernels", {}).items():
         ent["traffic_bytes"] = ent.get("fetch_bytes", 0) + ent.get("write_bytes", 0)
         alg = [ln.bytes for ln in wl_obj.launches if ln.label == label]
@@ -687,9 +699,14 @@ def counter_table(path: str, wl_obj: Workload) -> str:
     if "TCP_PENDING_STALL_CYCLES_sum" in counters:
         derived.append("L1 stalled on L2 data")
     out = ["| " + " | ".join(head + derived) + " |", "|" + "---|" * (len(head) + len(derived))]
-    for label, frag in KERNEL_NAMES.items():
+    rows = []
+    for label, frags in KERNEL_NAMES.items():
         if label not in step_labels:
             continue
+        frags = (frags,) if isinstance(frags, str) else frags
+        for j, frag in enumerate(frags):   # one row per kernel the launch dispatches
+            rows.append((label if j == 0 else "%s: %s" % (label, frag), frag))
+    for label, frag in rows:
         ds = [d for d in disp.values() if frag in d["name"]]
         if not ds:
             continue
@@ -882,8 +899,8 @@ def main():
             "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
         }), **{
             "traffic": traffic["gemm"]["traffic_bytes"] if traffic and "gemm" in traffic else None,
-            "kernel": "gemm_kernel" + ({"grouped_fprop": " (grouped over M)",
-                                        "grouped_dgrad": " (grouped over M)",
+            "kernel": "gemm_kernel" + ({"grouped_fprop": " (grouped over M) + grouped_fixup_kernel",
+                                        "grouped_dgrad": " (grouped over M) + grouped_fixup_kernel",
                                         "grouped_wgrad": " (grouped over K)",
                                         "grouped_wgrad_cached": " (grouped over K)",
                                         "mx_fprop": " (microscaling)"}.get(args.config, "")),

@@ -80,6 +80,9 @@ _LIB_PATH = os.environ.get("FP8Q_LIBRARY") or os.path.join(_HERE, "libfp8q.so")
 
 TILE_1x128 = 0
 TILE_128x1 = 1
+# device bytes that let fp8_grouped_gemm split every partial last round
+# (FP8Q_GROUPED_WORKSPACE_BYTES)
+GROUPED_WORKSPACE_BYTES = 256 * 32 + 256 * 256 * 256 * 4
 BSCALE_BLOCK128 = 0
 BSCALE_ROW128 = 1
 OUT_BF16 = 0
@@ -123,7 +126,7 @@ def _load() -> ctypes.CDLL:
     L.fp8_grouped_gemm_wgrad.argtypes = [i32, p, i64, i64, i64, p, i64, p, i64, p, i64, p, i64,
                                          p, i64, i64, cint, p]
     L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
-                                   i64, p, i64, cint, p]
+                                   i64, p, i64, cint, p, i64, p]
     L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
@@ -527,12 +530,16 @@ def fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: t
 def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | None,
                      a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
                      out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
-                     stream=None) -> torch.Tensor:
+                     stream=None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """MoE expert Fprop: rows ``[off[e], off[e+1])`` of ``a`` times ``W_e = b[e]``.
 
     ``group_offsets``: int32 GPU tensor ``[E+1]`` (multiples of 128);
     ``group_rows``: int32 GPU tensor ``[E]`` of real rows, or None; padding rows
     of the output are zero. ``b[E][n][k]`` codes, ``b_scale[E][n/128][k/128]``.
+    ``workspace``: a contiguous uint8 GPU tensor for the K-split of a partial
+    last round of tiles (``GROUPED_WORKSPACE_BYTES`` allow every split; an
+    empty one turns the split off); None takes one from torch's allocator on
+    the output's stream.
     """
     _need_gpu(group_offsets, group_rows, a, a_scale, b, b_scale, out)
     _rowmajor(a, "a")
@@ -555,11 +562,17 @@ def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | Non
     _check_tensor(a_scale, (k // 128, m_total), _F32, "a_scale")
     _check_tensor(b_scale, (groups, n // 128, k // 128), _F32, "b_scale")
     out = _gemm_out(out, (m_total, n), out_dtype, a.device, stream)
+    if workspace is None:
+        workspace = _empty((GROUPED_WORKSPACE_BYTES,), torch.uint8, a.device, stream)
+    _need_gpu(workspace)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise Fp8qError("workspace must be a contiguous uint8 tensor")
     st = _load().fp8_grouped_gemm(
         groups, _ptr(group_offsets), _ptr(group_rows), m_total, n, k,
         _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
         _ptr(b), b.stride(1), b.stride(0), _ptr(b_scale), b_scale.stride(1), b_scale.stride(0),
-        _ptr(out), out.stride(0), oc, _stream(stream))
+        _ptr(out), out.stride(0), oc, _ptr(workspace) if workspace.numel() else None, workspace.numel(),
+        _stream(stream))
     _check(st, "fp8_grouped_gemm")
     return out
 

@@ -325,8 +325,9 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
                      const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
                      const uint8_t* b, int64_t ldb, int64_t stride_b,
                      const float* b_scale, int64_t ld_bs, int64_t stride_bs,
-                     void* c, int64_t ldc, int out_dtype, hipStream_t stream) {
-    if (groups < 0 || m_total < 0 || n < 0 || k < 0) return FP8Q_ERR_SHAPE;
+                     void* c, int64_t ldc, int out_dtype,
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    if (groups < 0 || m_total < 0 || n < 0 || k < 0 || workspace_bytes < 0) return FP8Q_ERR_SHAPE;
     if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
     if (groups == 0 || m_total == 0 || n == 0) return FP8Q_OK;
     if (!group_offsets) return FP8Q_ERR_NULL;
@@ -337,6 +338,7 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     // the experts' weights are only read: their rows may interleave
     if (stride_b < 0 || stride_bs < 0) return FP8Q_ERR_SHAPE;
     if (stride_b % 16 != 0) return FP8Q_ERR_ALIGN;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return FP8Q_ERR_ALIGN;
     if (!grid_ok((m_total / 128) * ((n + 255) / 256) + 256)) return FP8Q_ERR_SHAPE;
     if (debug_checks()) {
         st = check_segments_on_host(groups, group_offsets, group_rows, m_total, stream);
@@ -350,6 +352,7 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
     g.groups = groups; g.group_offsets = group_offsets; g.group_rows = group_rows;
     g.stride_b = stride_b; g.stride_bs = stride_bs;
+    g.workspace = workspace; g.workspace_bytes = workspace ? workspace_bytes : 0;
     return hip_status(fp8q::launch_grouped_gemm(g, stream));
 }
 

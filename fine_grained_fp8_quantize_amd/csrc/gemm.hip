@@ -36,7 +36,10 @@
 // scale per lane per m-subtile, and the B block scale is wave-uniform per
 // 16-column subtile. Waves whose rows are all past the real rows (grouped
 // padding, ragged M) skip their MFMAs.
+#include "fp8q.h"
 #include "gemm_common.h"
+
+#include <algorithm>
 
 // Cache policy of the LDS-DMA copies: the expert weights of a grouped-over-M
 // GEMM are streamed from HBM once per m-tile, so they are loaded
@@ -302,9 +305,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         // scale of slab j, loaded into registers one step ahead.
         const int row_a0 = (int)(wrow - tr.m0) + fi;       // the lane's row in m-subtile 0
         const int row_a_last = (int)(m_last - tr.m0);
-        const float* const bscale_row = tr.b_scale + min(wcol, n_last) / 128 * p.ld_bs;
+        const float* const bscale_row = tr.b_scale + min(wcol, n_last) / 128 * p.ld_bs + tr.slab0;
         auto load_scales = [&](int j, float (&sa)[kMSub], float& sb) {
-            const float* as = p.a_scale + tr.m0 + (int64_t)j * p.ld_as;
+            const float* as = p.a_scale + tr.m0 + (int64_t)(tr.slab0 + j) * p.ld_as;
 #pragma unroll
             for (int s = 0; s < kMSub; ++s) sa[s] = as[min(row_a0 + 16 * s, row_a_last)];
             sb = bscale_row[j];
@@ -620,6 +623,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         // ---- epilogue: lane holds C[m][n..n+3] for each (n-subtile, m-subtile).
         // (k == 0: the scales may be NULL and are not read; C is zero)
         const float alpha = (TENSOR && p.k > 0) ? p.a_scale[0] * p.b_scale[0] : 1.0f;
+        if constexpr (GROUPED) {
+            if (tr.piece >= 0) {
+                // a K piece of a split tile: the FP32 partial in fragment order
+                // (one store instruction writes 1 KB), for the fix-up kernel
+                v4f* const dst = reinterpret_cast<v4f*>(p.split_ws) +
+                                 ((int64_t)tr.piece * 8 + wave) * (NSUB * kMSub * 64) + lane;
+#pragma unroll
+                for (int t = 0; t < NSUB; ++t)
+#pragma unroll
+                    for (int s = 0; s < kMSub; ++s) dst[(t * kMSub + s) * 64] = acc[t][s];
+                return;
+            }
+        }
         if constexpr (ROUNDS) {
             // whole tiles: no edge guards (their branches would keep these loops
             // rolled inside the tile loop)
@@ -678,6 +694,67 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Params p) {
         if (!has_next) break;
         tr = nx;
         prefetched = true;
+    }
+}
+
+// Sum of the K pieces of each split tile of a grouped GEMM's last round
+// (see tail_split), in piece order, stored to C as the GEMM stores a whole
+// tile: rows past row_hi untouched, padding rows zero. The work is cut into
+// units of 256 output vectors (an eighth of one GEMM wave's 64 x 128 outputs,
+// in its fragment order), 64 per tail tile; block b takes units b, b + grid,
+// ..., one vector per thread: the blocks get equal shares, every load
+// instruction reads 1 KB contiguous per wave, and a unit's partial loads and
+// its tile record (written by the tile's first piece) are in flight together.
+// When nothing was split the blocks return after the scan.
+constexpr int kFixupThreads = 256;
+constexpr int kFixupBlocks = 1024;
+
+template <bool OUT_F32>
+__global__ __launch_bounds__(kFixupThreads) void grouped_fixup_kernel(Params p) {
+    constexpr int BN = 256, WN = BN / 2, NSUB = WN / 16;
+    constexpr int kItems = NSUB * kMSub * 64;           // one GEMM wave's partial, in v4f
+    constexpr int kUnits = 8 * kItems / kFixupThreads;  // units per tile
+    const TailSplit ts = tail_split<BN>(p);
+    if (ts.split < 2) return;
+    const v4f* const part = reinterpret_cast<const v4f*>(p.split_ws);
+    for (int unit = (int)blockIdx.x; unit < ts.tiles * kUnits; unit += (int)gridDim.x) {
+        const int r = unit / kUnits;
+        const int flat = (unit % kUnits) * kFixupThreads + (int)threadIdx.x;  // in [0, 8 kItems)
+        const int w = flat / kItems, item = flat % kItems;
+        v4f pv[kMaxSplit];
+#pragma unroll
+        for (int i = 0; i < kMaxSplit; ++i)
+            if (i < ts.split) pv[i] = part[((int64_t)(i * ts.tiles + r) * 8 + w) * kItems + item];
+        const TailRecord tr = p.split_records[r];
+        const int lane = item & 63, s = (item >> 6) % kMSub, t = (item >> 6) / kMSub;
+        const int64_t m = tr.m0 + (w >> 1) * kWaveM + s * 16 + (lane & 15);
+        const int64_t n = tr.n0 + (w & 1) * WN + t * 16 + 4 * (lane >> 4);
+        if (m >= tr.row_hi) continue;
+        v4f v = {0.f, 0.f, 0.f, 0.f};
+        if (m < tr.real_end) {
+#pragma unroll
+            for (int i = 0; i < kMaxSplit; ++i)
+                if (i < ts.split) v += pv[i];
+        }
+        if constexpr (OUT_F32) {
+            float* dst = reinterpret_cast<float*>(p.c) + m * p.ldc + n;
+            if (n + 3 < p.n) {
+                *reinterpret_cast<v4f*>(dst) = v;
+            } else {
+                for (int q = 0; q < 4; ++q)
+                    if (n + q < p.n) dst[q] = v[q];
+            }
+        } else {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + m * p.ldc + n;
+            const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+            if (n + 3 < p.n) {
+                *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+            } else {
+                const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+                for (int q = 0; q < 4; ++q)
+                    if (n + q < p.n) dst[q] = h[q];
+            }
+        }
     }
 }
 
@@ -746,13 +823,32 @@ hipError_t dispatch_tensor(const GemmProblem& g, int64_t blocks, hipStream_t str
 
 // blocks: a multiple of 256 (see grouped_tile). Grouped GEMMs take 128x128
 // block scales only.
+constexpr int64_t kRecordBytes = kTailRecords * (int64_t)sizeof(TailRecord);
+constexpr int64_t kPartBytes = kSplitFloats * (int64_t)sizeof(float);
+static_assert(FP8Q_GROUPED_WORKSPACE_BYTES == kRecordBytes + kMaxPieces * kPartBytes,
+              "the workspace size in fp8q.h holds every record and partial a call can use");
+
 hipError_t dispatch_grouped(const GemmProblem& g, int64_t blocks, hipStream_t stream) {
-    const Params p = to_params(g);
+    Params p = to_params(g);
+    // workspace: the tile records, then as many partial tiles as fit (two at
+    // least, or no split)
+    const int64_t pieces = g.workspace ? std::min<int64_t>((g.workspace_bytes - kRecordBytes) / kPartBytes, kMaxPieces) : 0;
+    if (pieces >= 2) {
+        p.split_records = static_cast<TailRecord*>(g.workspace);
+        p.split_ws = reinterpret_cast<float*>(static_cast<char*>(g.workspace) + kRecordBytes);
+        p.split_pieces = (int32_t)pieces;
+    }
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (g.out_f32)
         hipLaunchKernelGGL((gemm_kernel<256, false, true, kGroupedM>), grid, block, 0, stream, p);
     else
         hipLaunchKernelGGL((gemm_kernel<256, false, false, kGroupedM>), grid, block, 0, stream, p);
+    if (p.split_ws == nullptr) return hipGetLastError();
+    const dim3 fgrid(kFixupBlocks), fblock(kFixupThreads);
+    if (g.out_f32)
+        hipLaunchKernelGGL((grouped_fixup_kernel<true>), fgrid, fblock, 0, stream, p);
+    else
+        hipLaunchKernelGGL((grouped_fixup_kernel<false>), fgrid, fblock, 0, stream, p);
     return hipGetLastError();
 }
 

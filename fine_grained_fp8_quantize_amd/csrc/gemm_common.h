@@ -38,6 +38,15 @@ constexpr int kTileBytes = kBM * kSlab;
 // subtile-relative rows give the same chunk.
 __device__ __forceinline__ int swz_chunk(int c, int row) { return c ^ ((row >> 1) & 7); }
 
+// Where the K pieces of a split tile (see tail_split) write: a record of the
+// tile's rows, from its first piece, and one FP32 partial tile per piece.
+struct TailRecord {
+    int64_t m0, row_hi, real_end, n0;
+};
+constexpr int kMaxPieces = 256;    // the pieces fill at most one round of slots
+constexpr int kTailRecords = 256;  // one per tile of that round
+constexpr int kSplitFloats = kBM * kBNMax;  // one partial tile
+
 struct Params {
     int64_t m, n, k;
     const uint8_t* a;
@@ -56,6 +65,11 @@ struct Params {
     int64_t stride_b;
     int64_t stride_bs;
     int64_t stride_c_bytes;  // grouped over K: distance between expert outputs
+    // grouped over M, K-split last round: the tiles' records, the FP32 partial
+    // tiles (NULL: no split) and how many of them fit
+    TailRecord* split_records;
+    float* split_ws;
+    int32_t split_pieces;
 };
 
 // Which rows of the output a block tile owns.
@@ -69,6 +83,7 @@ struct TileRows {
     int slab0;         // first K slab of the tile's contraction
     int slabs;         // number of K slabs
     void* c;           // output matrix the tile belongs to
+    int piece;         // >= 0: a K piece of a split tile, stored as FP32 partial `piece`
 };
 
 // Kernel modes: one GEMM; grouped over M (MoE Fprop/Dgrad: experts own row
@@ -114,6 +129,7 @@ __device__ __forceinline__ bool dense_tile(const Params& p, int i, TileRows& t) 
     t.slab0 = 0;
     t.slabs = (int)(p.k / kSlab);
     t.c = p.c;
+    t.piece = -1;
     return true;
 }
 
@@ -145,20 +161,43 @@ __device__ __forceinline__ ExpertSplit expert_split(const Params& p, int e) {
     return x;
 }
 
-// Block b runs on XCD b % 8; round r of that XCD's 32 CUs takes the 32
-// consecutive slots 256 r + 32 (b % 8) + [0, 32). Every round is then spread
-// evenly over the XCDs and panel reuse stays inside one L2. The grid is a
-// multiple of 256 blocks, so this is a bijection onto its slots.
+// The experts are found by a scan over the wave rather than a walk over the
+// offsets (a chain of dependent scalar loads, about 5 us for 32 experts):
+// lane l takes the expert at position base + l of the order, one load each.
+// Tiles of that expert (zero past the last one):
+__device__ __forceinline__ int lane_expert_tiles(const Params& p, int base, int tiles_n) {
+    const int pos = base + (int)(threadIdx.x & 63);
+    if (pos >= p.groups) return 0;
+    return expert_split(p, p.groups - 1 - pos).tiles * tiles_n;
+}
+
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    const int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int u = __shfl_up(v, d);
+        if (lane >= d) v += u;
+    }
+    return v;
+}
+
+// Tile `slot` of the grouped order (see above), or false past the last tile.
+// Every lane of the wave must take part.
 template <int BN>
-__device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
+__device__ __forceinline__ bool grouped_slot(const Params& p, int slot, TileRows& t) {
     const int tiles_n = (int)((p.n + BN - 1) / BN);
-    const int q = (int)(blockIdx.x >> 3);
-    int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
-    for (int ee = 0; ee < p.groups; ++ee) {
-        const int e = p.groups - 1 - ee;
-        const ExpertSplit x = expert_split(p, e);
-        const int k = x.tiles;
-        if (slot < k * tiles_n) {
+    for (int base = 0; base < p.groups; base += 64) {
+        const int cnt = lane_expert_tiles(p, base, tiles_n);
+        const int incl = wave_inclusive_sum(cnt);
+        const int chunk = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        if (slot < chunk) {
+            // the first lane whose running total passes the slot holds its expert
+            const unsigned long long hit = __ballot(incl > slot);
+            const int l = __builtin_amdgcn_readfirstlane(__ffsll(hit) - 1);
+            slot -= __builtin_amdgcn_readfirstlane(__shfl(incl - cnt, l));
+            const int e = p.groups - 1 - (base + l);
+            const ExpertSplit x = expert_split(p, e);
+            const int k = x.tiles;
             const int tn = slot / k, mt = slot % k;
             const int end = x.beg + max(p.group_offsets[e + 1] - x.beg, 0);
             t.m0 = x.beg + (int64_t)mt * kBM;
@@ -174,11 +213,74 @@ __device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
             t.slab0 = 0;
             t.slabs = (int)(p.k / kSlab);
             t.c = p.c;
+            t.piece = -1;
             return true;
         }
-        slot -= k * tiles_n;
+        slot -= chunk;
     }
     return false;
+}
+
+// The last, partial round of a grouped GEMM: its `tiles` tiles (slots from
+// `first` on) leave most CUs idle for a whole tile time, so each is cut into
+// `split` pieces of about K / split. Piece i of tail tile r takes slot
+// first + i * tiles + r (the same piece of neighbouring tiles -- which share
+// weight or activation panels -- run side by side on one XCD) and stores its
+// FP32 partial as partial i * tiles + r; a second kernel adds a tile's
+// partials in piece order. split = 1: no split (no workspace, a round at
+// least half full, or too few slabs).
+constexpr int kMaxSplit = 8;
+constexpr int kMinSplitSlabs = 4;
+
+struct TailSplit {
+    int first;
+    int tiles;
+    int split;
+};
+
+template <int BN>
+__device__ __forceinline__ TailSplit tail_split(const Params& p) {
+    const int tiles_n = (int)((p.n + BN - 1) / BN);
+    int total = 0;
+    for (int base = 0; base < p.groups; base += 64)
+        total += __builtin_amdgcn_readfirstlane(__shfl(wave_inclusive_sum(lane_expert_tiles(p, base, tiles_n)), 63));
+    TailSplit ts;
+    ts.first = total / 256 * 256;
+    ts.tiles = total - ts.first;
+    ts.split = 1;
+    if (p.split_ws != nullptr && ts.tiles > 0) {
+        const int s = min(min(256 / ts.tiles, kMaxSplit),
+                          min(p.split_pieces / ts.tiles, (int)(p.k / kSlab) / kMinSplitSlabs));
+        ts.split = max(s, 1);
+    }
+    return ts;
+}
+
+// Block b runs on XCD b % 8; round r of that XCD's 32 CUs takes the 32
+// consecutive slots 256 r + 32 (b % 8) + [0, 32). Every round is then spread
+// evenly over the XCDs and panel reuse stays inside one L2. The grid is a
+// multiple of 256 blocks, so this is a bijection onto its slots (the pieces
+// of a split last round fill at most the 256 slots of that round).
+template <int BN>
+__device__ __forceinline__ bool grouped_tile(const Params& p, TileRows& t) {
+    const int q = (int)(blockIdx.x >> 3);
+    const int slot = ((q >> 5) << 8) + ((int)(blockIdx.x & 7) << 5) + (q & 31);
+    if (p.split_ws != nullptr) {
+        const TailSplit ts = tail_split<BN>(p);
+        if (ts.split > 1 && slot >= ts.first) {
+            const int u = slot - ts.first;
+            if (u >= ts.tiles * ts.split) return false;
+            const int r = u % ts.tiles, i = u / ts.tiles;
+            if (!grouped_slot<BN>(p, ts.first + r, t)) return false;
+            const int slabs = t.slabs;
+            t.slab0 = i * slabs / ts.split;
+            t.slabs = (i + 1) * slabs / ts.split - t.slab0;
+            t.piece = u;
+            if (i == 0 && threadIdx.x == 0) p.split_records[r] = TailRecord{t.m0, t.row_hi, t.real_end, t.n0};
+            return true;
+        }
+    }
+    return grouped_slot<BN>(p, slot, t);
 }
 
 // Grouped-over-K tiles (MoE Wgrad): expert e contracts over its token segment
@@ -216,6 +318,7 @@ __device__ __forceinline__ bool grouped_k_tile(const Params& p, TileRows& t) {
     t.slab0 = beg / kSlab;
     t.slabs = seg / kSlab;
     t.c = static_cast<char*>(p.c) + (int64_t)e * p.stride_c_bytes;
+    t.piece = -1;
     return true;
 }
 
@@ -267,6 +370,9 @@ Params to_params(const GemmProblem& g) {
     p.stride_b = g.stride_b;
     p.stride_bs = g.stride_bs;
     p.stride_c_bytes = g.stride_c * (g.out_f32 ? 4 : 2);
+    p.split_records = nullptr;
+    p.split_ws = nullptr;
+    p.split_pieces = 0;
     return p;
 }
 

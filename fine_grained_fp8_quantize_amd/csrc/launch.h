@@ -74,6 +74,10 @@ struct GemmProblem {
     int64_t stride_b;
     int64_t stride_bs;
     int64_t stride_c;  // grouped over K: elements between expert outputs
+    // grouped over M: the caller's workspace for a K-split last round of
+    // tiles (NULL or too small: no split)
+    void* workspace;
+    int64_t workspace_bytes;
 };
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);

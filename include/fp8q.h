@@ -319,21 +319,38 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
  *               then b + e*N with ldb = E*N (stride_b = N), and its block
  *               scales b_scale + e*N/128 with ld_bs = E*N/128.
  * c             [m_total][ldc]; out_dtype as in fp8_gemm.
+ * workspace     DEVICE scratch of workspace_bytes bytes owned by the caller,
+ *               or NULL. The 256 x 256 output tiles run in rounds of the 256
+ *               compute units; when the last round is less than half full,
+ *               each of its tiles is cut along K into pieces that run on the
+ *               otherwise idle units and leave FP32 partial tiles here, and a
+ *               second kernel on `stream` adds each tile's pieces in a fixed
+ *               order and writes C (the result is deterministic; it differs
+ *               from the unsplit sum by FP32 rounding only). A workspace of
+ *               FP8Q_GROUPED_WORKSPACE_BYTES allows every split; a smaller
+ *               one limits it, and NULL (or fewer bytes than two partial
+ *               tiles need) turns it off. Its contents need no
+ *               initialisation and are left unspecified; calls whose work
+ *               overlaps in time must not share a workspace.
  * Shapes:       n % 128 == 0, k % 128 == 0; lda, ldb and the scale
- *               spans within the GEMM limits above.
- * Alignment:    as fp8_gemm; stride_b % 16 == 0.
+ *               spans within the GEMM limits above; workspace_bytes >= 0.
+ * Alignment:    as fp8_gemm; stride_b % 16 == 0; workspace 256-byte aligned.
  * The device arrays are trusted: offsets that break the contract give
- * unspecified output (the kernels still stay within the m_total rows);
- * with FP8Q_DEBUG=1 they are checked on the host first (see above).
+ * unspecified output (the kernels still stay within the m_total rows and
+ * the workspace); with FP8Q_DEBUG=1 they are checked on the host first (see
+ * above).
  * Errors: FP8Q_ERR_NULL, FP8Q_ERR_SHAPE, FP8Q_ERR_ALIGN, FP8Q_ERR_ENUM,
  *         FP8Q_ERR_HIP.
  */
+#define FP8Q_GROUPED_WORKSPACE_BYTES 67117056LL /* 64 MiB of partial tiles + 8 KiB of records */
+
 int fp8_grouped_gemm(int32_t groups, const int32_t *group_offsets, const int32_t *group_rows,
                      int64_t m_total, int64_t n, int64_t k,
                      const uint8_t *a, int64_t lda, const float *a_scale, int64_t ld_as,
                      const uint8_t *b, int64_t ldb, int64_t stride_b,
                      const float *b_scale, int64_t ld_bs, int64_t stride_bs,
-                     void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+                     void *c, int64_t ldc, int out_dtype,
+                     void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * fp8_grouped_gemm_wgrad -- MoE expert Wgrad: one weight gradient per expert,

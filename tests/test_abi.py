@@ -66,6 +66,8 @@ def test_header_status_codes_match_binding():
     assert int(codes["FP8Q_BSCALE_ROW128"]) == fq.BSCALE_ROW128
     assert int(codes["FP8Q_OUT_BF16"]) == fq.OUT_BF16
     assert int(codes["FP8Q_OUT_F32"]) == fq.OUT_F32
+    sizes = dict(re.findall(r"#define\s+(FP8Q_\w+)\s+(\d+)LL", text))
+    assert int(sizes["FP8Q_GROUPED_WORKSPACE_BYTES"]) == fq.GROUPED_WORKSPACE_BYTES
 
 
 def test_status_strings(lib):
@@ -208,9 +210,9 @@ def test_gemm_operand_pitch_limits(lib):
 
 
 def _gg(lib, groups=4, off=A16, rows=0, m=512, n=256, k=256, a=A16b, lda=256, a_s=A4, ld_as=512,
-        b=A16c, ldb=256, sb=256 * 256, b_s=A4, ld_bs=2, sbs=4, c=A16, ldc=256, out=0):
+        b=A16c, ldb=256, sb=256 * 256, b_s=A4, ld_bs=2, sbs=4, c=A16, ldc=256, out=0, ws=0, wsb=0):
     return lib.fp8_grouped_gemm(groups, off, rows, m, n, k, a, lda, a_s, ld_as, b, ldb, sb,
-                                b_s, ld_bs, sbs, c, ldc, out, None)
+                                b_s, ld_bs, sbs, c, ldc, out, ws, wsb, None)
 
 
 def test_grouped_gemm_validation(lib):
@@ -224,6 +226,8 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, sb=-256) == ERR_SHAPE
     assert _gg(lib, sbs=-1) == ERR_SHAPE
     assert _gg(lib, sb=256 * 256 + 8) == ERR_ALIGN
+    assert _gg(lib, ws=A16, wsb=-1) == ERR_SHAPE            # negative workspace size
+    assert _gg(lib, ws=A16 + 128, wsb=1 << 20) == ERR_ALIGN  # workspace not 256-byte aligned
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="would launch on the fake pointers")

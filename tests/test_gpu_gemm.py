@@ -191,8 +191,11 @@ def _moe_expert_weights(n, k, rows, seed=0):
     return cached(("moe_w", n, k, tuple(int(r) for r in rows), seed), make)
 
 
-def _grouped_case(rows, n, k, seed=0, group_rows=True, out="bf16", pad_extra=None):
+def _grouped_case(rows, n, k, seed=0, group_rows=True, out="bf16", pad_extra=None, workspace=None,
+                  return_out=False):
     rows = np.asarray(rows, dtype=np.int64)
+    key = (tuple(int(r) for r in rows), n, k, seed, group_rows,
+           None if pad_extra is None else tuple(int(p) for p in pad_extra))
     g, b_q, b_s = _moe_expert_weights(n, k, rows, seed)
     offsets = g["offsets"].copy()
     if pad_extra is not None:   # enlarge some segments beyond the 128-padding
@@ -203,18 +206,18 @@ def _grouped_case(rows, n, k, seed=0, group_rows=True, out="bf16", pad_extra=Non
             x[offsets[e]:offsets[e] + rows[e]] = g["x"][g["offsets"][e]:g["offsets"][e] + rows[e]]
     else:
         x = g["x"]
-    a_q, a_s = oracle.quant_act_1x128(x)
+    a_q, a_s = cached(("grouped_a",) + key, lambda: oracle.quant_act_1x128(x))
     off_d = torch.from_numpy(offsets.astype(np.int32)).cuda()
     rows_d = torch.from_numpy(rows.astype(np.int32)).cuda() if group_rows else None
     c = nan_out((a_q.shape[0], n), OUT[out])
     fq.fp8_grouped_gemm(off_d, rows_d, dev_codes(a_q), dev_f32(a_s), dev_codes(b_q), dev_f32(b_s), OUT[out],
-                        out=c)
+                        out=c, workspace=workspace)
     torch.cuda.synchronize()
     got = host_out(c)
     real = rows if group_rows else np.diff(offsets)
-    ref = oracle.grouped_gemm(offsets, real, a_q, a_s, b_q, b_s)
+    ref = cached(("grouped_ref",) + key, lambda: oracle.grouped_gemm(offsets, real, a_q, a_s, b_q, b_s))
     e = assert_grouped_close(got, ref, offsets, real, "grouped %d experts n=%d k=%d" % (len(rows), n, k))
-    return e
+    return (e, got) if return_out else e
 
 
 def test_grouped_edge_row_counts():
@@ -230,11 +233,43 @@ def test_grouped_wide_padding_segments():
     _grouped_case([5, 0, 300], n=256, k=256, pad_extra=[256, 128, 128])
 
 
+def test_grouped_more_experts_than_a_wave():
+    # 70 experts: the tile scan takes them in chunks of 64
+    rows = np.random.default_rng(7).integers(0, 300, 70)
+    rows[[3, 64, 69]] = 0
+    _grouped_case(rows, n=256, k=256)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_grouped_split_last_round(out):
+    # 7 m-tiles x 2 n-tiles = 14 tiles, one partial round: each tile is cut
+    # into 4 K pieces of 4 or 5 slabs (18 slabs) and summed by the fix-up
+    # kernel; N = 384 leaves the second n-tile half outside C, and the
+    # segments hold padding rows and an empty expert
+    _grouped_case([300, 5, 0, 128, 257, 40], n=384, k=18 * 128, out=out)
+
+
 def test_grouped_moe_config_full():
     """The MoE config: 32 experts, Zipf(1.1) routing of 8192 tokens, N=4096,
     K=7168; every real row of every expert compared."""
     e = _grouped_case(wl.moe_rows(0), n=4096, k=7168)
     print("grouped MoE errors", e)
+
+
+def test_grouped_moe_config_workspace_sizes():
+    """The MoE config's 816 tiles leave a last round of 48: with the full
+    workspace each of them is cut into 5 K pieces, with room for 100 partial
+    tiles into 2, and with no workspace not at all. Every result meets the bar
+    against the oracle, and a second call with the full workspace gives the
+    same bits (the pieces are added in a fixed order)."""
+    full = torch.empty(fq.GROUPED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    part = torch.empty(256 * 32 + 100 * 256 * 256 * 4, dtype=torch.uint8, device="cuda")
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for name, ws in (("full", full), ("100 partials", part), ("none", none), ("full again", full)):
+        e, outs[name] = _grouped_case(wl.moe_rows(0), n=4096, k=7168, workspace=ws, return_out=True)
+        print("workspace", name, e)
+    assert np.array_equal(outs["full"], outs["full again"])
 
 
 # --------------------------------------------------------------- end to end
