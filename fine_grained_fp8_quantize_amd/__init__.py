@@ -21,6 +21,8 @@ Layouts (row-major, K contiguous for GEMM operands):
 * ``fp8_grouped_gemm(offsets, rows, a, a_scale, b, b_scale)`` -- per-expert
   Fprop (or Dgrad, with transposed weights) over an expert-sorted, 128-padded
   row layout.
+* ``fp8_grouped_gemm_noalloc(...)`` -- the same on the library's per-GPU
+  scratch instead of a workspace, for callers that cannot allocate.
 * ``fp8_quantize_weight_grouped(w)`` -- ``w[E][n][k]`` quantized in one
   launch, optionally with per-expert transposed copies.
 * ``fp8_quantize_act_weight(x, w)`` -- a Linear layer's activation (1x128)
@@ -62,6 +64,7 @@ __all__ = [
     "fp8_quantize_mx_pair",
     "fp8_gemm",
     "fp8_grouped_gemm",
+    "fp8_grouped_gemm_noalloc",
     "fp8_grouped_gemm_wgrad",
     "fp8_quantize_mx",
     "fp8_gemm_mx",
@@ -127,13 +130,15 @@ def _load() -> ctypes.CDLL:
                                          p, i64, i64, cint, p]
     L.fp8_grouped_gemm.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
                                    i64, p, i64, cint, p, i64, p]
+    L.fp8_grouped_gemm_noalloc.argtypes = [i32, p, p, i64, i64, i64, p, i64, p, i64, p, i64, i64, p, i64,
+                                           i64, p, i64, cint, p]
     L.fp8_retile_act_128x1.argtypes = [p, i64, i64, i64, p, i64, p, i64, p, i64, p]
     L.fp8_gemm_tensor.argtypes = [i64, i64, i64, p, i64, p, p, i64, p, p, i64, cint, p]
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
                  "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair",
-                 "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
-                 "fp8_quantize_mx", "fp8_quantize_mx_pair", "fp8_gemm_mx", "fp8_retile_act_128x1",
-                 "fp8_gemm_tensor"):
+                 "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_noalloc",
+                 "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_quantize_mx_pair", "fp8_gemm_mx",
+                 "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         getattr(L, name).restype = cint
     L.fp8q_status_string.argtypes = [cint]
     L.fp8q_status_string.restype = ctypes.c_char_p
@@ -527,20 +532,8 @@ def fp8_gemm(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: t
     return out
 
 
-def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | None,
-                     a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
-                     out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
-                     stream=None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """MoE expert Fprop: rows ``[off[e], off[e+1])`` of ``a`` times ``W_e = b[e]``.
-
-    ``group_offsets``: int32 GPU tensor ``[E+1]`` (multiples of 128);
-    ``group_rows``: int32 GPU tensor ``[E]`` of real rows, or None; padding rows
-    of the output are zero. ``b[E][n][k]`` codes, ``b_scale[E][n/128][k/128]``.
-    ``workspace``: a contiguous uint8 GPU tensor for the K-split of a partial
-    last round of tiles (``GROUPED_WORKSPACE_BYTES`` allow every split; an
-    empty one turns the split off); None takes one from torch's allocator on
-    the output's stream.
-    """
+def _grouped_gemm_args(group_offsets, group_rows, a, a_scale, b, b_scale, out_dtype, out, stream):
+    """Checked arguments of the grouped Fprop GEMM entry points, up to out_dtype."""
     _need_gpu(group_offsets, group_rows, a, a_scale, b, b_scale, out)
     _rowmajor(a, "a")
     _codes(a, "a")
@@ -562,18 +555,49 @@ def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | Non
     _check_tensor(a_scale, (k // 128, m_total), _F32, "a_scale")
     _check_tensor(b_scale, (groups, n // 128, k // 128), _F32, "b_scale")
     out = _gemm_out(out, (m_total, n), out_dtype, a.device, stream)
+    args = (groups, _ptr(group_offsets), _ptr(group_rows), m_total, n, k,
+            _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
+            _ptr(b), b.stride(1), b.stride(0), _ptr(b_scale), b_scale.stride(1), b_scale.stride(0),
+            _ptr(out), out.stride(0), oc)
+    return args, out
+
+
+def fp8_grouped_gemm(group_offsets: torch.Tensor, group_rows: torch.Tensor | None,
+                     a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
+                     out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                     stream=None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """MoE expert Fprop: rows ``[off[e], off[e+1])`` of ``a`` times ``W_e = b[e]``.
+
+    ``group_offsets``: int32 GPU tensor ``[E+1]`` (multiples of 128);
+    ``group_rows``: int32 GPU tensor ``[E]`` of real rows, or None; padding rows
+    of the output are zero. ``b[E][n][k]`` codes, ``b_scale[E][n/128][k/128]``.
+    ``workspace``: a contiguous uint8 GPU tensor for the K-split of a partial
+    last round of tiles (``GROUPED_WORKSPACE_BYTES`` allow every split; an
+    empty one turns the split off); None takes one from torch's allocator on
+    the output's stream.
+    """
+    args, out = _grouped_gemm_args(group_offsets, group_rows, a, a_scale, b, b_scale, out_dtype, out, stream)
     if workspace is None:
         workspace = _empty((GROUPED_WORKSPACE_BYTES,), torch.uint8, a.device, stream)
     _need_gpu(workspace)
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
         raise Fp8qError("workspace must be a contiguous uint8 tensor")
-    st = _load().fp8_grouped_gemm(
-        groups, _ptr(group_offsets), _ptr(group_rows), m_total, n, k,
-        _ptr(a), a.stride(0), _ptr(a_scale), a_scale.stride(0),
-        _ptr(b), b.stride(1), b.stride(0), _ptr(b_scale), b_scale.stride(1), b_scale.stride(0),
-        _ptr(out), out.stride(0), oc, _ptr(workspace) if workspace.numel() else None, workspace.numel(),
-        _stream(stream))
+    st = _load().fp8_grouped_gemm(*args, _ptr(workspace) if workspace.numel() else None, workspace.numel(),
+                                  _stream(stream))
     _check(st, "fp8_grouped_gemm")
+    return out
+
+
+def fp8_grouped_gemm_noalloc(group_offsets: torch.Tensor, group_rows: torch.Tensor | None,
+                             a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor, b_scale: torch.Tensor,
+                             out_dtype=torch.bfloat16, out: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+    """``fp8_grouped_gemm`` on the library's own per-GPU scratch: the C call
+    allocates nothing (pass ``out`` to keep this wrapper from allocating it).
+    Calls that overlap in time on one GPU share the scratch and race."""
+    args, out = _grouped_gemm_args(group_offsets, group_rows, a, a_scale, b, b_scale, out_dtype, out, stream)
+    st = _load().fp8_grouped_gemm_noalloc(*args, _stream(stream))
+    _check(st, "fp8_grouped_gemm_noalloc")
     return out
 
 

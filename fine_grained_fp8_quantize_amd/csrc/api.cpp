@@ -320,13 +320,15 @@ int fp8_gemm(int64_t m, int64_t n, int64_t k,
     return hip_status(fp8q::launch_gemm(g, stream));
 }
 
-int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t* group_rows,
-                     int64_t m_total, int64_t n, int64_t k,
-                     const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
-                     const uint8_t* b, int64_t ldb, int64_t stride_b,
-                     const float* b_scale, int64_t ld_bs, int64_t stride_bs,
-                     void* c, int64_t ldc, int out_dtype,
-                     void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+// fp8_grouped_gemm with the caller's workspace, or (scratch) with the
+// library's own.
+static int grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t* group_rows,
+                        int64_t m_total, int64_t n, int64_t k,
+                        const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
+                        const uint8_t* b, int64_t ldb, int64_t stride_b,
+                        const float* b_scale, int64_t ld_bs, int64_t stride_bs,
+                        void* c, int64_t ldc, int out_dtype,
+                        void* workspace, int64_t workspace_bytes, bool scratch, hipStream_t stream) {
     if (groups < 0 || m_total < 0 || n < 0 || k < 0 || workspace_bytes < 0) return FP8Q_ERR_SHAPE;
     if (out_dtype != FP8Q_OUT_BF16 && out_dtype != FP8Q_OUT_F32) return FP8Q_ERR_ENUM;
     if (groups == 0 || m_total == 0 || n == 0) return FP8Q_OK;
@@ -352,8 +354,34 @@ int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t
     g.c = c; g.ldc = ldc; g.out_f32 = out_dtype == FP8Q_OUT_F32;
     g.groups = groups; g.group_offsets = group_offsets; g.group_rows = group_rows;
     g.stride_b = stride_b; g.stride_bs = stride_bs;
+    if (scratch) {
+        const hipError_t e = fp8q::grouped_scratch(&workspace);
+        if (e != hipSuccess) return hip_status(e);
+        workspace_bytes = FP8Q_GROUPED_WORKSPACE_BYTES;
+    }
     g.workspace = workspace; g.workspace_bytes = workspace ? workspace_bytes : 0;
     return hip_status(fp8q::launch_grouped_gemm(g, stream));
+}
+
+int fp8_grouped_gemm(int32_t groups, const int32_t* group_offsets, const int32_t* group_rows,
+                     int64_t m_total, int64_t n, int64_t k,
+                     const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
+                     const uint8_t* b, int64_t ldb, int64_t stride_b,
+                     const float* b_scale, int64_t ld_bs, int64_t stride_bs,
+                     void* c, int64_t ldc, int out_dtype,
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return grouped_gemm(groups, group_offsets, group_rows, m_total, n, k, a, lda, a_scale, ld_as, b, ldb, stride_b,
+                        b_scale, ld_bs, stride_bs, c, ldc, out_dtype, workspace, workspace_bytes, false, stream);
+}
+
+int fp8_grouped_gemm_noalloc(int32_t groups, const int32_t* group_offsets, const int32_t* group_rows,
+                             int64_t m_total, int64_t n, int64_t k,
+                             const uint8_t* a, int64_t lda, const float* a_scale, int64_t ld_as,
+                             const uint8_t* b, int64_t ldb, int64_t stride_b,
+                             const float* b_scale, int64_t ld_bs, int64_t stride_bs,
+                             void* c, int64_t ldc, int out_dtype, hipStream_t stream) {
+    return grouped_gemm(groups, group_offsets, group_rows, m_total, n, k, a, lda, a_scale, ld_as, b, ldb, stride_b,
+                        b_scale, ld_bs, stride_bs, c, ldc, out_dtype, nullptr, 0, true, stream);
 }
 
 int fp8_grouped_gemm_wgrad(int32_t groups, const int32_t* group_offsets, int64_t k_total,

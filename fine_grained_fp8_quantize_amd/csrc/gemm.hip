@@ -40,6 +40,7 @@
 #include "gemm_common.h"
 
 #include <algorithm>
+#include <mutex>
 
 // Cache policy of the LDS-DMA copies: the expert weights of a grouped-over-M
 // GEMM are streamed from HBM once per m-tile, so they are loaded
@@ -930,6 +931,33 @@ hipError_t launch_gemm_tensor(const GemmProblem& g, hipStream_t stream) {
     }
     const int64_t tiles = ((g.m + kBM - 1) / kBM) * ((g.n + 255) / 256);
     return dispatch_tensor<256>(g, (tiles + 7) / 8 * 8, stream);
+}
+
+// Scratch of the allocation-free grouped GEMM (fp8_grouped_gemm_noalloc): the
+// largest workspace a call uses, one copy on every GPU the library runs on,
+// held until the process ends. In host code the array's name is a host-side
+// stand-in, not a device address: host code uses only the address that
+// hipGetSymbolAddress gives with the device current, kept per device.
+__device__ __align__(256) uint8_t scratch[FP8Q_GROUPED_WORKSPACE_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+
+hipError_t grouped_scratch(void** ptr) {
+    static std::mutex mu;
+    static void* per_device[kMaxScratchDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_device[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
 }
 
 }  // namespace fp8q

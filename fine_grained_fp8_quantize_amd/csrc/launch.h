@@ -82,6 +82,9 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmProblem& p, hipStream_t stream);
+// Device address of the library's grouped-GEMM scratch on the current device
+// (FP8Q_GROUPED_WORKSPACE_BYTES), looked up once per device.
+hipError_t grouped_scratch(void** ptr);
 hipError_t launch_grouped_k_gemm(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_gemm_mx(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_gemm_tensor(const GemmProblem& p, hipStream_t stream);

@@ -353,6 +353,33 @@ int fp8_grouped_gemm(int32_t groups, const int32_t *group_offsets, const int32_t
                      void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * fp8_grouped_gemm_noalloc -- fp8_grouped_gemm for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.
+ *
+ * Arguments, results and errors are those of fp8_grouped_gemm with a
+ * workspace of FP8Q_GROUPED_WORKSPACE_BYTES. The workspace is the library's
+ * own scratch: a file-scope device array of FP8Q_GROUPED_WORKSPACE_BYTES
+ * (64 MiB + 8 KiB) that each GPU the library runs on holds until the process
+ * ends. That is the largest workspace any call uses, so no shape is refused
+ * for its size; shapes past the limits of fp8_grouped_gemm return
+ * FP8Q_ERR_SHAPE as there. The call allocates nothing (no hipMalloc, hipFree
+ * or allocating library routine). Its first call on a device looks up the
+ * array's address there with that device current (make it before a graph
+ * capture); a device id of 64 or more returns FP8Q_ERR_HIP. Nothing in the
+ * scratch needs to start at zero, and it keeps the last call's partial
+ * tiles. All calls on one GPU share it: calls whose work overlaps in time on
+ * one GPU (on several streams, or graph replays in flight together) race and
+ * give unspecified output.
+ */
+int fp8_grouped_gemm_noalloc(int32_t groups, const int32_t *group_offsets, const int32_t *group_rows,
+                             int64_t m_total, int64_t n, int64_t k,
+                             const uint8_t *a, int64_t lda, const float *a_scale, int64_t ld_as,
+                             const uint8_t *b, int64_t ldb, int64_t stride_b,
+                             const float *b_scale, int64_t ld_bs, int64_t stride_bs,
+                             void *c, int64_t ldc, int out_dtype, hipStream_t stream);
+
+/*
  * fp8_grouped_gemm_wgrad -- MoE expert Wgrad: one weight gradient per expert,
  * each contracting over that expert's own token segment.
  *

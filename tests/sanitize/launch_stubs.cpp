@@ -39,6 +39,7 @@ hipError_t launch_quant_weight(int64_t, const uint16_t*, int64_t, int64_t, int64
                                int64_t, hipStream_t) { return kNoGpu; }
 hipError_t launch_gemm(const GemmProblem&, hipStream_t) { return kNoGpu; }
 hipError_t launch_grouped_gemm(const GemmProblem&, hipStream_t) { return kNoGpu; }
+hipError_t grouped_scratch(void**) { return kNoGpu; }
 hipError_t launch_grouped_k_gemm(const GemmProblem&, hipStream_t) { return kNoGpu; }
 hipError_t launch_gemm_mx(const GemmProblem&, hipStream_t) { return kNoGpu; }
 hipError_t launch_gemm_tensor(const GemmProblem&, hipStream_t) { return kNoGpu; }

@@ -230,6 +230,26 @@ def test_grouped_gemm_validation(lib):
     assert _gg(lib, ws=A16 + 128, wsb=1 << 20) == ERR_ALIGN  # workspace not 256-byte aligned
 
 
+def _ggn(lib, groups=4, off=A16, rows=0, m=512, n=256, k=256, a=A16b, lda=256, a_s=A4, ld_as=512,
+         b=A16c, ldb=256, sb=256 * 256, b_s=A4, ld_bs=2, sbs=4, c=A16, ldc=256, out=0):
+    return lib.fp8_grouped_gemm_noalloc(groups, off, rows, m, n, k, a, lda, a_s, ld_as, b, ldb, sb,
+                                        b_s, ld_bs, sbs, c, ldc, out, None)
+
+
+def test_grouped_gemm_noalloc_validation(lib):
+    """The allocation-free entry point checks its arguments as
+    fp8_grouped_gemm does, before it looks for its scratch."""
+    assert _ggn(lib, groups=0) == OK
+    assert _ggn(lib, m=0) == OK
+    assert _ggn(lib, groups=-1) == ERR_SHAPE
+    assert _ggn(lib, out=5) == ERR_ENUM
+    assert _ggn(lib, off=0) == ERR_NULL
+    assert _ggn(lib, m=500, ld_as=512) == ERR_SHAPE
+    assert _ggn(lib, n=200, ldc=256) == ERR_SHAPE
+    assert _ggn(lib, sb=256 * 256 + 8) == ERR_ALIGN
+    assert _ggn(lib, lda=(1 << 23)) == ERR_SHAPE
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="would launch on the fake pointers")
 def test_grouped_gemm_accepts_interleaved_expert_weights(lib):
     """The weights are only read, so experts' rows may interleave: the
@@ -441,9 +461,9 @@ def test_quantize_weight_grouped_validation(lib):
 def test_binding_names_match_c_entry_points():
     for name in ("fp8_quantize_act", "fp8_quantize_act_scatter", "fp8_quantize_weight",
                  "fp8_quantize_weight_grouped", "fp8_quantize_act_weight", "fp8_quantize_act_128x1_pair",
-                 "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_wgrad",
-                 "fp8_quantize_mx", "fp8_quantize_mx_pair", "fp8_gemm_mx", "fp8_retile_act_128x1",
-                 "fp8_gemm_tensor"):
+                 "fp8_quantize_act_128x1_retile", "fp8_gemm", "fp8_grouped_gemm", "fp8_grouped_gemm_noalloc",
+                 "fp8_grouped_gemm_wgrad", "fp8_quantize_mx", "fp8_quantize_mx_pair", "fp8_gemm_mx",
+                 "fp8_retile_act_128x1", "fp8_gemm_tensor"):
         assert callable(getattr(fq, name))
 
 
