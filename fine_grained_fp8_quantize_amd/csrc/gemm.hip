@@ -730,7 +730,9 @@ __global__ __launch_bounds__(kFixupThreads) void grouped_fixup_kernel(Params p) 
         const int lane = item & 63, s = (item >> 6) % kMSub, t = (item >> 6) / kMSub;
         const int64_t m = tr.m0 + (w >> 1) * kWaveM + s * 16 + (lane & 15);
         const int64_t n = tr.n0 + (w & 1) * WN + t * 16 + 4 * (lane >> 4);
-        if (m >= tr.row_hi) continue;
+        // (offsets that break the contract can leave a piece unrun and its
+        // record from an earlier call: the stores still stay inside C)
+        if (m >= tr.row_hi || m >= p.m || tr.m0 < 0 || tr.n0 < 0) continue;
         v4f v = {0.f, 0.f, 0.f, 0.f};
         if (m < tr.real_end) {
 #pragma unroll

@@ -249,6 +249,14 @@ def test_grouped_split_last_round(out):
     _grouped_case([300, 5, 0, 128, 257, 40], n=384, k=18 * 128, out=out)
 
 
+def test_grouped_split_last_round_wide_padding_and_all_real():
+    # 5 m-tiles in one partial round, split into 2 K pieces (8 slabs): one
+    # tail tile holds padding only (its pieces do no MFMA work and the fix-up
+    # writes zeros), one expert is empty; then every row real, fp32 out
+    _grouped_case([5, 0, 300], n=256, k=8 * 128, pad_extra=[256, 128, 128])
+    _grouped_case([128, 256, 384], n=512, k=8 * 128, group_rows=False, out="f32")
+
+
 def test_grouped_moe_config_full():
     """The MoE config: 32 experts, Zipf(1.1) routing of 8192 tokens, N=4096,
     K=7168; every real row of every expert compared."""
