@@ -1,7 +1,8 @@
 """The library on the caller's streams: calls hold no state, so work enqueued
 on two streams at once gives the same bytes as the same work done one call
-after another, and a quantize + GEMM step captured into a HIP graph replays
-to the eager result (the kernels use no memset and no atomics).
+after another; a quantize + GEMM step, and the grouped GEMM with its K-split
+fix-up (caller workspace or the library's scratch), captured into a HIP graph
+replay to the eager result (the kernels use no memset and no atomics).
 """
 from __future__ import annotations
 
@@ -88,3 +89,59 @@ def test_graph_replay_matches_eager():
         for a, b, what in zip(bufs, ref, ("q", "scale", "wq", "wscale", "y")):
             assert _same(a, b), "replay %d: %s differs from eager" % (rep, what)
     assert not np.isnan(bufs[4].float().cpu().numpy()).any()
+
+
+def test_grouped_gemm_graph_replay_matches_eager():
+    """The grouped GEMM with its K-split last round (the GEMM kernel, then the
+    fix-up kernel over the workspace) captured into a HIP graph, once with a
+    caller workspace and once through the allocation-free entry point (whose
+    scratch address is looked up by a call made before the capture); every
+    replay, with new activations copied in eagerly between replays, equals
+    an eager call bit for bit."""
+    rows = np.array([300, 5, 0, 128, 257, 40])
+    n, k = 384, 18 * 128                        # 14 tiles: 4 K pieces each
+    off = wl.pad_offsets(rows)
+    m_total = int(off[-1])
+    E = len(rows)
+    xs = [dev_bf16(wl.activation(9, "grouped_fprop", 150 + i, m_total, k, 50.0)) for i in range(3)]
+    w = dev_bf16(wl.weight(9, "grouped_fprop", 160, E * n, k))
+    wq, wsc = fq.fp8_quantize_weight(w)
+    wq, wsc = wq.view(E, n, k), wsc.view(E, n // 128, k // 128)
+    off_d = torch.from_numpy(off.astype(np.int32)).cuda()
+    rows_d = torch.from_numpy(rows.astype(np.int32)).cuda()
+    a = torch.empty((m_total, k), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((k // 128, m_total), dtype=torch.float32, device="cuda")
+    ws = torch.empty(fq.GROUPED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+    y_ws = torch.empty((m_total, n), dtype=torch.bfloat16, device="cuda")
+    y_na = torch.empty((m_total, n), dtype=torch.bfloat16, device="cuda")
+    ref = torch.empty((m_total, n), dtype=torch.bfloat16, device="cuda")
+    ref_ws = torch.empty(fq.GROUPED_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda")
+
+    def quant(x):
+        fq.fp8_quantize_act(x, q=a, scale=sa)
+
+    def gemms():
+        fq.fp8_grouped_gemm(off_d, rows_d, a, sa, wq, wsc, torch.bfloat16, out=y_ws, workspace=ws)
+        fq.fp8_grouped_gemm_noalloc(off_d, rows_d, a, sa, wq, wsc, torch.bfloat16, out=y_na)
+
+    quant(xs[0])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm up (and look up the scratch) on the capture stream
+        gemms()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gemms()
+    torch.cuda.synchronize()
+    for rep in range(6):
+        quant(xs[rep % 3])           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        fq.fp8_grouped_gemm(off_d, rows_d, a, sa, wq, wsc, torch.bfloat16, out=ref, workspace=ref_ws)
+        torch.cuda.synchronize()
+        assert _same(y_ws, ref), "replay %d: workspace entry point differs from eager" % rep
+        assert _same(y_na, ref), "replay %d: allocation-free entry point differs from eager" % rep
+    assert torch.isfinite(ref.float()).all()
