@@ -33,7 +33,8 @@
  *
  * Conventions for every entry point:
  *   - all data pointers are device memory (HBM) owned by the caller; the
- *     library never allocates, frees or synchronizes, and inputs are const;
+ *     library never allocates, frees or synchronizes, and inputs are const
+ *     (its one device array is the scratch of fp8_grouped_gemm_noalloc);
  *   - bf16 tensors are passed as their uint16 bit patterns; FP8 tensors as
  *     uint8 E4M3 codes; matrices are row-major with a leading dimension (ld)
  *     counted in elements;
@@ -41,7 +42,8 @@
  *     the call returns once the launch is enqueued;
  *   - arguments are validated on the host before anything is launched; on any
  *     error nothing is launched and nothing is written;
- *   - calls are thread-safe and keep no state besides the last HIP error code;
+ *   - calls are thread-safe and keep no state besides the last HIP error code
+ *     (and fp8_grouped_gemm_noalloc's per-device scratch address);
  *   - FP8Q_DEBUG=1 in the environment adds host-side checks of the device
  *     arrays the grouped GEMMs trust (fp8_grouped_gemm, fp8_grouped_gemm_wgrad):
  *     they are copied to the host on `stream`, which is then synchronized, and a
