@@ -162,8 +162,9 @@ __device__ __forceinline__ ExpertSplit expert_split(const Params& p, int e) {
 }
 
 // The experts are found by a scan over the wave rather than a walk over the
-// offsets (a chain of dependent scalar loads, about 5 us for 32 experts):
-// lane l takes the expert at position base + l of the order, one load each.
+// offsets (a chain of dependent scalar loads, one round trip per expert, at
+// the start of every block): lane l takes the expert at position base + l of
+// the order, one load each.
 // Tiles of that expert (zero past the last one):
 __device__ __forceinline__ int lane_expert_tiles(const Params& p, int base, int tiles_n) {
     const int pos = base + (int)(threadIdx.x & 63);
@@ -227,8 +228,8 @@ __device__ __forceinline__ bool grouped_slot(const Params& p, int slot, TileRows
 // first + i * tiles + r (the same piece of neighbouring tiles -- which share
 // weight or activation panels -- run side by side on one XCD) and stores its
 // FP32 partial as partial i * tiles + r; a second kernel adds a tile's
-// partials in piece order. split = 1: no split (no workspace, a round at
-// least half full, or too few slabs).
+// partials in piece order. split = 1: no split (no workspace, a last round
+// more than half full, or too few slabs).
 constexpr int kMaxSplit = 8;
 constexpr int kMinSplitSlabs = 4;
 
