@@ -142,3 +142,41 @@ def test_counter_table_means_and_derived_columns(tmp_path):
     table = bench.counter_table(str(p), W()).splitlines()
     assert len(table) == 3 and table[2].startswith("| gemm | 2 | 100.00 |")
     assert table[2].rstrip(" |").endswith("0.500 | 0.250")
+
+
+def test_pmc_summary_counts_the_fixup_kernel_in_the_gemm_launch(tmp_path):
+    """A grouped GEMM launch dispatches gemm_kernel and then the split-K
+    fix-up kernel: its per-launch traffic is the average of each kernel's
+    dispatches added together, and both count as dispatches of the launch."""
+    fetch, write = str(tmp_path / "f.csv"), str(tmp_path / "w.csv")
+    _write(fetch, "FETCH_SIZE", [(1, "__amd_rocclr_copyBuffer", 512.0),
+                                 (2, "void fp8q::gemm_kernel<256, false, false, 1>(Params)", 10.0),
+                                 (3, "void fp8q::grouped_fixup_kernel<false>(Params)", 2.0),
+                                 (4, "void fp8q::gemm_kernel<256, false, false, 1>(Params)", 14.0),
+                                 (5, "void fp8q::grouped_fixup_kernel<false>(Params)", 4.0)])
+    _write(write, "WRITE_SIZE", [(1, "__amd_rocclr_copyBuffer", 1024.0),
+                                 (2, "void fp8q::gemm_kernel<256, false, false, 1>(Params)", 5.0),
+                                 (3, "void fp8q::grouped_fixup_kernel<false>(Params)", 1.0),
+                                 (4, "void fp8q::gemm_kernel<256, false, false, 1>(Params)", 5.0),
+                                 (5, "void fp8q::grouped_fixup_kernel<false>(Params)", 1.0)])
+    res = bench.pmc_summary(fetch, write, "grouped_fprop", 1, str(tmp_path / "t.json"), _Stub())
+    g = res["kernels"]["gemm"]
+    assert g["fetch_bytes"] == (12 + 3) * 1024 * 2     # averages 12 and 3 KiB, factor 2
+    assert g["write_bytes"] == (5 + 1) * 1024
+    assert g["dispatches"] == 4
+
+
+def test_counter_table_gives_the_fixup_kernel_its_own_row(tmp_path):
+    path = str(tmp_path / "c.csv")
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                                          "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        for did, name, ns in ((1, "void fp8q::gemm_kernel<256>(Params)", 300000),
+                              (2, "void fp8q::grouped_fixup_kernel<false>(Params)", 15000)):
+            w.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": "SQ_WAVES",
+                        "Counter_Value": 8.0, "Start_Timestamp": 0, "End_Timestamp": ns})
+    table = bench.counter_table(path, _Stub())
+    rows = [l for l in table.splitlines() if l.startswith("| gemm")]
+    assert rows[0].startswith("| gemm | 1 | 300.00")
+    assert rows[1].startswith("| gemm: grouped_fixup_kernel | 1 | 15.00")
