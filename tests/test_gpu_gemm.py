@@ -131,6 +131,26 @@ def test_padded_leading_dims_and_scale_strides(kind):
                       "padded %s" % kind)
 
 
+def test_operand_pitch_at_the_limit():
+    """lda = ldb = FP8Q_MAX_GEMM_LD (2^23 - 128 bytes), the largest pitch the
+    host accepts: a tile's last row then sits 255 pitches (just under 2^31
+    bytes) past the tile origin, the most its 31-bit lane offsets reach. Two
+    m-tiles (the second ragged) over 2.5 GB and 2.1 GB operand buffers."""
+    ld = 8388480
+    m, n, k = 296, 256, 256
+    a_q, a_s = oracle.quant_act_1x128(wl.activation(6, "tiny_fprop", 98, m, k, 50.0))
+    b_q, b_s = oracle.quant_weight_128x128(wl.weight(6, "tiny_fprop", 99, n, k))
+    ap = torch.zeros((m, ld), dtype=torch.uint8, device="cuda")
+    bp = torch.zeros((n, ld), dtype=torch.uint8, device="cuda")
+    ap[:, :k] = dev_codes(a_q).view(torch.uint8)
+    bp[:, :k] = dev_codes(b_q).view(torch.uint8)
+    c = nan_out((m, n), torch.bfloat16)
+    fq.fp8_gemm(ap[:, :k], dev_f32(a_s), bp[:, :k], dev_f32(b_s), "block", torch.bfloat16, out=c)
+    torch.cuda.synchronize()
+    del ap, bp
+    assert_gemm_close(host_out(c), oracle.gemm(a_q, a_s, b_q, b_s, "block"), "pitch at the limit")
+
+
 def test_k_zero_writes_zeros():
     """K = 0: the product is the zero matrix; every element of the window is
     written and nothing is read from the (unused) operands."""
