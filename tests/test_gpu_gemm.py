@@ -151,6 +151,27 @@ def test_operand_pitch_at_the_limit():
     assert_gemm_close(host_out(c), oracle.gemm(a_q, a_s, b_q, b_s, "block"), "pitch at the limit")
 
 
+def test_scale_pitches_at_the_limit():
+    """The A scales' and the 128x128 B block scales' row pitches at the
+    largest values the host accepts for 2 rows (a span just under
+    FP8Q_MAX_SCALE_SPAN = 2^29 floats): the second n-block's scales sit
+    almost 1 GiB past the first, the most a lane offset of the block-scale
+    copy reaches. Two 2 GB scale buffers."""
+    ld = (1 << 28) - 16
+    m, n, k = 256, 256, 256
+    a_q, a_s = oracle.quant_act_1x128(wl.activation(6, "tiny_fprop", 100, m, k, 50.0))
+    b_q, b_s = oracle.quant_weight_128x128(wl.weight(6, "tiny_fprop", 101, n, k))
+    asp = torch.zeros((k // 128, ld), dtype=torch.float32, device="cuda")
+    bsp = torch.zeros((n // 128, ld), dtype=torch.float32, device="cuda")
+    asp[:, :m] = dev_f32(a_s)
+    bsp[:, :k // 128] = dev_f32(b_s)
+    c = nan_out((m, n), torch.bfloat16)
+    fq.fp8_gemm(dev_codes(a_q), asp[:, :m], dev_codes(b_q), bsp[:, :k // 128], "block", torch.bfloat16, out=c)
+    torch.cuda.synchronize()
+    del asp, bsp
+    assert_gemm_close(host_out(c), oracle.gemm(a_q, a_s, b_q, b_s, "block"), "scale pitches at the limit")
+
+
 def test_k_zero_writes_zeros():
     """K = 0: the product is the zero matrix; every element of the window is
     written and nothing is read from the (unused) operands."""
