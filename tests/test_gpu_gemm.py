@@ -298,6 +298,35 @@ def test_grouped_split_last_round_wide_padding_and_all_real():
     _grouped_case([128, 256, 384], n=512, k=8 * 128, group_rows=False, out="f32")
 
 
+def test_grouped_operand_pitch_at_the_limit():
+    """The grouped kernel (which recomputes its copy offsets every step) at
+    the largest operand pitch the host accepts: lda = ldb = 2^23 - 128 bytes,
+    two experts (one a full 256-row tile, one ragged), 3.2 GB of activation
+    rows and 4.3 GB of expert weights."""
+    ld = 8388480
+    rows = np.array([100, 256])
+    n, k = 256, 256
+    offsets = wl.pad_offsets(rows)
+    m_total = int(offsets[-1])
+    x = wl.activation(6, "grouped_fprop", 102, m_total, k, 50.0)
+    a_q, a_s = oracle.quant_act_1x128(x)
+    w = wl.weight(6, "grouped_fprop", 103, 2, n, k)
+    b_q = np.stack([oracle.quant_weight_128x128(w[e])[0] for e in range(2)])
+    b_s = np.stack([oracle.quant_weight_128x128(w[e])[1] for e in range(2)])
+    ap = torch.zeros((m_total, ld), dtype=torch.uint8, device="cuda")
+    bp = torch.zeros((2, n, ld), dtype=torch.uint8, device="cuda")
+    ap[:, :k] = dev_codes(a_q).view(torch.uint8)
+    bp[:, :, :k] = dev_codes(b_q).view(torch.uint8)
+    c = nan_out((m_total, n), torch.bfloat16)
+    fq.fp8_grouped_gemm(torch.from_numpy(offsets.astype(np.int32)).cuda(),
+                        torch.from_numpy(rows.astype(np.int32)).cuda(),
+                        ap[:, :k], dev_f32(a_s), bp[:, :, :k], dev_f32(b_s), torch.bfloat16, out=c)
+    torch.cuda.synchronize()
+    del ap, bp
+    ref = oracle.grouped_gemm(offsets, rows, a_q, a_s, b_q, b_s)
+    assert_grouped_close(host_out(c), ref, offsets, rows, "grouped pitch at the limit")
+
+
 def test_grouped_moe_config_full():
     """The MoE config: 32 experts, Zipf(1.1) routing of 8192 tokens, N=4096,
     K=7168; every real row of every expert compared."""
